@@ -1,0 +1,150 @@
+"""CPU oracle for MoE expert-parallel layout / dispatch / combine.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.
+It is a thin numpy front end over ``ep_oracle.c`` (plain C, gcc, no HIP),
+which holds every step of the arithmetic; see that file's header for the
+passages each function follows and the readings taken where the pages are
+silent.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+
+_LIBS = {}
+
+
+def lib(path: str = None):
+    """Load the oracle library (default: liboracle_ep.so, compiled if missing)."""
+    if path is None:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+    if path not in _LIBS:
+        L = ctypes.CDLL(path)
+        L.oracle_layout.argtypes = [_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p]
+        L.oracle_layout.restype = ctypes.c_int
+        L.oracle_dispatch.argtypes = [_u8p, ctypes.c_int64, _u8p, ctypes.c_int64, _f32p, _i32p,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                      _u8p, _u8p, _f32p]
+        L.oracle_dispatch.restype = ctypes.c_int
+        L.oracle_combine.argtypes = [_u16p, ctypes.c_int32, _f32p, _i32p, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int64, _u16p]
+        L.oracle_combine.restype = ctypes.c_int
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        _LIBS[path] = L
+    return _LIBS[path]
+
+
+def _ptr(a, typ):
+    if a is None:
+        return ctypes.cast(None, typ)
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(typ)
+
+
+def layout(topk_idx: np.ndarray, num_experts: int, expert_alignment: int, _lib=None):
+    """Counts, aligned exclusive offsets, slots and receive metadata.
+
+    Returns a dict with ``counts`` int32[E], ``offsets`` int32[E+1],
+    ``dst_slot`` int32[T,K], ``recv_src_metadata`` int32[num_recv,K+2]
+    and ``num_recv`` (int).
+    """
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, K = idx.shape
+    E, A = int(num_experts), int(expert_alignment)
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    dst = np.zeros((T, K), np.int32)
+    meta = np.zeros((max(T, 1), K + 2), np.int32)
+    nrecv = np.zeros(1, np.int32)
+    rc = lib(_lib).oracle_layout(_ptr(idx, _i32p), T, K, E, A, _ptr(counts, _i32p),
+                             _ptr(offsets, _i32p), _ptr(dst, _i32p), _ptr(meta, _i32p),
+                             _ptr(nrecv, _i32p))
+    if rc != 0:
+        raise ValueError("oracle_layout rejected its arguments")
+    n = int(nrecv[0])
+    return {"counts": counts, "offsets": offsets, "dst_slot": dst,
+            "recv_src_metadata": meta[:n].copy(), "num_recv": n}
+
+
+def dispatch(x_bytes: np.ndarray, dst_slot: np.ndarray, capacity_rows: int,
+             x_scales: np.ndarray = None, topk_weights: np.ndarray = None,
+             expand_x: np.ndarray = None, expand_scales: np.ndarray = None,
+             expand_weights: np.ndarray = None, _lib=None):
+    """Permute-copy token rows (any dtype, moved as bytes) to the expand buffer.
+
+    ``x_bytes`` is [T, row_bytes] uint8 (a view of bf16 or fp8 rows). When the
+    output buffers are not given they are allocated zero-filled, so padding
+    rows read back as zero. Returns (expand_x, expand_scales, expand_weights).
+    """
+    xb = np.ascontiguousarray(x_bytes).view(np.uint8)
+    T = xb.shape[0]
+    xb = xb.reshape(T, -1)
+    row_bytes = xb.shape[1]
+    dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
+    K = dst.shape[1]
+    cap = int(capacity_rows)
+    if expand_x is None:
+        expand_x = np.zeros((cap, row_bytes), np.uint8)
+    sb = 0
+    xs = None
+    if x_scales is not None:
+        xs = np.ascontiguousarray(x_scales).view(np.uint8).reshape(T, -1)
+        sb = xs.shape[1]
+        if expand_scales is None:
+            expand_scales = np.zeros((cap, sb), np.uint8)
+    w = None
+    if topk_weights is not None:
+        w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+        if expand_weights is None:
+            expand_weights = np.zeros(cap, np.float32)
+    ex = expand_x.view(np.uint8).reshape(cap, -1)
+    es = None if expand_scales is None else expand_scales.view(np.uint8).reshape(cap, -1)
+    rc = lib(_lib).oracle_dispatch(_ptr(xb, _u8p), row_bytes, _ptr(xs, _u8p), sb, _ptr(w, _f32p),
+                               _ptr(dst, _i32p), T, K, cap, _ptr(ex, _u8p), _ptr(es, _u8p),
+                               _ptr(expand_weights if w is not None else None, _f32p))
+    if rc != 0:
+        raise ValueError("oracle_dispatch rejected its arguments")
+    return expand_x, expand_scales, expand_weights
+
+
+def combine(y_bf16_bits: np.ndarray, dst_slot: np.ndarray, topk_weights: np.ndarray = None,
+            _lib=None):
+    """Weighted gather-reduce of bf16 expert outputs back to token order.
+
+    ``y_bf16_bits`` is uint16 [capacity, H] holding bf16 bit patterns;
+    returns uint16 [T, H] bf16 bit patterns.
+    """
+    y = np.ascontiguousarray(y_bf16_bits).view(np.uint16)
+    cap, H = y.shape
+    dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
+    T, K = dst.shape
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    out = np.empty((T, H), np.uint16)
+    rc = lib(_lib).oracle_combine(_ptr(y, _u16p), H, _ptr(w, _f32p), _ptr(dst, _i32p), T, K,
+                              cap, _ptr(out, _u16p))
+    if rc != 0:
+        raise ValueError("oracle_combine rejected its arguments")
+    return out
+
+
+def f32_to_bf16(f: float, _lib=None) -> int:
+    """The oracle's binary32 -> bf16 rounding (round to nearest even)."""
+    return int(lib(_lib).oracle_f32_to_bf16(float(f)))
+
+
+def bf16_to_f32(b: int, _lib=None) -> float:
+    return float(lib(_lib).oracle_bf16_to_f32(int(b)))

@@ -1,0 +1,168 @@
+"""Independent checks that pin the oracle (and, by extension, the GPU path).
+
+Nothing here calls the oracle. Each check derives the expected result by a
+different route than the oracle's loops: brute force over all pairs, numpy
+library routines (bincount, stable argsort, fancy indexing), invariants that
+any correct layout satisfies, and a float64 evaluation of the weighted sum
+with a rigorous binary32 error bound. The mutation test plants mistakes in a
+copy of the oracle and requires every one of them to trip at least one check.
+"""
+import numpy as np
+
+U32 = 2.0 ** -24  # binary32 unit roundoff
+
+
+# --------------------------------------------------------------------------
+# Layout
+# --------------------------------------------------------------------------
+
+def _valid(idx, E):
+    return (idx >= 0) & (idx < E)
+
+
+def layout_bruteforce(idx, E, A):
+    """Definition-by-enumeration; O((T*K)^2), for tiny inputs only."""
+    T, K = idx.shape
+    flat = idx.ravel()
+    n = flat.size
+    counts = np.array([sum(1 for i in range(n) if flat[i] == e) for e in range(E)], np.int64)
+    offsets = [0]
+    for e in range(E):
+        offsets.append(offsets[-1] + int(np.ceil(counts[e] / A)) * A if counts[e] else offsets[-1])
+    dst = np.full(n, -1, np.int64)
+    for i in range(n):
+        e = flat[i]
+        if 0 <= e < E:
+            before = sum(1 for j in range(i) if flat[j] == e)
+            dst[i] = offsets[e] + before
+    dst = dst.reshape(T, K)
+    rows = [[t, 0] + list(dst[t]) for t in range(T) if (dst[t] >= 0).any()]
+    return counts, np.array(offsets), dst, rows
+
+
+def layout_by_argsort(idx, E, A):
+    """Library route: bincount for counts, stable argsort for ranks."""
+    T, K = idx.shape
+    flat = idx.ravel().astype(np.int64)
+    v = _valid(flat, E)
+    counts = np.bincount(flat[v], minlength=E)
+    padded = -(-counts // A) * A
+    offsets = np.concatenate([[0], np.cumsum(padded)])
+    key = np.where(v, flat, E)                      # masked entries sort last
+    order = np.argsort(key, kind="stable")          # token-major within each expert
+    sorted_key = key[order]
+    first = np.searchsorted(sorted_key, sorted_key, side="left")
+    rank = np.empty_like(order)
+    rank[order] = np.arange(order.size) - first
+    dst = np.where(v, offsets[np.minimum(key, E - 1)] + rank, -1) if E > 0 else np.full_like(flat, -1)
+    dst = dst.reshape(T, K)
+    has = (dst >= 0).any(axis=1)
+    toks = np.nonzero(has)[0]
+    meta = np.concatenate([toks[:, None], np.zeros((toks.size, 1), np.int64), dst[toks]], axis=1) \
+        if toks.size else np.zeros((0, K + 2), np.int64)
+    return counts, offsets, dst, meta
+
+
+def check_layout_invariants(idx, E, A, res):
+    T, K = idx.shape
+    counts, offsets, dst = res["counts"].astype(np.int64), res["offsets"].astype(np.int64), \
+        res["dst_slot"].astype(np.int64)
+    v = _valid(idx, E)
+    n_valid = int(v.sum())
+    assert counts.sum() == n_valid, "counts must sum to the number of unmasked entries"
+    assert offsets[0] == 0
+    assert np.all(offsets % A == 0), "every segment starts on an alignment boundary"
+    seg = np.diff(offsets)
+    assert np.all(seg >= counts) and np.all(seg - counts < A), "segment = count padded up to A"
+    assert np.all((counts == 0) == (seg == 0)), "an empty expert gets no rows"
+    assert n_valid <= offsets[-1] <= T * K + E * (A - 1), "capacity bound"
+    assert np.all(dst[~v] == -1), "masked entries have no slot"
+    for e in range(E):
+        mine = dst[idx == e]  # token-major order
+        local = mine - offsets[e]
+        assert np.array_equal(local, np.arange(counts[e])), \
+            f"expert {e}: slots must be offset + 0..count-1 in token-major order"
+    has = v.any(axis=1)
+    assert res["num_recv"] == int(has.sum())
+    meta = np.asarray(res["recv_src_metadata"], np.int64)
+    assert meta.shape == (int(has.sum()), K + 2)
+    assert np.array_equal(meta[:, 0], np.nonzero(has)[0])
+    assert np.all(meta[:, 1] == 0)
+    assert np.array_equal(meta[:, 2:], dst[has])
+
+
+def check_layout_matches(res, counts, offsets, dst, meta):
+    assert np.array_equal(res["counts"], counts), "counts"
+    assert np.array_equal(res["offsets"], offsets), "offsets"
+    assert np.array_equal(res["dst_slot"], dst), "dst_slot"
+    assert np.array_equal(np.asarray(res["recv_src_metadata"]).reshape(-1, dst.shape[1] + 2),
+                          np.asarray(meta).reshape(-1, dst.shape[1] + 2)), "recv_src_metadata"
+
+
+# --------------------------------------------------------------------------
+# Dispatch
+# --------------------------------------------------------------------------
+
+def check_dispatch(x_rows, dst, before, after):
+    """x_rows [T, B] bytes; before/after [cap, B]: expand buffer around the call."""
+    T, K = dst.shape
+    v = dst >= 0
+    d = dst[v]
+    t = np.repeat(np.arange(T), K).reshape(T, K)[v]
+    assert np.unique(d).size == d.size, "each real row is written exactly once"
+    assert np.array_equal(after[d], x_rows[t]), "expand row dst[t,k] holds x[t]"
+    untouched = np.ones(after.shape[0], bool)
+    untouched[d] = False
+    assert np.array_equal(after[untouched], before[untouched]), "padding rows are not written"
+
+
+# --------------------------------------------------------------------------
+# Combine
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_ulp(x64):
+    """Spacing of bf16 numbers at |x| (8 significant bits, binary32 exponent range)."""
+    a = np.abs(x64)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -126.0)
+    return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+def combine_exact(y_bits, dst, w):
+    """float64 value of sum_k w[t,k] * y[dst[t,k]] over unmasked k, and sum |terms|."""
+    T, K = dst.shape
+    yf = bf16_bits_to_f64(y_bits)
+    v = dst >= 0
+    rows = yf[np.where(v, dst, 0)] * v[..., None]
+    wf = np.ones((T, K)) if w is None else np.asarray(w, np.float32).astype(np.float64)
+    p = rows * wf[..., None]
+    return p.sum(axis=1), np.abs(p).sum(axis=1)
+
+
+def check_combine_bound(y_bits, dst, w, out_bits):
+    """|out - exact| <= gamma_K * sum|w y| + half a bf16 ulp of out.
+
+    gamma_K = K u / (1 - K u) bounds K binary32 roundings per term (one
+    product, at most K-1 sums) in a recursive sum; the final bf16 rounding
+    to nearest adds at most half a spacing of the result.
+    """
+    T, K = dst.shape
+    exact, absum = combine_exact(y_bits, dst, w)
+    out = bf16_bits_to_f64(out_bits)
+    gamma = K * U32 / (1 - K * U32)
+    bound = gamma * absum + 0.5 * bf16_ulp(out) + 2.0 ** -50 * absum
+    err = np.abs(out - exact)
+    bad = err > bound
+    assert not bad.any(), f"{int(bad.sum())} outputs exceed the error bound, worst {err[bad].max()}"
+
+
+def bf16_ulp_distance(a_bits, b_bits):
+    """Distance in units of bf16 spacing between two bf16 bit arrays (ordered integers)."""
+    def ordered(b):
+        b = np.asarray(b, np.uint16).astype(np.int32)
+        return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)
+    return np.abs(ordered(a_bits) - ordered(b_bits))

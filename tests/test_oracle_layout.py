@@ -1,0 +1,117 @@
+"""Pins for the oracle's layout pass (counts, aligned offsets, slots, metadata).
+
+Sources: DeepEP overall-architecture page, EPHandle structure and the
+dispatch data-flow figure (notify warps count per expert and compute target
+slots). Pins: hand-worked examples, brute force, bincount / stable argsort,
+invariants.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from combine_ep_layout_amd import inputs as I
+from tests import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_hand_worked_examples(oracle_mod):
+    data = json.load(open(os.path.join(GOLDEN, "layout_worked_examples.json")))
+    assert data["source"]
+    for c in data["cases"]:
+        idx = np.array(c["topk_idx"], np.int32)
+        res = oracle_mod.layout(idx, c["E"], c["A"])
+        pins.check_layout_matches(res, np.array(c["counts"]), np.array(c["offsets"]),
+                                  np.array(c["dst_slot"]), np.array(c["recv_src_metadata"]))
+        assert res["num_recv"] == c["num_recv"], c["name"]
+
+
+def _random_idx(seed, T, E, K, mask_frac=0.0, dup=False):
+    g = np.random.default_rng([seed, 99])
+    if dup:
+        idx = g.integers(0, E, (T, K)).astype(np.int32)
+    else:
+        idx = I.routing_uniform(g, T, E, K)
+    if mask_frac:
+        idx[g.random(idx.shape) < mask_frac] = -1
+    return idx
+
+
+TINY = [(seed, T, E, K, A, m, dup)
+        for seed, (T, E, K, A, m, dup) in enumerate([
+            (1, 1, 1, 1, 0.0, False), (5, 3, 2, 1, 0.0, False), (7, 4, 3, 2, 0.0, False),
+            (9, 5, 2, 3, 0.3, False), (12, 8, 4, 4, 0.0, False), (6, 3, 3, 5, 0.5, True),
+            (10, 16, 2, 1, 0.0, True), (4, 2, 2, 8, 1.0, False), (0, 4, 2, 2, 0.0, False),
+            (11, 6, 6, 3, 0.2, False)])]
+
+
+@pytest.mark.parametrize("seed,T,E,K,A,mask,dup", TINY)
+def test_bruteforce_tiny(oracle_mod, seed, T, E, K, A, mask, dup):
+    idx = _random_idx(seed, T, E, K, mask, dup)
+    res = oracle_mod.layout(idx, E, A)
+    counts, offsets, dst, rows = pins.layout_bruteforce(idx, E, A)
+    pins.check_layout_matches(res, counts, offsets, dst, np.array(rows, np.int64).reshape(-1, K + 2))
+
+
+MID = [(1, 333, 16, 2, 1, 0.0), (2, 1000, 64, 8, 1, 0.0), (3, 517, 256, 8, 128, 0.0),
+       (4, 129, 256, 8, 1, 0.1), (5, 2048, 32, 6, 16, 0.0), (6, 250, 7, 1, 3, 0.05),
+       (7, 777, 256, 8, 64, 0.25)]
+
+
+@pytest.mark.parametrize("seed,T,E,K,A,mask", MID)
+def test_argsort_and_invariants_mid(oracle_mod, seed, T, E, K, A, mask):
+    idx = _random_idx(seed, T, E, K, mask)
+    res = oracle_mod.layout(idx, E, A)
+    pins.check_layout_matches(res, *pins.layout_by_argsort(idx, E, A))
+    pins.check_layout_invariants(idx, E, A, res)
+
+
+@pytest.mark.parametrize("name", list(I.WORKLOADS))
+def test_workload_routing(oracle_mod, name):
+    w = I.WORKLOADS[name]
+    idx = I.make_routing(w.routing, w.seed, w.T, w.E, w.K)
+    res = oracle_mod.layout(idx, w.E, w.A)
+    pins.check_layout_matches(res, *pins.layout_by_argsort(idx, w.E, w.A))
+    pins.check_layout_invariants(idx, w.E, w.A, res)
+    assert res["counts"].sum() == w.T * w.K           # generators never mask
+    assert res["offsets"][-1] <= w.cap                 # the worst-case capacity holds
+    assert res["num_recv"] == w.T
+
+
+def test_a1_reduces_to_cumsum(oracle_mod):
+    idx = _random_idx(21, 500, 40, 4)
+    res = oracle_mod.layout(idx, 40, 1)
+    assert np.array_equal(res["offsets"], np.concatenate([[0], np.cumsum(np.bincount(idx.ravel(), minlength=40))]))
+
+
+def test_empty_and_degenerate(oracle_mod):
+    # no tokens
+    res = oracle_mod.layout(np.zeros((0, 8), np.int32), 16, 4)
+    assert res["counts"].sum() == 0 and np.all(res["offsets"] == 0) and res["num_recv"] == 0
+    # everything masked
+    res = oracle_mod.layout(np.full((5, 3), -1, np.int32), 4, 2)
+    assert np.all(res["dst_slot"] == -1) and res["num_recv"] == 0 and res["offsets"][-1] == 0
+    # one expert takes everything, alignment larger than the total
+    idx = np.zeros((3, 1), np.int32)
+    res = oracle_mod.layout(idx, 1, 128)
+    assert res["offsets"].tolist() == [0, 128] and res["dst_slot"].ravel().tolist() == [0, 1, 2]
+    # ids outside [0, E) are masked like -1
+    idx = np.array([[0, 5], [7, 1]], np.int32)
+    res = oracle_mod.layout(idx, 2, 1)
+    assert res["dst_slot"].tolist() == [[0, -1], [-1, 1]]
+    assert res["counts"].tolist() == [1, 1]
+
+
+def test_duplicate_experts_in_a_token(oracle_mod):
+    # not produced by the workloads, still well defined: both entries get rows
+    idx = np.array([[2, 2, 0], [2, 0, 0]], np.int32)
+    res = oracle_mod.layout(idx, 3, 1)
+    assert res["counts"].tolist() == [3, 0, 3]
+    assert res["dst_slot"].tolist() == [[3, 4, 0], [5, 1, 2]]
+
+
+def test_rejects_bad_scalars(oracle_mod):
+    with pytest.raises(ValueError):
+        oracle_mod.layout(np.zeros((2, 2), np.int32), 4, 0)
