@@ -1,0 +1,234 @@
+"""Benchmark: MoE expert-parallel layout + dispatch + combine on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic
+input already resident in HBM: ep_layout (counts, aligned offsets, slots,
+receive metadata), ep_dispatch (permute-copy into the expand buffer) and
+ep_combine (weighted gather-reduce back to token order), all through the
+C ABI on torch's current stream. Default workload: 4096 tokens, hidden 7168,
+256 experts, top-8 uniform distinct routing, expert alignment 128, bf16.
+
+Prints ONE JSON line. `value` is whole-step throughput: algorithmic HBM
+bytes of the three passes per step divided by the wall-clock step time
+(K steps bracketed by device synchronisation). Per-kernel times come from
+HIP events recorded on the same stream around each call; the roofline
+object reports the dominant kernel's algorithmic bytes over its mean event
+duration against the MI355X HBM peak (8 TB/s). The CPU baseline times the
+CPU oracle on the host (test infrastructure, never on the product path).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "dispatch+combine effective HBM GB/s (% of peak) + tokens/s, 1 MI355X"
+KERNEL_SOURCES = ["combine_ep_layout_amd/csrc/ep_dispatch.hip",
+                  "combine_ep_layout_amd/csrc/ep_combine.hip",
+                  "combine_ep_layout_amd/csrc/ep_layout.hip",
+                  "combine_ep_layout_amd/csrc/ep_device.hpp"]
+
+
+def algorithmic_bytes(w, n_valid: int, n_recv: int) -> dict:
+    """Bytes each pass must move at minimum (padding rows are never touched)."""
+    elt = 1 if w.dtype == 2 else 2
+    S = w.H // 128
+    row_in = w.H * elt + (4 * S if w.dtype == 2 else 0)  # payload (+ fp8 scales)
+    L = w.T * w.K * 4 + 4 * w.E + 4 * (w.E + 1) + w.T * w.K * 4 + n_recv * (w.K + 2) * 4 + 4
+    D = w.T * row_in + n_valid * row_in + w.T * w.K * 4
+    C = n_valid * w.H * 2 + w.T * w.H * 2 + w.T * w.K * 8
+    return {"layout": L, "dispatch": D, "combine": C}
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if current."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("sources_digest") != sources_digest():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 5):
+    """Time the CPU oracle (as it stands) on the same workload on the host."""
+    import oracle
+
+    w = case.w
+    rowb = case.x.view(np.uint8).reshape(w.T, -1).shape[1]
+    expand = np.zeros((w.cap, rowb), np.uint8)
+    expand_s = np.zeros((w.cap, w.H // 128 * 4), np.uint8) if case.x_scales is not None else None
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_reps and (len(times) < 2 or time.perf_counter() - t_start < budget_s):
+        t0 = time.perf_counter()
+        lay = oracle.layout(case.topk_idx, w.E, w.A)
+        oracle.dispatch(case.x, lay["dst_slot"], w.cap, x_scales=case.x_scales,
+                        expand_x=expand, expand_scales=expand_s)
+        oracle.combine(case.y, lay["dst_slot"], case.topk_weights)
+        times.append(time.perf_counter() - t0)
+    n_valid = int((lay["dst_slot"] >= 0).sum())
+    b = algorithmic_bytes(w, n_valid, lay["num_recv"])
+    sec = float(np.median(times))
+    return {"value": round(sum(b.values()) / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds_per_step": round(sec, 3),
+            "sample": f"the full {w.name} workload (layout + dispatch + combine), "
+                      f"{len(times)} single-threaded runs, median"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill_aligned")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every expert is local, a world of one); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from combine_ep_layout_amd import binding as B
+    from combine_ep_layout_amd import inputs as I
+
+    B.lib()  # fail loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = I.WORKLOADS[args.workload]
+    print(f"# workload {w.name}: T={w.T} H={w.H} E={w.E} K={w.K} A={w.A} dtype={w.dtype} "
+          f"cap={w.cap}", file=sys.stderr, flush=True)
+    case = I.make_case(w)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    idx, wts, x, y = up(case.topk_idx), up(case.topk_weights), up(case.x), up(case.y)
+    xs = up(case.x_scales) if case.x_scales is not None else None
+    rowb = case.x.view(np.uint8).reshape(w.T, -1).shape[1]
+    counts = torch.empty(w.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device=dev)
+    dst = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
+    meta = torch.empty((w.T, w.K + 2), dtype=torch.int32, device=dev)
+    nrecv = torch.empty(1, dtype=torch.int32, device=dev)
+    wsb = B.ep_layout_workspace_bytes(w.T, w.K, w.E)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    expand = torch.zeros((w.cap, rowb), dtype=torch.uint8, device=dev)
+    expand_s = torch.zeros((w.cap, w.H // 128), dtype=torch.float32, device=dev) if xs is not None else None
+    out = torch.empty((w.T, w.H), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws, wsb, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.ep_dispatch(x, xs, None, dst, w.T, w.H, w.K, w.dtype, w.cap, expand, expand_s, None, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        B.ep_combine(y, wts, dst, w.T, w.H, w.K, B.EP_BF16, w.cap, out, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    us = {"layout": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3,
+          "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
+          "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3}
+
+    # Validate the timed path against the oracle: layout in full, dispatch and combine sampled.
+    import oracle
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    got_dst = dst.cpu().numpy()
+    ok = (np.array_equal(got_dst, ref["dst_slot"]) and np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+          and np.array_equal(counts.cpu().numpy(), ref["counts"]) and int(nrecv.item()) == ref["num_recv"])
+    sample = np.random.default_rng(0).choice(w.T, size=min(w.T, 256), replace=False)
+    xb = case.x.view(np.uint8).reshape(w.T, -1)
+    rows = ref["dst_slot"][sample]
+    got_rows = expand[torch.from_numpy(rows.ravel().astype(np.int64)).to(dev)].cpu().numpy()
+    ok = ok and np.array_equal(got_rows, np.repeat(xb[sample], w.K, axis=0))
+    ref_out = oracle.combine(case.y, ref["dst_slot"][sample], case.topk_weights[sample])
+    got_out = out.cpu().numpy().view(np.uint16)[sample]
+    ordered = lambda b: np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)  # noqa: E731
+    ok = ok and np.abs(ordered(got_out.astype(np.int32)) - ordered(ref_out.astype(np.int32))).max() <= 1
+    if not ok:
+        print("bench: GPU results do not match the oracle; refusing to report", file=sys.stderr)
+        sys.exit(1)
+
+    n_valid = int((ref["dst_slot"] >= 0).sum())
+    nb = algorithmic_bytes(w, n_valid, ref["num_recv"])
+    total_bytes = sum(nb.values())
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    dc_us = us["dispatch"] + us["combine"]
+    dc_gbps = (nb["dispatch"] + nb["combine"]) / (dc_us * 1e-6) / 1e9
+    dom = max(("dispatch", "combine"), key=lambda k: us[k])
+    achieved = nb[dom] / (us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(w.name, dom),
+                "algorithmic_bytes_per_launch": nb[dom], "avg_launch_us": round(us[dom], 2)}
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8" if w.dtype == 2 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "topk": w.K,
+                   "expert_alignment": w.A, "capacity_rows": w.cap, "routing": w.routing,
+                   "parallelism": "one GPU, all experts local"},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(w.T / (ms_per_step * 1e-3), 1),
+        "dispatch_combine_GBps": round(dc_gbps, 1),
+        "dispatch_combine_pct_of_peak": round(100 * dc_gbps / HBM_PEAK_GBPS, 2),
+        "dispatch_combine_tokens_per_s": round(w.T / (dc_us * 1e-6), 1),
+        "kernel_us": {k: round(v, 2) for k, v in us.items()},
+        "algorithmic_bytes": nb,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

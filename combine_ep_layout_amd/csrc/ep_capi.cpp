@@ -1,0 +1,197 @@
+// C ABI of the library (declared in include/ep_mi355x.h).
+//
+// Every entry point validates its scalars and pointers on the host before
+// anything is enqueued, reports errors by return code plus a per-thread
+// message, never throws and never allocates, copies or synchronises
+// ("MORI JIT v2", section 3.5: invalid configurations are rejected before any
+// work; section 4: nothing but launches on the call path; section 6: C entry
+// points catch everything and report through a last-error string).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <exception>
+
+#include "ep_launch.hpp"
+#include "ep_mi355x.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local hipError_t g_hip_error = hipSuccess;
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int from_launch(int rc, const char *what) {
+  if (rc == 0) {
+    g_last_error[0] = '\0';
+    return EP_OK;
+  }
+  if (rc == -2) return fail(EP_EUNSUPPORTED, "%s: no compiled kernel for this shape", what);
+  return fail(EP_EHIP, "%s: kernel launch failed: %s", what, hipGetErrorString(g_hip_error));
+}
+
+int check_topk(const char *what, int32_t T, int32_t K) {
+  if (T < 0) return fail(EP_EINVAL, "%s: num_tokens must be >= 0 (got %d)", what, T);
+  if (K < 1 || K > EP_MAX_TOPK)
+    return fail(EP_EINVAL, "%s: topk must be in 1..%d (got %d)", what, EP_MAX_TOPK, K);
+  if ((int64_t)T * K > INT32_MAX) return fail(EP_EINVAL, "%s: num_tokens*topk overflows int32", what);
+  return EP_OK;
+}
+
+}  // namespace
+
+hipError_t &ep::last_hip_error() { return g_hip_error; }
+
+extern "C" {
+
+const char *ep_last_error(void) { return g_last_error; }
+
+int ep_supported(int32_t pass, int32_t hidden, int32_t topk, int32_t dtype) {
+  try {
+    if (pass == 0) return ep::has_layout(topk) ? 1 : 0;
+    if (pass == 1) return ep::has_dispatch(hidden, topk, dtype) ? 1 : 0;
+    if (pass == 2) return dtype == EP_BF16 && ep::has_combine(hidden, topk) ? 1 : 0;
+  } catch (...) {
+  }
+  return 0;
+}
+
+size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_experts) {
+  try {
+    if (num_tokens < 0 || topk < 1 || topk > EP_MAX_TOPK || num_experts < 1 ||
+        num_experts > EP_MAX_EXPERTS)
+      return 0;
+    return ep::layout_workspace(num_tokens, topk, num_experts);
+  } catch (...) {
+    return 0;
+  }
+}
+
+int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t num_experts,
+              int32_t expert_alignment, int64_t capacity_rows, int32_t *counts,
+              int32_t *offsets, int32_t *dst_slot, int32_t *recv_src_metadata,
+              int32_t *num_recv, void *workspace, size_t workspace_bytes, void *stream) {
+  try {
+    const char *what = "ep_layout";
+    if (int rc = check_topk(what, num_tokens, topk)) return rc;
+    if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
+      return fail(EP_EINVAL, "%s: num_experts must be in 1..%d (got %d)", what, EP_MAX_EXPERTS,
+                  num_experts);
+    if (expert_alignment < 1)
+      return fail(EP_EINVAL, "%s: expert_alignment must be >= 1 (got %d)", what, expert_alignment);
+    const int64_t worst =
+        (int64_t)num_tokens * topk + (int64_t)num_experts * (expert_alignment - 1);
+    if (worst > INT32_MAX)
+      return fail(EP_EINVAL, "%s: worst-case expand rows %lld overflow int32", what,
+                  (long long)worst);
+    if (capacity_rows < worst)
+      return fail(EP_ECAPACITY, "%s: capacity_rows %lld < worst case T*K + E*(A-1) = %lld", what,
+                  (long long)capacity_rows, (long long)worst);
+    if (!counts || !offsets || !num_recv || (num_tokens > 0 && (!topk_idx || !dst_slot || !recv_src_metadata)))
+      return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
+    if (!ep::has_layout(topk))
+      return fail(EP_EUNSUPPORTED, "%s: topk %d has no compiled layout kernel", what, topk);
+    const size_t need = ep::layout_workspace(num_tokens, topk, num_experts);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+      return fail(EP_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", what, need,
+                  workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (need > 0 && !aligned(workspace, 16))
+      return fail(EP_EINVAL, "%s: workspace must be 16-byte aligned", what);
+    ep::LayoutArgs a{topk_idx, num_tokens, topk, num_experts, expert_alignment, counts, offsets,
+                     dst_slot, recv_src_metadata, num_recv, workspace, (hipStream_t)stream};
+    return from_launch(ep::launch_layout(a), what);
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_layout: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_layout: unknown exception");
+  }
+}
+
+int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
+                const int32_t *dst_slot, int32_t num_tokens, int32_t hidden, int32_t topk,
+                int32_t dtype, int64_t capacity_rows, void *expand_x, float *expand_scales,
+                float *expand_weights, void *stream) {
+  try {
+    const char *what = "ep_dispatch";
+    if (int rc = check_topk(what, num_tokens, topk)) return rc;
+    if (hidden < 1) return fail(EP_EINVAL, "%s: hidden must be >= 1 (got %d)", what, hidden);
+    if (capacity_rows < 0) return fail(EP_EINVAL, "%s: capacity_rows must be >= 0", what);
+    int elt;
+    if (dtype == EP_BF16) elt = 2;
+    else if (dtype == EP_FP8_E4M3) elt = 1;
+    else if (dtype == EP_FP32 || dtype == EP_FP4X2)
+      return fail(EP_EUNSUPPORTED, "%s: dtype %d has no compiled dispatch kernel", what, dtype);
+    else return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
+    if (((int64_t)hidden * elt) % 16 != 0)
+      return fail(EP_EINVAL, "%s: token bytes (%lld) must be a multiple of 16", what,
+                  (long long)hidden * elt);
+    if (dtype == EP_FP8_E4M3) {
+      if (hidden % 128 != 0)
+        return fail(EP_EINVAL, "%s: fp8 needs hidden %% 128 == 0 (got %d)", what, hidden);
+      if (num_tokens > 0 && (!x_scales || !expand_scales))
+        return fail(EP_EINVAL, "%s: fp8 needs x_scales and expand_scales", what);
+    } else if (x_scales || expand_scales) {
+      return fail(EP_EINVAL, "%s: scales are only moved for fp8", what);
+    }
+    if (num_tokens > 0 && (!x || !dst_slot || !expand_x))
+      return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
+    if (!aligned(x, 16) || !aligned(expand_x, 16) || !aligned(x_scales, 16) ||
+        !aligned(expand_scales, 16) || !aligned(dst_slot, 4) || !aligned(topk_weights, 4) ||
+        !aligned(expand_weights, 4))
+      return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
+    if (!ep::has_dispatch(hidden, topk, dtype))
+      return fail(EP_EUNSUPPORTED, "%s: (hidden %d, topk %d, dtype %d) has no compiled kernel",
+                  what, hidden, topk, dtype);
+    ep::DispatchArgs a{x, x_scales, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,
+                       capacity_rows, expand_x, expand_scales, expand_weights,
+                       (hipStream_t)stream};
+    return from_launch(ep::launch_dispatch(a), what);
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_dispatch: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_dispatch: unknown exception");
+  }
+}
+
+int ep_combine(const void *expert_out, const float *topk_weights, const int32_t *dst_slot,
+               int32_t num_tokens, int32_t hidden, int32_t topk, int32_t dtype,
+               int64_t capacity_rows, void *out, void *stream) {
+  try {
+    const char *what = "ep_combine";
+    if (int rc = check_topk(what, num_tokens, topk)) return rc;
+    if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2)
+      return fail(EP_EINVAL, "%s: combine sums its input; byte dtype %d is rejected", what, dtype);
+    if (dtype == EP_FP32)
+      return fail(EP_EUNSUPPORTED, "%s: fp32 expert outputs have no compiled kernel", what);
+    if (dtype != EP_BF16) return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
+    if (hidden < 1 || (hidden * 2) % 16 != 0)
+      return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 (hidden %d)", what,
+                  hidden);
+    if (capacity_rows < 0) return fail(EP_EINVAL, "%s: capacity_rows must be >= 0", what);
+    if (num_tokens > 0 && (!expert_out || !dst_slot || !out))
+      return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
+    if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(dst_slot, 4) ||
+        !aligned(topk_weights, 4))
+      return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
+    if (!ep::has_combine(hidden, topk))
+      return fail(EP_EUNSUPPORTED, "%s: (hidden %d, topk %d) has no compiled kernel", what,
+                  hidden, topk);
+    ep::CombineArgs a{expert_out, topk_weights, dst_slot, num_tokens, hidden, topk,
+                      capacity_rows, out, (hipStream_t)stream};
+    return from_launch(ep::launch_combine(a), what);
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_combine: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_combine: unknown exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+// Gather combine for gfx950: out[t] = bf16( sum_k w[t,k] * y[dst_slot[t,k]] )
+// with binary32 accumulation in k order and a round-to-nearest-even store.
+//
+// Follows the DeepEP overall-architecture page, combine data-flow figure
+// (the reduce epilogue weights each expert output by topk_weights and sums
+// back into token order; no bias here) and "MORI JIT v2", section 3.7
+// (combine reduces bf16 rows; byte dtypes are rejected upstream).
+//
+// Design (MI355X): HBM-bound (read T*K rows, write T rows, about 1 flop per
+// byte). A token's row is cut into slices of two 16-byte chunks per lane
+// (2 KiB); one wave64 owns one (token, slice), so a 14,336-byte row is
+// served by 7 waves. A wave loads its token's K slots and weights with K
+// lanes and broadcasts them with readlane, so row addresses are
+// wave-uniform; it issues all K*2 loads (16 KiB per wave) before the first
+// is consumed, then folds the K rows in k order. Many short waves keep the
+// memory system full (a long-lived wave walking a whole row stalls between
+// passes). Loads and stores are non-temporal: expert outputs are read once
+// and the output written once. Products and sums are rounded separately
+// (contraction off), so the result is a pure function of the inputs; the
+// final pack uses the hardware binary32 -> bf16 convert, which rounds to
+// nearest even.
+#include "ep_device.hpp"
+#include "ep_launch.hpp"
+
+namespace ep {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// Waves per token and 16-byte chunks per lane per pass for a row of CH chunks:
+// each wave takes two chunks per lane (2 KiB of each of the K rows) when the
+// row divides evenly, else one; small rows keep one wave per token.
+template <int CH>
+struct CombineGeometry {
+  static constexpr int CPL = (CH + kWave - 1) / kWave;  // chunks per lane for a whole row
+  static constexpr int G = CPL % 2 == 0 ? 2 : 1;         // chunks per lane per wave
+  static constexpr int SPLIT = CPL / G;                  // waves per token
+};
+
+template <int H, int K>
+__global__ __launch_bounds__(kThreads) void ep_combine_gather(
+    const u32x4 *__restrict__ y, const float *__restrict__ topk_weights,
+    const int32_t *__restrict__ dst_slot, int T, int64_t capacity, u32x4 *__restrict__ out) {
+#pragma clang fp contract(off)
+  constexpr int CH = H * 2 / 16;  // 16-byte chunks per row
+  using Geo = CombineGeometry<CH>;
+  constexpr int G = Geo::G, SPLIT = Geo::SPLIT;
+  static_assert((H * 2) % 16 == 0, "row geometry");
+  static_assert(K >= 1 && K <= kWave, "topk must fit one wavefront");
+
+  const int lane = lane_id();
+  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t first = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
+  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+
+  for (int64_t gw = first; gw < (int64_t)T * SPLIT; gw += stride) {
+    const int t = (int)(gw / SPLIT);
+    const int c0 = (int)(gw - (int64_t)t * SPLIT) * G;  // first chunk (per lane) of this wave
+    int my_dst = -1;
+    float my_w = 0.f;
+    if (lane < K) {
+      my_dst = dst_slot[(int64_t)t * K + lane];
+      if (my_dst >= capacity) my_dst = -1;
+      my_w = topk_weights ? topk_weights[(int64_t)t * K + lane] : 1.0f;
+    }
+    int d[K];
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      d[k] = read_lane(my_dst, k);
+      wk[k] = read_lane(my_w, k);
+    }
+
+    // Issue every load of this wave before the first is consumed. Expert
+    // outputs are read exactly once: non-temporal loads keep them from
+    // displacing useful lines in the caches.
+    u32x4 v[K][G];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (d[k] < 0) continue;
+      const u32x4 *row = y + (int64_t)d[k] * CH;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int i = (c0 + g) * kWave + lane;
+        if (CH % kWave == 0 || i < CH) v[k][g] = __builtin_nontemporal_load(row + i);
+      }
+    }
+    float acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {  // fixed k order
+      if (d[k] < 0) continue;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t word = v[k][g][j];
+          const float lo = __uint_as_float(word << 16);
+          const float hi = __uint_as_float(word & 0xffff0000u);
+          const float plo = wk[k] * lo;
+          const float phi = wk[k] * hi;
+          acc[g][2 * j] = acc[g][2 * j] + plo;
+          acc[g][2 * j + 1] = acc[g][2 * j + 1] + phi;
+        }
+      }
+    }
+    u32x4 *o = out + (int64_t)t * CH;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int i = (c0 + g) * kWave + lane;
+      if (CH % kWave == 0 || i < CH) {
+        u32x4 r;
+        r[0] = pack_bf16x2(acc[g][0], acc[g][1]);
+        r[1] = pack_bf16x2(acc[g][2], acc[g][3]);
+        r[2] = pack_bf16x2(acc[g][4], acc[g][5]);
+        r[3] = pack_bf16x2(acc[g][6], acc[g][7]);
+        __builtin_nontemporal_store(r, o + i);
+      }
+    }
+  }
+}
+
+template <int H, int K>
+int combine_impl(const CombineArgs &a) {
+  if (a.T == 0) return 0;
+  constexpr int SPLIT = CombineGeometry<H * 2 / 16>::SPLIT;
+  const int64_t waves = (int64_t)a.T * SPLIT;
+  const int blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  ep_combine_gather<H, K><<<blocks, kThreads, 0, a.stream>>>(
+      (const u32x4 *)a.y, a.topk_weights, a.dst_slot, a.T, a.capacity, (u32x4 *)a.out);
+  return launch_status();
+}
+
+}  // namespace
+
+#define EP_COMBINE_K(K) \
+  case K:               \
+    return combine_impl<H_, K>(a);
+
+template <int H_>
+static int combine_k(const CombineArgs &a) {
+  switch (a.K) { EP_FOR_EACH_TOPK(EP_COMBINE_K) default: return -2; }
+}
+
+#define EP_COMBINE_H(H) \
+  case H:               \
+    return combine_k<H>(a);
+
+int launch_combine(const CombineArgs &a) {
+  switch (a.H) { EP_FOR_EACH_HIDDEN_BF16(EP_COMBINE_H) default: return -2; }
+}
+
+}  // namespace ep

@@ -1,0 +1,72 @@
+// Host-side interface between the C ABI (ep_capi.cpp) and the kernel
+// launchers (ep_layout.hip, ep_dispatch.hip, ep_combine.hip). Arguments are
+// validated by the C ABI before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// The compiled shape set. Shapes are template constants of the kernels, so
+// loops over a row and over k unroll completely; anything outside these
+// lists is rejected by the capability gate in the C ABI.
+#define EP_FOR_EACH_TOPK(X) X(1) X(2) X(4) X(6) X(8)
+#define EP_FOR_EACH_HIDDEN_BF16(X) X(256) X(512) X(1024) X(2048) X(4096) X(7168)
+#define EP_FOR_EACH_HIDDEN_FP8(X) X(512) X(1024) X(2048) X(4096) X(7168)
+
+namespace ep {
+
+struct LayoutArgs {
+  const int32_t *topk_idx;
+  int T, K, E, A;
+  int32_t *counts, *offsets, *dst_slot, *meta, *num_recv;
+  void *workspace;
+  hipStream_t stream;
+};
+
+struct DispatchArgs {
+  const void *x;
+  const float *x_scales;
+  const float *topk_weights;
+  const int32_t *dst_slot;
+  int T, H, K, dtype;
+  int64_t capacity;
+  void *expand_x;
+  float *expand_scales;
+  float *expand_weights;
+  hipStream_t stream;
+};
+
+struct CombineArgs {
+  const void *y;
+  const float *topk_weights;
+  const int32_t *dst_slot;
+  int T, H, K;
+  int64_t capacity;
+  void *out;
+  hipStream_t stream;
+};
+
+// HIP error of the last failed launch on this thread (set by launch_status).
+hipError_t &last_hip_error();
+
+// Checks the launch just enqueued: 0, or -1 with last_hip_error() set.
+inline int launch_status() {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return 0;
+  last_hip_error() = e;
+  return -1;
+}
+
+// Each returns 0 on success, -1 if the HIP runtime reported an error on
+// launch, -2 if the shape has no compiled kernel.
+int launch_layout(const LayoutArgs &a);
+size_t layout_workspace(int T, int K, int E);
+int launch_dispatch(const DispatchArgs &a);
+int launch_combine(const CombineArgs &a);
+
+bool has_layout(int K);
+bool has_dispatch(int H, int K, int dtype);
+bool has_combine(int H, int K);
+
+}  // namespace ep

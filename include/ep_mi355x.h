@@ -1,0 +1,186 @@
+/*
+ * ep_mi355x.h: C ABI of the MI355X (gfx950) MoE expert-parallel hot path,
+ * taken at one GPU's share: every expert is resident locally (a world of
+ * one), so there are no peers and no collectives.
+ *
+ *   ep_layout    topk_idx -> per-expert counts, aligned exclusive offsets,
+ *                a destination slot per (token, k), receive metadata
+ *   ep_dispatch  permute-copy token rows (bf16, or fp8 e4m3 plus fp32
+ *                per-128-channel scales) into the expert-major expand buffer
+ *   ep_combine   gather each token's top-k expert-output rows, weight them
+ *                by the router weights, sum in binary32 in k order, store bf16
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array arguments are DEVICE pointers owned by the caller; the library
+ *   never allocates, frees, copies to the host or synchronises. Every call
+ *   only enqueues kernels on `stream` (a hipStream_t passed as void*; NULL
+ *   is the default stream) and returns; results are ready when the stream
+ *   reaches that point. Calls are stream-ordered and capturable.
+ * - Arrays are dense and row-major with the shapes given below. Row pointers
+ *   of x, expand_x, expert_out, out and the scale arrays must be 16-byte
+ *   aligned; int32 / fp32 arrays 4-byte aligned.
+ * - Return value: EP_OK (0) on success, a negative EP_E* code on error.
+ *   Arguments are checked on the host before anything is enqueued; on an
+ *   error nothing is launched and ep_last_error() returns a message (per
+ *   calling thread). No entry point throws or aborts.
+ * - Shapes (hidden, topk, dtype) select kernels compiled ahead of time with
+ *   those values as template constants; a shape outside the compiled set is
+ *   rejected with EP_EUNSUPPORTED before any work (capability gate).
+ * - dtype numbering follows the MORI v2 EpDType enumeration ("MORI JIT v2",
+ *   section 3.7): bf16 = 0, fp32 = 1, fp8 = 2, fp4x2 = 3.
+ *
+ * Sources: "DeepEP 整体架构分析" (DeepEP overall architecture), the EPHandle
+ * structure and the dispatch / combine data-flow figure; "MORI JIT v2",
+ * section 3.5 (invalid configurations are rejected before any work: token
+ * bytes 16-byte aligned, topk within one wavefront, receive capacity covers
+ * the worst case), section 3.7 (dtype is a transport attribute: dispatch
+ * moves bytes, combine reduces and rejects byte dtypes), section 4 (no
+ * compile, allocation or host synchronisation on the launch path; graph
+ * capture), section 6 (every C entry point reports errors by return value
+ * plus a last-error string).
+ */
+#ifndef EP_MI355X_H
+#define EP_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define EP_OK 0
+#define EP_EINVAL (-1)        /* an argument is out of range or misaligned        */
+#define EP_EUNSUPPORTED (-2)  /* no compiled kernel for this (hidden, topk, dtype) */
+#define EP_ECAPACITY (-3)     /* capacity_rows cannot hold the worst case          */
+#define EP_EHIP (-4)          /* the HIP runtime reported an error on launch       */
+
+/* Element types (MORI v2 EpDType numbering). */
+#define EP_BF16 0
+#define EP_FP32 1
+#define EP_FP8_E4M3 2
+#define EP_FP4X2 3
+
+/* Largest expert count and top-k the layout kernels accept. */
+#define EP_MAX_EXPERTS 1024
+#define EP_MAX_TOPK 64
+
+/*
+ * Bytes of device workspace ep_layout needs for (num_tokens, topk,
+ * num_experts): per-tile expert histograms and per-tile received-token
+ * counts used between its two kernels. Returns 0 for out-of-range
+ * arguments. The workspace is scratch: its contents on entry do not matter
+ * and are overwritten; two ep_layout calls in flight at once must not share
+ * one workspace.
+ */
+size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_experts);
+
+/*
+ * Routing layout (DeepEP overall architecture, EPHandle fields
+ * num_unaligned_recv_tokens_perpert, psum_num_recv_tokens_per_expert,
+ * dst_buffer_slot_idx, recv_src_metadata, num_recv_tokens,
+ * num_expanded_tokens; notify warps "count per expert, compute target slot").
+ *
+ * Inputs
+ *   topk_idx          int32 [num_tokens, topk]: expert id of each (t, k);
+ *                     an id outside [0, num_experts) masks the entry
+ *                     (it gets no slot and is not counted).
+ *   num_tokens        T >= 0
+ *   topk              K in 1 .. EP_MAX_TOPK (compiled set, see EP_EUNSUPPORTED)
+ *   num_experts       E in 1 .. EP_MAX_EXPERTS
+ *   expert_alignment  A >= 1: every expert segment is padded to a multiple of A
+ *   capacity_rows     rows of the expand buffer the caller will dispatch into;
+ *                     must be >= T*K + E*(A-1) (the worst case), else
+ *                     EP_ECAPACITY
+ * Outputs (device, written in full unless noted)
+ *   counts            int32 [E]: unmasked entries routed to each expert
+ *   offsets           int32 [E+1]: offsets[0] = 0, offsets[e+1] = offsets[e]
+ *                     + A*ceil(counts[e]/A); offsets[E] = num_expanded_tokens
+ *   dst_slot          int32 [T, K]: expand row of (t, k), or -1 when masked.
+ *                     Inside an expert segment rows are handed out in
+ *                     token-major (t, then k) order starting at offsets[e];
+ *                     the padding rows of a segment belong to nobody.
+ *   recv_src_metadata int32 [T, K+2]: row i describes the i-th token (in
+ *                     ascending t) with at least one unmasked entry:
+ *                     [t, source rank (always 0 here), dst_slot[t, 0..K-1]].
+ *                     Rows i >= *num_recv are left untouched.
+ *   num_recv          int32 [1]: number of such tokens (stays on the device)
+ *   workspace         device scratch of >= ep_layout_workspace_bytes(T, K, E)
+ * Results are a pure function of the inputs (no atomics whose order matters).
+ */
+int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t num_experts,
+              int32_t expert_alignment, int64_t capacity_rows, int32_t *counts,
+              int32_t *offsets, int32_t *dst_slot, int32_t *recv_src_metadata,
+              int32_t *num_recv, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Dispatch in the expand layout (DeepEP overall architecture, dispatch copy
+ * epilogue writing token data and scale factors; "MORI JIT v2", section 3.7:
+ * the payload is moved as bytes, fp8 arrives already quantised).
+ *
+ * For every (t, k) with 0 <= dst_slot[t, k] < capacity_rows:
+ *   expand_x[dst, :]        = x[t, :]            (bytes of one row)
+ *   expand_scales[dst, :]   = x_scales[t, :]     (fp8 only)
+ *   expand_weights[dst]     = topk_weights[t, k] (only if both are non-NULL)
+ * Rows no entry points at (alignment padding) are not written. Entries
+ * outside [0, capacity_rows) are skipped.
+ *
+ *   x               dtype EP_BF16: bf16 [T, hidden]; EP_FP8_E4M3: e4m3 bytes [T, hidden]
+ *   x_scales        fp32 [T, hidden/128], required for EP_FP8_E4M3 (hidden % 128 == 0),
+ *                   must be NULL otherwise
+ *   topk_weights    fp32 [T, K] or NULL
+ *   dst_slot        int32 [T, K], as produced by ep_layout
+ *   expand_x        [capacity_rows, hidden] of the same element type as x
+ *   expand_scales   fp32 [capacity_rows, hidden/128] (fp8) or NULL
+ *   expand_weights  fp32 [capacity_rows] or NULL
+ * Errors: EP_EINVAL for a NULL required pointer, misalignment, hidden*bytes
+ * not a multiple of 16, a missing or unexpected scale pointer;
+ * EP_EUNSUPPORTED for (hidden, topk, dtype) outside the compiled set.
+ */
+int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
+                const int32_t *dst_slot, int32_t num_tokens, int32_t hidden, int32_t topk,
+                int32_t dtype, int64_t capacity_rows, void *expand_x, float *expand_scales,
+                float *expand_weights, void *stream);
+
+/*
+ * Gather combine (DeepEP overall architecture, combine reduce epilogue
+ * weighting expert outputs by topk_weights; "MORI JIT v2", section 3.7:
+ * combine reduces bf16 rows and rejects byte dtypes). No bias term.
+ *
+ * For every token t and channel h:
+ *   acc = +0.0f
+ *   for k = 0 .. K-1 with 0 <= dst_slot[t, k] < capacity_rows:
+ *       acc = acc + w[t, k] * float(expert_out[dst_slot[t, k], h])
+ *   out[t, h] = bf16(acc), round to nearest even
+ * Each product and each sum is rounded to binary32 on its own (no fused
+ * multiply-add), in k order, so the result is a pure function of the inputs.
+ * w[t, k] = topk_weights[t, k], or 1 when topk_weights is NULL.
+ *
+ *   expert_out      bf16 [capacity_rows, hidden] (dtype must be EP_BF16)
+ *   topk_weights    fp32 [T, K] or NULL
+ *   dst_slot        int32 [T, K]
+ *   out             bf16 [T, hidden]; every row is written
+ * Errors: EP_EINVAL for a byte dtype (fp8 / fp4x2), NULL or misaligned
+ * pointers; EP_EUNSUPPORTED for (hidden, topk, dtype) outside the compiled set.
+ */
+int ep_combine(const void *expert_out, const float *topk_weights, const int32_t *dst_slot,
+               int32_t num_tokens, int32_t hidden, int32_t topk, int32_t dtype,
+               int64_t capacity_rows, void *out, void *stream);
+
+/* Message for the last failed call on the calling thread ("" if none). */
+const char *ep_last_error(void);
+
+/*
+ * 1 if (hidden, topk, dtype) has compiled kernels for the given pass
+ * (0 = layout, which ignores hidden and dtype; 1 = dispatch; 2 = combine),
+ * else 0. Never fails.
+ */
+int ep_supported(int32_t pass, int32_t hidden, int32_t topk, int32_t dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_H */

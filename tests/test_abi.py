@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host with the documented codes (no GPU needed: every check
+runs before anything is enqueued, and no test here makes a compute call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_ep_layout_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep_mi355x.h")
+FAKE = 1 << 20  # a 16-byte aligned, never dereferenced address
+ODD = FAKE + 4  # misaligned for rows
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from combine_ep_layout_amd import build
+        build.build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(B.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert isinstance(getattr(L, name), ctypes._CFuncPtr)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (EP_[A-Z0-9_]+) \(?(-?\d+)\)?", text))
+    for k, v in consts.items():
+        assert getattr(B, k) == int(v), k
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        B.lib(str(tmp_path / "nope.so"))
+
+
+def test_supported_set(L):
+    assert B.ep_supported(0, 0, 8, 0)
+    assert B.ep_supported(1, 7168, 8, B.EP_BF16)
+    assert B.ep_supported(1, 7168, 8, B.EP_FP8_E4M3)
+    assert B.ep_supported(2, 7168, 8, B.EP_BF16)
+    assert not B.ep_supported(2, 7168, 8, B.EP_FP8_E4M3)
+    assert not B.ep_supported(1, 7168, 3, B.EP_BF16)
+    assert not B.ep_supported(1, 1000, 8, B.EP_BF16)
+    assert not B.ep_supported(7, 7168, 8, B.EP_BF16)
+
+
+def test_workspace_bytes(L):
+    assert B.ep_layout_workspace_bytes(64, 2, 16) == 0          # one tile: no workspace
+    assert B.ep_layout_workspace_bytes(4096, 8, 256) >= 32 * 257 * 4
+    assert B.ep_layout_workspace_bytes(-1, 8, 256) == 0
+    assert B.ep_layout_workspace_bytes(10, 8, 5000) == 0
+
+
+def _code(fn, *a):
+    with pytest.raises(B.EpError) as ei:
+        fn(*a)
+    assert B.ep_last_error() and str(ei.value)
+    return ei.value.code
+
+
+def lay(T=4096, K=8, E=256, A=128, cap=65280, ws=FAKE, wsb=1 << 20, idx=FAKE, counts=FAKE):
+    return (idx, T, K, E, A, cap, counts, FAKE, FAKE, FAKE, FAKE, ws, wsb)
+
+
+def test_layout_rejections(L):
+    assert _code(B.ep_layout, *lay(T=-1)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(K=0)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(K=65)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(E=0)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(E=1025)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(A=0)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(cap=65279)) == B.EP_ECAPACITY
+    assert _code(B.ep_layout, *lay(K=3, cap=1 << 20)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_layout, *lay(ws=None)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(wsb=16)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(idx=None)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(counts=None)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(T=1 << 28, cap=1 << 40)) == B.EP_EINVAL  # T*K overflows int32
+
+
+def disp(x=FAKE, xs=None, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280, X=FAKE, Xs=None):
+    return (x, xs, None, dst, T, H, K, dt, cap, X, Xs, None)
+
+
+def test_dispatch_rejections(L):
+    assert _code(B.ep_dispatch, *disp(H=7169)) == B.EP_EINVAL           # 16-byte rows
+    assert _code(B.ep_dispatch, *disp(H=7000)) == B.EP_EUNSUPPORTED     # aligned but not compiled
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP8_E4M3)) == B.EP_EINVAL  # fp8 without scales
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP8_E4M3, H=7184, xs=FAKE, Xs=FAKE)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch, *disp(xs=FAKE, Xs=FAKE)) == B.EP_EINVAL  # scales for bf16
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP4X2)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_dispatch, *disp(dt=9)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch, *disp(x=ODD)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch, *disp(X=None)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch, *disp(cap=-1)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch, *disp(K=5)) == B.EP_EUNSUPPORTED
+
+
+def comb(y=FAKE, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280, out=FAKE):
+    return (y, None, dst, T, H, K, dt, cap, out)
+
+
+def test_combine_rejections(L):
+    assert _code(B.ep_combine, *comb(dt=B.EP_FP8_E4M3)) == B.EP_EINVAL  # byte dtypes cannot be summed
+    assert _code(B.ep_combine, *comb(dt=B.EP_FP4X2)) == B.EP_EINVAL
+    assert _code(B.ep_combine, *comb(dt=B.EP_FP32)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_combine, *comb(H=7172)) == B.EP_EINVAL
+    assert _code(B.ep_combine, *comb(H=7176)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_combine, *comb(out=ODD)) == B.EP_EINVAL
+    assert _code(B.ep_combine, *comb(y=None)) == B.EP_EINVAL
+    assert _code(B.ep_combine, *comb(K=0)) == B.EP_EINVAL

@@ -1,0 +1,228 @@
+"""GPU path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Bar: layout, metadata and dispatch bytes bit-exact; combine within 1 bf16
+ulp (ordered bit-pattern distance <= 1; the kernels use the same binary32
+operation order as the oracle, so the tests also report exact matches).
+Covers the five workloads at full size (in the launch configuration the
+benchmark times), small shapes spanning several layout tiles with ragged
+tails, masking, empty and degenerate inputs, and special values.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - only on CPU hosts
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+from combine_ep_layout_amd import binding as B  # noqa: E402
+from combine_ep_layout_amd import inputs as I  # noqa: E402
+from tests import pins  # noqa: E402
+from tests.gpu_util import DeviceCase, dev_layout, layout_to_host, to_dev, to_host  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def check_layout(got, ref):
+    assert np.array_equal(got["counts"], ref["counts"]), "counts"
+    assert np.array_equal(got["offsets"], ref["offsets"]), "offsets"
+    assert np.array_equal(got["dst_slot"], ref["dst_slot"]), "dst_slot"
+    assert got["num_recv"] == ref["num_recv"], "num_recv"
+    assert np.array_equal(got["recv_src_metadata"], ref["recv_src_metadata"]), "recv_src_metadata"
+    # rows past num_recv are not written
+    assert np.all(got["meta_full"][ref["num_recv"]:] == -7)
+
+
+def check_dispatch(dc: DeviceCase, ref_dst):
+    w, case = dc.w, dc.case
+    got = to_host(dc.expand_x)
+    xb = case.x.view(np.uint8).reshape(w.T, -1)
+    before = np.full_like(got, dc.sentinel)
+    pins.check_dispatch(xb, ref_dst, before, got)
+    v = ref_dst >= 0
+    gw = to_host(dc.expand_w)
+    assert np.array_equal(gw[ref_dst[v]], case.topk_weights[v]), "expand_weights"
+    untouched = np.ones(w.cap, bool)
+    untouched[ref_dst[v]] = False
+    assert np.all(gw[untouched] == -5.0), "padding weights untouched"
+    if dc.expand_s is not None:
+        gs = to_host(dc.expand_s)
+        pins.check_dispatch(case.x_scales.view(np.uint8).reshape(w.T, -1), ref_dst,
+                            np.full_like(gs, -3.0).view(np.uint8), gs.view(np.uint8))
+
+
+def check_combine(got_bits, ref_bits, label=""):
+    d = pins.bf16_ulp_distance(got_bits, ref_bits)
+    exact = int((d == 0).sum())
+    _say(f"combine {label}: {exact}/{d.size} exact, max ulp distance {int(d.max()) if d.size else 0}")
+    assert d.size == 0 or d.max() <= 1, f"combine beyond 1 bf16 ulp: {int((d > 1).sum())} elements"
+
+
+@pytest.mark.parametrize("name", list(I.WORKLOADS))
+def test_workload_full_size(name):
+    w = I.WORKLOADS[name]
+    _say(f"[workload {name}] T={w.T} H={w.H} E={w.E} K={w.K} A={w.A} dtype={w.dtype} cap={w.cap}")
+    case = I.make_case(w)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case)
+    dc.layout()
+    dc.dispatch()
+    out = dc.combine()
+    torch.cuda.synchronize()
+    check_layout(layout_to_host(dc.lay), ref)
+    check_dispatch(dc, ref["dst_slot"])
+    ref_out = oracle.combine(case.y, ref["dst_slot"], case.topk_weights)
+    check_combine(to_host(out, np.uint16), ref_out, name)
+
+
+RAGGED = [
+    # T, H, E, K, A, mask, dtype, routing
+    (1000, 256, 16, 2, 1, 0.0, I.BF16, "uniform"),
+    (1500, 512, 64, 8, 4, 0.0, I.BF16, "uniform"),
+    (777, 1024, 256, 6, 16, 0.1, I.BF16, "uniform"),
+    (300, 2048, 1024, 4, 1, 0.0, I.BF16, "uniform"),
+    (3000, 256, 1, 1, 8, 0.0, I.BF16, "uniform"),
+    (129, 7168, 256, 8, 128, 0.0, I.BF16, "uniform"),
+    (128, 7168, 256, 8, 1, 0.0, I.BF16, "zipf"),
+    (4097, 256, 256, 8, 128, 0.02, I.BF16, "uniform"),
+    (513, 1024, 32, 4, 2, 0.0, I.FP8_E4M3, "hot8"),
+    (200, 256, 8, 2, 1, 1.0, I.BF16, "uniform"),
+    (1, 4096, 128, 8, 32, 0.0, I.BF16, "uniform"),
+    (2049, 512, 300, 8, 7, 0.05, I.BF16, "zipf"),
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,A,mask,dtype,routing", RAGGED)
+def test_ragged_shapes(T, H, E, K, A, mask, dtype, routing):
+    w = I.custom(f"r{T}_{H}_{E}_{K}", 1000 + T, T, H, E, K, A, dtype, routing)
+    _say(f"[ragged] {w}")
+    case = I.make_case(w, mask_frac=mask)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case)
+    dc.layout()
+    dc.dispatch()
+    out = dc.combine()
+    torch.cuda.synchronize()
+    check_layout(layout_to_host(dc.lay), ref)
+    check_dispatch(dc, ref["dst_slot"])
+    check_combine(to_host(out, np.uint16), oracle.combine(case.y, ref["dst_slot"], case.topk_weights),
+                  w.name)
+    # unweighted combine (weight 1)
+    out = dc.combine(weights=False)
+    check_combine(to_host(out, np.uint16), oracle.combine(case.y, ref["dst_slot"], None), "w=1")
+
+
+def test_empty_input():
+    w = I.custom("empty", 5, 0, 256, 16, 2, 4)
+    lay = dev_layout(None, 0, 2, 16, 4, w.cap)
+    torch.cuda.synchronize()
+    h = layout_to_host(lay)
+    assert np.all(h["counts"] == 0) and np.all(h["offsets"] == 0) and h["num_recv"] == 0
+    B.ep_dispatch(None, None, None, None, 0, 256, 2, B.EP_BF16, 0, None, None, None)
+    B.ep_combine(None, None, None, 0, 256, 2, B.EP_BF16, 0, None)
+
+
+def test_out_of_range_and_duplicate_ids():
+    T, H, E, K, A = 300, 256, 12, 4, 3
+    g = np.random.default_rng(9)
+    idx = g.integers(-3, E + 4, (T, K)).astype(np.int32)  # duplicates, negatives, >= E
+    w = I.custom("odd", 77, T, H, E, K, A)
+    case = I.make_case(w)
+    case.topk_idx = idx
+    ref = oracle.layout(idx, E, A)
+    dc = DeviceCase(case)
+    dc.layout()
+    dc.dispatch()
+    out = dc.combine()
+    torch.cuda.synchronize()
+    check_layout(layout_to_host(dc.lay), ref)
+    check_dispatch(dc, ref["dst_slot"])
+    check_combine(to_host(out, np.uint16), oracle.combine(case.y, ref["dst_slot"], case.topk_weights))
+
+
+def test_identity_expert_round_trip_full_size():
+    """dispatch -> identity expert (y = expand buffer) -> combine returns x bit-exactly."""
+    w = I.WORKLOADS["prefill_aligned"]
+    case = I.make_case(w, with_y=False)
+    dc = DeviceCase(case, with_y=False)
+    dc.layout()
+    dc.dispatch()
+    out = dc.combine(y=dc.expand_x)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(out, np.uint16), case.x)
+
+
+def test_repeat_runs_are_bit_identical():
+    w = I.WORKLOADS["mori_default"]
+    case = I.make_case(w)
+    dc = DeviceCase(case)
+    results = []
+    for _ in range(2):
+        dc.layout()
+        dc.dispatch()
+        out = dc.combine()
+        torch.cuda.synchronize()
+        results.append([to_host(dc.lay["dst_slot"]), to_host(dc.lay["meta"]), to_host(dc.expand_x),
+                        to_host(out).copy()])
+    for a, b in zip(*results):
+        assert np.array_equal(a, b)
+
+
+def test_combine_hand_worked_on_gpu():
+    data = json.load(open(os.path.join(GOLDEN, "combine_worked_examples.json")))
+    H = 256
+    for c in data["combine"]:
+        rows = np.zeros((len(c["y_rows_hex"]), H), np.uint16)
+        for r, row in enumerate(c["y_rows_hex"]):
+            rows[r, :len(row)] = [int(v, 16) for v in row]
+        dst = np.array(c["dst_slot"], np.int32)
+        wts_h = None if c["topk_weights"] is None else np.array(c["topk_weights"], np.float32)
+        while not B.ep_supported(2, H, dst.shape[1], B.EP_BF16):  # pad with masked entries
+            dst = np.concatenate([dst, np.full((dst.shape[0], 1), -1, np.int32)], axis=1)
+            if wts_h is not None:
+                wts_h = np.concatenate([wts_h, np.zeros((dst.shape[0], 1), np.float32)], axis=1)
+        T, K = dst.shape
+        wts = None if wts_h is None else to_dev(wts_h)
+        out = torch.full((T, H), 0x7FC1, dtype=torch.int16, device="cuda:0")
+        B.ep_combine(to_dev(rows), wts, to_dev(dst), T, H, K, B.EP_BF16, rows.shape[0], out)
+        torch.cuda.synchronize()
+        got = to_host(out, np.uint16)
+        exp = np.array([[int(v, 16) for v in r] for r in c["out_hex"]], np.uint16)
+        assert np.array_equal(got[:, :exp.shape[1]], exp), c["name"]
+        assert np.all(got[:, exp.shape[1]:] == 0)
+
+
+def test_combine_rounding_ties_and_specials():
+    """Sums that land exactly on bf16 ties, overflow, infinities and NaNs."""
+    H, T, K = 1024, 64, 2
+    g = np.random.default_rng(5)
+    cap = T * K
+    y = np.zeros((cap, H), np.uint16)
+    m = g.integers(0, 128, (T, H)).astype(np.uint16)
+    y[0::2] = 0x3F80 | m                                   # 1 + m/128
+    y[1::2] = 0x3B80                                       # 2^-8: every sum is a tie
+    y[1::2, :16] = g.integers(0, 0x10000, (T, 16)).astype(np.uint16)  # random bits incl. inf / NaN
+    y[0::2, 16] = 0x7F7F                                   # max finite + max finite -> inf
+    y[1::2, 16] = 0x7F7F
+    y[0::2, 17] = 0x7F80                                   # +inf + -inf -> NaN
+    y[1::2, 17] = 0xFF80
+    dst = np.arange(cap, dtype=np.int32).reshape(T, K)
+    out = torch.zeros((T, H), dtype=torch.int16, device="cuda:0")
+    B.ep_combine(to_dev(y), None, to_dev(dst), T, H, K, B.EP_BF16, cap, out)
+    torch.cuda.synchronize()
+    got = to_host(out, np.uint16)
+    ref = oracle.combine(y, dst, None)
+    nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    nan_r = ((ref & 0x7F80) == 0x7F80) & ((ref & 0x7F) != 0)
+    assert np.array_equal(nan_g, nan_r), "NaN positions"
+    assert np.array_equal(got[~nan_r], ref[~nan_r]), "non-NaN results bit-exact"
+    assert np.all(got[:, 16] == 0x7F80)
