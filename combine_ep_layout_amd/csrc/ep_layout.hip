@@ -10,20 +10,20 @@
 // chance; here every slot is a pure function of topk_idx: inside a segment
 // rows go to entries in token-major (t, then k) order.
 //
-// Design (MI355X): entries are cut into tiles of whole tokens, at most 1024
-// entries, one workgroup of 16 wave64s per tile, one entry per thread.
-//   1. Inside a wavefront, lanes holding the same expert are grouped with a
-//      ballot loop (one iteration per distinct expert of the wave); a lane's
-//      rank is the popcount of its group's ballot below it (mbcnt).
-//   2. Per-wave group sizes go to an LDS histogram [16 waves][E]; a scan over
-//      the 16 waves gives each wave its base, so rank-in-tile is exact.
-//   3. A tile's per-expert totals are written to the workspace. A second
-//      launch reduces, per expert, the totals of earlier tiles (prefix) and
-//      of all tiles (count), pads each count to the alignment, scans over
-//      experts in LDS, and writes slot = offset + prefix + rank-in-tile.
+// Design (MI355X): entries are cut into tiles of whole tokens (up to 1024
+// entries: 16, 8 or 4 wave64s of entries as E grows), one 1024-thread
+// workgroup per tile, one entry per thread.
+//   1. Every entry ORs its lane bit into an LDS word mask[e][wave] (the
+//      result of an OR does not depend on the order of the ORs). For each
+//      expert, a pass over its wave words gives the entries of that expert in
+//      earlier waves; an entry's rank in the tile is that base plus the
+//      popcount of its own wave word below its lane (mbcnt).
+//   2. A tile's per-expert totals go to the workspace. A second launch
+//      reduces, per expert, the totals of earlier tiles (prefix) and of all
+//      tiles (count), pads each count to the alignment, scans over experts,
+//      and writes slot = offset + prefix + rank-in-tile and the metadata.
 // A single tile (small T*K) runs both halves in one launch with no
-// workspace. Integer LDS atomics are never used, so results do not depend
-// on scheduling.
+// workspace. Results do not depend on scheduling.
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -31,13 +31,17 @@ namespace ep {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kWavesMax = kThreads / kWave;
 constexpr int kRankBits = 10;  // rank inside a tile < 1024
 
-template <int K>
+// Waves of entries per tile for E experts: the lane masks (E x NW x 8 bytes)
+// stay within 32 KiB of LDS.
+constexpr int tile_waves(int E) { return E <= 256 ? 16 : (E <= 512 ? 8 : 4); }
+
+template <int K, int NW>
 struct Tile {
-  static constexpr int tokens = kThreads / K;  // whole tokens per tile
-  static constexpr int entries = tokens * K;   // <= kThreads
+  static constexpr int tokens = NW * kWave / K;  // whole tokens per tile
+  static constexpr int entries = tokens * K;     // <= NW * 64
 };
 
 struct EntryRank {
@@ -45,74 +49,119 @@ struct EntryRank {
   int rank;  // entries of the same expert earlier in the tile
 };
 
-// Steps 1 and 2 above. s_wcnt: uint16 [kWaves][E]; s_total: int [E] receives
-// the tile's per-expert counts.
-template <int K>
+__host__ __device__ constexpr size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+// LDS of the rank phase: lane masks [E][NW], per-wave bases [E][NW], tile
+// totals [E], token flags [kThreads].
+__host__ __device__ constexpr size_t rank_lds_bytes(int E, int NW) {
+  return align16((size_t)E * NW * 8) + align16((size_t)E * NW * 2) + align16((size_t)E * 4) +
+         (size_t)kThreads * 4;
+}
+
+extern __shared__ __align__(16) unsigned char g_smem[];
+
+struct RankLds {
+  uint64_t *mask;
+  uint16_t *wbase;
+  int *total;
+  int *tok;
+};
+
+__device__ __forceinline__ RankLds rank_lds(int E, int NW) {
+  unsigned char *p = g_smem;
+  RankLds s;
+  s.mask = (uint64_t *)p;
+  p += align16((size_t)E * NW * 8);
+  s.wbase = (uint16_t *)p;
+  p += align16((size_t)E * NW * 2);
+  s.total = (int *)p;
+  p += align16((size_t)E * 4);
+  s.tok = (int *)p;
+  return s;
+}
+
+// Step 1. Also leaves s.tok[j] = 1 for every token j of the tile with an
+// unmasked entry (0 otherwise) and s.total[e] = entries of expert e.
+template <int K, int NW>
 __device__ EntryRank tile_rank(const int32_t *__restrict__ topk_idx, int64_t t0, int ntok, int E,
-                               uint16_t *s_wcnt, int *s_total) {
+                               const RankLds &s) {
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  for (int i = tid; i < kWaves * E; i += kThreads) s_wcnt[i] = 0;
+  for (int i = tid; i < E * NW; i += kThreads) s.mask[i] = 0;
+  if (tid < Tile<K, NW>::tokens) s.tok[tid] = 0;
   int e = -1;
   if (tid < ntok * K) {
     const int v = topk_idx[t0 * K + tid];
     e = (v >= 0 && v < E) ? v : -1;
   }
   __syncthreads();
-  int rank = 0;
-  uint64_t pending = ballot(e >= 0);
-  while (pending) {  // wave-uniform: one pass per distinct expert in the wave
-    const int leader = __builtin_ctzll(pending);
-    const int le = read_lane(e, leader);
-    const uint64_t group = ballot(e == le);
-    if (e == le) rank = count_below(group);
-    if (lane == leader) s_wcnt[w * E + le] = (uint16_t)__popcll(group);
-    pending &= ~group;
+  if (e >= 0) {
+    __hip_atomic_fetch_or(&s.mask[e * NW + w], 1ull << lane, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_WORKGROUP);
+    s.tok[tid / K] = 1;  // every writer stores the same value
   }
   __syncthreads();
   for (int ex = tid; ex < E; ex += kThreads) {
+    uint64_t m[NW];
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) m[ww] = s.mask[ex * NW + ww];
     int run = 0;
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const int c = s_wcnt[ww * E + ex];
-      s_wcnt[ww * E + ex] = (uint16_t)run;
-      run += c;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      s.wbase[ex * NW + ww] = (uint16_t)run;
+      run += __popcll(m[ww]);
     }
-    s_total[ex] = run;
+    s.total[ex] = run;
   }
   __syncthreads();
-  if (e >= 0) rank += s_wcnt[w * E + e];
+  int rank = 0;
+  if (e >= 0) rank = s.wbase[e * NW + w] + count_below(s.mask[e * NW + w]);
   return {e, rank};
 }
 
-// Thread j (< ntok) gets 1 if token j of the tile has an unmasked entry.
-// s_tok: int [Tile<K>::tokens].
-template <int K>
-__device__ int tile_token_flag(int e, int ntok, int *s_tok) {
-  const int tid = threadIdx.x;
-  if (tid < Tile<K>::tokens) s_tok[tid] = 0;
+// Sum of one int per thread over the block (deterministic: fixed tree).
+__device__ __forceinline__ int block_sum(int v, int *s_wtot) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  v = wave_sum(v);
+  if (lane == 0) s_wtot[w] = v;
   __syncthreads();
-  if (e >= 0) s_tok[tid / K] = 1;  // every writer stores the same value
+  int tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWavesMax; ++ww) tot += s_wtot[ww];
   __syncthreads();
-  const int f = (tid < ntok) ? s_tok[tid] : 0;
-  __syncthreads();
-  return f;
+  return tot;
 }
 
-// Final slots of the tile's entries and their metadata rows. `slot` is the
-// entry's slot or -1; `flag` is thread j's token flag; `vpre` the number of
-// received tokens before this tile.
-template <int K>
-__device__ void write_slots_and_meta(int64_t t0, int ntok, int slot, int flag, int vpre,
-                                     int32_t *__restrict__ dst_slot,
-                                     int32_t *__restrict__ meta, int *s_tok, int *s_tmp) {
-  const int tid = threadIdx.x;
-  int n_flagged;
-  const int tok_rank = block_exclusive_scan<kThreads>(flag, s_tmp, n_flagged);
-  if (tid < ntok) s_tok[tid] = flag ? vpre + tok_rank : -1;
+// Number of threads below the caller (in thread order) whose flag is set;
+// `total` receives the block-wide count.
+__device__ __forceinline__ int block_flag_rank(bool f, int *s_wtot, int &total) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const uint64_t bits = ballot(f);
+  if (lane == 0) s_wtot[w] = __popcll(bits);
   __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWavesMax; ++ww) {
+    const int c = s_wtot[ww];
+    before += ww < w ? c : 0;
+    tot += c;
+  }
+  total = tot;
+  __syncthreads();
+  return before + count_below(bits);
+}
+
+// Writes the tile's final slots and metadata rows. s_row[j] must hold the
+// receive row of token j of the tile, or -1.
+template <int K>
+__device__ __forceinline__ void write_slots_and_meta(int64_t t0, int ntok, int slot,
+                                                     const int *s_row,
+                                                     int32_t *__restrict__ dst_slot,
+                                                     int32_t *__restrict__ meta) {
+  const int tid = threadIdx.x;
   if (tid < ntok * K) {
     dst_slot[t0 * K + tid] = slot;
     const int j = tid / K, k = tid - j * K;
-    const int row = s_tok[j];
+    const int row = s_row[j];
     if (row >= 0) {
       int32_t *m = meta + (int64_t)row * (K + 2);
       m[2 + k] = slot;
@@ -124,27 +173,19 @@ __device__ void write_slots_and_meta(int64_t t0, int ntok, int slot, int flag, i
   }
 }
 
-__host__ __device__ constexpr size_t wcnt_bytes(int E) {
-  return ((size_t)kWaves * E * sizeof(uint16_t) + 15) & ~(size_t)15;
-}
-
 // One launch for T*K that fits a single tile (including T = 0).
-template <int K>
+template <int K, int NW>
 __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
     int32_t *__restrict__ num_recv) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t *s_wcnt = (uint16_t *)smem;
-  int *s_total = (int *)(smem + wcnt_bytes(E));
-  int *s_off = s_total + E;  // E + 1
-  __shared__ int s_tok[Tile<K>::tokens];
-  __shared__ int s_tmp[kWaves];
+  __shared__ int s_tmp[kWavesMax];
+  const RankLds s = rank_lds(E, NW);
+  int *s_off = (int *)(g_smem + rank_lds_bytes(E, NW));  // E
   const int tid = threadIdx.x;
-  const int ntok = T;
 
-  const EntryRank r = tile_rank<K>(topk_idx, 0, ntok, E, s_wcnt, s_total);
-  const int cnt = tid < E ? s_total[tid] : 0;
+  const EntryRank r = tile_rank<K, NW>(topk_idx, 0, T, E, s);
+  const int cnt = tid < E ? s.total[tid] : 0;
   const int padded = ((cnt + A - 1) / A) * A;
   int rows;
   const int off = block_exclusive_scan<kThreads>(padded, s_tmp, rows);
@@ -154,41 +195,38 @@ __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
     offsets[tid] = off;
   }
   if (tid == 0) offsets[E] = rows;
-  __syncthreads();
-  const int slot = r.e >= 0 ? s_off[r.e] + r.rank : -1;
-  const int flag = tile_token_flag<K>(r.e, ntok, s_tok);
+  const bool f = tid < T && s.tok[tid] != 0;
   int nrecv;
-  block_exclusive_scan<kThreads>(flag, s_tmp, nrecv);
+  const int tok_rank = block_flag_rank(f, s_tmp, nrecv);  // barriers publish s_off too
   if (tid == 0) *num_recv = nrecv;
-  write_slots_and_meta<K>(0, ntok, slot, flag, 0, dst_slot, meta, s_tok, s_tmp);
+  const int slot = r.e >= 0 ? s_off[r.e] + r.rank : -1;
+  if (tid < T) s.tok[tid] = f ? tok_rank : -1;
+  __syncthreads();
+  write_slots_and_meta<K>(0, T, slot, s.tok, dst_slot, meta);
 }
 
 // First launch of the multi-tile path: per-tile histograms and ranks.
 // dst_slot temporarily holds (expert << kRankBits | rank-in-tile), or -1.
-template <int K>
+template <int K, int NW>
 __global__ __launch_bounds__(kThreads) void ep_layout_tile_histogram(
     const int32_t *__restrict__ topk_idx, int T, int E, int32_t *__restrict__ dst_slot,
     int32_t *__restrict__ tile_counts, int32_t *__restrict__ tile_recv) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t *s_wcnt = (uint16_t *)smem;
-  int *s_total = (int *)(smem + wcnt_bytes(E));
-  __shared__ int s_tok[Tile<K>::tokens];
-  __shared__ int s_tmp[kWaves];
+  __shared__ int s_wtot[kWavesMax];
+  const RankLds s = rank_lds(E, NW);
   const int tid = threadIdx.x, b = blockIdx.x;
-  const int64_t t0 = (int64_t)b * Tile<K>::tokens;
-  const int ntok = (int)min((int64_t)Tile<K>::tokens, (int64_t)T - t0);
+  const int64_t t0 = (int64_t)b * Tile<K, NW>::tokens;
+  const int ntok = (int)min((int64_t)Tile<K, NW>::tokens, (int64_t)T - t0);
 
-  const EntryRank r = tile_rank<K>(topk_idx, t0, ntok, E, s_wcnt, s_total);
+  const EntryRank r = tile_rank<K, NW>(topk_idx, t0, ntok, E, s);
   if (tid < ntok * K) dst_slot[t0 * K + tid] = r.e >= 0 ? (r.e << kRankBits) | r.rank : -1;
-  for (int ex = tid; ex < E; ex += kThreads) tile_counts[(int64_t)b * E + ex] = s_total[ex];
-  const int flag = tile_token_flag<K>(r.e, ntok, s_tok);
-  int nflag;
-  block_exclusive_scan<kThreads>(flag, s_tmp, nflag);
-  if (tid == 0) tile_recv[b] = nflag;
+  for (int ex = tid; ex < E; ex += kThreads) tile_counts[(int64_t)b * E + ex] = s.total[ex];
+  const bool f = tid < ntok && s.tok[tid] != 0;
+  const int nrecv = block_sum(f ? 1 : 0, s_wtot);
+  if (tid == 0) tile_recv[b] = nrecv;
 }
 
 // Second launch: offsets, final slots and metadata for tile blockIdx.x.
-template <int K>
+template <int K, int NW>
 __global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
     int T, int E, int A, int num_tiles, const int32_t *__restrict__ tile_counts,
     const int32_t *__restrict__ tile_recv, int32_t *__restrict__ counts,
@@ -196,15 +234,18 @@ __global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
     int32_t *__restrict__ num_recv) {
   __shared__ int s_pre[kThreads];
   __shared__ int s_tot[kThreads];
-  __shared__ int s_tok[Tile<K>::tokens];
-  __shared__ int s_tmp[kWaves];
-  extern __shared__ __align__(16) unsigned char smem[];
-  int *s_base = (int *)smem;  // E
-  int *s_off = s_base + E;    // E
+  __shared__ int s_row[kThreads];
+  __shared__ int s_tmp[kWavesMax];
+  int *s_base = (int *)g_smem;  // E
+  int *s_off = s_base + E;      // E
   const int tid = threadIdx.x, b = blockIdx.x;
+  const int64_t t0 = (int64_t)b * Tile<K, NW>::tokens;
+  const int ntok = (int)min((int64_t)Tile<K, NW>::tokens, (int64_t)T - t0);
 
+  // Every global load of the block is issued before the first barrier.
+  const int packed = tid < ntok * K ? dst_slot[t0 * K + tid] : -1;
   // Per expert: entries in tiles before b, and in all tiles. P threads share
-  // an expert so that all the loads of a thread are in flight together.
+  // an expert so that each thread has only a few loads, all in flight.
   const int epad = E <= 1 ? 1 : 1 << (32 - __builtin_clz((unsigned)(E - 1)));
   const int P = kThreads / epad;
   const int ex = tid % epad, part = tid / epad;
@@ -217,9 +258,18 @@ __global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
       pre += bb < b ? c : 0;
     }
   }
+  int vpre = 0, vtot = 0;
+  for (int bb = tid; bb < num_tiles; bb += kThreads) {
+    const int c = tile_recv[bb];
+    vtot += c;
+    vpre += bb < b ? c : 0;
+  }
   s_pre[tid] = pre;
   s_tot[tid] = tot;
-  __syncthreads();
+  if (tid < Tile<K, NW>::tokens) s_row[tid] = 0;
+  const int recv_before = block_sum(vpre, s_tmp);  // its barriers publish s_pre / s_tot
+  const int recv_total = block_sum(vtot, s_tmp);
+
   int base = 0, cnt = 0;
   if (tid < E) {
     for (int j = 0; j < P; ++j) {
@@ -239,53 +289,44 @@ __global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
       counts[tid] = cnt;
       offsets[tid] = off;
     }
-    if (tid == 0) offsets[E] = rows;
-  }
-
-  // Received tokens before this tile, and in all tiles.
-  int vpre = 0, vtot = 0;
-  for (int bb = tid; bb < num_tiles; bb += kThreads) {
-    const int c = tile_recv[bb];
-    vtot += c;
-    vpre += bb < b ? c : 0;
-  }
-  int vpre_all, vtot_all;
-  block_exclusive_scan<kThreads>(vpre, s_tmp, vpre_all);
-  block_exclusive_scan<kThreads>(vtot, s_tmp, vtot_all);
-  if (b == 0 && tid == 0) *num_recv = vtot_all;
-
-  const int64_t t0 = (int64_t)b * Tile<K>::tokens;
-  const int ntok = (int)min((int64_t)Tile<K>::tokens, (int64_t)T - t0);
-  int slot = -1, e = -1;
-  if (tid < ntok * K) {
-    const int p = dst_slot[t0 * K + tid];
-    if (p >= 0) {
-      e = p >> kRankBits;
-      slot = s_off[e] + s_base[e] + (p & ((1 << kRankBits) - 1));
+    if (tid == 0) {
+      offsets[E] = rows;
+      *num_recv = recv_total;
     }
   }
-  const int flag = tile_token_flag<K>(e, ntok, s_tok);
-  write_slots_and_meta<K>(t0, ntok, slot, flag, vpre_all, dst_slot, meta, s_tok, s_tmp);
+  if (packed >= 0) s_row[tid / K] = 1;
+  __syncthreads();
+  int slot = -1;
+  if (packed >= 0) {
+    const int e = packed >> kRankBits;
+    slot = s_off[e] + s_base[e] + (packed & ((1 << kRankBits) - 1));
+  }
+  const bool f = tid < ntok && s_row[tid] != 0;
+  int nflag;
+  const int tok_rank = block_flag_rank(f, s_tmp, nflag);
+  if (tid < ntok) s_row[tid] = f ? recv_before + tok_rank : -1;
+  __syncthreads();
+  write_slots_and_meta<K>(t0, ntok, slot, s_row, dst_slot, meta);
 }
 
-template <int K>
+template <int K, int NW>
 int tiles_for(int T) {
-  return (T + Tile<K>::tokens - 1) / Tile<K>::tokens;
+  return (T + Tile<K, NW>::tokens - 1) / Tile<K, NW>::tokens;
 }
 
-template <int K>
+template <int K, int NW>
 int layout_impl(const LayoutArgs &a) {
-  const int B = tiles_for<K>(a.T);
-  const size_t shm_hist = wcnt_bytes(a.E) + sizeof(int) * (size_t)(2 * a.E + 1);
+  const int B = tiles_for<K, NW>(a.T);
+  const size_t shm_rank = rank_lds_bytes(a.E, NW);
   if (B <= 1) {
-    ep_layout_single_tile<K><<<1, kThreads, shm_hist, a.stream>>>(
+    ep_layout_single_tile<K, NW><<<1, kThreads, shm_rank + sizeof(int) * (size_t)a.E, a.stream>>>(
         a.topk_idx, a.T, a.E, a.A, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
   } else {
     int32_t *tile_counts = (int32_t *)a.workspace;
     int32_t *tile_recv = tile_counts + (size_t)B * a.E;
-    ep_layout_tile_histogram<K><<<B, kThreads, shm_hist, a.stream>>>(
+    ep_layout_tile_histogram<K, NW><<<B, kThreads, shm_rank, a.stream>>>(
         a.topk_idx, a.T, a.E, a.dst_slot, tile_counts, tile_recv);
-    ep_layout_tile_assign<K><<<B, kThreads, sizeof(int) * (size_t)(2 * a.E), a.stream>>>(
+    ep_layout_tile_assign<K, NW><<<B, kThreads, sizeof(int) * (size_t)(2 * a.E), a.stream>>>(
         a.T, a.E, a.A, B, tile_counts, tile_recv, a.counts, a.offsets, a.dst_slot, a.meta,
         a.num_recv);
   }
@@ -293,8 +334,22 @@ int layout_impl(const LayoutArgs &a) {
 }
 
 template <int K>
-size_t workspace_impl(int T, int E) {
-  const int B = tiles_for<K>(T);
+int layout_k(const LayoutArgs &a) {
+  switch (tile_waves(a.E)) {
+    case 16: return layout_impl<K, 16>(a);
+    case 8: return layout_impl<K, 8>(a);
+    default: return layout_impl<K, 4>(a);
+  }
+}
+
+template <int K>
+size_t workspace_k(int T, int E) {
+  int B;
+  switch (tile_waves(E)) {
+    case 16: B = tiles_for<K, 16>(T); break;
+    case 8: B = tiles_for<K, 8>(T); break;
+    default: B = tiles_for<K, 4>(T); break;
+  }
   return B <= 1 ? 0 : (((size_t)B * E + B) * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
@@ -302,7 +357,7 @@ size_t workspace_impl(int T, int E) {
 
 #define EP_LAYOUT_CASE(K) \
   case K:                 \
-    return layout_impl<K>(a);
+    return layout_k<K>(a);
 
 int launch_layout(const LayoutArgs &a) {
   switch (a.K) { EP_FOR_EACH_TOPK(EP_LAYOUT_CASE) default: return -2; }
@@ -310,7 +365,7 @@ int launch_layout(const LayoutArgs &a) {
 
 #define EP_WS_CASE(K) \
   case K:             \
-    return workspace_impl<K>(T, E);
+    return workspace_k<K>(T, E);
 
 size_t layout_workspace(int T, int K, int E) {
   switch (K) { EP_FOR_EACH_TOPK(EP_WS_CASE) default: return 0; }

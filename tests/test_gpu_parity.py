@@ -98,6 +98,9 @@ RAGGED = [
     (200, 256, 8, 2, 1, 1.0, I.BF16, "uniform"),
     (1, 4096, 128, 8, 32, 0.0, I.BF16, "uniform"),
     (2049, 512, 300, 8, 7, 0.05, I.BF16, "zipf"),
+    (40, 256, 1024, 6, 3, 0.1, I.BF16, "uniform"),      # one tile of 4 waves (E > 512)
+    (64, 256, 512, 8, 2, 0.0, I.BF16, "zipf"),          # one tile of 8 waves (256 < E <= 512)
+    (1100, 1024, 512, 2, 5, 0.0, I.FP8_E4M3, "uniform"),
 ]
 
 
