@@ -67,6 +67,65 @@ def measured_traffic(workload: str, kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+CALIBRATION_BYTES = 1 << 30  # fp32 elementwise negate: reads and writes this many bytes
+KERNEL_TAGS = {"dispatch": "ep_dispatch_expand", "combine": "ep_combine_gather",
+               "layout_histogram": "ep_layout_tile_histogram", "layout_assign": "ep_layout_tile_assign"}
+
+
+def _counter_means(path: str) -> dict:
+    """Mean counter value (KiB) per kernel-name tag from a rocprofv3 counter_collection CSV."""
+    import csv
+    sums, counts = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name", "")
+            tag = None
+            for k, t in KERNEL_TAGS.items():
+                if t in name:
+                    tag = k
+            if tag is None and "neg_kernel" in name:
+                tag = "calibration"
+            if tag is None:
+                continue
+            v = float(r["Counter_Value"])
+            sums[tag] = sums.get(tag, 0.0) + v
+            counts[tag] = counts.get(tag, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> str:
+    """Turn FETCH_SIZE / WRITE_SIZE counter runs into HBM bytes per launch.
+
+    Each counter is scaled by the factor that maps its reading for the
+    calibration kernel (an fp32 negate of CALIBRATION_BYTES, which must read
+    and write exactly that many bytes) to the true byte count.
+    """
+    fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
+    if "calibration" not in fetch or "calibration" not in write:
+        raise SystemExit("counter CSVs hold no calibration kernel: profile with --copy-calibration")
+    f_scale = CALIBRATION_BYTES / (fetch["calibration"] * 1024.0)
+    w_scale = CALIBRATION_BYTES / (write["calibration"] * 1024.0)
+    kernels = {}
+    for k in KERNEL_TAGS:
+        if k in fetch and k in write:
+            rd = fetch[k] * 1024.0 * f_scale
+            wr = write[k] * 1024.0 * w_scale
+            kernels[k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
+                          "hbm_read_bytes": int(rd), "hbm_write_bytes": int(wr),
+                          "hbm_bytes_per_launch": int(rd + wr)}
+    out = {"workload": workload, "sources_digest": sources_digest(),
+           "calibration": {"kernel": "torch.neg fp32, 1 GiB in, 1 GiB out",
+                           "fetch_kib": round(fetch["calibration"], 1),
+                           "write_kib": round(write["calibration"], 1),
+                           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+           "kernels": kernels}
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return path
+
+
 def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 5):
     """Time the CPU oracle (as it stands) on the same workload on the host."""
     import oracle
@@ -100,7 +159,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_aligned")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB fp32 negate first (a plain streaming kernel of known size "
+                         "for scaling hardware byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 FETCH_SIZE and "
+                         "WRITE_SIZE counter CSVs, then exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(write_traffic(args.workload, *args.traffic_from))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(every expert is local, a world of one); run with --gpus 1", file=sys.stderr)
@@ -140,6 +208,13 @@ def main():
     expand_s = torch.zeros((w.cap, w.H // 128), dtype=torch.float32, device=dev) if xs is not None else None
     out = torch.empty((w.T, w.H), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        a = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
 
     def step(ev=None):
         if ev is not None:
