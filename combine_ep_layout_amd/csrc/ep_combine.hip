@@ -47,11 +47,56 @@ struct CombineGeometry {
   static constexpr int SPLIT = CPL / G;                  // waves per token
 };
 
+// Loads the wave's slice (G chunks per lane) of each of the K rows and folds
+// them in k order into acc. ALL_VALID: every slot is a real row, so the
+// loads are straight-line code and each row is consumed as soon as its loads
+// land; otherwise rows with a negative slot are skipped.
+template <int CH, int K, int G, bool ALL_VALID>
+__device__ __forceinline__ void gather_fold(const u32x4 *__restrict__ y, const int (&d)[K],
+                                            const float (&wk)[K], int c0, int lane,
+                                            float (&acc)[G][8]) {
+#pragma clang fp contract(off)
+  u32x4 v[K][G];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (!ALL_VALID && d[k] < 0) continue;
+    const u32x4 *row = y + (int64_t)d[k] * CH;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int i = (c0 + g) * kWave + lane;
+      if (CH % kWave == 0 || i < CH) v[k][g] = __builtin_nontemporal_load(row + i);
+    }
+  }
+  // Keep every load above the arithmetic: the scheduler would otherwise sink
+  // some of them below it to save registers, halving the bytes in flight.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {  // fixed k order
+    if (!ALL_VALID && d[k] < 0) continue;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t word = v[k][g][j];
+        const float lo = __uint_as_float(word << 16);
+        const float hi = __uint_as_float(word & 0xffff0000u);
+        const float plo = wk[k] * lo;
+        const float phi = wk[k] * hi;
+        acc[g][2 * j] = acc[g][2 * j] + plo;
+        acc[g][2 * j + 1] = acc[g][2 * j + 1] + phi;
+      }
+    }
+  }
+}
+
 template <int H, int K>
 __global__ __launch_bounds__(kThreads) void ep_combine_gather(
     const u32x4 *__restrict__ y, const float *__restrict__ topk_weights,
     const int32_t *__restrict__ dst_slot, int T, int64_t capacity, u32x4 *__restrict__ out) {
-#pragma clang fp contract(off)
   constexpr int CH = H * 2 / 16;  // 16-byte chunks per row
   using Geo = CombineGeometry<CH>;
   constexpr int G = Geo::G, SPLIT = Geo::SPLIT;
@@ -73,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void ep_combine_gather(
       if (my_dst >= capacity) my_dst = -1;
       my_w = topk_weights ? topk_weights[(int64_t)t * K + lane] : 1.0f;
     }
+    const bool all_valid = ballot(lane < K && my_dst >= 0) == (K == 64 ? ~0ull : (1ull << K) - 1);
     int d[K];
     float wk[K];
 #pragma unroll
@@ -80,43 +126,12 @@ __global__ __launch_bounds__(kThreads) void ep_combine_gather(
       d[k] = read_lane(my_dst, k);
       wk[k] = read_lane(my_w, k);
     }
-
-    // Issue every load of this wave before the first is consumed. Expert
-    // outputs are read exactly once: non-temporal loads keep them from
-    // displacing useful lines in the caches.
-    u32x4 v[K][G];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      if (d[k] < 0) continue;
-      const u32x4 *row = y + (int64_t)d[k] * CH;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int i = (c0 + g) * kWave + lane;
-        if (CH % kWave == 0 || i < CH) v[k][g] = __builtin_nontemporal_load(row + i);
-      }
-    }
+    // Expert outputs are read exactly once: non-temporal loads keep them
+    // from displacing useful lines in the caches.
     float acc[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {  // fixed k order
-      if (d[k] < 0) continue;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t word = v[k][g][j];
-          const float lo = __uint_as_float(word << 16);
-          const float hi = __uint_as_float(word & 0xffff0000u);
-          const float plo = wk[k] * lo;
-          const float phi = wk[k] * hi;
-          acc[g][2 * j] = acc[g][2 * j] + plo;
-          acc[g][2 * j + 1] = acc[g][2 * j + 1] + phi;
-        }
-      }
-    }
+    if (all_valid) gather_fold<CH, K, G, true>(y, d, wk, c0, lane, acc);
+    else gather_fold<CH, K, G, false>(y, d, wk, c0, lane, acc);
+
     u32x4 *o = out + (int64_t)t * CH;
 #pragma unroll
     for (int g = 0; g < G; ++g) {

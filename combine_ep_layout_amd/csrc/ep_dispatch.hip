@@ -7,15 +7,15 @@
 // one-byte elements) and the DeepEP overall-architecture page, dispatch
 // data-flow figure (copy epilogue writing token data plus scale factors).
 //
-// Design (MI355X): the pass is HBM-bound (read T rows, write T*K rows). A
-// source row is cut into slices of two 16-byte chunks per lane (2 KiB); one
-// wave64 owns one (token, slice): it loads its slice once into registers and
-// writes it to each of the token's K destinations, so every x byte is read
-// from HBM once and a 14,336-byte row is served by 7 waves. The K
-// destination indices are loaded by K lanes and broadcast with readlane, so
-// row addresses are wave-uniform (scalar base + lane offset) and every store
-// instruction writes 1 KiB contiguous. Row bytes and K are template
-// constants: the per-row loops unroll fully.
+// Design (MI355X): the pass is HBM-bound on its writes (read T rows, write
+// T*K rows). One wave64 moves one 1 KiB slice of one (token, k) row: a
+// 16-byte load per lane from x and one non-temporal 16-byte store per lane
+// into the expand row, whose address is wave-uniform (the slot is loaded
+// once and made scalar with readfirstlane). Waves are ordered token-major,
+// then k, then slice, so the write stream is one destination row after
+// another, each written front to back; the K waves that need the same source
+// slice run on the same XCD, so x is read from HBM about once. Row bytes and
+// K are template constants.
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -24,83 +24,70 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;  // 4 waves, one token per wave at a time
+constexpr int kThreads = 256;  // 4 waves
 constexpr int kWavesPerBlock = kThreads / kWave;
 
-// Waves per token and 16-byte chunks per lane for a row of CH chunks: each
-// wave moves two chunks per lane (2 KiB of the row) when the row divides
-// evenly, else one; small rows keep one wave per token.
-template <int CH>
-struct DispatchGeometry {
-  static constexpr int CPL = (CH + kWave - 1) / kWave;
-  static constexpr int G = CPL % 2 == 0 ? 2 : 1;
-  static constexpr int SPLIT = CPL / G;
-};
+// Blocks run on the 8 XCDs round-robin (block b on XCD b % 8). Renumbering
+// them so that each XCD gets one contiguous eighth of the work keeps the K
+// waves that copy the same source slice on one XCD, where all but the first
+// read it from that XCD's L2. The grid is padded to a multiple of 8.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_contiguous_block() {
+  const int64_t nb = gridDim.x, b = blockIdx.x;
+  return (b % kXcds) * (nb / kXcds) + b / kXcds;
+}
 
+// One wave per (token, k, 1 KiB slice of the row): it reads 16 bytes per lane
+// of x[t] and writes them to expand_x[dst_slot[t, k]] with one non-temporal
+// store. Consecutive waves write consecutive KiB of one destination row, the
+// order in which HBM absorbs writes fastest (a wave that scatters to K rows
+// in turn is slower). The fp8 scale row and the router weight travel with
+// slice 0.
 template <int ROWB, int SCB, int K>
 __global__ __launch_bounds__(kThreads) void ep_dispatch_expand(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
     int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
     float *__restrict__ expand_weights) {
-  constexpr int CH = ROWB / 16;  // 16-byte chunks per row
-  using Geo = DispatchGeometry<CH>;
-  constexpr int G = Geo::G, SPLIT = Geo::SPLIT;
-  constexpr int SCH = SCB / 16;  // 16-byte chunks per scale row
+  constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
+  constexpr int SLICES = (CH + kWave - 1) / kWave;  // 1 KiB slices per row
+  constexpr int SCH = SCB / 16;                    // 16-byte chunks per scale row
   static_assert(ROWB % 16 == 0 && SCB % 16 == 0 && SCH <= kWave, "row geometry");
   static_assert(K >= 1 && K <= kWave, "topk must fit one wavefront");
 
   const int lane = lane_id();
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t first = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
+  const int64_t total = (int64_t)T * K * SLICES;
   const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-
-  for (int64_t gw = first; gw < (int64_t)T * SPLIT; gw += stride) {
-    const int t = (int)(gw / SPLIT);
-    const int part = (int)(gw - (int64_t)t * SPLIT);
-    const int c0 = part * G;
-    int my_dst = -1;
-    if (lane < K) {
-      my_dst = dst_slot[(int64_t)t * K + lane];
-      if (my_dst >= capacity) my_dst = -1;
+  for (int64_t gw = xcd_contiguous_block() * kWavesPerBlock + wave_in_block; gw < total;
+       gw += stride) {
+    const int64_t tk = gw / SLICES;  // flat (token, k)
+    const int slice = (int)(gw - tk * SLICES);
+    const int64_t t = tk / K;
+    const int d = __builtin_amdgcn_readfirstlane(dst_slot[tk]);
+    if (d < 0 || d >= capacity) continue;
+    const int i = slice * kWave + lane;
+    if (CH % kWave == 0 || i < CH)
+      __builtin_nontemporal_store(x[t * CH + i], expand_x + (int64_t)d * CH + i);
+    if (slice == 0) {
+      if (SCH > 0 && lane < SCH)
+        __builtin_nontemporal_store(x_scales[t * SCH + lane],
+                                    expand_scales + (int64_t)d * SCH + lane);
+      if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[tk];
     }
-    u32x4 v[G];
-    const u32x4 *src = x + (int64_t)t * CH;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int i = (c0 + g) * kWave + lane;
-      if (CH % kWave == 0 || i < CH) v[g] = src[i];
-    }
-    u32x4 s = {0u, 0u, 0u, 0u};
-    const bool scale_lane = SCH > 0 && part == 0 && lane < SCH;
-    if (scale_lane) s = x_scales[(int64_t)t * SCH + lane];
-    // The expand buffer is written once and read by a later kernel:
-    // non-temporal stores stream it to HBM without holding cache lines.
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int d = read_lane(my_dst, k);
-      if (d < 0) continue;
-      u32x4 *o = expand_x + (int64_t)d * CH;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int i = (c0 + g) * kWave + lane;
-        if (CH % kWave == 0 || i < CH) __builtin_nontemporal_store(v[g], o + i);
-      }
-      if (scale_lane) __builtin_nontemporal_store(s, expand_scales + (int64_t)d * SCH + lane);
-    }
-    if (expand_weights != nullptr && part == 0 && lane < K && my_dst >= 0)
-      expand_weights[my_dst] = topk_weights[(int64_t)t * K + lane];
   }
 }
 
 template <int ROWB, int SCB, int K>
 int dispatch_impl(const DispatchArgs &a) {
   if (a.T == 0) return 0;
-  constexpr int SPLIT = DispatchGeometry<ROWB / 16>::SPLIT;
-  const int64_t waves = (int64_t)a.T * SPLIT;
-  const int blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  constexpr int SLICES = (ROWB / 16 + kWave - 1) / kWave;
+  const int64_t waves = (int64_t)a.T * K * SLICES;
+  int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  blocks = blocks < (1 << 24) ? blocks : (1 << 24);  // larger inputs loop
+  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   const bool fwd_w = a.topk_weights != nullptr && a.expand_weights != nullptr;
-  ep_dispatch_expand<ROWB, SCB, K><<<blocks, kThreads, 0, a.stream>>>(
+  ep_dispatch_expand<ROWB, SCB, K><<<(unsigned)blocks, kThreads, 0, a.stream>>>(
       (const u32x4 *)a.x, (const u32x4 *)a.x_scales, a.topk_weights, a.dst_slot, a.T,
       a.capacity, (u32x4 *)a.expand_x, (u32x4 *)a.expand_scales,
       fwd_w ? a.expand_weights : nullptr);
