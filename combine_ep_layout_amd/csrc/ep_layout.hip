@@ -23,7 +23,8 @@
 //      tiles (count), pads each count to the alignment, scans over experts,
 //      and writes slot = offset + prefix + rank-in-tile and the metadata.
 // A single tile (small T*K) runs both halves in one launch with no
-// workspace. Results do not depend on scheduling.
+// workspace; so do up to 2^14 entries, with every block also scanning all
+// entries (see ep_layout_fused_tiles). Results do not depend on scheduling.
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -33,6 +34,11 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWavesMax = kThreads / kWave;
 constexpr int kRankBits = 10;  // rank inside a tile < 1024
+// Largest T*K laid out by the single-launch multi-tile kernel (every block
+// scans all entries); above it, two launches share per-tile histograms
+// through the workspace. Measured on MI355X (E=256, top-8): one launch wins
+// up to 16K entries (11.4 vs 12.8 us), two launches from 32K (12.3 vs 13.3).
+constexpr int64_t kFusedMaxEntries = 1 << 14;
 
 // Waves of entries per tile for E experts: the lane masks (E x NW x 8 bytes)
 // stay within 32 KiB of LDS.
@@ -205,6 +211,79 @@ __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
   write_slots_and_meta<K>(0, T, slot, s.tok, dst_slot, meta);
 }
 
+// One launch for several tiles when T*K is small enough: besides ranking its
+// own tile, every block streams all of topk_idx (from L2) into LDS integer
+// histograms of the entries before its tile and of all entries, and counts
+// received tokens the same way. Integer sums do not depend on the order of
+// the atomic adds, so the result is still a pure function of topk_idx. The
+// redundant scan costs O(T*K) per block, which is why larger inputs take the
+// two-launch path instead.
+template <int K, int NW>
+__global__ __launch_bounds__(kThreads) void ep_layout_fused_tiles(
+    const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
+    int32_t *__restrict__ num_recv) {
+  __shared__ int s_tmp[kWavesMax];
+  const RankLds s = rank_lds(E, NW);
+  int *s_pre = (int *)(g_smem + rank_lds_bytes(E, NW));  // E: entries before this tile
+  int *s_all = s_pre + E;                                // E: all entries
+  int *s_off = s_all + E;                                // E
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int64_t t0 = (int64_t)b * Tile<K, NW>::tokens;
+  const int ntok = (int)min((int64_t)Tile<K, NW>::tokens, (int64_t)T - t0);
+
+  for (int ex = tid; ex < E; ex += kThreads) {
+    s_pre[ex] = 0;
+    s_all[ex] = 0;
+  }
+  // Barriers inside tile_rank order the zeroing above before the adds below.
+  const EntryRank r = tile_rank<K, NW>(topk_idx, t0, ntok, E, s);
+  int vpre = 0, vall = 0;
+  for (int64_t j = tid; j < T; j += kThreads) {  // token-major: coalesced rows of K ids
+    int ids[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) ids[k] = topk_idx[j * K + k];
+    const bool before = j < t0;
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[k];
+      if (e >= 0 && e < E) {
+        any = true;
+        __hip_atomic_fetch_add(&s_all[e], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (before)
+          __hip_atomic_fetch_add(&s_pre[e], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    vall += any ? 1 : 0;
+    vpre += (any && before) ? 1 : 0;
+  }
+  const int recv_before = block_sum(vpre, s_tmp);  // its barriers publish the histograms
+  const int recv_total = block_sum(vall, s_tmp);
+  const int cnt = tid < E ? s_all[tid] : 0;
+  const int padded = ((cnt + A - 1) / A) * A;
+  int rows;
+  const int off = block_exclusive_scan<kThreads>(padded, s_tmp, rows);
+  if (tid < E) s_off[tid] = off;
+  if (b == 0) {
+    if (tid < E) {
+      counts[tid] = cnt;
+      offsets[tid] = off;
+    }
+    if (tid == 0) {
+      offsets[E] = rows;
+      *num_recv = recv_total;
+    }
+  }
+  const bool f = tid < ntok && s.tok[tid] != 0;
+  int nflag;
+  const int tok_rank = block_flag_rank(f, s_tmp, nflag);  // barriers publish s_off
+  const int slot = r.e >= 0 ? s_off[r.e] + s_pre[r.e] + r.rank : -1;
+  if (tid < ntok) s.tok[tid] = f ? recv_before + tok_rank : -1;
+  __syncthreads();
+  write_slots_and_meta<K>(t0, ntok, slot, s.tok, dst_slot, meta);
+}
+
 // First launch of the multi-tile path: per-tile histograms and ranks.
 // dst_slot temporarily holds (expert << kRankBits | rank-in-tile), or -1.
 template <int K, int NW>
@@ -321,6 +400,10 @@ int layout_impl(const LayoutArgs &a) {
   if (B <= 1) {
     ep_layout_single_tile<K, NW><<<1, kThreads, shm_rank + sizeof(int) * (size_t)a.E, a.stream>>>(
         a.topk_idx, a.T, a.E, a.A, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
+  } else if ((int64_t)a.T * K <= kFusedMaxEntries) {
+    ep_layout_fused_tiles<K, NW>
+        <<<B, kThreads, shm_rank + sizeof(int) * (size_t)(3 * a.E), a.stream>>>(
+            a.topk_idx, a.T, a.E, a.A, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
   } else {
     int32_t *tile_counts = (int32_t *)a.workspace;
     int32_t *tile_recv = tile_counts + (size_t)B * a.E;
@@ -350,7 +433,8 @@ size_t workspace_k(int T, int E) {
     case 8: B = tiles_for<K, 8>(T); break;
     default: B = tiles_for<K, 4>(T); break;
   }
-  return B <= 1 ? 0 : (((size_t)B * E + B) * sizeof(int32_t) + 255) & ~(size_t)255;
+  if (B <= 1 || (int64_t)T * K <= kFusedMaxEntries) return 0;
+  return (((size_t)B * E + B) * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
 }  // namespace

@@ -64,7 +64,8 @@ def test_supported_set(L):
 
 def test_workspace_bytes(L):
     assert B.ep_layout_workspace_bytes(64, 2, 16) == 0          # one tile: no workspace
-    assert B.ep_layout_workspace_bytes(4096, 8, 256) >= 32 * 257 * 4
+    assert B.ep_layout_workspace_bytes(1024, 8, 256) == 0       # single-launch multi-tile path
+    assert B.ep_layout_workspace_bytes(4096, 8, 256) >= 32 * 257 * 4  # two-launch path
     assert B.ep_layout_workspace_bytes(-1, 8, 256) == 0
     assert B.ep_layout_workspace_bytes(10, 8, 5000) == 0
 
@@ -89,8 +90,10 @@ def test_layout_rejections(L):
     assert _code(B.ep_layout, *lay(A=0)) == B.EP_EINVAL
     assert _code(B.ep_layout, *lay(cap=65279)) == B.EP_ECAPACITY
     assert _code(B.ep_layout, *lay(K=3, cap=1 << 20)) == B.EP_EUNSUPPORTED
-    assert _code(B.ep_layout, *lay(ws=None)) == B.EP_EINVAL
-    assert _code(B.ep_layout, *lay(wsb=16)) == B.EP_EINVAL
+    big = dict(T=32768, cap=32768 * 8 + 256 * 127)                   # needs a workspace
+    assert _code(B.ep_layout, *lay(ws=None, **big)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(wsb=16, **big)) == B.EP_EINVAL
+    assert _code(B.ep_layout, *lay(ws=ODD, **big)) == B.EP_EINVAL
     assert _code(B.ep_layout, *lay(idx=None)) == B.EP_EINVAL
     assert _code(B.ep_layout, *lay(counts=None)) == B.EP_EINVAL
     assert _code(B.ep_layout, *lay(T=1 << 28, cap=1 << 40)) == B.EP_EINVAL  # T*K overflows int32

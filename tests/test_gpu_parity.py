@@ -101,6 +101,11 @@ RAGGED = [
     (40, 256, 1024, 6, 3, 0.1, I.BF16, "uniform"),      # one tile of 4 waves (E > 512)
     (64, 256, 512, 8, 2, 0.0, I.BF16, "zipf"),          # one tile of 8 waves (256 < E <= 512)
     (1100, 1024, 512, 2, 5, 0.0, I.FP8_E4M3, "uniform"),
+    # above 2^14 entries: the two-launch layout path with a workspace
+    (20000, 256, 256, 8, 4, 0.01, I.BF16, "uniform"),
+    (70001, 256, 64, 2, 1, 0.0, I.BF16, "zipf"),
+    (40000, 256, 1024, 4, 2, 0.0, I.BF16, "uniform"),
+    (22000, 512, 300, 6, 3, 0.02, I.FP8_E4M3, "hot8"),
 ]
 
 
