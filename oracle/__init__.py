@@ -40,6 +40,9 @@ def lib(path: str = None):
         L.oracle_combine.argtypes = [_u16p, ctypes.c_int32, _f32p, _i32p, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int64, _u16p]
         L.oracle_combine.restype = ctypes.c_int
+        L.oracle_combine_f32.argtypes = [_f32p, ctypes.c_int32, _f32p, _i32p, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int64, _f32p]
+        L.oracle_combine_f32.restype = ctypes.c_int
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -138,6 +141,21 @@ def combine(y_bf16_bits: np.ndarray, dst_slot: np.ndarray, topk_weights: np.ndar
                               cap, _ptr(out, _u16p))
     if rc != 0:
         raise ValueError("oracle_combine rejected its arguments")
+    return out
+
+
+def combine_f32(y: np.ndarray, dst_slot: np.ndarray, topk_weights: np.ndarray = None, _lib=None):
+    """Weighted gather-reduce of fp32 expert outputs [capacity, H] into fp32 [T, H]."""
+    yf = np.ascontiguousarray(y, dtype=np.float32)
+    cap, H = yf.shape
+    dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
+    T, K = dst.shape
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    out = np.empty((T, H), np.float32)
+    rc = lib(_lib).oracle_combine_f32(_ptr(yf, _f32p), H, _ptr(w, _f32p), _ptr(dst, _i32p), T, K,
+                                      cap, _ptr(out, _f32p))
+    if rc != 0:
+        raise ValueError("oracle_combine_f32 rejected its arguments")
     return out
 
 

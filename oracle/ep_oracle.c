@@ -231,6 +231,34 @@ int oracle_combine(const uint16_t *y, int32_t H, const float *topk_weights,
   return 0;
 }
 
+/*
+ * The same reduction for binary32 expert outputs ("MORI JIT v2", section 3.7:
+ * combine reduces bf16 or fp32 rows and writes the same type): binary32 in,
+ * binary32 accumulation from +0.0 in k order, binary32 out (no final
+ * rounding step).
+ */
+int oracle_combine_f32(const float *y, int32_t H, const float *topk_weights,
+                       const int32_t *dst_slot, int32_t T, int32_t K,
+                       int64_t capacity_rows, float *out) {
+  if (T < 0 || K < 1 || H < 0) return -1;
+  for (int32_t t = 0; t < T; ++t) {
+    const int32_t *d = dst_slot + (int64_t)t * K;
+    for (int32_t k = 0; k < K; ++k)
+      if (d[k] >= capacity_rows) return -1;
+    for (int32_t h = 0; h < H; ++h) {
+      float acc = 0.0f;
+      for (int32_t k = 0; k < K; ++k) {
+        if (d[k] < 0) continue;
+        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;
+        float prod = w * y[(int64_t)d[k] * H + h];
+        acc = acc + prod;
+      }
+      out[(int64_t)t * H + h] = acc;
+    }
+  }
+  return 0;
+}
+
 /* Exposed for the tests that pin the rounding against hand-worked values. */
 uint16_t oracle_f32_to_bf16(float f) { return float_to_bf16_bits_rne(f); }
 float oracle_bf16_to_f32(uint16_t b) { return bf16_bits_to_float(b); }

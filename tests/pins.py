@@ -160,6 +160,21 @@ def check_combine_bound(y_bits, dst, w, out_bits):
     assert not bad.any(), f"{int(bad.sum())} outputs exceed the error bound, worst {err[bad].max()}"
 
 
+def check_combine_bound_f32(y, dst, w, out):
+    """Binary32 output: |out - exact| <= gamma_K * sum|w y| (no final rounding step)."""
+    T, K = dst.shape
+    yf = np.asarray(y, np.float32).astype(np.float64)
+    v = dst >= 0
+    rows = yf[np.where(v, dst, 0)] * v[..., None]
+    wf = np.ones((T, K)) if w is None else np.asarray(w, np.float32).astype(np.float64)
+    p = rows * wf[..., None]
+    exact, absum = p.sum(axis=1), np.abs(p).sum(axis=1)
+    gamma = K * U32 / (1 - K * U32)
+    err = np.abs(np.asarray(out, np.float64) - exact)
+    bad = err > gamma * absum + 2.0 ** -50 * absum + 2.0 ** -149
+    assert not bad.any(), f"{int(bad.sum())} outputs exceed the binary32 error bound"
+
+
 def bf16_ulp_distance(a_bits, b_bits):
     """Distance in units of bf16 spacing between two bf16 bit arrays (ordered integers)."""
     def ordered(b):

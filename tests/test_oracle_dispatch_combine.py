@@ -167,3 +167,36 @@ def test_ulp_distance_helper():
     a = np.array([0x3F80, 0x8000, 0x0000, 0xBF80, 0x0001], np.uint16)
     b = np.array([0x3F81, 0x0000, 0x8001, 0xBF81, 0x8001], np.uint16)
     assert pins.bf16_ulp_distance(a, b).tolist() == [1, 0, 1, 1, 2]
+
+
+def test_combine_f32_hand_worked(oracle_mod):
+    data = json.load(open(os.path.join(GOLDEN, "combine_worked_examples.json")))
+    for c in data["combine_f32"]:
+        y = np.array(c["y_rows"], np.float32)
+        out = oracle_mod.combine_f32(y, np.array(c["dst_slot"], np.int32),
+                                     np.array(c["topk_weights"], np.float32))
+        exp = np.array(c["out"], np.float32)
+        assert np.array_equal(out.view(np.uint32), exp.view(np.uint32)), c["name"]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("weighted", [True, False])
+def test_combine_f32_error_bound(oracle_mod, w, weighted):
+    g = np.random.default_rng([w.seed, 7])
+    y = g.standard_normal((w.cap, w.H)).astype(np.float32)
+    _, lay = _layout(oracle_mod, w)
+    wts = I.router_weights(w.seed, w.T, w.K) if weighted else None
+    out = oracle_mod.combine_f32(y, lay["dst_slot"], wts)
+    pins.check_combine_bound_f32(y, lay["dst_slot"], wts, out)
+
+
+def test_combine_f32_k1_and_masking(oracle_mod):
+    w = I.custom("f32k1", 43, 70, 256, 12, 1, 2)
+    _, lay = _layout(oracle_mod, w)
+    y = np.random.default_rng(3).standard_normal((w.cap, w.H)).astype(np.float32)
+    out = oracle_mod.combine_f32(y, lay["dst_slot"], None)
+    assert np.array_equal(out, y[lay["dst_slot"][:, 0]])
+    dst = lay["dst_slot"].copy()
+    dst[::3] = -1
+    out = oracle_mod.combine_f32(y, dst, np.ones((w.T, 1), np.float32))
+    assert np.all(out[::3].view(np.uint32) == 0) and np.array_equal(out[1::3], y[dst[1::3, 0]])

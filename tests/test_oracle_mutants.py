@@ -35,16 +35,23 @@ MUTANTS = {
     "combine_truncate": ("u += 0x7fffu + lsb;", "u += 0u * lsb;"),
     "combine_round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u + 0u * lsb;"),
     "combine_drop_last_term": ("      for (int32_t k = 0; k < K; ++k) {\n        if (d[k] < 0) continue;",
-                               "      for (int32_t k = 0; k < K - 1; ++k) {\n        if (d[k] < 0) continue;"),
-    "combine_wrong_sign": ("acc = acc + prod;", "acc = acc - prod;"),
+                               "      for (int32_t k = 0; k < K - 1; ++k) {\n        if (d[k] < 0) continue;", 0),
+    "combine_wrong_sign": ("acc = acc + prod;", "acc = acc - prod;", 0),
     "combine_transposed_weight": ("float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;",
-                                  "float w = topk_weights ? topk_weights[(int64_t)k * T + t] : 1.0f;"),
+                                  "float w = topk_weights ? topk_weights[(int64_t)k * T + t] : 1.0f;", 0),
     "combine_row_k0": ("float v = bf16_bits_to_float(y[(int64_t)d[k] * H + h]);",
                        "float v = bf16_bits_to_float(y[(int64_t)d[0] * H + h]);"),
-    "combine_unweighted_default_zero": ("topk_weights[(int64_t)t * K + k] : 1.0f;", "topk_weights[(int64_t)t * K + k] : 0.5f;"),
+    "combine_unweighted_default_zero": ("topk_weights[(int64_t)t * K + k] : 1.0f;", "topk_weights[(int64_t)t * K + k] : 0.5f;", 0),
     "combine_nan_guard_dropped": ("  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)\n"
                                   "    return (uint16_t)((u >> 16) | 0x0040u);\n", ""),
     "combine_fp16_style_bias": ("uint32_t lsb = (u >> 16) & 1u;", "uint32_t lsb = (u >> 15) & 1u;"),
+    "combine_f32_wrong_sign": ("        float prod = w * y[(int64_t)d[k] * H + h];\n        acc = acc + prod;",
+                               "        float prod = w * y[(int64_t)d[k] * H + h];\n        acc = acc - prod;"),
+    "combine_f32_row_k0": ("float prod = w * y[(int64_t)d[k] * H + h];", "float prod = w * y[(int64_t)d[0] * H + h];"),
+    "combine_f32_drop_first_term": ("      for (int32_t k = 0; k < K; ++k) {\n        if (d[k] < 0) continue;\n        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod",
+                                    "      for (int32_t k = 1; k < K; ++k) {\n        if (d[k] < 0) continue;\n        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod"),
+    "combine_f32_weight_k0": ("        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod",
+                              "        float w = topk_weights ? topk_weights[(int64_t)t * K] : 1.0f;\n        float prod"),
 }
 
 
@@ -128,7 +135,17 @@ def _run_pins(libpath):
         out = oracle.combine(X.view(np.uint16).reshape(w.cap, w.H), dst, case.topk_weights, _lib=libpath)
         assert np.array_equal(out, case.x)
 
+    def combine_f32_pins():
+        for c in comb_gold["combine_f32"]:
+            out = oracle.combine_f32(np.array(c["y_rows"], np.float32), np.array(c["dst_slot"], np.int32),
+                                     np.array(c["topk_weights"], np.float32), _lib=libpath)
+            assert np.array_equal(out.view(np.uint32), np.array(c["out"], np.float32).view(np.uint32))
+        yf = np.random.default_rng(5).standard_normal((w.cap, w.H)).astype(np.float32)
+        for wts in (case.topk_weights, None):
+            pins.check_combine_bound_f32(yf, dst, wts, oracle.combine_f32(yf, dst, wts, _lib=libpath))
+
     for name, fn in [("golden_layout", golden_layout), ("golden_combine", golden_combine),
+                     ("combine_f32", combine_f32_pins),
                      ("bruteforce", bruteforce_and_invariants), ("argsort", argsort_mid),
                      ("dispatch", dispatch_pins), ("combine_bound", combine_bound),
                      ("identity", identity)]:
@@ -136,11 +153,18 @@ def _run_pins(libpath):
     return failed
 
 
-def _build_variant(tmp_path, name, find, repl):
+def _build_variant(tmp_path, name, find, repl, nth=None):
     src = open(obuild.SRC).read()
-    assert src.count(find) == 1, f"mutation {name}: pattern must occur exactly once"
+    if nth is None:
+        assert src.count(find) == 1, f"mutation {name}: pattern must occur exactly once"
+        at = src.index(find)
+    else:  # the nth occurrence (0-based) of a pattern shared by several functions
+        assert src.count(find) > nth, f"mutation {name}: pattern must occur at least {nth + 1} times"
+        at = -1
+        for _ in range(nth + 1):
+            at = src.index(find, at + 1)
     p = tmp_path / f"{name}.c"
-    p.write_text(src.replace(find, repl))
+    p.write_text(src[:at] + repl + src[at + len(find):])
     out = str(tmp_path / f"lib{name}.so")
     flags = [f for f in obuild.CFLAGS if f not in ("-Werror", "-Wextra")]
     subprocess.run(["gcc", *flags, "-o", out, str(p)], check=True)
@@ -153,7 +177,6 @@ def test_unmutated_oracle_passes_every_pin():
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(tmp_path, name):
-    find, repl = MUTANTS[name]
-    lib = _build_variant(tmp_path, name, find, repl)
+    lib = _build_variant(tmp_path, name, *MUTANTS[name])
     failed = _run_pins(lib)
     assert failed, f"planted mistake {name!r} passed every pin"
