@@ -58,7 +58,7 @@ int ep_supported(int32_t pass, int32_t hidden, int32_t topk, int32_t dtype) {
   try {
     if (pass == 0) return ep::has_layout(topk) ? 1 : 0;
     if (pass == 1) return ep::has_dispatch(hidden, topk, dtype) ? 1 : 0;
-    if (pass == 2) return dtype == EP_BF16 && ep::has_combine(hidden, topk) ? 1 : 0;
+    if (pass == 2) return ep::has_combine(hidden, topk, dtype) ? 1 : 0;
   } catch (...) {
   }
   return 0;
@@ -124,22 +124,26 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
     if (hidden < 1) return fail(EP_EINVAL, "%s: hidden must be >= 1 (got %d)", what, hidden);
     if (capacity_rows < 0) return fail(EP_EINVAL, "%s: capacity_rows must be >= 0", what);
+    // Bytes per hidden unit: hidden counts elements, except for fp4x2 where it
+    // counts bytes (two e2m1 values per byte, as the caller packs them).
     int elt;
     if (dtype == EP_BF16) elt = 2;
-    else if (dtype == EP_FP8_E4M3) elt = 1;
-    else if (dtype == EP_FP32 || dtype == EP_FP4X2)
-      return fail(EP_EUNSUPPORTED, "%s: dtype %d has no compiled dispatch kernel", what, dtype);
+    else if (dtype == EP_FP32) elt = 4;
+    else if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2) elt = 1;
     else return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
     if (((int64_t)hidden * elt) % 16 != 0)
       return fail(EP_EINVAL, "%s: token bytes (%lld) must be a multiple of 16", what,
                   (long long)hidden * elt);
-    if (dtype == EP_FP8_E4M3) {
-      if (hidden % 128 != 0)
-        return fail(EP_EINVAL, "%s: fp8 needs hidden %% 128 == 0 (got %d)", what, hidden);
-      if (num_tokens > 0 && (!x_scales || !expand_scales))
-        return fail(EP_EINVAL, "%s: fp8 needs x_scales and expand_scales", what);
-    } else if (x_scales || expand_scales) {
-      return fail(EP_EINVAL, "%s: scales are only moved for fp8", what);
+    const bool byte_dtype = dtype == EP_FP8_E4M3 || dtype == EP_FP4X2;
+    if ((x_scales == nullptr) != (expand_scales == nullptr))
+      return fail(EP_EINVAL, "%s: x_scales and expand_scales go together", what);
+    if (x_scales != nullptr) {
+      if (!byte_dtype)
+        return fail(EP_EINVAL, "%s: scale rows travel only with fp8 / fp4x2 rows", what);
+      const int64_t elems = dtype == EP_FP4X2 ? 2 * (int64_t)hidden : hidden;
+      if (elems % 128 != 0)
+        return fail(EP_EINVAL, "%s: scales need a multiple of 128 elements per row (got %lld)",
+                    what, (long long)elems);
     }
     if (num_tokens > 0 && (!x || !dst_slot || !expand_x))
       return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
@@ -169,10 +173,10 @@ int ep_combine(const void *expert_out, const float *topk_weights, const int32_t 
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
     if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2)
       return fail(EP_EINVAL, "%s: combine sums its input; byte dtype %d is rejected", what, dtype);
-    if (dtype == EP_FP32)
-      return fail(EP_EUNSUPPORTED, "%s: fp32 expert outputs have no compiled kernel", what);
-    if (dtype != EP_BF16) return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
-    if (hidden < 1 || (hidden * 2) % 16 != 0)
+    if (dtype != EP_BF16 && dtype != EP_FP32)
+      return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
+    const int elt = dtype == EP_BF16 ? 2 : 4;
+    if (hidden < 1 || ((int64_t)hidden * elt) % 16 != 0)
       return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 (hidden %d)", what,
                   hidden);
     if (capacity_rows < 0) return fail(EP_EINVAL, "%s: capacity_rows must be >= 0", what);
@@ -181,10 +185,10 @@ int ep_combine(const void *expert_out, const float *topk_weights, const int32_t 
     if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(dst_slot, 4) ||
         !aligned(topk_weights, 4))
       return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
-    if (!ep::has_combine(hidden, topk))
-      return fail(EP_EUNSUPPORTED, "%s: (hidden %d, topk %d) has no compiled kernel", what,
-                  hidden, topk);
-    ep::CombineArgs a{expert_out, topk_weights, dst_slot, num_tokens, hidden, topk,
+    if (!ep::has_combine(hidden, topk, dtype))
+      return fail(EP_EUNSUPPORTED, "%s: (hidden %d, topk %d, dtype %d) has no compiled kernel",
+                  what, hidden, topk, dtype);
+    ep::CombineArgs a{expert_out, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,
                       capacity_rows, out, (hipStream_t)stream};
     return from_launch(ep::launch_combine(a), what);
   } catch (const std::exception &e) {

@@ -47,15 +47,49 @@ struct CombineGeometry {
   static constexpr int SPLIT = CPL / G;                  // waves per token
 };
 
+// Element type of the rows: EP_BF16 (0) packs 8 values per 16-byte chunk,
+// EP_FP32 (1) packs 4.
+template <int DT>
+struct Elem {
+  static constexpr int BYTES = DT == 0 ? 2 : 4;
+  static constexpr int PER_CHUNK = 16 / BYTES;
+  // Value j of a chunk, widened to binary32 (exact).
+  static __device__ __forceinline__ float get(const u32x4 &c, int j) {
+    if constexpr (DT == 0) {
+      const uint32_t word = c[j >> 1];
+      return __uint_as_float((j & 1) ? (word & 0xffff0000u) : (word << 16));
+    } else {
+      return __uint_as_float(c[j]);
+    }
+  }
+  // A chunk of sums stored in the row's type (bf16: round to nearest even).
+  static __device__ __forceinline__ u32x4 put(const float (&acc)[PER_CHUNK]) {
+    u32x4 r;
+    if constexpr (DT == 0) {
+      r[0] = pack_bf16x2(acc[0], acc[1]);
+      r[1] = pack_bf16x2(acc[2], acc[3]);
+      r[2] = pack_bf16x2(acc[4], acc[5]);
+      r[3] = pack_bf16x2(acc[6], acc[7]);
+    } else {
+      r[0] = __float_as_uint(acc[0]);
+      r[1] = __float_as_uint(acc[1]);
+      r[2] = __float_as_uint(acc[2]);
+      r[3] = __float_as_uint(acc[3]);
+    }
+    return r;
+  }
+};
+
 // Loads the wave's slice (G chunks per lane) of each of the K rows and folds
 // them in k order into acc. ALL_VALID: every slot is a real row, so the
 // loads are straight-line code and each row is consumed as soon as its loads
 // land; otherwise rows with a negative slot are skipped.
-template <int CH, int K, int G, bool ALL_VALID>
+template <int DT, int CH, int K, int G, bool ALL_VALID>
 __device__ __forceinline__ void gather_fold(const u32x4 *__restrict__ y, const int (&d)[K],
                                             const float (&wk)[K], int c0, int lane,
-                                            float (&acc)[G][8]) {
+                                            float (&acc)[G][Elem<DT>::PER_CHUNK]) {
 #pragma clang fp contract(off)
+  constexpr int PC = Elem<DT>::PER_CHUNK;
   u32x4 v[K][G];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
@@ -73,34 +107,30 @@ __device__ __forceinline__ void gather_fold(const u32x4 *__restrict__ y, const i
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[g][j] = 0.0f;
+    for (int j = 0; j < PC; ++j) acc[g][j] = 0.0f;
 #pragma unroll
   for (int k = 0; k < K; ++k) {  // fixed k order
     if (!ALL_VALID && d[k] < 0) continue;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t word = v[k][g][j];
-        const float lo = __uint_as_float(word << 16);
-        const float hi = __uint_as_float(word & 0xffff0000u);
-        const float plo = wk[k] * lo;
-        const float phi = wk[k] * hi;
-        acc[g][2 * j] = acc[g][2 * j] + plo;
-        acc[g][2 * j + 1] = acc[g][2 * j + 1] + phi;
+      for (int j = 0; j < PC; ++j) {
+        const float p = wk[k] * Elem<DT>::get(v[k][g], j);
+        acc[g][j] = acc[g][j] + p;
       }
     }
   }
 }
 
-template <int H, int K>
+template <int DT, int H, int K>
 __global__ __launch_bounds__(kThreads) void ep_combine_gather(
     const u32x4 *__restrict__ y, const float *__restrict__ topk_weights,
     const int32_t *__restrict__ dst_slot, int T, int64_t capacity, u32x4 *__restrict__ out) {
-  constexpr int CH = H * 2 / 16;  // 16-byte chunks per row
+  constexpr int CH = H * Elem<DT>::BYTES / 16;  // 16-byte chunks per row
+  constexpr int PC = Elem<DT>::PER_CHUNK;
   using Geo = CombineGeometry<CH>;
   constexpr int G = Geo::G, SPLIT = Geo::SPLIT;
-  static_assert((H * 2) % 16 == 0, "row geometry");
+  static_assert((H * Elem<DT>::BYTES) % 16 == 0, "row geometry");
   static_assert(K >= 1 && K <= kWave, "topk must fit one wavefront");
 
   const int lane = lane_id();
@@ -128,33 +158,26 @@ __global__ __launch_bounds__(kThreads) void ep_combine_gather(
     }
     // Expert outputs are read exactly once: non-temporal loads keep them
     // from displacing useful lines in the caches.
-    float acc[G][8];
-    if (all_valid) gather_fold<CH, K, G, true>(y, d, wk, c0, lane, acc);
-    else gather_fold<CH, K, G, false>(y, d, wk, c0, lane, acc);
+    float acc[G][PC];
+    if (all_valid) gather_fold<DT, CH, K, G, true>(y, d, wk, c0, lane, acc);
+    else gather_fold<DT, CH, K, G, false>(y, d, wk, c0, lane, acc);
 
     u32x4 *o = out + (int64_t)t * CH;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int i = (c0 + g) * kWave + lane;
-      if (CH % kWave == 0 || i < CH) {
-        u32x4 r;
-        r[0] = pack_bf16x2(acc[g][0], acc[g][1]);
-        r[1] = pack_bf16x2(acc[g][2], acc[g][3]);
-        r[2] = pack_bf16x2(acc[g][4], acc[g][5]);
-        r[3] = pack_bf16x2(acc[g][6], acc[g][7]);
-        __builtin_nontemporal_store(r, o + i);
-      }
+      if (CH % kWave == 0 || i < CH) __builtin_nontemporal_store(Elem<DT>::put(acc[g]), o + i);
     }
   }
 }
 
-template <int H, int K>
+template <int DT, int H, int K>
 int combine_impl(const CombineArgs &a) {
   if (a.T == 0) return 0;
-  constexpr int SPLIT = CombineGeometry<H * 2 / 16>::SPLIT;
+  constexpr int SPLIT = CombineGeometry<H * Elem<DT>::BYTES / 16>::SPLIT;
   const int64_t waves = (int64_t)a.T * SPLIT;
   const int blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-  ep_combine_gather<H, K><<<blocks, kThreads, 0, a.stream>>>(
+  ep_combine_gather<DT, H, K><<<blocks, kThreads, 0, a.stream>>>(
       (const u32x4 *)a.y, a.topk_weights, a.dst_slot, a.T, a.capacity, (u32x4 *)a.out);
   return launch_status();
 }
@@ -163,19 +186,36 @@ int combine_impl(const CombineArgs &a) {
 
 #define EP_COMBINE_K(K) \
   case K:               \
-    return combine_impl<H_, K>(a);
+    return combine_impl<DT, H_, K>(a);
 
-template <int H_>
+template <int DT, int H_>
 static int combine_k(const CombineArgs &a) {
   switch (a.K) { EP_FOR_EACH_TOPK(EP_COMBINE_K) default: return -2; }
 }
 
 #define EP_COMBINE_H(H) \
   case H:               \
-    return combine_k<H>(a);
+    return combine_k<DT, H>(a);
+
+template <int DT>
+static int combine_dt(const CombineArgs &a);
+template <>
+int combine_dt<0>(const CombineArgs &a) {
+  constexpr int DT = 0;
+  switch (a.H) { EP_FOR_EACH_HIDDEN_BF16(EP_COMBINE_H) default: return -2; }
+}
+template <>
+int combine_dt<1>(const CombineArgs &a) {
+  constexpr int DT = 1;
+  switch (a.H) { EP_FOR_EACH_HIDDEN_FP32(EP_COMBINE_H) default: return -2; }
+}
 
 int launch_combine(const CombineArgs &a) {
-  switch (a.H) { EP_FOR_EACH_HIDDEN_BF16(EP_COMBINE_H) default: return -2; }
+  switch (a.dtype) {
+    case 0: return combine_dt<0>(a);
+    case 1: return combine_dt<1>(a);
+    default: return -2;
+  }
 }
 
 }  // namespace ep

@@ -43,7 +43,9 @@ __device__ __forceinline__ int64_t xcd_contiguous_block() {
 // order in which HBM absorbs writes fastest (a wave that scatters to K rows
 // in turn is slower). The fp8 scale row and the router weight travel with
 // slice 0.
-template <int ROWB, int SCB, int K>
+// DT (the EP_* dtype) only names the kernel: every dtype moves bytes, so
+// instances with equal ROWB and SCB have the same body.
+template <int DT, int ROWB, int SCB, int K>
 __global__ __launch_bounds__(kThreads) void ep_dispatch_expand(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void ep_dispatch_expand(
   }
 }
 
-template <int ROWB, int SCB, int K>
+template <int DT, int ROWB, int SCB, int K>
 int dispatch_impl(const DispatchArgs &a) {
   if (a.T == 0) return 0;
   constexpr int SLICES = (ROWB / 16 + kWave - 1) / kWave;
@@ -87,51 +89,71 @@ int dispatch_impl(const DispatchArgs &a) {
   blocks = blocks < (1 << 24) ? blocks : (1 << 24);  // larger inputs loop
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   const bool fwd_w = a.topk_weights != nullptr && a.expand_weights != nullptr;
-  ep_dispatch_expand<ROWB, SCB, K><<<(unsigned)blocks, kThreads, 0, a.stream>>>(
+  ep_dispatch_expand<DT, ROWB, SCB, K><<<(unsigned)blocks, kThreads, 0, a.stream>>>(
       (const u32x4 *)a.x, (const u32x4 *)a.x_scales, a.topk_weights, a.dst_slot, a.T,
       a.capacity, (u32x4 *)a.expand_x, (u32x4 *)a.expand_scales,
       fwd_w ? a.expand_weights : nullptr);
   return launch_status();
 }
 
-template <int H, int K>
-int dispatch_bf16(const DispatchArgs &a) { return dispatch_impl<H * 2, 0, K>(a); }
-template <int H, int K>
-int dispatch_fp8(const DispatchArgs &a) { return dispatch_impl<H, (H / 128) * 4, K>(a); }
+// Row and scale-row bytes per dtype. hidden counts elements for bf16, fp32
+// and fp8, bytes for fp4x2; a scale row holds one fp32 per 128 elements.
+template <int DT, int H, bool SCALES, int K>
+int dispatch_dt(const DispatchArgs &a) {
+  constexpr int ELT_BYTES_X2 = DT == 0 ? 4 : DT == 1 ? 8 : 2;  // twice the bytes per hidden unit
+  constexpr int ROWB = H * ELT_BYTES_X2 / 2;
+  constexpr int ELEMS = DT == 3 ? 2 * H : H;
+  constexpr int SCB = SCALES ? (ELEMS / 128) * 4 : 0;
+  return dispatch_impl<DT, ROWB, SCB, K>(a);
+}
 
 }  // namespace
 
-#define EP_DISPATCH_K_BF16(K) \
-  case K:                     \
-    return dispatch_bf16<H_, K>(a);
-#define EP_DISPATCH_K_FP8(K) \
-  case K:                    \
-    return dispatch_fp8<H_, K>(a);
+#define EP_DISPATCH_K(K) \
+  case K:                \
+    return dispatch_dt<DT, H, SCALES, K>(a);
 
-template <int H_>
-static int dispatch_bf16_k(const DispatchArgs &a) {
-  switch (a.K) { EP_FOR_EACH_TOPK(EP_DISPATCH_K_BF16) default: return -2; }
-}
-template <int H_>
-static int dispatch_fp8_k(const DispatchArgs &a) {
-  switch (a.K) { EP_FOR_EACH_TOPK(EP_DISPATCH_K_FP8) default: return -2; }
+template <int DT, int H, bool SCALES>
+static int dispatch_k(const DispatchArgs &a) {
+  switch (a.K) { EP_FOR_EACH_TOPK(EP_DISPATCH_K) default: return -2; }
 }
 
-#define EP_DISPATCH_H_BF16(H) \
-  case H:                     \
-    return dispatch_bf16_k<H>(a);
-#define EP_DISPATCH_H_FP8(H) \
-  case H:                    \
-    return dispatch_fp8_k<H>(a);
+#define EP_DISPATCH_H_PLAIN(H) \
+  case H:                      \
+    return dispatch_k<DT, H, false>(a);
+#define EP_DISPATCH_H_BYTES(H)                                                         \
+  case H:                                                                              \
+    return a.x_scales ? dispatch_k<DT, H, true>(a) : dispatch_k<DT, H, false>(a);
+
+template <int DT>
+static int dispatch_plain(const DispatchArgs &a);
+template <>
+int dispatch_plain<0>(const DispatchArgs &a) {
+  constexpr int DT = 0;
+  switch (a.H) { EP_FOR_EACH_HIDDEN_BF16(EP_DISPATCH_H_PLAIN) default: return -2; }
+}
+template <>
+int dispatch_plain<1>(const DispatchArgs &a) {
+  constexpr int DT = 1;
+  switch (a.H) { EP_FOR_EACH_HIDDEN_FP32(EP_DISPATCH_H_PLAIN) default: return -2; }
+}
+static int dispatch_fp8(const DispatchArgs &a) {
+  constexpr int DT = 2;
+  switch (a.H) { EP_FOR_EACH_HIDDEN_FP8(EP_DISPATCH_H_BYTES) default: return -2; }
+}
+static int dispatch_fp4x2(const DispatchArgs &a) {
+  constexpr int DT = 3;
+  switch (a.H) { EP_FOR_EACH_HIDDEN_FP4X2(EP_DISPATCH_H_BYTES) default: return -2; }
+}
 
 int launch_dispatch(const DispatchArgs &a) {
-  if (a.dtype == 0) {
-    switch (a.H) { EP_FOR_EACH_HIDDEN_BF16(EP_DISPATCH_H_BF16) default: return -2; }
+  switch (a.dtype) {
+    case 0: return dispatch_plain<0>(a);
+    case 1: return dispatch_plain<1>(a);
+    case 2: return dispatch_fp8(a);
+    case 3: return dispatch_fp4x2(a);
+    default: return -2;
   }
-  if (a.dtype == 2) {
-    switch (a.H) { EP_FOR_EACH_HIDDEN_FP8(EP_DISPATCH_H_FP8) default: return -2; }
-  }
-  return -2;
 }
 
 #define EP_IS(V) \
@@ -146,18 +168,22 @@ bool has_layout(int K) { return has_topk(K); }
 
 bool has_dispatch(int H, int K, int dtype) {
   if (!has_topk(K)) return false;
-  if (dtype == 0) {
-    switch (H) { EP_FOR_EACH_HIDDEN_BF16(EP_IS) default: return false; }
+  switch (dtype) {
+    case 0: switch (H) { EP_FOR_EACH_HIDDEN_BF16(EP_IS) default: return false; }
+    case 1: switch (H) { EP_FOR_EACH_HIDDEN_FP32(EP_IS) default: return false; }
+    case 2: switch (H) { EP_FOR_EACH_HIDDEN_FP8(EP_IS) default: return false; }
+    case 3: switch (H) { EP_FOR_EACH_HIDDEN_FP4X2(EP_IS) default: return false; }
+    default: return false;
   }
-  if (dtype == 2) {
-    switch (H) { EP_FOR_EACH_HIDDEN_FP8(EP_IS) default: return false; }
-  }
-  return false;
 }
 
-bool has_combine(int H, int K) {
+bool has_combine(int H, int K, int dtype) {
   if (!has_topk(K)) return false;
-  switch (H) { EP_FOR_EACH_HIDDEN_BF16(EP_IS) default: return false; }
+  switch (dtype) {
+    case 0: switch (H) { EP_FOR_EACH_HIDDEN_BF16(EP_IS) default: return false; }
+    case 1: switch (H) { EP_FOR_EACH_HIDDEN_FP32(EP_IS) default: return false; }
+    default: return false;
+  }
 }
 
 }  // namespace ep

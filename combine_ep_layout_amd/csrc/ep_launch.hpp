@@ -12,7 +12,10 @@
 // lists is rejected by the capability gate in the C ABI.
 #define EP_FOR_EACH_TOPK(X) X(1) X(2) X(4) X(6) X(8)
 #define EP_FOR_EACH_HIDDEN_BF16(X) X(256) X(512) X(1024) X(2048) X(4096) X(7168)
+#define EP_FOR_EACH_HIDDEN_FP32(X) X(256) X(512) X(1024) X(2048) X(4096) X(7168)
 #define EP_FOR_EACH_HIDDEN_FP8(X) X(512) X(1024) X(2048) X(4096) X(7168)
+// fp4x2: hidden counts bytes (two e2m1 values per byte); 3584 bytes = 7168 values.
+#define EP_FOR_EACH_HIDDEN_FP4X2(X) X(256) X(512) X(1024) X(2048) X(3584)
 
 namespace ep {
 
@@ -41,7 +44,7 @@ struct CombineArgs {
   const void *y;
   const float *topk_weights;
   const int32_t *dst_slot;
-  int T, H, K;
+  int T, H, K, dtype;
   int64_t capacity;
   void *out;
   hipStream_t stream;
@@ -67,6 +70,6 @@ int launch_combine(const CombineArgs &a);
 
 bool has_layout(int K);
 bool has_dispatch(int H, int K, int dtype);
-bool has_combine(int H, int K);
+bool has_combine(int H, int K, int dtype);
 
 }  // namespace ep

@@ -47,6 +47,8 @@ class Workload:
     dtype: int
     routing: str
     capacity: int = 0  # 0 -> worst case T*K + E*(A-1)
+    out_dtype: int = BF16  # element type of the expert outputs and the combined rows
+    scales: bool = True    # fp8 / fp4x2: a scale row travels with each token
 
     @property
     def cap(self) -> int:
@@ -168,6 +170,23 @@ def normal_bf16(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
     return out
 
 
+def normal_f32(seed: int, stream: int, rows: int, cols: int) -> np.ndarray:
+    """N(0, 1) binary32 values."""
+    return rng(seed, stream).standard_normal((rows, cols), dtype=np.float32)
+
+
+def fp4x2_rows(seed: int, T: int, H_bytes: int):
+    """Packed e2m1 pairs (any byte is a valid pair of codes) and fp32 scales.
+
+    One scale per 128 values (64 bytes), s ~ U[0.01, 1]. Returns (uint8 [T, H_bytes],
+    float32 [T, 2*H_bytes/128]).
+    """
+    q = rng(seed, STREAM_X).integers(0, 256, (T, H_bytes), dtype=np.uint8)
+    S = max(1, (2 * H_bytes) // 128)
+    s = rng(seed, STREAM_SCALES).uniform(0.01, 1.0, (T, S)).astype(np.float32)
+    return q, s
+
+
 def fp8_rows(seed: int, T: int, H: int):
     """e4m3fn activations with one fp32 scale per 128-channel block.
 
@@ -191,9 +210,9 @@ class Case:
     w: Workload
     topk_idx: np.ndarray            # int32 [T, K]
     topk_weights: np.ndarray        # float32 [T, K]
-    x: np.ndarray                   # bf16 bits uint16 [T, H] or e4m3 uint8 [T, H]
-    x_scales: Optional[np.ndarray]  # float32 [T, H/128] for fp8, else None
-    y: Optional[np.ndarray] = None  # bf16 bits uint16 [cap, H] (expert outputs)
+    x: np.ndarray                   # bf16 bits uint16, fp32, e4m3 or packed e2m1 bytes [T, H]
+    x_scales: Optional[np.ndarray]  # float32 [T, values/128] for fp8 / fp4x2, else None
+    y: Optional[np.ndarray] = None  # expert outputs [cap, H]: bf16 bits uint16 or fp32
     extra: dict = field(default_factory=dict)
 
 
@@ -204,15 +223,26 @@ def make_case(w: Workload, with_y: bool = True, mask_frac: float = 0.0) -> Case:
     wts = router_weights(w.seed, w.T, w.K)
     if w.dtype == FP8_E4M3:
         x, xs = fp8_rows(w.seed, w.T, w.H)
+    elif w.dtype == FP4X2:
+        x, xs = fp4x2_rows(w.seed, w.T, w.H)
     elif w.dtype == BF16:
         x, xs = normal_bf16(w.seed, STREAM_X, w.T, w.H), None
+    elif w.dtype == FP32:
+        x, xs = normal_f32(w.seed, STREAM_X, w.T, w.H), None
     else:
-        raise ValueError("only bf16 and fp8 e4m3 workloads are synthesised")
-    y = normal_bf16(w.seed, STREAM_Y, w.cap, w.H) if with_y else None
+        raise ValueError(f"unknown dtype {w.dtype}")
+    if not w.scales:
+        xs = None
+    y = None
+    if with_y:
+        H_out = 2 * w.H if w.dtype == FP4X2 else w.H  # combine sees one value per element
+        y = (normal_bf16(w.seed, STREAM_Y, w.cap, H_out) if w.out_dtype == BF16
+             else normal_f32(w.seed, STREAM_Y, w.cap, H_out))
     return Case(w, idx, wts, x, xs, y)
 
 
 def custom(name: str, seed: int, T: int, H: int, E: int, K: int, A: int = 1,
-           dtype: int = BF16, routing: str = "uniform", capacity: int = 0) -> Workload:
+           dtype: int = BF16, routing: str = "uniform", capacity: int = 0,
+           out_dtype: int = BF16, scales: bool = True) -> Workload:
     """A workload of arbitrary shape (for edge cases and ragged tails)."""
-    return Workload(name, seed, T, H, E, K, A, dtype, routing, capacity)
+    return Workload(name, seed, T, H, E, K, A, dtype, routing, capacity, out_dtype, scales)

@@ -5,10 +5,12 @@
  *
  *   ep_layout    topk_idx -> per-expert counts, aligned exclusive offsets,
  *                a destination slot per (token, k), receive metadata
- *   ep_dispatch  permute-copy token rows (bf16, or fp8 e4m3 plus fp32
- *                per-128-channel scales) into the expert-major expand buffer
- *   ep_combine   gather each token's top-k expert-output rows, weight them
- *                by the router weights, sum in binary32 in k order, store bf16
+ *   ep_dispatch  permute-copy token rows (bf16, fp32, or fp8 e4m3 / fp4x2
+ *                bytes with optional fp32 per-128-value scales) into the
+ *                expert-major expand buffer
+ *   ep_combine   gather each token's top-k expert-output rows (bf16 or fp32),
+ *                weight them by the router weights, sum in binary32 in k
+ *                order, store in the rows' type
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -70,8 +72,9 @@ extern "C" {
 /*
  * Bytes of device workspace ep_layout needs for (num_tokens, topk,
  * num_experts): per-tile expert histograms and per-tile received-token
- * counts used between its two kernels. Returns 0 for out-of-range
- * arguments. The workspace is scratch: its contents on entry do not matter
+ * counts passed between its two kernels when num_tokens*topk is above 2^14
+ * (smaller inputs take one launch and need none: the result is 0). Returns 0
+ * for out-of-range arguments. The workspace is scratch: its contents on entry do not matter
  * and are overwritten; two ep_layout calls in flight at once must not share
  * one workspace.
  */
@@ -118,25 +121,28 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
 /*
  * Dispatch in the expand layout (DeepEP overall architecture, dispatch copy
  * epilogue writing token data and scale factors; "MORI JIT v2", section 3.7:
- * the payload is moved as bytes, fp8 arrives already quantised).
+ * the payload is moved as bytes whatever its dtype, fp8 / fp4x2 arrive
+ * already quantised, and for fp4x2 hidden counts bytes).
  *
  * For every (t, k) with 0 <= dst_slot[t, k] < capacity_rows:
  *   expand_x[dst, :]        = x[t, :]            (bytes of one row)
- *   expand_scales[dst, :]   = x_scales[t, :]     (fp8 only)
+ *   expand_scales[dst, :]   = x_scales[t, :]     (only if both are non-NULL)
  *   expand_weights[dst]     = topk_weights[t, k] (only if both are non-NULL)
  * Rows no entry points at (alignment padding) are not written. Entries
  * outside [0, capacity_rows) are skipped.
  *
- *   x               dtype EP_BF16: bf16 [T, hidden]; EP_FP8_E4M3: e4m3 bytes [T, hidden]
- *   x_scales        fp32 [T, hidden/128], required for EP_FP8_E4M3 (hidden % 128 == 0),
- *                   must be NULL otherwise
+ *   x               EP_BF16: bf16 [T, hidden]; EP_FP32: fp32 [T, hidden];
+ *                   EP_FP8_E4M3: e4m3 bytes [T, hidden];
+ *                   EP_FP4X2: packed e2m1 pairs, [T, hidden] bytes (2*hidden values)
+ *   x_scales        fp32 [T, S] with S = values per row / 128, or NULL; only for
+ *                   fp8 and fp4x2 (values per row a multiple of 128)
  *   topk_weights    fp32 [T, K] or NULL
  *   dst_slot        int32 [T, K], as produced by ep_layout
  *   expand_x        [capacity_rows, hidden] of the same element type as x
- *   expand_scales   fp32 [capacity_rows, hidden/128] (fp8) or NULL
+ *   expand_scales   fp32 [capacity_rows, S], given exactly when x_scales is
  *   expand_weights  fp32 [capacity_rows] or NULL
- * Errors: EP_EINVAL for a NULL required pointer, misalignment, hidden*bytes
- * not a multiple of 16, a missing or unexpected scale pointer;
+ * Errors: EP_EINVAL for a NULL required pointer, misalignment, row bytes
+ * not a multiple of 16, scales for bf16 / fp32 or only one scale pointer;
  * EP_EUNSUPPORTED for (hidden, topk, dtype) outside the compiled set.
  */
 int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
@@ -147,21 +153,22 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
 /*
  * Gather combine (DeepEP overall architecture, combine reduce epilogue
  * weighting expert outputs by topk_weights; "MORI JIT v2", section 3.7:
- * combine reduces bf16 rows and rejects byte dtypes). No bias term.
+ * combine reduces bf16 or fp32 rows, writes the same type, and rejects byte
+ * dtypes). No bias term.
  *
  * For every token t and channel h:
  *   acc = +0.0f
  *   for k = 0 .. K-1 with 0 <= dst_slot[t, k] < capacity_rows:
  *       acc = acc + w[t, k] * float(expert_out[dst_slot[t, k], h])
- *   out[t, h] = bf16(acc), round to nearest even
+ *   out[t, h] = acc stored as dtype (bf16: round to nearest even)
  * Each product and each sum is rounded to binary32 on its own (no fused
  * multiply-add), in k order, so the result is a pure function of the inputs.
  * w[t, k] = topk_weights[t, k], or 1 when topk_weights is NULL.
  *
- *   expert_out      bf16 [capacity_rows, hidden] (dtype must be EP_BF16)
+ *   expert_out      [capacity_rows, hidden] of dtype EP_BF16 or EP_FP32
  *   topk_weights    fp32 [T, K] or NULL
  *   dst_slot        int32 [T, K]
- *   out             bf16 [T, hidden]; every row is written
+ *   out             [T, hidden] of the same dtype; every row is written
  * Errors: EP_EINVAL for a byte dtype (fp8 / fp4x2), NULL or misaligned
  * pointers; EP_EUNSUPPORTED for (hidden, topk, dtype) outside the compiled set.
  */

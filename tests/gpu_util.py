@@ -60,13 +60,18 @@ class DeviceCase:
         self.x = to_dev(case.x)
         self.xs = to_dev(case.x_scales) if case.x_scales is not None else None
         self.y = to_dev(case.y) if (with_y and case.y is not None) else None
-        elt = 1 if w.dtype == I.FP8_E4M3 else 2
+        elt = {I.BF16: 2, I.FP32: 4, I.FP8_E4M3: 1, I.FP4X2: 1}[w.dtype]
         self.row_bytes = w.H * elt
         self.expand_x = torch.full((w.cap, self.row_bytes), sentinel, dtype=torch.uint8, device=DEV)
-        self.expand_s = (torch.full((w.cap, w.H // 128), -3.0, dtype=torch.float32, device=DEV)
-                         if self.xs is not None else None)
+        self.expand_s = (torch.full((w.cap, case.x_scales.shape[1]), -3.0, dtype=torch.float32,
+                                    device=DEV) if self.xs is not None else None)
         self.expand_w = torch.full((w.cap,), -5.0, dtype=torch.float32, device=DEV)
-        self.out = torch.full((max(w.T, 1), w.H), 0x7FC1, dtype=torch.int16, device=DEV)
+        self.H_out = 2 * w.H if w.dtype == I.FP4X2 else w.H  # combine sees one value per element
+        if w.out_dtype == I.FP32:
+            self.out = torch.full((max(w.T, 1), self.H_out), float("nan"), dtype=torch.float32,
+                                  device=DEV)
+        else:
+            self.out = torch.full((max(w.T, 1), self.H_out), 0x7FC1, dtype=torch.int16, device=DEV)
         self.sentinel = sentinel
 
     def layout(self, stream=None):
@@ -83,5 +88,6 @@ class DeviceCase:
     def combine(self, y=None, weights=True, stream=None):
         w = self.w
         B.ep_combine(self.y if y is None else y, self.wts if weights else None,
-                     self.lay["dst_slot"], w.T, w.H, w.K, B.EP_BF16, w.cap, self.out, stream)
+                     self.lay["dst_slot"], w.T, self.H_out, w.K, w.out_dtype, w.cap, self.out,
+                     stream)
         return self.out[:w.T]

@@ -56,6 +56,10 @@ def test_supported_set(L):
     assert B.ep_supported(1, 7168, 8, B.EP_BF16)
     assert B.ep_supported(1, 7168, 8, B.EP_FP8_E4M3)
     assert B.ep_supported(2, 7168, 8, B.EP_BF16)
+    assert B.ep_supported(2, 7168, 8, B.EP_FP32)
+    assert B.ep_supported(1, 7168, 8, B.EP_FP32)
+    assert B.ep_supported(1, 3584, 8, B.EP_FP4X2)      # hidden counts bytes for fp4x2
+    assert not B.ep_supported(1, 7168, 8, B.EP_FP4X2)
     assert not B.ep_supported(2, 7168, 8, B.EP_FP8_E4M3)
     assert not B.ep_supported(1, 7168, 3, B.EP_BF16)
     assert not B.ep_supported(1, 1000, 8, B.EP_BF16)
@@ -106,10 +110,14 @@ def disp(x=FAKE, xs=None, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280
 def test_dispatch_rejections(L):
     assert _code(B.ep_dispatch, *disp(H=7169)) == B.EP_EINVAL           # 16-byte rows
     assert _code(B.ep_dispatch, *disp(H=7000)) == B.EP_EUNSUPPORTED     # aligned but not compiled
-    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP8_E4M3)) == B.EP_EINVAL  # fp8 without scales
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP8_E4M3, xs=FAKE)) == B.EP_EINVAL  # one scale pointer
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP8_E4M3, Xs=FAKE)) == B.EP_EINVAL
     assert _code(B.ep_dispatch, *disp(dt=B.EP_FP8_E4M3, H=7184, xs=FAKE, Xs=FAKE)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP4X2, H=3616, xs=FAKE, Xs=FAKE)) == B.EP_EINVAL
     assert _code(B.ep_dispatch, *disp(xs=FAKE, Xs=FAKE)) == B.EP_EINVAL  # scales for bf16
-    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP4X2)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP32, xs=FAKE, Xs=FAKE)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP4X2)) == B.EP_EUNSUPPORTED   # 7168 bytes not compiled
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP32, H=7172)) == B.EP_EUNSUPPORTED
     assert _code(B.ep_dispatch, *disp(dt=9)) == B.EP_EINVAL
     assert _code(B.ep_dispatch, *disp(x=ODD)) == B.EP_EINVAL
     assert _code(B.ep_dispatch, *disp(X=None)) == B.EP_EINVAL
@@ -124,7 +132,8 @@ def comb(y=FAKE, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280, out=FAK
 def test_combine_rejections(L):
     assert _code(B.ep_combine, *comb(dt=B.EP_FP8_E4M3)) == B.EP_EINVAL  # byte dtypes cannot be summed
     assert _code(B.ep_combine, *comb(dt=B.EP_FP4X2)) == B.EP_EINVAL
-    assert _code(B.ep_combine, *comb(dt=B.EP_FP32)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_combine, *comb(dt=B.EP_FP32, H=7172)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_combine, *comb(dt=5)) == B.EP_EINVAL
     assert _code(B.ep_combine, *comb(H=7172)) == B.EP_EINVAL
     assert _code(B.ep_combine, *comb(H=7176)) == B.EP_EUNSUPPORTED
     assert _code(B.ep_combine, *comb(out=ODD)) == B.EP_EINVAL

@@ -234,3 +234,41 @@ def test_combine_rounding_ties_and_specials():
     assert np.array_equal(nan_g, nan_r), "NaN positions"
     assert np.array_equal(got[~nan_r], ref[~nan_r]), "non-NaN results bit-exact"
     assert np.all(got[:, 16] == 0x7F80)
+
+
+DTYPES = [
+    # T, H, E, K, A, dtype, scales, combine dtype
+    (700, 1024, 64, 8, 4, I.FP32, False, I.FP32),
+    (513, 3584, 256, 8, 1, I.FP4X2, True, I.BF16),    # 7168 e2m1 values + 56 scales per token
+    (300, 256, 32, 4, 2, I.FP4X2, False, I.BF16),
+    (1000, 7168, 128, 6, 16, I.FP8_E4M3, False, I.BF16),
+    (2049, 7168, 256, 8, 128, I.BF16, False, I.FP32),  # fp32 combine at the full hidden size
+    (40, 2048, 16, 1, 1, I.FP32, False, I.FP32),
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,A,dtype,scales,out_dtype", DTYPES)
+def test_dtype_variants(T, H, E, K, A, dtype, scales, out_dtype):
+    """fp32 / fp4x2 / scale-less fp8 dispatch and fp32 combine against the oracle."""
+    w = I.custom(f"d{dtype}_{T}_{H}", 3000 + T, T, H, E, K, A, dtype, "uniform",
+                 out_dtype=out_dtype, scales=scales)
+    _say(f"[dtype] {w}")
+    case = I.make_case(w, mask_frac=0.03)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case)
+    dc.layout()
+    dc.dispatch()
+    out = dc.combine()
+    torch.cuda.synchronize()
+    check_layout(layout_to_host(dc.lay), ref)
+    check_dispatch(dc, ref["dst_slot"])
+    if out_dtype == I.FP32:
+        got = to_host(out)
+        exp = oracle.combine_f32(case.y, ref["dst_slot"], case.topk_weights)
+        assert np.array_equal(np.isnan(got), np.isnan(exp))
+        same = got.view(np.uint32) == exp.view(np.uint32)
+        _say(f"combine fp32: {int(same.sum())}/{same.size} bit-exact")
+        assert same.all(), "fp32 combine differs from the oracle's binary32 arithmetic"
+    else:
+        check_combine(to_host(out, np.uint16), oracle.combine(case.y, ref["dst_slot"], case.topk_weights),
+                      w.name)
