@@ -37,10 +37,10 @@ def lib(path: str = None):
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                       _u8p, _u8p, _f32p]
         L.oracle_dispatch.restype = ctypes.c_int
-        L.oracle_combine.argtypes = [_u16p, ctypes.c_int32, _f32p, _i32p, ctypes.c_int32,
+        L.oracle_combine.argtypes = [_u16p, ctypes.c_int32, _f32p, _u16p, _i32p, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_int64, _u16p]
         L.oracle_combine.restype = ctypes.c_int
-        L.oracle_combine_f32.argtypes = [_f32p, ctypes.c_int32, _f32p, _i32p, ctypes.c_int32,
+        L.oracle_combine_f32.argtypes = [_f32p, ctypes.c_int32, _f32p, _f32p, _i32p, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int64, _f32p]
         L.oracle_combine_f32.restype = ctypes.c_int
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
@@ -125,35 +125,38 @@ def dispatch(x_bytes: np.ndarray, dst_slot: np.ndarray, capacity_rows: int,
 
 
 def combine(y_bf16_bits: np.ndarray, dst_slot: np.ndarray, topk_weights: np.ndarray = None,
-            _lib=None):
+            bias_bf16_bits: np.ndarray = None, _lib=None):
     """Weighted gather-reduce of bf16 expert outputs back to token order.
 
-    ``y_bf16_bits`` is uint16 [capacity, H] holding bf16 bit patterns;
-    returns uint16 [T, H] bf16 bit patterns.
+    ``y_bf16_bits`` is uint16 [capacity, H] holding bf16 bit patterns, the
+    optional bias uint16 [T, H]; returns uint16 [T, H] bf16 bit patterns.
     """
     y = np.ascontiguousarray(y_bf16_bits).view(np.uint16)
     cap, H = y.shape
     dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
     T, K = dst.shape
     w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    b = None if bias_bf16_bits is None else np.ascontiguousarray(bias_bf16_bits).view(np.uint16)
     out = np.empty((T, H), np.uint16)
-    rc = lib(_lib).oracle_combine(_ptr(y, _u16p), H, _ptr(w, _f32p), _ptr(dst, _i32p), T, K,
-                              cap, _ptr(out, _u16p))
+    rc = lib(_lib).oracle_combine(_ptr(y, _u16p), H, _ptr(w, _f32p), _ptr(b, _u16p),
+                                  _ptr(dst, _i32p), T, K, cap, _ptr(out, _u16p))
     if rc != 0:
         raise ValueError("oracle_combine rejected its arguments")
     return out
 
 
-def combine_f32(y: np.ndarray, dst_slot: np.ndarray, topk_weights: np.ndarray = None, _lib=None):
+def combine_f32(y: np.ndarray, dst_slot: np.ndarray, topk_weights: np.ndarray = None,
+                bias: np.ndarray = None, _lib=None):
     """Weighted gather-reduce of fp32 expert outputs [capacity, H] into fp32 [T, H]."""
     yf = np.ascontiguousarray(y, dtype=np.float32)
     cap, H = yf.shape
     dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
     T, K = dst.shape
     w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
     out = np.empty((T, H), np.float32)
-    rc = lib(_lib).oracle_combine_f32(_ptr(yf, _f32p), H, _ptr(w, _f32p), _ptr(dst, _i32p), T, K,
-                                      cap, _ptr(out, _f32p))
+    rc = lib(_lib).oracle_combine_f32(_ptr(yf, _f32p), H, _ptr(w, _f32p), _ptr(b, _f32p),
+                                      _ptr(dst, _i32p), T, K, cap, _ptr(out, _f32p))
     if rc != 0:
         raise ValueError("oracle_combine_f32 rejected its arguments")
     return out

@@ -34,9 +34,9 @@
  *     one), slot of k = 0 .. K-1] for the i-th token (ascending) that has
  *     at least one unmasked entry; rows past num_recv are not written;
  *   - combine accumulates in fp32, starting at +0.0, in k order, each
- *     product and each sum rounded separately, then rounds to bf16 with
- *     round-to-nearest-even (NaN becomes a quiet NaN with its sign); a null
- *     weight pointer means weight 1.
+ *     product and each sum rounded separately, adds the bias (if any) last,
+ *     then rounds to bf16 with round-to-nearest-even (NaN becomes a quiet
+ *     NaN with its sign); a null weight pointer means weight 1.
  *
  * Parity is pinned (tests in tests/test_oracle_*.py) by brute force on tiny
  * inputs, by library routines (bincount, stable argsort, fancy indexing), by
@@ -203,13 +203,15 @@ static uint16_t float_to_bf16_bits_rne(float f) {
 }
 
 /*
- * [DeepEP] combine reduce epilogue (reduce weighted by topk_weights) and
- * [MORI] 3.7 (combine reduces bf16 rows): for each token t and channel h,
+ * [DeepEP] combine reduce epilogue (reduce weighted by topk_weights, plus a
+ * bias) and [MORI] 3.7 (combine reduces bf16 rows): for each token t and
+ * channel h,
  *   acc = +0.0f; for k = 0 .. K-1 with dst >= 0: acc = acc + w[t,k] * y[dst,h]
- * in binary32, then out[t,h] = bf16_rne(acc). No bias term.
+ *   if bias: acc = acc + bias[t,h]
+ * in binary32, then out[t,h] = bf16_rne(acc). bias is bf16 [T, H] or NULL.
  */
 int oracle_combine(const uint16_t *y, int32_t H, const float *topk_weights,
-                   const int32_t *dst_slot, int32_t T, int32_t K,
+                   const uint16_t *bias, const int32_t *dst_slot, int32_t T, int32_t K,
                    int64_t capacity_rows, uint16_t *out) {
   if (T < 0 || K < 1 || H < 0) return -1;
   for (int32_t t = 0; t < T; ++t) {
@@ -225,6 +227,7 @@ int oracle_combine(const uint16_t *y, int32_t H, const float *topk_weights,
         float prod = w * v;
         acc = acc + prod;
       }
+      if (bias) acc = acc + bf16_bits_to_float(bias[(int64_t)t * H + h]);
       out[(int64_t)t * H + h] = float_to_bf16_bits_rne(acc);
     }
   }
@@ -234,11 +237,11 @@ int oracle_combine(const uint16_t *y, int32_t H, const float *topk_weights,
 /*
  * The same reduction for binary32 expert outputs ("MORI JIT v2", section 3.7:
  * combine reduces bf16 or fp32 rows and writes the same type): binary32 in,
- * binary32 accumulation from +0.0 in k order, binary32 out (no final
- * rounding step).
+ * binary32 accumulation from +0.0 in k order, then the binary32 bias
+ * (fp32 [T, H] or NULL), binary32 out (no final rounding step).
  */
 int oracle_combine_f32(const float *y, int32_t H, const float *topk_weights,
-                       const int32_t *dst_slot, int32_t T, int32_t K,
+                       const float *bias, const int32_t *dst_slot, int32_t T, int32_t K,
                        int64_t capacity_rows, float *out) {
   if (T < 0 || K < 1 || H < 0) return -1;
   for (int32_t t = 0; t < T; ++t) {
@@ -253,6 +256,7 @@ int oracle_combine_f32(const float *y, int32_t H, const float *topk_weights,
         float prod = w * y[(int64_t)d[k] * H + h];
         acc = acc + prod;
       }
+      if (bias) acc = acc + bias[(int64_t)t * H + h];
       out[(int64_t)t * H + h] = acc;
     }
   }

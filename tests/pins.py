@@ -132,36 +132,41 @@ def bf16_ulp(x64):
     return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
 
 
-def combine_exact(y_bits, dst, w):
-    """float64 value of sum_k w[t,k] * y[dst[t,k]] over unmasked k, and sum |terms|."""
+def combine_exact(y_bits, dst, w, bias_bits=None):
+    """float64 value of sum_k w[t,k] * y[dst[t,k]] (+ bias) over unmasked k, and sum |terms|."""
     T, K = dst.shape
     yf = bf16_bits_to_f64(y_bits)
     v = dst >= 0
     rows = yf[np.where(v, dst, 0)] * v[..., None]
     wf = np.ones((T, K)) if w is None else np.asarray(w, np.float32).astype(np.float64)
     p = rows * wf[..., None]
-    return p.sum(axis=1), np.abs(p).sum(axis=1)
+    exact, absum = p.sum(axis=1), np.abs(p).sum(axis=1)
+    if bias_bits is not None:
+        b = bf16_bits_to_f64(bias_bits)
+        exact, absum = exact + b, absum + np.abs(b)
+    return exact, absum
 
 
-def check_combine_bound(y_bits, dst, w, out_bits):
-    """|out - exact| <= gamma_K * sum|w y| + half a bf16 ulp of out.
+def check_combine_bound(y_bits, dst, w, out_bits, bias_bits=None):
+    """|out - exact| <= gamma_n * sum|terms| + half a bf16 ulp of out.
 
-    gamma_K = K u / (1 - K u) bounds K binary32 roundings per term (one
-    product, at most K-1 sums) in a recursive sum; the final bf16 rounding
-    to nearest adds at most half a spacing of the result.
+    gamma_n = n u / (1 - n u) bounds n binary32 roundings per term (one
+    product, at most K-1 sums, one more for a bias) in a recursive sum; the
+    final bf16 rounding to nearest adds at most half a spacing of the result.
     """
     T, K = dst.shape
-    exact, absum = combine_exact(y_bits, dst, w)
+    exact, absum = combine_exact(y_bits, dst, w, bias_bits)
     out = bf16_bits_to_f64(out_bits)
-    gamma = K * U32 / (1 - K * U32)
+    n = K + (bias_bits is not None)
+    gamma = n * U32 / (1 - n * U32)
     bound = gamma * absum + 0.5 * bf16_ulp(out) + 2.0 ** -50 * absum
     err = np.abs(out - exact)
     bad = err > bound
     assert not bad.any(), f"{int(bad.sum())} outputs exceed the error bound, worst {err[bad].max()}"
 
 
-def check_combine_bound_f32(y, dst, w, out):
-    """Binary32 output: |out - exact| <= gamma_K * sum|w y| (no final rounding step)."""
+def check_combine_bound_f32(y, dst, w, out, bias=None):
+    """Binary32 output: |out - exact| <= gamma_n * sum|terms| (no final rounding step)."""
     T, K = dst.shape
     yf = np.asarray(y, np.float32).astype(np.float64)
     v = dst >= 0
@@ -169,7 +174,11 @@ def check_combine_bound_f32(y, dst, w, out):
     wf = np.ones((T, K)) if w is None else np.asarray(w, np.float32).astype(np.float64)
     p = rows * wf[..., None]
     exact, absum = p.sum(axis=1), np.abs(p).sum(axis=1)
-    gamma = K * U32 / (1 - K * U32)
+    if bias is not None:
+        b = np.asarray(bias, np.float32).astype(np.float64)
+        exact, absum = exact + b, absum + np.abs(b)
+    n = K + (bias is not None)
+    gamma = n * U32 / (1 - n * U32)
     err = np.abs(np.asarray(out, np.float64) - exact)
     bad = err > gamma * absum + 2.0 ** -50 * absum + 2.0 ** -149
     assert not bad.any(), f"{int(bad.sum())} outputs exceed the binary32 error bound"

@@ -200,3 +200,29 @@ def test_combine_f32_k1_and_masking(oracle_mod):
     dst[::3] = -1
     out = oracle_mod.combine_f32(y, dst, np.ones((w.T, 1), np.float32))
     assert np.all(out[::3].view(np.uint32) == 0) and np.array_equal(out[1::3], y[dst[1::3, 0]])
+
+
+def test_combine_bias_hand_worked(oracle_mod):
+    data = json.load(open(os.path.join(GOLDEN, "combine_worked_examples.json")))
+    for c in data["combine_bias"]:
+        y = np.array([[_hex(v) for v in row] for row in c["y_rows_hex"]], np.uint16)
+        b = np.array([[_hex(v) for v in row] for row in c["bias_hex"]], np.uint16)
+        out = oracle_mod.combine(y, np.array(c["dst_slot"], np.int32), None, b)
+        assert np.array_equal(out, np.array([[_hex(v) for v in r] for r in c["out_hex"]], np.uint16))
+    for c in data["combine_f32_bias"]:
+        out = oracle_mod.combine_f32(np.array(c["y_rows"], np.float32), np.array(c["dst_slot"], np.int32),
+                                     np.array(c["topk_weights"], np.float32), np.array(c["bias"], np.float32))
+        assert np.array_equal(out.view(np.uint32), np.array(c["out"], np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("w", CASES[:3], ids=lambda w: w.name)
+def test_combine_bias_error_bound(oracle_mod, w):
+    case = I.make_case(w)
+    _, lay = _layout(oracle_mod, w)
+    bias = I.normal_bf16(w.seed, 9, w.T, w.H)
+    out = oracle_mod.combine(case.y, lay["dst_slot"], case.topk_weights, bias)
+    pins.check_combine_bound(case.y, lay["dst_slot"], case.topk_weights, out, bias)
+    yf = np.random.default_rng(2).standard_normal((w.cap, w.H)).astype(np.float32)
+    bf = np.random.default_rng(3).standard_normal((w.T, w.H)).astype(np.float32)
+    out = oracle_mod.combine_f32(yf, lay["dst_slot"], case.topk_weights, bf)
+    pins.check_combine_bound_f32(yf, lay["dst_slot"], case.topk_weights, out, bf)

@@ -50,6 +50,10 @@ MUTANTS = {
     "combine_f32_row_k0": ("float prod = w * y[(int64_t)d[k] * H + h];", "float prod = w * y[(int64_t)d[0] * H + h];"),
     "combine_f32_drop_first_term": ("      for (int32_t k = 0; k < K; ++k) {\n        if (d[k] < 0) continue;\n        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod",
                                     "      for (int32_t k = 1; k < K; ++k) {\n        if (d[k] < 0) continue;\n        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod"),
+    "combine_bias_dropped": ("      if (bias) acc = acc + bf16_bits_to_float(bias[(int64_t)t * H + h]);\n", ""),
+    "combine_bias_twice": ("float acc = 0.0f;", "float acc = bias ? bf16_bits_to_float(bias[(int64_t)t * H + h]) : 0.0f;", 0),
+    "combine_f32_bias_dropped": ("      if (bias) acc = acc + bias[(int64_t)t * H + h];\n", ""),
+    "combine_f32_bias_first": ("float acc = 0.0f;", "float acc = bias ? bias[(int64_t)t * H + h] : 0.0f;", 1),
     "combine_f32_weight_k0": ("        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod",
                               "        float w = topk_weights ? topk_weights[(int64_t)t * K] : 1.0f;\n        float prod"),
 }
@@ -135,6 +139,22 @@ def _run_pins(libpath):
         out = oracle.combine(X.view(np.uint16).reshape(w.cap, w.H), dst, case.topk_weights, _lib=libpath)
         assert np.array_equal(out, case.x)
 
+    def bias_pins():
+        h = lambda v: int(v, 16)  # noqa: E731
+        for c in comb_gold["combine_bias"]:
+            y = np.array([[h(v) for v in row] for row in c["y_rows_hex"]], np.uint16)
+            b = np.array([[h(v) for v in row] for row in c["bias_hex"]], np.uint16)
+            out = oracle.combine(y, np.array(c["dst_slot"], np.int32), None, b, _lib=libpath)
+            assert np.array_equal(out, np.array([[h(v) for v in r] for r in c["out_hex"]], np.uint16))
+        for c in comb_gold["combine_f32_bias"]:
+            out = oracle.combine_f32(np.array(c["y_rows"], np.float32), np.array(c["dst_slot"], np.int32),
+                                     np.array(c["topk_weights"], np.float32),
+                                     np.array(c["bias"], np.float32), _lib=libpath)
+            assert np.array_equal(out.view(np.uint32), np.array(c["out"], np.float32).view(np.uint32))
+        bias = np.random.default_rng(8).integers(0, 0x3f00, (w.T, w.H)).astype(np.uint16)
+        pins.check_combine_bound(case.y, dst, case.topk_weights,
+                                 oracle.combine(case.y, dst, case.topk_weights, bias, _lib=libpath), bias)
+
     def combine_f32_pins():
         for c in comb_gold["combine_f32"]:
             out = oracle.combine_f32(np.array(c["y_rows"], np.float32), np.array(c["dst_slot"], np.int32),
@@ -145,7 +165,7 @@ def _run_pins(libpath):
             pins.check_combine_bound_f32(yf, dst, wts, oracle.combine_f32(yf, dst, wts, _lib=libpath))
 
     for name, fn in [("golden_layout", golden_layout), ("golden_combine", golden_combine),
-                     ("combine_f32", combine_f32_pins),
+                     ("combine_f32", combine_f32_pins), ("bias", bias_pins),
                      ("bruteforce", bruteforce_and_invariants), ("argsort", argsort_mid),
                      ("dispatch", dispatch_pins), ("combine_bound", combine_bound),
                      ("identity", identity)]:
