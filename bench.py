@@ -231,7 +231,7 @@ def main():
         B.ep_dispatch(x, xs, None, dst, w.T, w.H, w.K, w.dtype, w.cap, expand, expand_s, None, stream)
         if ev is not None:
             ev[2].record(stream)
-        B.ep_combine(y, wts, dst, w.T, w.H, w.K, B.EP_BF16, w.cap, out, stream)
+        B.ep_combine(y, wts, None, dst, w.T, w.H, w.K, B.EP_BF16, w.cap, out, stream)
         if ev is not None:
             ev[3].record(stream)
 

@@ -63,7 +63,7 @@ def lib(path: str = None) -> ctypes.CDLL:
     L.ep_layout.restype = ctypes.c_int
     L.ep_dispatch.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp]
     L.ep_dispatch.restype = ctypes.c_int
-    L.ep_combine.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp]
+    L.ep_combine.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp]
     L.ep_combine.restype = ctypes.c_int
     L.ep_last_error.argtypes = []
     L.ep_last_error.restype = ctypes.c_char_p
@@ -125,7 +125,7 @@ def ep_dispatch(x, x_scales, topk_weights, dst_slot, num_tokens, hidden, topk, d
                              _p(expand_weights), _s(stream)))
 
 
-def ep_combine(expert_out, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,
+def ep_combine(expert_out, topk_weights, bias, dst_slot, num_tokens, hidden, topk, dtype,
                capacity_rows, out, stream=None):
-    _check(lib().ep_combine(_p(expert_out), _p(topk_weights), _p(dst_slot), num_tokens, hidden,
-                            topk, dtype, capacity_rows, _p(out), _s(stream)))
+    _check(lib().ep_combine(_p(expert_out), _p(topk_weights), _p(bias), _p(dst_slot), num_tokens,
+                            hidden, topk, dtype, capacity_rows, _p(out), _s(stream)))

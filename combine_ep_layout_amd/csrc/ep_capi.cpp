@@ -165,9 +165,9 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
   }
 }
 
-int ep_combine(const void *expert_out, const float *topk_weights, const int32_t *dst_slot,
-               int32_t num_tokens, int32_t hidden, int32_t topk, int32_t dtype,
-               int64_t capacity_rows, void *out, void *stream) {
+int ep_combine(const void *expert_out, const float *topk_weights, const void *bias,
+               const int32_t *dst_slot, int32_t num_tokens, int32_t hidden, int32_t topk,
+               int32_t dtype, int64_t capacity_rows, void *out, void *stream) {
   try {
     const char *what = "ep_combine";
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
@@ -182,13 +182,13 @@ int ep_combine(const void *expert_out, const float *topk_weights, const int32_t 
     if (capacity_rows < 0) return fail(EP_EINVAL, "%s: capacity_rows must be >= 0", what);
     if (num_tokens > 0 && (!expert_out || !dst_slot || !out))
       return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
-    if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(dst_slot, 4) ||
-        !aligned(topk_weights, 4))
+    if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(bias, 16) ||
+        !aligned(dst_slot, 4) || !aligned(topk_weights, 4))
       return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
     if (!ep::has_combine(hidden, topk, dtype))
       return fail(EP_EUNSUPPORTED, "%s: (hidden %d, topk %d, dtype %d) has no compiled kernel",
                   what, hidden, topk, dtype);
-    ep::CombineArgs a{expert_out, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,
+    ep::CombineArgs a{expert_out, topk_weights, bias, dst_slot, num_tokens, hidden, topk, dtype,
                       capacity_rows, out, (hipStream_t)stream};
     return from_launch(ep::launch_combine(a), what);
   } catch (const std::exception &e) {

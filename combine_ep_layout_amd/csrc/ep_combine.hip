@@ -1,10 +1,11 @@
-// Gather combine for gfx950: out[t] = bf16( sum_k w[t,k] * y[dst_slot[t,k]] )
-// with binary32 accumulation in k order and a round-to-nearest-even store.
+// Gather combine for gfx950: out[t] = sum_k w[t,k] * y[dst_slot[t,k]] (+ bias[t])
+// with binary32 accumulation in k order, the bias added last, and a store in
+// the rows' type (bf16: round to nearest even).
 //
 // Follows the DeepEP overall-architecture page, combine data-flow figure
-// (the reduce epilogue weights each expert output by topk_weights and sums
-// back into token order; no bias here) and "MORI JIT v2", section 3.7
-// (combine reduces bf16 rows; byte dtypes are rejected upstream).
+// (the reduce epilogue weights each expert output by topk_weights, adds a
+// bias and writes back in token order) and "MORI JIT v2", section 3.7
+// (combine reduces bf16 or fp32 rows; byte dtypes are rejected upstream).
 //
 // Design (MI355X): HBM-bound (read T*K rows, write T rows, about 1 flop per
 // byte). A token's row is cut into slices of two 16-byte chunks per lane
@@ -122,10 +123,11 @@ __device__ __forceinline__ void gather_fold(const u32x4 *__restrict__ y, const i
   }
 }
 
-template <int DT, int H, int K>
+template <int DT, int H, int K, bool BIAS>
 __global__ __launch_bounds__(kThreads) void ep_combine_gather(
     const u32x4 *__restrict__ y, const float *__restrict__ topk_weights,
-    const int32_t *__restrict__ dst_slot, int T, int64_t capacity, u32x4 *__restrict__ out) {
+    const u32x4 *__restrict__ bias, const int32_t *__restrict__ dst_slot, int T,
+    int64_t capacity, u32x4 *__restrict__ out) {
   constexpr int CH = H * Elem<DT>::BYTES / 16;  // 16-byte chunks per row
   constexpr int PC = Elem<DT>::PER_CHUNK;
   using Geo = CombineGeometry<CH>;
@@ -166,7 +168,15 @@ __global__ __launch_bounds__(kThreads) void ep_combine_gather(
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int i = (c0 + g) * kWave + lane;
-      if (CH % kWave == 0 || i < CH) __builtin_nontemporal_store(Elem<DT>::put(acc[g]), o + i);
+      if (CH % kWave == 0 || i < CH) {
+        if constexpr (BIAS) {  // added once, after the k-order sum
+#pragma clang fp contract(off)
+          const u32x4 b = bias[(int64_t)t * CH + i];
+#pragma unroll
+          for (int j = 0; j < PC; ++j) acc[g][j] = acc[g][j] + Elem<DT>::get(b, j);
+        }
+        __builtin_nontemporal_store(Elem<DT>::put(acc[g]), o + i);
+      }
     }
   }
 }
@@ -177,8 +187,14 @@ int combine_impl(const CombineArgs &a) {
   constexpr int SPLIT = CombineGeometry<H * Elem<DT>::BYTES / 16>::SPLIT;
   const int64_t waves = (int64_t)a.T * SPLIT;
   const int blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-  ep_combine_gather<DT, H, K><<<blocks, kThreads, 0, a.stream>>>(
-      (const u32x4 *)a.y, a.topk_weights, a.dst_slot, a.T, a.capacity, (u32x4 *)a.out);
+  if (a.bias)
+    ep_combine_gather<DT, H, K, true><<<blocks, kThreads, 0, a.stream>>>(
+        (const u32x4 *)a.y, a.topk_weights, (const u32x4 *)a.bias, a.dst_slot, a.T, a.capacity,
+        (u32x4 *)a.out);
+  else
+    ep_combine_gather<DT, H, K, false><<<blocks, kThreads, 0, a.stream>>>(
+        (const u32x4 *)a.y, a.topk_weights, nullptr, a.dst_slot, a.T, a.capacity,
+        (u32x4 *)a.out);
   return launch_status();
 }
 

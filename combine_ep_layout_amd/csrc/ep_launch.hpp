@@ -43,6 +43,7 @@ struct DispatchArgs {
 struct CombineArgs {
   const void *y;
   const float *topk_weights;
+  const void *bias;
   const int32_t *dst_slot;
   int T, H, K, dtype;
   int64_t capacity;

@@ -152,14 +152,15 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
 
 /*
  * Gather combine (DeepEP overall architecture, combine reduce epilogue
- * weighting expert outputs by topk_weights; "MORI JIT v2", section 3.7:
- * combine reduces bf16 or fp32 rows, writes the same type, and rejects byte
- * dtypes). No bias term.
+ * weighting expert outputs by topk_weights and adding a bias; "MORI JIT v2",
+ * section 3.7: combine reduces bf16 or fp32 rows, writes the same type, and
+ * rejects byte dtypes).
  *
  * For every token t and channel h:
  *   acc = +0.0f
  *   for k = 0 .. K-1 with 0 <= dst_slot[t, k] < capacity_rows:
  *       acc = acc + w[t, k] * float(expert_out[dst_slot[t, k], h])
+ *   if bias: acc = acc + float(bias[t, h])
  *   out[t, h] = acc stored as dtype (bf16: round to nearest even)
  * Each product and each sum is rounded to binary32 on its own (no fused
  * multiply-add), in k order, so the result is a pure function of the inputs.
@@ -167,14 +168,15 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
  *
  *   expert_out      [capacity_rows, hidden] of dtype EP_BF16 or EP_FP32
  *   topk_weights    fp32 [T, K] or NULL
+ *   bias            [T, hidden] of the same dtype, or NULL
  *   dst_slot        int32 [T, K]
  *   out             [T, hidden] of the same dtype; every row is written
  * Errors: EP_EINVAL for a byte dtype (fp8 / fp4x2), NULL or misaligned
  * pointers; EP_EUNSUPPORTED for (hidden, topk, dtype) outside the compiled set.
  */
-int ep_combine(const void *expert_out, const float *topk_weights, const int32_t *dst_slot,
-               int32_t num_tokens, int32_t hidden, int32_t topk, int32_t dtype,
-               int64_t capacity_rows, void *out, void *stream);
+int ep_combine(const void *expert_out, const float *topk_weights, const void *bias,
+               const int32_t *dst_slot, int32_t num_tokens, int32_t hidden, int32_t topk,
+               int32_t dtype, int64_t capacity_rows, void *out, void *stream);
 
 /* Message for the last failed call on the calling thread ("" if none). */
 const char *ep_last_error(void);

@@ -85,9 +85,9 @@ class DeviceCase:
                       w.H, w.K, w.dtype, w.cap, self.expand_x, self.expand_s,
                       self.expand_w if weights else None, stream)
 
-    def combine(self, y=None, weights=True, stream=None):
+    def combine(self, y=None, weights=True, bias=None, stream=None):
         w = self.w
-        B.ep_combine(self.y if y is None else y, self.wts if weights else None,
+        B.ep_combine(self.y if y is None else y, self.wts if weights else None, bias,
                      self.lay["dst_slot"], w.T, self.H_out, w.K, w.out_dtype, w.cap, self.out,
                      stream)
         return self.out[:w.T]

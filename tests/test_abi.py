@@ -125,8 +125,8 @@ def test_dispatch_rejections(L):
     assert _code(B.ep_dispatch, *disp(K=5)) == B.EP_EUNSUPPORTED
 
 
-def comb(y=FAKE, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280, out=FAKE):
-    return (y, None, dst, T, H, K, dt, cap, out)
+def comb(y=FAKE, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280, out=FAKE, bias=None):
+    return (y, None, bias, dst, T, H, K, dt, cap, out)
 
 
 def test_combine_rejections(L):
@@ -137,5 +137,6 @@ def test_combine_rejections(L):
     assert _code(B.ep_combine, *comb(H=7172)) == B.EP_EINVAL
     assert _code(B.ep_combine, *comb(H=7176)) == B.EP_EUNSUPPORTED
     assert _code(B.ep_combine, *comb(out=ODD)) == B.EP_EINVAL
+    assert _code(B.ep_combine, *comb(bias=ODD)) == B.EP_EINVAL
     assert _code(B.ep_combine, *comb(y=None)) == B.EP_EINVAL
     assert _code(B.ep_combine, *comb(K=0)) == B.EP_EINVAL

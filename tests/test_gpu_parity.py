@@ -136,7 +136,7 @@ def test_empty_input():
     h = layout_to_host(lay)
     assert np.all(h["counts"] == 0) and np.all(h["offsets"] == 0) and h["num_recv"] == 0
     B.ep_dispatch(None, None, None, None, 0, 256, 2, B.EP_BF16, 0, None, None, None)
-    B.ep_combine(None, None, None, 0, 256, 2, B.EP_BF16, 0, None)
+    B.ep_combine(None, None, None, None, 0, 256, 2, B.EP_BF16, 0, None)
 
 
 def test_out_of_range_and_duplicate_ids():
@@ -201,7 +201,7 @@ def test_combine_hand_worked_on_gpu():
         T, K = dst.shape
         wts = None if wts_h is None else to_dev(wts_h)
         out = torch.full((T, H), 0x7FC1, dtype=torch.int16, device="cuda:0")
-        B.ep_combine(to_dev(rows), wts, to_dev(dst), T, H, K, B.EP_BF16, rows.shape[0], out)
+        B.ep_combine(to_dev(rows), wts, None, to_dev(dst), T, H, K, B.EP_BF16, rows.shape[0], out)
         torch.cuda.synchronize()
         got = to_host(out, np.uint16)
         exp = np.array([[int(v, 16) for v in r] for r in c["out_hex"]], np.uint16)
@@ -225,7 +225,7 @@ def test_combine_rounding_ties_and_specials():
     y[1::2, 17] = 0xFF80
     dst = np.arange(cap, dtype=np.int32).reshape(T, K)
     out = torch.zeros((T, H), dtype=torch.int16, device="cuda:0")
-    B.ep_combine(to_dev(y), None, to_dev(dst), T, H, K, B.EP_BF16, cap, out)
+    B.ep_combine(to_dev(y), None, None, to_dev(dst), T, H, K, B.EP_BF16, cap, out)
     torch.cuda.synchronize()
     got = to_host(out, np.uint16)
     ref = oracle.combine(y, dst, None)
@@ -272,3 +272,89 @@ def test_dtype_variants(T, H, E, K, A, dtype, scales, out_dtype):
     else:
         check_combine(to_host(out, np.uint16), oracle.combine(case.y, ref["dst_slot"], case.topk_weights),
                       w.name)
+
+
+def test_combine_with_bias():
+    """Combine adds a per-token bias once, after the k-order sum (bf16 and fp32)."""
+    data = json.load(open(os.path.join(GOLDEN, "combine_worked_examples.json")))
+    c = data["combine_bias"][0]
+    H = 256
+    rows = np.zeros((2, H), np.uint16)
+    bias = np.zeros((1, H), np.uint16)
+    for r, row in enumerate(c["y_rows_hex"]):
+        rows[r, :8] = [int(v, 16) for v in row]
+    bias[0, :8] = [int(v, 16) for v in c["bias_hex"][0]]
+    dst = np.array([[0, 1]], np.int32)
+    out = torch.zeros((1, H), dtype=torch.int16, device="cuda:0")
+    B.ep_combine(to_dev(rows), None, to_dev(bias), to_dev(dst), 1, H, 2, B.EP_BF16, 2, out)
+    torch.cuda.synchronize()
+    got = to_host(out, np.uint16)
+    assert np.array_equal(got[0, :8], [int(v, 16) for v in c["out_hex"][0]])
+    for out_dtype in (I.BF16, I.FP32):
+        w = I.custom(f"bias{out_dtype}", 61, 1500, 2048, 64, 8, 2, I.BF16, "uniform",
+                     out_dtype=out_dtype)
+        case = I.make_case(w, mask_frac=0.02)
+        ref = oracle.layout(case.topk_idx, w.E, w.A)
+        dc = DeviceCase(case)
+        dc.layout()
+        if out_dtype == I.BF16:
+            bias = I.normal_bf16(w.seed, 9, w.T, w.H)
+            out = dc.combine(bias=to_dev(bias))
+            torch.cuda.synchronize()
+            check_combine(to_host(out, np.uint16),
+                          oracle.combine(case.y, ref["dst_slot"], case.topk_weights, bias), "bias")
+        else:
+            bias = I.normal_f32(w.seed, 9, w.T, w.H)
+            out = dc.combine(bias=to_dev(bias))
+            torch.cuda.synchronize()
+            exp = oracle.combine_f32(case.y, ref["dst_slot"], case.topk_weights, bias)
+            assert np.array_equal(to_host(out).view(np.uint32), exp.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["prefill_aligned", "mori_default"])
+def test_graph_capture_replay(name):
+    """layout -> dispatch -> combine captured into one HIP graph (nothing on the path allocates,
+    synchronises or records a memset); every replay, with eager steps in between, matches eager."""
+    w = I.WORKLOADS[name]
+    case = I.make_case(w)
+    dev = "cuda:0"
+    idx, wts, x, y = to_dev(case.topk_idx), to_dev(case.topk_weights), to_dev(case.x), to_dev(case.y)
+    counts = torch.zeros(w.E, dtype=torch.int32, device=dev)
+    offs = torch.zeros(w.E + 1, dtype=torch.int32, device=dev)
+    dst = torch.zeros((w.T, w.K), dtype=torch.int32, device=dev)
+    meta = torch.zeros((w.T, w.K + 2), dtype=torch.int32, device=dev)
+    nrecv = torch.zeros(1, dtype=torch.int32, device=dev)
+    wsb = B.ep_layout_workspace_bytes(w.T, w.K, w.E)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+    X = torch.zeros((w.cap, w.H), dtype=torch.int16, device=dev)
+    out = torch.zeros((w.T, w.H), dtype=torch.int16, device=dev)
+
+    def step(stream):
+        B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offs, dst, meta, nrecv, ws, wsb, stream)
+        B.ep_dispatch(x, None, None, dst, w.T, w.H, w.K, B.EP_BF16, w.cap, X, None, None, stream)
+        B.ep_combine(y, wts, None, dst, w.T, w.H, w.K, B.EP_BF16, w.cap, out, stream)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    outs = (counts, offs, dst, meta, nrecv, X, out)
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for r in range(4):
+        for t in outs:
+            t.zero_()  # a fill kernel outside the graph, so every replay must rewrite everything
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), f"replay {r} differs from eager"
+        step(torch.cuda.current_stream())  # eager work between replays
+        torch.cuda.synchronize()
