@@ -43,6 +43,9 @@ def lib(path: str = None):
         L.oracle_combine_f32.argtypes = [_f32p, ctypes.c_int32, _f32p, _f32p, _i32p, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int64, _f32p]
         L.oracle_combine_f32.restype = ctypes.c_int
+        L.oracle_zero_padding.argtypes = [_u8p, ctypes.c_int64, _u8p, ctypes.c_int64, _f32p, _i32p,
+                                          _i32p, ctypes.c_int32, ctypes.c_int64]
+        L.oracle_zero_padding.restype = ctypes.c_int
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -121,6 +124,22 @@ def dispatch(x_bytes: np.ndarray, dst_slot: np.ndarray, capacity_rows: int,
                                _ptr(expand_weights if w is not None else None, _f32p))
     if rc != 0:
         raise ValueError("oracle_dispatch rejected its arguments")
+    return expand_x, expand_scales, expand_weights
+
+
+def zero_padding(expand_x: np.ndarray, counts: np.ndarray, offsets: np.ndarray,
+                 expand_scales: np.ndarray = None, expand_weights: np.ndarray = None, _lib=None):
+    """Zero the alignment padding rows of the expand buffers in place (and return them)."""
+    cap = expand_x.shape[0]
+    ex = expand_x.view(np.uint8).reshape(cap, -1)
+    es = None if expand_scales is None else expand_scales.view(np.uint8).reshape(cap, -1)
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    o = np.ascontiguousarray(offsets, dtype=np.int32)
+    rc = lib(_lib).oracle_zero_padding(_ptr(ex, _u8p), ex.shape[1], _ptr(es, _u8p),
+                                       0 if es is None else es.shape[1], _ptr(expand_weights, _f32p),
+                                       _ptr(c, _i32p), _ptr(o, _i32p), c.size, cap)
+    if rc != 0:
+        raise ValueError("oracle_zero_padding rejected its arguments")
     return expand_x, expand_scales, expand_weights
 
 

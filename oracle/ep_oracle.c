@@ -179,6 +179,29 @@ int oracle_dispatch(const uint8_t *x, int64_t row_bytes, const uint8_t *x_scales
   return 0;
 }
 
+/*
+ * Optional clean-up of the expand layout: the alignment padding rows of each
+ * expert segment, [offsets[e] + counts[e], offsets[e+1]), are set to zero in
+ * expand_x (and in expand_scales / expand_weights when given), so a consumer
+ * that walks whole aligned segments reads zeros there. Real rows are not
+ * touched.
+ */
+int oracle_zero_padding(uint8_t *expand_x, int64_t row_bytes, uint8_t *expand_scales,
+                        int64_t scale_row_bytes, float *expand_weights,
+                        const int32_t *counts, const int32_t *offsets, int32_t E,
+                        int64_t capacity_rows) {
+  if (E < 1 || row_bytes < 0) return -1;
+  for (int32_t e = 0; e < E; ++e) {
+    for (int64_t r = (int64_t)offsets[e] + counts[e]; r < offsets[e + 1]; ++r) {
+      if (r >= capacity_rows) return -1;
+      memset(expand_x + r * row_bytes, 0, (size_t)row_bytes);
+      if (expand_scales) memset(expand_scales + r * scale_row_bytes, 0, (size_t)scale_row_bytes);
+      if (expand_weights) expand_weights[r] = 0.0f;
+    }
+  }
+  return 0;
+}
+
 /* ---------------------------------------------------------------------- */
 /* Combine: weighted gather-reduce back to token order.                    */
 /* ---------------------------------------------------------------------- */

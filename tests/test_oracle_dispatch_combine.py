@@ -226,3 +226,24 @@ def test_combine_bias_error_bound(oracle_mod, w):
     bf = np.random.default_rng(3).standard_normal((w.T, w.H)).astype(np.float32)
     out = oracle_mod.combine_f32(yf, lay["dst_slot"], case.topk_weights, bf)
     pins.check_combine_bound_f32(yf, lay["dst_slot"], case.topk_weights, out, bf)
+
+
+@pytest.mark.parametrize("w", [I.custom("zp1", 71, 300, 256, 16, 4, 8), I.custom("zp2", 72, 40, 512, 64, 2, 32),
+                               I.custom("zp3", 73, 100, 256, 8, 8, 1)], ids=lambda w: w.name)
+def test_zero_padding(oracle_mod, w):
+    """Exactly the padding rows [off[e] + count[e], off[e+1]) become zero (counts and offsets
+    from the library route, not the oracle); every other row keeps its bytes."""
+    idx = I.make_routing(w.routing, w.seed, w.T, w.E, w.K)
+    counts, offsets, _, _ = pins.layout_by_argsort(idx, w.E, w.A)
+    g = np.random.default_rng(w.seed)
+    X = g.integers(1, 256, (w.cap, w.H), dtype=np.uint8)
+    S = g.integers(1, 256, (w.cap, 16), dtype=np.uint8)
+    Wt = g.random(w.cap).astype(np.float32) + 1
+    before = (X.copy(), S.copy(), Wt.copy())
+    oracle_mod.zero_padding(X, counts, offsets, S, Wt)
+    pad = np.zeros(w.cap, bool)
+    for e in range(w.E):
+        pad[offsets[e] + counts[e]:offsets[e + 1]] = True
+    assert pad.sum() == offsets[-1] - counts.sum()
+    for a, b in zip((X, S, Wt), before):
+        assert np.all(a[pad] == 0) and np.array_equal(a[~pad], b[~pad])

@@ -54,6 +54,11 @@ MUTANTS = {
     "combine_bias_twice": ("float acc = 0.0f;", "float acc = bias ? bf16_bits_to_float(bias[(int64_t)t * H + h]) : 0.0f;", 0),
     "combine_f32_bias_dropped": ("      if (bias) acc = acc + bias[(int64_t)t * H + h];\n", ""),
     "combine_f32_bias_first": ("float acc = 0.0f;", "float acc = bias ? bias[(int64_t)t * H + h] : 0.0f;", 1),
+    "zero_padding_from_segment_start": ("for (int64_t r = (int64_t)offsets[e] + counts[e]; r < offsets[e + 1]; ++r) {",
+                                        "for (int64_t r = (int64_t)offsets[e]; r < offsets[e + 1]; ++r) {"),
+    "zero_padding_one_short": ("for (int64_t r = (int64_t)offsets[e] + counts[e]; r < offsets[e + 1]; ++r) {",
+                               "for (int64_t r = (int64_t)offsets[e] + counts[e]; r < offsets[e + 1] - 1; ++r) {"),
+    "zero_padding_weights_kept": ("      if (expand_weights) expand_weights[r] = 0.0f;\n", ""),
     "combine_f32_weight_k0": ("        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod",
                               "        float w = topk_weights ? topk_weights[(int64_t)t * K] : 1.0f;\n        float prod"),
 }
@@ -155,6 +160,21 @@ def _run_pins(libpath):
         pins.check_combine_bound(case.y, dst, case.topk_weights,
                                  oracle.combine(case.y, dst, case.topk_weights, bias, _lib=libpath), bias)
 
+    def zero_padding_pins():
+        wz = I.custom("mutzp", 79, 120, 256, 16, 4, 8)
+        idx = I.make_routing(wz.routing, wz.seed, wz.T, wz.E, wz.K)
+        counts, offsets, _, _ = pins.layout_by_argsort(idx, wz.E, wz.A)
+        g = np.random.default_rng(1)
+        X = g.integers(1, 256, (wz.cap, wz.H), dtype=np.uint8)
+        Wt = g.random(wz.cap).astype(np.float32) + 1
+        before = (X.copy(), Wt.copy())
+        oracle.zero_padding(X, counts, offsets, None, Wt, _lib=libpath)
+        pad = np.zeros(wz.cap, bool)
+        for e in range(wz.E):
+            pad[offsets[e] + counts[e]:offsets[e + 1]] = True
+        for a, b in zip((X, Wt), before):
+            assert np.all(a[pad] == 0) and np.array_equal(a[~pad], b[~pad])
+
     def combine_f32_pins():
         for c in comb_gold["combine_f32"]:
             out = oracle.combine_f32(np.array(c["y_rows"], np.float32), np.array(c["dst_slot"], np.int32),
@@ -166,6 +186,7 @@ def _run_pins(libpath):
 
     for name, fn in [("golden_layout", golden_layout), ("golden_combine", golden_combine),
                      ("combine_f32", combine_f32_pins), ("bias", bias_pins),
+                     ("zero_padding", zero_padding_pins),
                      ("bruteforce", bruteforce_and_invariants), ("argsort", argsort_mid),
                      ("dispatch", dispatch_pins), ("combine_bound", combine_bound),
                      ("identity", identity)]:
