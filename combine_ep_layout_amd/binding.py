@@ -28,7 +28,7 @@ EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 64
 
 SYMBOLS = ("ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
-           "ep_last_error", "ep_supported")
+           "ep_zero_padding", "ep_last_error", "ep_supported")
 
 
 class EpError(RuntimeError):
@@ -65,6 +65,8 @@ def lib(path: str = None) -> ctypes.CDLL:
     L.ep_dispatch.restype = ctypes.c_int
     L.ep_combine.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp]
     L.ep_combine.restype = ctypes.c_int
+    L.ep_zero_padding.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i64, _vp]
+    L.ep_zero_padding.restype = ctypes.c_int
     L.ep_last_error.argtypes = []
     L.ep_last_error.restype = ctypes.c_char_p
     L.ep_supported.argtypes = [_i32, _i32, _i32, _i32]
@@ -129,3 +131,10 @@ def ep_combine(expert_out, topk_weights, bias, dst_slot, num_tokens, hidden, top
                capacity_rows, out, stream=None):
     _check(lib().ep_combine(_p(expert_out), _p(topk_weights), _p(bias), _p(dst_slot), num_tokens,
                             hidden, topk, dtype, capacity_rows, _p(out), _s(stream)))
+
+
+def ep_zero_padding(expand_x, row_bytes, expand_scales, scale_cols, expand_weights, counts, offsets,
+                    num_experts, expert_alignment, capacity_rows, stream=None):
+    _check(lib().ep_zero_padding(_p(expand_x), row_bytes, _p(expand_scales), scale_cols,
+                                 _p(expand_weights), _p(counts), _p(offsets), num_experts,
+                                 expert_alignment, capacity_rows, _s(stream)))

@@ -198,4 +198,36 @@ int ep_combine(const void *expert_out, const float *topk_weights, const void *bi
   }
 }
 
+int ep_zero_padding(void *expand_x, int64_t row_bytes, float *expand_scales, int64_t scale_cols,
+                    float *expand_weights, const int32_t *counts, const int32_t *offsets,
+                    int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
+                    void *stream) {
+  try {
+    const char *what = "ep_zero_padding";
+    if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
+      return fail(EP_EINVAL, "%s: num_experts must be in 1..%d (got %d)", what, EP_MAX_EXPERTS,
+                  num_experts);
+    if (expert_alignment < 1)
+      return fail(EP_EINVAL, "%s: expert_alignment must be >= 1 (got %d)", what, expert_alignment);
+    if (row_bytes < 16 || row_bytes % 16 != 0)
+      return fail(EP_EINVAL, "%s: row_bytes must be a positive multiple of 16 (got %lld)", what,
+                  (long long)row_bytes);
+    if (capacity_rows < 0 || scale_cols < 0)
+      return fail(EP_EINVAL, "%s: capacity_rows and scale_cols must be >= 0", what);
+    if (!expand_x || !counts || !offsets || (scale_cols > 0 && !expand_scales))
+      return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
+    if (!aligned(expand_x, 16) || !aligned(expand_scales, 4) || !aligned(expand_weights, 4) ||
+        !aligned(counts, 4) || !aligned(offsets, 4))
+      return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
+    ep::ZeroPaddingArgs a{expand_x, row_bytes, scale_cols > 0 ? expand_scales : nullptr,
+                          scale_cols, expand_weights, counts, offsets, num_experts,
+                          expert_alignment, capacity_rows, (hipStream_t)stream};
+    return from_launch(ep::launch_zero_padding(a), what);
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_zero_padding: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_zero_padding: unknown exception");
+  }
+}
+
 }  // extern "C"

@@ -51,6 +51,18 @@ struct CombineArgs {
   hipStream_t stream;
 };
 
+struct ZeroPaddingArgs {
+  void *expand_x;
+  int64_t row_bytes;
+  float *expand_scales;
+  int64_t scale_cols;
+  float *expand_weights;
+  const int32_t *counts, *offsets;
+  int E, A;
+  int64_t capacity;
+  hipStream_t stream;
+};
+
 // HIP error of the last failed launch on this thread (set by launch_status).
 hipError_t &last_hip_error();
 
@@ -68,6 +80,7 @@ int launch_layout(const LayoutArgs &a);
 size_t layout_workspace(int T, int K, int E);
 int launch_dispatch(const DispatchArgs &a);
 int launch_combine(const CombineArgs &a);
+int launch_zero_padding(const ZeroPaddingArgs &a);
 
 bool has_layout(int K);
 bool has_dispatch(int H, int K, int dtype);

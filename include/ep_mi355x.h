@@ -178,6 +178,26 @@ int ep_combine(const void *expert_out, const float *topk_weights, const void *bi
                const int32_t *dst_slot, int32_t num_tokens, int32_t hidden, int32_t topk,
                int32_t dtype, int64_t capacity_rows, void *out, void *stream);
 
+/*
+ * Optional clean-up of the expand layout: zero the alignment padding rows of
+ * every expert segment, rows [offsets[e] + counts[e], offsets[e+1]), so a
+ * consumer that walks whole aligned segments (DeepEP overall architecture,
+ * EPHandle expert_alignment; the pages leave padding content open and
+ * ep_dispatch does not write it) reads zeros there. Real rows are untouched.
+ *
+ *   expand_x        [capacity_rows, row_bytes] bytes (row_bytes a positive multiple of 16)
+ *   expand_scales   fp32 [capacity_rows, scale_cols], or NULL with scale_cols = 0
+ *   expand_weights  fp32 [capacity_rows] or NULL
+ *   counts, offsets int32 [E] and [E+1] as written by ep_layout (device)
+ *   expert_alignment the A given to ep_layout (A = 1: nothing to do)
+ * Rows at or beyond capacity_rows are never written. Errors: EP_EINVAL for
+ * out-of-range scalars, NULL or misaligned pointers.
+ */
+int ep_zero_padding(void *expand_x, int64_t row_bytes, float *expand_scales, int64_t scale_cols,
+                    float *expand_weights, const int32_t *counts, const int32_t *offsets,
+                    int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
+                    void *stream);
+
 /* Message for the last failed call on the calling thread ("" if none). */
 const char *ep_last_error(void);
 

@@ -140,3 +140,19 @@ def test_combine_rejections(L):
     assert _code(B.ep_combine, *comb(bias=ODD)) == B.EP_EINVAL
     assert _code(B.ep_combine, *comb(y=None)) == B.EP_EINVAL
     assert _code(B.ep_combine, *comb(K=0)) == B.EP_EINVAL
+
+
+def test_zero_padding_rejections(L):
+    ok = dict(x=FAKE, rb=14336, s=None, sc=0, w=None, c=FAKE, o=FAKE, E=256, A=128, cap=65280)
+
+    def zp(**kw):
+        a = {**ok, **kw}
+        return (a["x"], a["rb"], a["s"], a["sc"], a["w"], a["c"], a["o"], a["E"], a["A"], a["cap"])
+    assert _code(B.ep_zero_padding, *zp(rb=14330)) == B.EP_EINVAL
+    assert _code(B.ep_zero_padding, *zp(rb=0)) == B.EP_EINVAL
+    assert _code(B.ep_zero_padding, *zp(E=0)) == B.EP_EINVAL
+    assert _code(B.ep_zero_padding, *zp(A=0)) == B.EP_EINVAL
+    assert _code(B.ep_zero_padding, *zp(x=None)) == B.EP_EINVAL
+    assert _code(B.ep_zero_padding, *zp(x=ODD)) == B.EP_EINVAL
+    assert _code(B.ep_zero_padding, *zp(sc=56)) == B.EP_EINVAL          # scale columns without a pointer
+    assert _code(B.ep_zero_padding, *zp(c=None)) == B.EP_EINVAL

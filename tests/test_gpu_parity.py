@@ -358,3 +358,30 @@ def test_graph_capture_replay(name):
             assert torch.equal(a, b), f"replay {r} differs from eager"
         step(torch.cuda.current_stream())  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,H,E,K,A,dtype", [(4096, 256, 256, 8, 128, I.BF16),
+                                              (700, 512, 64, 4, 16, I.FP8_E4M3),
+                                              (300, 1024, 16, 2, 1, I.BF16)])
+def test_zero_padding_after_dispatch(T, H, E, K, A, dtype):
+    """Whole expand buffers (rows, scale rows, weights) match the oracle after dispatch + zero-fill."""
+    w = I.custom(f"zp{T}", 4000 + T, T, H, E, K, A, dtype, "uniform")
+    case = I.make_case(w, with_y=False)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case, with_y=False)
+    dc.layout()
+    dc.dispatch()
+    S = 0 if dc.expand_s is None else dc.expand_s.shape[1]
+    B.ep_zero_padding(dc.expand_x, dc.row_bytes, dc.expand_s, S, dc.expand_w, dc.lay["counts"],
+                      dc.lay["offsets"], w.E, w.A, w.cap)
+    torch.cuda.synchronize()
+    X = np.full((w.cap, dc.row_bytes), dc.sentinel, np.uint8)
+    Xs = None if S == 0 else np.full((w.cap, S), -3.0, np.float32)
+    Xw = np.full(w.cap, -5.0, np.float32)
+    oracle.dispatch(case.x, ref["dst_slot"], w.cap, x_scales=case.x_scales,
+                    topk_weights=case.topk_weights, expand_x=X, expand_scales=Xs, expand_weights=Xw)
+    oracle.zero_padding(X, ref["counts"], ref["offsets"], Xs, Xw)
+    assert np.array_equal(to_host(dc.expand_x), X)
+    assert np.array_equal(to_host(dc.expand_w).view(np.uint32), Xw.view(np.uint32))
+    if Xs is not None:
+        assert np.array_equal(to_host(dc.expand_s).view(np.uint32), Xs.view(np.uint32))
