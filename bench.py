@@ -38,14 +38,25 @@ KERNEL_SOURCES = ["combine_ep_layout_amd/csrc/ep_dispatch.hip",
                   "combine_ep_layout_amd/csrc/ep_device.hpp"]
 
 
+ELT_BYTES = {0: 2, 1: 4, 2: 1, 3: 1}  # bf16, fp32, fp8, fp4x2 (hidden counts bytes)
+DTYPE_NAMES = {0: "bf16", 1: "f32", 2: "fp8_e4m3", 3: "fp4x2"}
+
+
+def geometry(w):
+    """Row bytes moved by dispatch (payload + scale row) and combine's row width and element size."""
+    values = 2 * w.H if w.dtype == 3 else w.H
+    scale_cols = values // 128 if (w.dtype in (2, 3) and w.scales) else 0
+    row_in = w.H * ELT_BYTES[w.dtype] + 4 * scale_cols
+    H_out = values  # combine sees one value per element
+    return row_in, scale_cols, H_out, ELT_BYTES[w.out_dtype]
+
+
 def algorithmic_bytes(w, n_valid: int, n_recv: int) -> dict:
     """Bytes each pass must move at minimum (padding rows are never touched)."""
-    elt = 1 if w.dtype == 2 else 2
-    S = w.H // 128
-    row_in = w.H * elt + (4 * S if w.dtype == 2 else 0)  # payload (+ fp8 scales)
+    row_in, _, H_out, elt_out = geometry(w)
     L = w.T * w.K * 4 + 4 * w.E + 4 * (w.E + 1) + w.T * w.K * 4 + n_recv * (w.K + 2) * 4 + 4
     D = w.T * row_in + n_valid * row_in + w.T * w.K * 4
-    C = n_valid * w.H * 2 + w.T * w.H * 2 + w.T * w.K * 8
+    C = n_valid * H_out * elt_out + w.T * H_out * elt_out + w.T * w.K * 8
     return {"layout": L, "dispatch": D, "combine": C}
 
 
@@ -136,7 +147,8 @@ def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 5):
     w = case.w
     rowb = case.x.view(np.uint8).reshape(w.T, -1).shape[1]
     expand = np.zeros((w.cap, rowb), np.uint8)
-    expand_s = np.zeros((w.cap, w.H // 128 * 4), np.uint8) if case.x_scales is not None else None
+    expand_s = (np.zeros((w.cap, case.x_scales.shape[1] * 4), np.uint8)
+                if case.x_scales is not None else None)
     times = []
     t_start = time.perf_counter()
     while len(times) < max_reps and (len(times) < 2 or time.perf_counter() - t_start < budget_s):
@@ -144,7 +156,10 @@ def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 5):
         lay = oracle.layout(case.topk_idx, w.E, w.A)
         oracle.dispatch(case.x, lay["dst_slot"], w.cap, x_scales=case.x_scales,
                         expand_x=expand, expand_scales=expand_s)
-        oracle.combine(case.y, lay["dst_slot"], case.topk_weights)
+        if w.out_dtype == 1:
+            oracle.combine_f32(case.y, lay["dst_slot"], case.topk_weights)
+        else:
+            oracle.combine(case.y, lay["dst_slot"], case.topk_weights)
         times.append(time.perf_counter() - t0)
     n_valid = int((lay["dst_slot"] >= 0).sum())
     b = algorithmic_bytes(w, n_valid, lay["num_recv"])
@@ -191,7 +206,7 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = I.WORKLOADS[args.workload]
+    w = {**I.WORKLOADS, **I.EXTRA_WORKLOADS}[args.workload]
     print(f"# workload {w.name}: T={w.T} H={w.H} E={w.E} K={w.K} A={w.A} dtype={w.dtype} "
           f"cap={w.cap}", file=sys.stderr, flush=True)
     case = I.make_case(w)
@@ -203,6 +218,7 @@ def main():
     idx, wts, x, y = up(case.topk_idx), up(case.topk_weights), up(case.x), up(case.y)
     xs = up(case.x_scales) if case.x_scales is not None else None
     rowb = case.x.view(np.uint8).reshape(w.T, -1).shape[1]
+    _, scale_cols, H_out, _ = geometry(w)
     counts = torch.empty(w.E, dtype=torch.int32, device=dev)
     offsets = torch.empty(w.E + 1, dtype=torch.int32, device=dev)
     dst = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
@@ -211,8 +227,10 @@ def main():
     wsb = B.ep_layout_workspace_bytes(w.T, w.K, w.E)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     expand = torch.zeros((w.cap, rowb), dtype=torch.uint8, device=dev)
-    expand_s = torch.zeros((w.cap, w.H // 128), dtype=torch.float32, device=dev) if xs is not None else None
-    out = torch.empty((w.T, w.H), dtype=torch.int16, device=dev)
+    expand_s = (torch.zeros((w.cap, scale_cols), dtype=torch.float32, device=dev)
+                if xs is not None else None)
+    out = torch.empty((w.T, H_out), dtype=torch.float32 if w.out_dtype == 1 else torch.int16,
+                      device=dev)
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
         a = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
@@ -231,7 +249,7 @@ def main():
         B.ep_dispatch(x, xs, None, dst, w.T, w.H, w.K, w.dtype, w.cap, expand, expand_s, None, stream)
         if ev is not None:
             ev[2].record(stream)
-        B.ep_combine(y, wts, None, dst, w.T, w.H, w.K, B.EP_BF16, w.cap, out, stream)
+        B.ep_combine(y, wts, None, dst, w.T, H_out, w.K, w.out_dtype, w.cap, out, stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -262,10 +280,15 @@ def main():
     rows = ref["dst_slot"][sample]
     got_rows = expand[torch.from_numpy(rows.ravel().astype(np.int64)).to(dev)].cpu().numpy()
     ok = ok and np.array_equal(got_rows, np.repeat(xb[sample], w.K, axis=0))
-    ref_out = oracle.combine(case.y, ref["dst_slot"][sample], case.topk_weights[sample])
-    got_out = out.cpu().numpy().view(np.uint16)[sample]
-    ordered = lambda b: np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)  # noqa: E731
-    ok = ok and np.abs(ordered(got_out.astype(np.int32)) - ordered(ref_out.astype(np.int32))).max() <= 1
+    if w.out_dtype == 1:
+        ref_out = oracle.combine_f32(case.y, ref["dst_slot"][sample], case.topk_weights[sample])
+        ok = ok and np.array_equal(out.cpu().numpy()[sample].view(np.uint32), ref_out.view(np.uint32))
+    else:
+        ref_out = oracle.combine(case.y, ref["dst_slot"][sample], case.topk_weights[sample])
+        got_out = out.cpu().numpy().view(np.uint16)[sample]
+        ordered = lambda b: np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)  # noqa: E731
+        ok = ok and np.abs(ordered(got_out.astype(np.int32))
+                           - ordered(ref_out.astype(np.int32))).max() <= 1
     if not ok:
         print("bench: GPU results do not match the oracle; refusing to report", file=sys.stderr)
         sys.exit(1)
@@ -293,10 +316,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8" if w.dtype == 2 else "bf16",
+        "dtype": DTYPE_NAMES[w.dtype] if w.out_dtype == 0 else
+                 f"{DTYPE_NAMES[w.dtype]}->{DTYPE_NAMES[w.out_dtype]}",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "hidden": w.H, "experts": w.E, "topk": w.K,
                    "expert_alignment": w.A, "capacity_rows": w.cap, "routing": w.routing,
+                   "dispatch_dtype": DTYPE_NAMES[w.dtype], "combine_dtype": DTYPE_NAMES[w.out_dtype],
                    "parallelism": "one GPU, all experts local"},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(w.T / (ms_per_step * 1e-3), 1),

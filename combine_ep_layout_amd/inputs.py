@@ -65,6 +65,16 @@ WORKLOADS = {
 }
 
 
+# The same prefill shape with the other transport / reduction types: fp4x2 rows
+# (3584 bytes = 7168 e2m1 values, 56 scales per token) and binary32 expert
+# outputs for combine.
+EXTRA_WORKLOADS = {
+    "prefill_fp4x2": Workload("prefill_fp4x2", 6, 4096, 3584, 256, 8, 128, FP4X2, "uniform"),
+    "prefill_fp32_combine": Workload("prefill_fp32_combine", 7, 4096, 7168, 256, 8, 128, BF16,
+                                     "uniform", out_dtype=FP32),
+}
+
+
 def capacity_rows(T: int, K: int, E: int, A: int) -> int:
     """Worst-case expand-buffer rows: every (t, k) real plus full padding per expert."""
     return T * K + E * (A - 1)
