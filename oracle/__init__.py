@@ -43,6 +43,13 @@ def lib(path: str = None):
         L.oracle_combine_f32.argtypes = [_f32p, ctypes.c_int32, _f32p, _f32p, _i32p, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int64, _f32p]
         L.oracle_combine_f32.restype = ctypes.c_int
+        L.oracle_dispatch_compact.argtypes = [_u8p, ctypes.c_int64, _u8p, ctypes.c_int64, _i32p, _f32p,
+                                              _i32p, _i32p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, _u8p, _u8p, _i32p, _f32p]
+        L.oracle_dispatch_compact.restype = ctypes.c_int
+        L.oracle_combine_compact.argtypes = [_u16p, ctypes.c_int32, _u16p, _i32p, _i32p, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, _u16p]
+        L.oracle_combine_compact.restype = ctypes.c_int
         L.oracle_zero_padding.argtypes = [_u8p, ctypes.c_int64, _u8p, ctypes.c_int64, _f32p, _i32p,
                                           _i32p, ctypes.c_int32, ctypes.c_int64]
         L.oracle_zero_padding.restype = ctypes.c_int
@@ -125,6 +132,53 @@ def dispatch(x_bytes: np.ndarray, dst_slot: np.ndarray, capacity_rows: int,
     if rc != 0:
         raise ValueError("oracle_dispatch rejected its arguments")
     return expand_x, expand_scales, expand_weights
+
+
+def dispatch_compact(x_bytes: np.ndarray, topk_idx: np.ndarray, dst_slot: np.ndarray,
+                     recv_src_metadata: np.ndarray, num_recv: int, x_scales: np.ndarray = None,
+                     topk_weights: np.ndarray = None, _lib=None):
+    """Non-expand dispatch: (recv_x bytes [num_recv, row_bytes], recv_scales bytes or None,
+    recv_topk_idx int32 [num_recv, K], recv_topk_weights float32 or None)."""
+    xb = np.ascontiguousarray(x_bytes).view(np.uint8)
+    T = xb.shape[0]
+    xb = xb.reshape(T, -1)
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
+    K = dst.shape[1]
+    meta = np.ascontiguousarray(recv_src_metadata, dtype=np.int32).reshape(-1, K + 2)
+    n = int(num_recv)
+    rx = np.zeros((n, xb.shape[1]), np.uint8)
+    xs = rs = None
+    if x_scales is not None:
+        xs = np.ascontiguousarray(x_scales).view(np.uint8).reshape(T, -1)
+        rs = np.zeros((n, xs.shape[1]), np.uint8)
+    w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
+    ri = np.zeros((n, K), np.int32)
+    rw = None if w is None else np.zeros((n, K), np.float32)
+    rc = lib(_lib).oracle_dispatch_compact(_ptr(xb, _u8p), xb.shape[1], _ptr(xs, _u8p),
+                                           0 if xs is None else xs.shape[1], _ptr(idx, _i32p),
+                                           _ptr(w, _f32p), _ptr(dst, _i32p), _ptr(meta, _i32p), n, T, K,
+                                           _ptr(rx, _u8p), _ptr(rs, _u8p), _ptr(ri, _i32p), _ptr(rw, _f32p))
+    if rc != 0:
+        raise ValueError("oracle_dispatch_compact rejected its arguments")
+    return rx, rs, ri, rw
+
+
+def combine_compact(y_bf16_bits: np.ndarray, dst_slot: np.ndarray, recv_src_metadata: np.ndarray,
+                    num_recv: int, bias_bf16_bits: np.ndarray = None, _lib=None):
+    """Non-expand combine: bf16 rows [>= num_recv, H] back to token order [T, H] (+ bias)."""
+    y = np.ascontiguousarray(y_bf16_bits).view(np.uint16)
+    H = y.shape[1]
+    dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
+    T, K = dst.shape
+    meta = np.ascontiguousarray(recv_src_metadata, dtype=np.int32).reshape(-1, K + 2)
+    b = None if bias_bf16_bits is None else np.ascontiguousarray(bias_bf16_bits).view(np.uint16)
+    out = np.empty((T, H), np.uint16)
+    rc = lib(_lib).oracle_combine_compact(_ptr(y, _u16p), H, _ptr(b, _u16p), _ptr(dst, _i32p),
+                                          _ptr(meta, _i32p), int(num_recv), T, K, _ptr(out, _u16p))
+    if rc != 0:
+        raise ValueError("oracle_combine_compact rejected its arguments")
+    return out
 
 
 def zero_padding(expand_x: np.ndarray, counts: np.ndarray, offsets: np.ndarray,

@@ -146,6 +146,25 @@ int oracle_layout(const int32_t *topk_idx, int32_t T, int32_t K, int32_t E,
   return 0;
 }
 
+/* bf16 is the upper half of an IEEE binary32. */
+static float bf16_bits_to_float(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+/* binary32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN. */
+static uint16_t float_to_bf16_bits_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+    return (uint16_t)((u >> 16) | 0x0040u);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
 /* ---------------------------------------------------------------------- */
 /* Dispatch: move bytes into the expert-major expand buffer.               */
 /* ---------------------------------------------------------------------- */
@@ -180,6 +199,82 @@ int oracle_dispatch(const uint8_t *x, int64_t row_bytes, const uint8_t *x_scales
 }
 
 /*
+ * Non-expand dispatch ([DeepEP] EPHandle do_expand = false; the dispatch
+ * copy epilogue writes recv_x, recv_topk_idx and recv_topk_weights): one row
+ * per received token, in receive order. For i < num_recv, with
+ * t = recv_src_metadata[i][0]:
+ *   recv_x[i] = x[t] (bytes), recv_scales[i] = x_scales[t] (if given),
+ *   recv_topk_idx[i][k] = topk_idx[t][k] where dst_slot[t][k] >= 0, else -1,
+ *   recv_topk_weights[i][k] = topk_weights[t][k] (if given).
+ */
+int oracle_dispatch_compact(const uint8_t *x, int64_t row_bytes, const uint8_t *x_scales,
+                            int64_t scale_row_bytes, const int32_t *topk_idx,
+                            const float *topk_weights, const int32_t *dst_slot,
+                            const int32_t *meta, int32_t num_recv, int32_t T, int32_t K,
+                            uint8_t *recv_x, uint8_t *recv_scales, int32_t *recv_topk_idx,
+                            float *recv_topk_weights) {
+  if (num_recv < 0 || num_recv > T || K < 1 || row_bytes < 0) return -1;
+  for (int32_t i = 0; i < num_recv; ++i) {
+    int32_t t = meta[(int64_t)i * (K + 2)];
+    if (t < 0 || t >= T) return -1;
+    memcpy(recv_x + (int64_t)i * row_bytes, x + (int64_t)t * row_bytes, (size_t)row_bytes);
+    if (x_scales && recv_scales)
+      memcpy(recv_scales + (int64_t)i * scale_row_bytes, x_scales + (int64_t)t * scale_row_bytes,
+             (size_t)scale_row_bytes);
+    for (int32_t k = 0; k < K; ++k) {
+      int64_t tk = (int64_t)t * K + k;
+      recv_topk_idx[(int64_t)i * K + k] = dst_slot[tk] >= 0 ? topk_idx[tk] : -1;
+      if (topk_weights && recv_topk_weights)
+        recv_topk_weights[(int64_t)i * K + k] = topk_weights[tk];
+    }
+  }
+  return 0;
+}
+
+/*
+ * Non-expand combine in a world of one: the expert side returns one row per
+ * received token with that token's experts already reduced, so the combine
+ * only puts rows back in token order and adds the bias: out[t] =
+ * bf16(float(y[i]) + float(bias[t])) for the token t of receive row i, and
+ * out[t] = bf16(+0.0 + float(bias[t])) for a token with no unmasked entry;
+ * without a bias, out[t] = y[i] (the same bits) or +0.
+ */
+int oracle_combine_compact(const uint16_t *y, int32_t H, const uint16_t *bias,
+                           const int32_t *dst_slot, const int32_t *meta, int32_t num_recv,
+                           int32_t T, int32_t K, uint16_t *out) {
+  if (num_recv < 0 || num_recv > T || K < 1 || H < 0) return -1;
+  int32_t *row_of = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  for (int32_t t = 0; t < T; ++t) row_of[t] = -1;
+  for (int32_t i = 0; i < num_recv; ++i) {
+    int32_t t = meta[(int64_t)i * (K + 2)];
+    if (t < 0 || t >= T) {
+      free(row_of);
+      return -1;
+    }
+    row_of[t] = i;
+  }
+  for (int32_t t = 0; t < T; ++t) {
+    int any = 0;
+    for (int32_t k = 0; k < K; ++k)
+      if (dst_slot[(int64_t)t * K + k] >= 0) any = 1;
+    int32_t i = any ? row_of[t] : -1;
+    for (int32_t h = 0; h < H; ++h) {
+      uint16_t v;
+      if (bias) {
+        float acc = i >= 0 ? bf16_bits_to_float(y[(int64_t)i * H + h]) : 0.0f;
+        acc = acc + bf16_bits_to_float(bias[(int64_t)t * H + h]);
+        v = float_to_bf16_bits_rne(acc);
+      } else {
+        v = i >= 0 ? y[(int64_t)i * H + h] : (uint16_t)0;
+      }
+      out[(int64_t)t * H + h] = v;
+    }
+  }
+  free(row_of);
+  return 0;
+}
+
+/*
  * Optional clean-up of the expand layout: the alignment padding rows of each
  * expert segment, [offsets[e] + counts[e], offsets[e+1]), are set to zero in
  * expand_x (and in expand_scales / expand_weights when given), so a consumer
@@ -205,25 +300,6 @@ int oracle_zero_padding(uint8_t *expand_x, int64_t row_bytes, uint8_t *expand_sc
 /* ---------------------------------------------------------------------- */
 /* Combine: weighted gather-reduce back to token order.                    */
 /* ---------------------------------------------------------------------- */
-
-/* bf16 is the upper half of an IEEE binary32. */
-static float bf16_bits_to_float(uint16_t b) {
-  uint32_t u = (uint32_t)b << 16;
-  float f;
-  memcpy(&f, &u, sizeof f);
-  return f;
-}
-
-/* binary32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN. */
-static uint16_t float_to_bf16_bits_rne(float f) {
-  uint32_t u;
-  memcpy(&u, &f, sizeof u);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
-    return (uint16_t)((u >> 16) | 0x0040u);
-  uint32_t lsb = (u >> 16) & 1u;
-  u += 0x7fffu + lsb;
-  return (uint16_t)(u >> 16);
-}
 
 /*
  * [DeepEP] combine reduce epilogue (reduce weighted by topk_weights, plus a

@@ -190,3 +190,36 @@ def bf16_ulp_distance(a_bits, b_bits):
         b = np.asarray(b, np.uint16).astype(np.int32)
         return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)
     return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+# --------------------------------------------------------------------------
+# Non-expand (one row per received token)
+# --------------------------------------------------------------------------
+
+def check_dispatch_compact(x_rows, topk_idx, dst, meta, num_recv, recv_x, recv_idx, w=None, recv_w=None):
+    """recv row i holds token meta[i, 0]; ids of masked entries read -1."""
+    toks = np.asarray(meta)[:num_recv, 0]
+    assert np.array_equal(recv_x[:num_recv], x_rows[toks]), "recv_x[i] = x[meta[i, 0]]"
+    masked = np.where(dst >= 0, topk_idx, -1)
+    assert np.array_equal(recv_idx[:num_recv], masked[toks]), "recv_topk_idx"
+    if w is not None:
+        assert np.array_equal(recv_w[:num_recv], np.asarray(w)[toks]), "recv_topk_weights"
+
+
+def check_combine_compact(y_bits, dst, meta, num_recv, out_bits, bias_bits=None):
+    """out[t] = y[row of t] (+ bias) with one rounding; +0 (+ bias) for unreceived tokens."""
+    T = dst.shape[0]
+    row_of = np.full(T, -1)
+    row_of[np.asarray(meta)[:num_recv, 0]] = np.arange(num_recv)
+    recv = (dst >= 0).any(axis=1)
+    assert np.array_equal(recv, row_of >= 0), "exactly the tokens with an unmasked entry are received"
+    yv = np.where(recv[:, None], bf16_bits_to_f64(np.asarray(y_bits)[np.maximum(row_of, 0)]), 0.0)
+    if bias_bits is None:
+        exp = np.where(recv[:, None], np.asarray(y_bits)[np.maximum(row_of, 0)], 0).astype(np.uint16)
+        assert np.array_equal(out_bits, exp), "without a bias rows come back bit for bit"
+        return
+    exact = yv + bf16_bits_to_f64(bias_bits)
+    out = bf16_bits_to_f64(out_bits)
+    # two binary32 roundings of a sum of two bf16 values (the first is exact) then bf16 rounding
+    bound = 0.5 * bf16_ulp(out) + U32 * np.abs(exact)
+    assert np.all(np.abs(out - exact) <= bound), "bias add outside half a bf16 ulp"

@@ -115,3 +115,46 @@ def test_duplicate_experts_in_a_token(oracle_mod):
 def test_rejects_bad_scalars(oracle_mod):
     with pytest.raises(ValueError):
         oracle_mod.layout(np.zeros((2, 2), np.int32), 4, 0)
+
+
+def test_non_expand_hand_worked(oracle_mod):
+    data = json.load(open(os.path.join(GOLDEN, "layout_worked_examples.json")))
+    h = lambda rows: np.array([[int(v, 16) for v in r] for r in rows], np.uint16)  # noqa: E731
+    for c in data["non_expand"]:
+        idx = np.array(c["topk_idx"], np.int32)
+        lay = oracle_mod.layout(idx, 2, 1)
+        assert np.array_equal(lay["dst_slot"], c["dst_slot"]) and lay["num_recv"] == c["num_recv"]
+        rx, _, ri, rw = oracle_mod.dispatch_compact(h(c["x_hex"]), idx, lay["dst_slot"],
+                                                    lay["recv_src_metadata"], lay["num_recv"],
+                                                    topk_weights=np.array(c["topk_weights"], np.float32))
+        assert np.array_equal(rx.view(np.uint16), h(c["recv_x_hex"]))
+        assert np.array_equal(ri, c["recv_topk_idx"])
+        assert np.array_equal(rw, np.array(c["recv_topk_weights"], np.float32))
+        out = oracle_mod.combine_compact(h(c["y_hex"]), lay["dst_slot"], lay["recv_src_metadata"],
+                                         lay["num_recv"], h(c["bias_hex"]))
+        assert np.array_equal(out, h(c["out_bias_hex"]))
+        out = oracle_mod.combine_compact(h(c["y_hex"]), lay["dst_slot"], lay["recv_src_metadata"],
+                                         lay["num_recv"])
+        assert np.array_equal(out, h(c["out_no_bias_hex"]))
+
+
+@pytest.mark.parametrize("mask", [0.0, 0.4])
+def test_non_expand_pins(oracle_mod, mask):
+    w = I.custom("ne", 81, 300, 256, 32, 4, 2)
+    case = I.make_case(w, with_y=False, mask_frac=mask)
+    case.topk_idx[::7, 0] = w.E + 3  # out-of-range ids are masked too
+    counts, offsets, dst, meta = pins.layout_by_argsort(case.topk_idx, w.E, w.A)
+    n = meta.shape[0]
+    xb = case.x.view(np.uint8).reshape(w.T, -1)
+    rx, _, ri, rw = oracle_mod.dispatch_compact(case.x, case.topk_idx, dst, meta, n,
+                                                topk_weights=case.topk_weights)
+    pins.check_dispatch_compact(xb, case.topk_idx, dst, meta, n, rx, ri, case.topk_weights, rw)
+    # round trip: combining the received rows unchanged returns x for every received token
+    out = oracle_mod.combine_compact(rx.view(np.uint16).reshape(n, w.H), dst, meta, n)
+    pins.check_combine_compact(rx.view(np.uint16).reshape(n, w.H), dst, meta, n, out)
+    recv = (dst >= 0).any(axis=1)
+    assert np.array_equal(out[recv], case.x[recv]) and np.all(out[~recv] == 0)
+    bias = I.normal_bf16(w.seed, 9, w.T, w.H)
+    y = I.normal_bf16(w.seed, 4, max(n, 1), w.H)
+    out = oracle_mod.combine_compact(y, dst, meta, n, bias)
+    pins.check_combine_compact(y, dst, meta, n, out, bias)

@@ -29,7 +29,7 @@ MUTANTS = {
     "meta_rank_is_token": ("row[1] = 0; /* source rank: a world of one */", "row[1] = t;"),
     "meta_slot_shift": ("row[2 + k] = dst_slot[(int64_t)t * K + k];", "row[2 + k] = dst_slot[(int64_t)t * K + (K - 1 - k)];"),
     "meta_token_index": ("row[0] = t;", "row[0] = i;"),
-    "dispatch_wrong_token": ("x + (int64_t)t * row_bytes", "x + (int64_t)(T - 1 - t) * row_bytes"),
+    "dispatch_wrong_token": ("x + (int64_t)t * row_bytes", "x + (int64_t)(T - 1 - t) * row_bytes", 0),
     "dispatch_scales_dropped": ("      if (x_scales && expand_scales)\n", "      if (0)\n"),
     "dispatch_weight_k0": ("expand_weights[d] = topk_weights[(int64_t)t * K + k];", "expand_weights[d] = topk_weights[(int64_t)t * K];"),
     "combine_truncate": ("u += 0x7fffu + lsb;", "u += 0u * lsb;"),
@@ -59,6 +59,12 @@ MUTANTS = {
     "zero_padding_one_short": ("for (int64_t r = (int64_t)offsets[e] + counts[e]; r < offsets[e + 1]; ++r) {",
                                "for (int64_t r = (int64_t)offsets[e] + counts[e]; r < offsets[e + 1] - 1; ++r) {"),
     "zero_padding_weights_kept": ("      if (expand_weights) expand_weights[r] = 0.0f;\n", ""),
+    "compact_wrong_token": ("memcpy(recv_x + (int64_t)i * row_bytes, x + (int64_t)t * row_bytes, (size_t)row_bytes);",
+                            "memcpy(recv_x + (int64_t)i * row_bytes, x + (int64_t)i * row_bytes, (size_t)row_bytes);"),
+    "compact_mask_kept": ("recv_topk_idx[(int64_t)i * K + k] = dst_slot[tk] >= 0 ? topk_idx[tk] : -1;",
+                          "recv_topk_idx[(int64_t)i * K + k] = topk_idx[tk];"),
+    "compact_combine_unreceived_kept": ("    int32_t i = any ? row_of[t] : -1;", "    int32_t i = row_of[t] >= 0 ? row_of[t] : 0;"),
+    "compact_combine_bias_dropped": ("        acc = acc + bf16_bits_to_float(bias[(int64_t)t * H + h]);\n", ""),
     "combine_f32_weight_k0": ("        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod",
                               "        float w = topk_weights ? topk_weights[(int64_t)t * K] : 1.0f;\n        float prod"),
 }
@@ -175,6 +181,19 @@ def _run_pins(libpath):
         for a, b in zip((X, Wt), before):
             assert np.all(a[pad] == 0) and np.array_equal(a[~pad], b[~pad])
 
+    def non_expand_pins():
+        h = lambda rows: np.array([[int(v, 16) for v in r] for r in rows], np.uint16)  # noqa: E731
+        for c in lay_gold["non_expand"]:
+            idx = np.array(c["topk_idx"], np.int32)
+            dst_, meta_ = np.array(c["dst_slot"], np.int32), np.array(c["recv_src_metadata"], np.int32)
+            rx, _, ri, _ = oracle.dispatch_compact(h(c["x_hex"]), idx, dst_, meta_, c["num_recv"], _lib=libpath)
+            assert np.array_equal(rx.view(np.uint16), h(c["recv_x_hex"]))
+            assert np.array_equal(ri, c["recv_topk_idx"])
+            out = oracle.combine_compact(h(c["y_hex"]), dst_, meta_, c["num_recv"], h(c["bias_hex"]), _lib=libpath)
+            assert np.array_equal(out, h(c["out_bias_hex"]))
+            out = oracle.combine_compact(h(c["y_hex"]), dst_, meta_, c["num_recv"], _lib=libpath)
+            assert np.array_equal(out, h(c["out_no_bias_hex"]))
+
     def combine_f32_pins():
         for c in comb_gold["combine_f32"]:
             out = oracle.combine_f32(np.array(c["y_rows"], np.float32), np.array(c["dst_slot"], np.int32),
@@ -186,7 +205,7 @@ def _run_pins(libpath):
 
     for name, fn in [("golden_layout", golden_layout), ("golden_combine", golden_combine),
                      ("combine_f32", combine_f32_pins), ("bias", bias_pins),
-                     ("zero_padding", zero_padding_pins),
+                     ("zero_padding", zero_padding_pins), ("non_expand", non_expand_pins),
                      ("bruteforce", bruteforce_and_invariants), ("argsort", argsort_mid),
                      ("dispatch", dispatch_pins), ("combine_bound", combine_bound),
                      ("identity", identity)]:
