@@ -28,7 +28,8 @@ EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 64
 
 SYMBOLS = ("ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
-           "ep_zero_padding", "ep_last_error", "ep_supported")
+           "ep_dispatch_compact", "ep_combine_compact", "ep_zero_padding", "ep_last_error",
+           "ep_supported")
 
 
 class EpError(RuntimeError):
@@ -65,6 +66,11 @@ def lib(path: str = None) -> ctypes.CDLL:
     L.ep_dispatch.restype = ctypes.c_int
     L.ep_combine.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp]
     L.ep_combine.restype = ctypes.c_int
+    L.ep_dispatch_compact.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                      _vp, _vp, _vp, _vp, _vp]
+    L.ep_dispatch_compact.restype = ctypes.c_int
+    L.ep_combine_compact.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
+    L.ep_combine_compact.restype = ctypes.c_int
     L.ep_zero_padding.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i64, _vp]
     L.ep_zero_padding.restype = ctypes.c_int
     L.ep_last_error.argtypes = []
@@ -138,3 +144,19 @@ def ep_zero_padding(expand_x, row_bytes, expand_scales, scale_cols, expand_weigh
     _check(lib().ep_zero_padding(_p(expand_x), row_bytes, _p(expand_scales), scale_cols,
                                  _p(expand_weights), _p(counts), _p(offsets), num_experts,
                                  expert_alignment, capacity_rows, _s(stream)))
+
+
+def ep_dispatch_compact(x, x_scales, topk_idx, topk_weights, dst_slot, recv_src_metadata, num_recv,
+                        num_tokens, hidden, topk, dtype, recv_x, recv_scales, recv_topk_idx,
+                        recv_topk_weights, stream=None):
+    _check(lib().ep_dispatch_compact(_p(x), _p(x_scales), _p(topk_idx), _p(topk_weights),
+                                     _p(dst_slot), _p(recv_src_metadata), _p(num_recv), num_tokens,
+                                     hidden, topk, dtype, _p(recv_x), _p(recv_scales),
+                                     _p(recv_topk_idx), _p(recv_topk_weights), _s(stream)))
+
+
+def ep_combine_compact(expert_out, bias, dst_slot, recv_src_metadata, num_recv, num_tokens, hidden,
+                       topk, dtype, out, stream=None):
+    _check(lib().ep_combine_compact(_p(expert_out), _p(bias), _p(dst_slot), _p(recv_src_metadata),
+                                    _p(num_recv), num_tokens, hidden, topk, dtype, _p(out),
+                                    _s(stream)))

@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libep_mi355x.so")
 
-SOURCES = ["ep_capi.cpp", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_padding.hip"]
+SOURCES = ["ep_capi.cpp", "ep_layout.hip", "ep_dispatch.hip", "ep_combine.hip", "ep_padding.hip",
+           "ep_compact.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

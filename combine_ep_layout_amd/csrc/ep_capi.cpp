@@ -230,4 +230,84 @@ int ep_zero_padding(void *expand_x, int64_t row_bytes, float *expand_scales, int
   }
 }
 
+int ep_dispatch_compact(const void *x, const float *x_scales, const int32_t *topk_idx,
+                        const float *topk_weights, const int32_t *dst_slot,
+                        const int32_t *recv_src_metadata, const int32_t *num_recv,
+                        int32_t num_tokens, int32_t hidden, int32_t topk, int32_t dtype,
+                        void *recv_x, float *recv_scales, int32_t *recv_topk_idx,
+                        float *recv_topk_weights, void *stream) {
+  try {
+    const char *what = "ep_dispatch_compact";
+    if (int rc = check_topk(what, num_tokens, topk)) return rc;
+    int elt;
+    if (dtype == EP_BF16) elt = 2;
+    else if (dtype == EP_FP32) elt = 4;
+    else if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2) elt = 1;
+    else return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
+    const int64_t row_bytes = (int64_t)hidden * elt;
+    if (hidden < 1 || row_bytes % 16 != 0)
+      return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 (got %lld)", what,
+                  (long long)row_bytes);
+    if ((x_scales == nullptr) != (recv_scales == nullptr))
+      return fail(EP_EINVAL, "%s: x_scales and recv_scales go together", what);
+    int64_t scale_cols = 0;
+    if (x_scales != nullptr) {
+      if (dtype != EP_FP8_E4M3 && dtype != EP_FP4X2)
+        return fail(EP_EINVAL, "%s: scale rows travel only with fp8 / fp4x2 rows", what);
+      const int64_t values = dtype == EP_FP4X2 ? 2 * (int64_t)hidden : hidden;
+      if (values % 128 != 0)
+        return fail(EP_EINVAL, "%s: scales need a multiple of 128 values per row", what);
+      scale_cols = values / 128;
+    }
+    if (num_tokens > 0 && (!x || !topk_idx || !dst_slot || !recv_src_metadata || !num_recv ||
+                           !recv_x || !recv_topk_idx))
+      return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
+    if (topk_weights != nullptr && recv_topk_weights == nullptr)
+      return fail(EP_EINVAL, "%s: topk_weights given without recv_topk_weights", what);
+    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(x_scales, 4) ||
+        !aligned(recv_scales, 4) || !aligned(topk_weights, 4) || !aligned(recv_topk_weights, 4))
+      return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
+    ep::CompactDispatchArgs a{x, row_bytes, x_scales, scale_cols, topk_idx,
+                              recv_topk_weights ? topk_weights : nullptr, dst_slot,
+                              recv_src_metadata, num_recv, num_tokens, topk, recv_x,
+                              recv_scales, recv_topk_idx,
+                              topk_weights ? recv_topk_weights : nullptr, (hipStream_t)stream};
+    return from_launch(ep::launch_dispatch_compact(a), what);
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_dispatch_compact: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_dispatch_compact: unknown exception");
+  }
+}
+
+int ep_combine_compact(const void *expert_out, const void *bias, const int32_t *dst_slot,
+                       const int32_t *recv_src_metadata, const int32_t *num_recv,
+                       int32_t num_tokens, int32_t hidden, int32_t topk, int32_t dtype, void *out,
+                       void *stream) {
+  try {
+    const char *what = "ep_combine_compact";
+    if (int rc = check_topk(what, num_tokens, topk)) return rc;
+    if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2)
+      return fail(EP_EINVAL, "%s: combine adds its input; byte dtype %d is rejected", what, dtype);
+    if (dtype == EP_FP32)
+      return fail(EP_EUNSUPPORTED, "%s: only bf16 rows are compiled for the non-expand combine",
+                  what);
+    if (dtype != EP_BF16) return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
+    if (hidden < 1 || ((int64_t)hidden * 2) % 16 != 0)
+      return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 (hidden %d)", what,
+                  hidden);
+    if (num_tokens > 0 && (!expert_out || !dst_slot || !recv_src_metadata || !num_recv || !out))
+      return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
+    if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(bias, 16))
+      return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
+    ep::CompactCombineArgs a{expert_out, (int64_t)hidden * 2, bias, dst_slot, recv_src_metadata,
+                             num_recv, num_tokens, topk, out, (hipStream_t)stream};
+    return from_launch(ep::launch_combine_compact(a), what);
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_combine_compact: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_combine_compact: unknown exception");
+  }
+}
+
 }  // extern "C"

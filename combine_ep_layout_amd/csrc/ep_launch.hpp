@@ -63,6 +63,32 @@ struct ZeroPaddingArgs {
   hipStream_t stream;
 };
 
+struct CompactDispatchArgs {
+  const void *x;
+  int64_t row_bytes;
+  const float *x_scales;
+  int64_t scale_cols;
+  const int32_t *topk_idx;
+  const float *topk_weights;
+  const int32_t *dst_slot, *meta, *num_recv;
+  int T, K;
+  void *recv_x;
+  float *recv_scales;
+  int32_t *recv_topk_idx;
+  float *recv_topk_weights;
+  hipStream_t stream;
+};
+
+struct CompactCombineArgs {
+  const void *y;
+  int64_t row_bytes;
+  const void *bias;
+  const int32_t *dst_slot, *meta, *num_recv;
+  int T, K;
+  void *out;
+  hipStream_t stream;
+};
+
 // HIP error of the last failed launch on this thread (set by launch_status).
 hipError_t &last_hip_error();
 
@@ -81,6 +107,8 @@ size_t layout_workspace(int T, int K, int E);
 int launch_dispatch(const DispatchArgs &a);
 int launch_combine(const CombineArgs &a);
 int launch_zero_padding(const ZeroPaddingArgs &a);
+int launch_dispatch_compact(const CompactDispatchArgs &a);
+int launch_combine_compact(const CompactCombineArgs &a);
 
 bool has_layout(int K);
 bool has_dispatch(int H, int K, int dtype);

@@ -179,6 +179,47 @@ int ep_combine(const void *expert_out, const float *topk_weights, const void *bi
                int32_t dtype, int64_t capacity_rows, void *out, void *stream);
 
 /*
+ * Non-expand dispatch (DeepEP overall architecture: EPHandle do_expand =
+ * false; the dispatch copy epilogue writes recv_x, recv_topk_idx and
+ * recv_topk_weights): one row per received token instead of one per
+ * (token, k). In a world of one the received tokens are those with an
+ * unmasked entry, in ascending order, as ep_layout lists them in
+ * recv_src_metadata. For i < *num_recv, with t = recv_src_metadata[i][0]:
+ *   recv_x[i]            = x[t]                      (bytes of one row)
+ *   recv_scales[i]       = x_scales[t]               (only if both are non-NULL)
+ *   recv_topk_idx[i][k]  = dst_slot[t][k] >= 0 ? topk_idx[t][k] : -1
+ *   recv_topk_weights[i] = topk_weights[t]           (only if both are non-NULL)
+ * Rows i >= *num_recv are not written. x, x_scales, dtype and hidden as for
+ * ep_dispatch; recv_x [T, hidden], recv_scales [T, S], recv_topk_idx int32
+ * [T, K], recv_topk_weights fp32 [T, K] (room for every token); topk_idx,
+ * dst_slot, recv_src_metadata and num_recv as written by ep_layout.
+ * Shapes are run-time values (no capability gate). Errors: EP_EINVAL.
+ */
+int ep_dispatch_compact(const void *x, const float *x_scales, const int32_t *topk_idx,
+                        const float *topk_weights, const int32_t *dst_slot,
+                        const int32_t *recv_src_metadata, const int32_t *num_recv,
+                        int32_t num_tokens, int32_t hidden, int32_t topk, int32_t dtype,
+                        void *recv_x, float *recv_scales, int32_t *recv_topk_idx,
+                        float *recv_topk_weights, void *stream);
+
+/*
+ * Non-expand combine (DeepEP overall architecture: combine reduce epilogue
+ * with bias, do_expand = false). The expert side returns one row per
+ * received token with that token's experts already reduced, so in a world
+ * of one combine only puts rows back in token order and adds the bias:
+ *   out[t] = bf16(float(expert_out[i]) + float(bias[t]))  for t = recv_src_metadata[i][0]
+ *   out[t] = bf16(+0.0 + float(bias[t]))                   for a token with no unmasked entry
+ * (without a bias: the row's bits, or +0). expert_out bf16 [T, hidden] (rows
+ * >= *num_recv are not read), bias bf16 [T, hidden] or NULL, out bf16
+ * [T, hidden], every row written. Errors: EP_EINVAL (byte dtypes rejected),
+ * EP_EUNSUPPORTED for fp32 rows.
+ */
+int ep_combine_compact(const void *expert_out, const void *bias, const int32_t *dst_slot,
+                       const int32_t *recv_src_metadata, const int32_t *num_recv,
+                       int32_t num_tokens, int32_t hidden, int32_t topk, int32_t dtype, void *out,
+                       void *stream);
+
+/*
  * Optional clean-up of the expand layout: zero the alignment padding rows of
  * every expert segment, rows [offsets[e] + counts[e], offsets[e+1]), so a
  * consumer that walks whole aligned segments (DeepEP overall architecture,

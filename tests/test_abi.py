@@ -156,3 +156,28 @@ def test_zero_padding_rejections(L):
     assert _code(B.ep_zero_padding, *zp(x=ODD)) == B.EP_EINVAL
     assert _code(B.ep_zero_padding, *zp(sc=56)) == B.EP_EINVAL          # scale columns without a pointer
     assert _code(B.ep_zero_padding, *zp(c=None)) == B.EP_EINVAL
+
+
+def test_compact_rejections(L):
+    def dc(**kw):
+        a = dict(x=FAKE, xs=None, idx=FAKE, w=None, dst=FAKE, meta=FAKE, n=FAKE, T=4096, H=7168, K=8,
+                 dt=B.EP_BF16, rx=FAKE, rs=None, ri=FAKE, rw=None)
+        a.update(kw)
+        return tuple(a.values())
+    assert _code(B.ep_dispatch_compact, *dc(H=7169)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch_compact, *dc(xs=FAKE)) == B.EP_EINVAL       # scales without recv_scales
+    assert _code(B.ep_dispatch_compact, *dc(xs=FAKE, rs=FAKE)) == B.EP_EINVAL  # scales with bf16
+    assert _code(B.ep_dispatch_compact, *dc(meta=None)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch_compact, *dc(w=FAKE)) == B.EP_EINVAL        # weights without a destination
+    assert _code(B.ep_dispatch_compact, *dc(rx=ODD)) == B.EP_EINVAL
+    assert _code(B.ep_dispatch_compact, *dc(dt=7)) == B.EP_EINVAL
+
+    def cc(**kw):
+        a = dict(y=FAKE, b=None, dst=FAKE, meta=FAKE, n=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, out=FAKE)
+        a.update(kw)
+        return tuple(a.values())
+    assert _code(B.ep_combine_compact, *cc(dt=B.EP_FP8_E4M3)) == B.EP_EINVAL
+    assert _code(B.ep_combine_compact, *cc(dt=B.EP_FP32)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_combine_compact, *cc(H=7172)) == B.EP_EINVAL
+    assert _code(B.ep_combine_compact, *cc(n=None)) == B.EP_EINVAL
+    assert _code(B.ep_combine_compact, *cc(b=ODD)) == B.EP_EINVAL

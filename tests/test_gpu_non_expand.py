@@ -1,0 +1,147 @@
+"""Non-expand dispatch / combine on the GPU vs the CPU oracle, through the C ABI.
+
+Source: DeepEP overall-architecture page, EPHandle do_expand = false (one
+row per received token; recv_x, recv_topk_idx, recv_topk_weights) and the
+combine reduce epilogue with bias. Bar: received rows, scale rows, ids and
+weights bit-exact; combine within 1 bf16 ulp (one binary32 add then RNE on
+both sides, so the test also reports exact matches). Rows past num_recv
+must stay untouched.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - only on CPU hosts
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+from combine_ep_layout_amd import binding as B  # noqa: E402
+from combine_ep_layout_amd import inputs as I  # noqa: E402
+from tests import pins  # noqa: E402
+from tests.gpu_util import DEV, dev_layout, layout_to_host, to_dev, to_host  # noqa: E402
+
+ELT = {I.BF16: 2, I.FP32: 4, I.FP8_E4M3: 1, I.FP4X2: 1}
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _run(w: I.Workload, mask: float = 0.0, weights: bool = True, bias: bool = True,
+         oob_every: int = 0):
+    """Layout -> non-expand dispatch -> non-expand combine on the GPU, each checked."""
+    _say(f"non-expand {w.name}: T={w.T} H={w.H} E={w.E} K={w.K} A={w.A} dtype={w.dtype} "
+         f"mask={mask} weights={weights} bias={bias}")
+    case = I.make_case(w, with_y=False, mask_frac=mask)
+    if oob_every:
+        case.topk_idx[::oob_every, -1] = w.E + 5  # ids outside [0, E) are masked like -1
+    T, K = w.T, w.K
+    idx_d, wts_d, x_d = to_dev(case.topk_idx), to_dev(case.topk_weights), to_dev(case.x)
+    xs_d = to_dev(case.x_scales) if case.x_scales is not None else None
+    lay = dev_layout(idx_d, T, K, w.E, w.A, w.cap)
+    got_lay = layout_to_host(lay)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    assert np.array_equal(got_lay["dst_slot"], ref["dst_slot"]) and got_lay["num_recv"] == ref["num_recv"]
+    assert np.array_equal(got_lay["recv_src_metadata"], ref["recv_src_metadata"])
+    n = ref["num_recv"]
+
+    row_bytes = w.H * ELT[w.dtype]
+    rows = max(T, 1)
+    recv_x = torch.full((rows, row_bytes), 0x5A, dtype=torch.uint8, device=DEV)
+    recv_s = (torch.full((rows, case.x_scales.shape[1]), -3.0, dtype=torch.float32, device=DEV)
+              if xs_d is not None else None)
+    recv_i = torch.full((rows, K), -7, dtype=torch.int32, device=DEV)
+    recv_w = torch.full((rows, K), -5.0, dtype=torch.float32, device=DEV) if weights else None
+    B.ep_dispatch_compact(x_d, xs_d, idx_d, wts_d if weights else None, lay["dst_slot"], lay["meta"],
+                          lay["num_recv"], T, w.H, K, w.dtype, recv_x, recv_s, recv_i, recv_w)
+    torch.cuda.synchronize()
+
+    rx, rs, ri, rw = oracle.dispatch_compact(case.x, case.topk_idx, ref["dst_slot"],
+                                             ref["recv_src_metadata"], n, case.x_scales,
+                                             case.topk_weights if weights else None)
+    gx, gi = to_host(recv_x), to_host(recv_i)
+    assert np.array_equal(gx[:n], rx), "recv_x"
+    assert np.all(gx[n:] == 0x5A), "rows past num_recv were written"
+    assert np.array_equal(gi[:n], ri), "recv_topk_idx"
+    assert np.all(gi[n:] == -7)
+    if recv_s is not None:
+        gs = to_host(recv_s)
+        assert np.array_equal(gs[:n].view(np.uint8), rs), "recv_scales"
+        assert np.all(gs[n:] == -3.0)
+    if weights:
+        gw = to_host(recv_w)
+        assert np.array_equal(gw[:n].view(np.uint32), rw.view(np.uint32)), "recv_topk_weights"
+        assert np.all(gw[n:] == -5.0)
+
+    # combine: the expert side hands back one bf16 row per received token
+    H_out = 2 * w.H if w.dtype == I.FP4X2 else w.H
+    y = I.normal_bf16(w.seed, 4, rows, H_out)
+    b = I.normal_bf16(w.seed, 9, rows, H_out)[:T] if bias else None
+    out = torch.full((rows, H_out), 0x7FC1, dtype=torch.int16, device=DEV)
+    B.ep_combine_compact(to_dev(y), to_dev(b) if bias else None, lay["dst_slot"], lay["meta"],
+                         lay["num_recv"], T, H_out, K, B.EP_BF16, out)
+    torch.cuda.synchronize()
+    got = to_host(out, np.uint16)[:T]
+    want = oracle.combine_compact(y, ref["dst_slot"], ref["recv_src_metadata"], n, b)
+    d = pins.bf16_ulp_distance(got, want)
+    _say(f"  num_recv={n} combine exact={np.mean(d == 0):.6f} max_ulp={int(d.max()) if d.size else 0}")
+    assert d.size == 0 or d.max() <= 1, "combine beyond 1 bf16 ulp"
+    if not bias:
+        assert np.array_equal(got, want), "without a bias rows come back bit for bit"
+    return case, ref, recv_x, n
+
+
+@pytest.mark.parametrize("name", ["prefill_aligned", "mori_default", "decode_zipf", "fp8_hot8"])
+def test_workload_full_size(name):
+    _run(I.WORKLOADS[name])
+
+
+def test_fp4x2_rows_with_scales():
+    _run(I.EXTRA_WORKLOADS["prefill_fp4x2"], mask=0.2)
+
+
+RAGGED = [
+    # T, H, E, K, A, dtype, mask, weights, bias
+    (1, 256, 8, 1, 1, I.BF16, 0.0, True, True),
+    (333, 520, 32, 4, 16, I.BF16, 0.3, True, True),     # 65 chunks per row: a one-chunk tail slice
+    (777, 7168, 256, 8, 128, I.BF16, 0.9, False, True),  # many tokens receive nothing
+    (1000, 104, 64, 6, 1, I.FP32, 0.25, True, False),     # fp32 rows move unchanged, 416 bytes
+    (513, 1024, 16, 2, 4, I.FP8_E4M3, 0.5, True, True),
+    (64, 7168, 256, 8, 1, I.BF16, 0.0, True, False),
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,A,dtype,mask,weights,bias", RAGGED)
+def test_ragged_shapes(T, H, E, K, A, dtype, mask, weights, bias):
+    w = I.custom(f"ne_{T}_{H}_{K}", 500 + T, T, H, E, K, A, dtype)
+    _run(w, mask=mask, weights=weights, bias=bias, oob_every=5)
+
+
+def test_nothing_received():
+    w = I.custom("ne_none", 7, 200, 256, 16, 4, 2)
+    _, ref, _, n = _run(w, mask=1.0)
+    assert n == 0 and ref["num_recv"] == 0
+
+
+def test_empty_input():
+    z = torch.zeros(16, dtype=torch.int32, device=DEV)
+    B.ep_dispatch_compact(None, None, None, None, None, None, z, 0, 256, 8, B.EP_BF16, None, None,
+                          None, None)
+    B.ep_combine_compact(None, None, None, None, z, 0, 256, 8, B.EP_BF16, None)
+    torch.cuda.synchronize()
+
+
+def test_round_trip_returns_x():
+    """Combining the received rows unchanged gives x back for every received token."""
+    w = I.custom("ne_rt", 33, 2048, 7168, 256, 8, 128)
+    case, ref, recv_x, n = _run(w, mask=0.3, bias=False)
+    T = w.T
+    out = torch.full((T, w.H), 0x7FC1, dtype=torch.int16, device=DEV)
+    lay = dev_layout(to_dev(case.topk_idx), T, w.K, w.E, w.A, w.cap)
+    B.ep_combine_compact(recv_x, None, lay["dst_slot"], lay["meta"], lay["num_recv"], T, w.H, w.K,
+                         B.EP_BF16, out)
+    got = to_host(out, np.uint16)
+    recv = (ref["dst_slot"] >= 0).any(axis=1)
+    assert np.array_equal(got[recv], case.x[recv]) and np.all(got[~recv] == 0)
