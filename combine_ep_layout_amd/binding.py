@@ -28,8 +28,8 @@ EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 64
 
 SYMBOLS = ("ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
-           "ep_dispatch_compact", "ep_combine_compact", "ep_zero_padding", "ep_last_error",
-           "ep_supported")
+           "ep_dispatch_compact", "ep_combine_compact", "ep_zero_padding", "ep_set_workgroup_limit",
+           "ep_get_workgroup_limit", "ep_last_error", "ep_supported")
 
 
 class EpError(RuntimeError):
@@ -71,6 +71,10 @@ def lib(path: str = None) -> ctypes.CDLL:
     L.ep_dispatch_compact.restype = ctypes.c_int
     L.ep_combine_compact.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
     L.ep_combine_compact.restype = ctypes.c_int
+    L.ep_set_workgroup_limit.argtypes = [_vp, _i32]
+    L.ep_set_workgroup_limit.restype = ctypes.c_int
+    L.ep_get_workgroup_limit.argtypes = [_vp]
+    L.ep_get_workgroup_limit.restype = ctypes.c_int
     L.ep_zero_padding.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i64, _vp]
     L.ep_zero_padding.restype = ctypes.c_int
     L.ep_last_error.argtypes = []
@@ -160,3 +164,11 @@ def ep_combine_compact(expert_out, bias, dst_slot, recv_src_metadata, num_recv, 
     _check(lib().ep_combine_compact(_p(expert_out), _p(bias), _p(dst_slot), _p(recv_src_metadata),
                                     _p(num_recv), num_tokens, hidden, topk, dtype, _p(out),
                                     _s(stream)))
+
+
+def ep_set_workgroup_limit(stream, max_workgroups):
+    _check(lib().ep_set_workgroup_limit(_s(stream), max_workgroups))
+
+
+def ep_get_workgroup_limit(stream) -> int:
+    return lib().ep_get_workgroup_limit(_s(stream))

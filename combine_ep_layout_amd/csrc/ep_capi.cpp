@@ -9,7 +9,11 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <exception>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "ep_launch.hpp"
 #include "ep_mi355x.h"
@@ -50,9 +54,69 @@ int check_topk(const char *what, int32_t T, int32_t K) {
 
 hipError_t &ep::last_hip_error() { return g_hip_error; }
 
+// Workgroup caps per stream handle. Launchers look them up on every launch;
+// while no cap is registered the lookup is one relaxed atomic load.
+namespace {
+std::mutex g_caps_mu;
+std::vector<std::pair<hipStream_t, int>> g_caps;
+std::atomic<int> g_caps_n{0};
+}  // namespace
+
+int ep::stream_workgroup_limit(hipStream_t stream) {
+  if (g_caps_n.load(std::memory_order_acquire) == 0) return 0;
+  std::lock_guard<std::mutex> lock(g_caps_mu);
+  for (const auto &c : g_caps)
+    if (c.first == stream) return c.second;
+  return 0;
+}
+
 extern "C" {
 
 const char *ep_last_error(void) { return g_last_error; }
+
+int ep_set_workgroup_limit(void *stream, int32_t max_workgroups) {
+  try {
+    if (max_workgroups < 0)
+      return fail(EP_EINVAL, "ep_set_workgroup_limit: max_workgroups must be >= 0 (got %d)",
+                  max_workgroups);
+    int cap = max_workgroups;
+    if (cap > 0) {  // never more workgroups than compute units
+      int dev = 0, cus = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess)
+        return fail(EP_EHIP, "ep_set_workgroup_limit: cannot read the compute-unit count: %s",
+                    hipGetErrorString(e));
+      if (cus > 0 && cap > cus) cap = cus;
+    }
+    const hipStream_t s = (hipStream_t)stream;
+    std::lock_guard<std::mutex> lock(g_caps_mu);
+    size_t i = 0;
+    while (i < g_caps.size() && g_caps[i].first != s) ++i;
+    if (cap == 0) {
+      if (i < g_caps.size()) g_caps.erase(g_caps.begin() + (ptrdiff_t)i);
+    } else if (i < g_caps.size()) {
+      g_caps[i].second = cap;
+    } else {
+      g_caps.emplace_back(s, cap);
+    }
+    g_caps_n.store((int)g_caps.size(), std::memory_order_release);
+    g_last_error[0] = '\0';
+    return EP_OK;
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_set_workgroup_limit: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_set_workgroup_limit: unknown exception");
+  }
+}
+
+int ep_get_workgroup_limit(void *stream) {
+  try {
+    return ep::stream_workgroup_limit((hipStream_t)stream);
+  } catch (...) {
+    return fail(EP_EHIP, "ep_get_workgroup_limit: unknown exception");
+  }
+}
 
 int ep_supported(int32_t pass, int32_t hidden, int32_t topk, int32_t dtype) {
   try {

@@ -30,9 +30,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
@@ -84,18 +81,19 @@ struct Elem {
 // Loads the wave's slice (G chunks per lane) of each of the K rows and folds
 // them in k order into acc. ALL_VALID: every slot is a real row, so the
 // loads are straight-line code and each row is consumed as soon as its loads
-// land; otherwise rows with a negative slot are skipped.
+// land; otherwise rows with a negative slot d[k] are skipped by the fold,
+// and their loads read src[k], another row of the same token, so that the
+// loads stay straight-line code (no partly loaded register array).
 template <int DT, int CH, int K, int G, bool ALL_VALID>
-__device__ __forceinline__ void gather_fold(const u32x4 *__restrict__ y, const int (&d)[K],
-                                            const float (&wk)[K], int c0, int lane,
-                                            float (&acc)[G][Elem<DT>::PER_CHUNK]) {
+__device__ __forceinline__ void gather_fold(const u32x4 *__restrict__ y, const int (&src)[K],
+                                            const int (&d)[K], const float (&wk)[K], int c0,
+                                            int lane, float (&acc)[G][Elem<DT>::PER_CHUNK]) {
 #pragma clang fp contract(off)
   constexpr int PC = Elem<DT>::PER_CHUNK;
   u32x4 v[K][G];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    if (!ALL_VALID && d[k] < 0) continue;
-    const u32x4 *row = y + (int64_t)d[k] * CH;
+    const u32x4 *row = y + (int64_t)src[k] * CH;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int i = (c0 + g) * kWave + lane;
@@ -123,8 +121,13 @@ __device__ __forceinline__ void gather_fold(const u32x4 *__restrict__ y, const i
   }
 }
 
-template <int DT, int H, int K, bool BIAS>
-__global__ __launch_bounds__(kThreads) void ep_combine_gather(
+// NT threads per workgroup: 256 normally; 1024 under a workgroup cap (16
+// waves, 16 KiB of loads in flight each, on the one compute unit the
+// workgroup occupies; at most 128 registers per lane).
+constexpr int kCombineCappedThreads = kCappedThreads;
+
+template <int DT, int H, int K, bool BIAS, int NT>
+__global__ __launch_bounds__(NT) void ep_combine_gather(
     const u32x4 *__restrict__ y, const float *__restrict__ topk_weights,
     const u32x4 *__restrict__ bias, const int32_t *__restrict__ dst_slot, int T,
     int64_t capacity, u32x4 *__restrict__ out) {
@@ -137,8 +140,9 @@ __global__ __launch_bounds__(kThreads) void ep_combine_gather(
 
   const int lane = lane_id();
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t first = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
-  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+  constexpr int wpb = NT / kWave;
+  const int64_t first = (int64_t)blockIdx.x * wpb + wave_in_block;
+  const int64_t stride = (int64_t)gridDim.x * wpb;
 
   for (int64_t gw = first; gw < (int64_t)T * SPLIT; gw += stride) {
     const int t = (int)(gw / SPLIT);
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void ep_combine_gather(
       if (my_dst >= capacity) my_dst = -1;
       my_w = topk_weights ? topk_weights[(int64_t)t * K + lane] : 1.0f;
     }
-    const bool all_valid = ballot(lane < K && my_dst >= 0) == (K == 64 ? ~0ull : (1ull << K) - 1);
+    const uint64_t valid = ballot(lane < K && my_dst >= 0);
     int d[K];
     float wk[K];
 #pragma unroll
@@ -161,8 +165,20 @@ __global__ __launch_bounds__(kThreads) void ep_combine_gather(
     // Expert outputs are read exactly once: non-temporal loads keep them
     // from displacing useful lines in the caches.
     float acc[G][PC];
-    if (all_valid) gather_fold<DT, CH, K, G, true>(y, d, wk, c0, lane, acc);
-    else gather_fold<DT, CH, K, G, false>(y, d, wk, c0, lane, acc);
+    if (valid == (K == 64 ? ~0ull : (1ull << K) - 1)) {
+      gather_fold<DT, CH, K, G, true>(y, d, d, wk, c0, lane, acc);
+    } else if (valid != 0) {  // masked slots load a valid row of the token, unused
+      const int any = read_lane(my_dst, __builtin_ctzll(valid));
+      int src[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) src[k] = d[k] >= 0 ? d[k] : any;
+      gather_fold<DT, CH, K, G, false>(y, src, d, wk, c0, lane, acc);
+    } else {  // no expert output for this token: the sum of no terms
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < PC; ++j) acc[g][j] = 0.0f;
+    }
 
     u32x4 *o = out + (int64_t)t * CH;
 #pragma unroll
@@ -181,21 +197,27 @@ __global__ __launch_bounds__(kThreads) void ep_combine_gather(
   }
 }
 
+template <int DT, int H, int K, int NT>
+int combine_launch(const CombineArgs &a, const WaveGrid &g) {
+  if (a.bias)
+    ep_combine_gather<DT, H, K, true, NT><<<g.blocks, NT, 0, a.stream>>>(
+        (const u32x4 *)a.y, a.topk_weights, (const u32x4 *)a.bias, a.dst_slot, a.T, a.capacity,
+        (u32x4 *)a.out);
+  else
+    ep_combine_gather<DT, H, K, false, NT><<<g.blocks, NT, 0, a.stream>>>(
+        (const u32x4 *)a.y, a.topk_weights, nullptr, a.dst_slot, a.T, a.capacity,
+        (u32x4 *)a.out);
+  return launch_status();
+}
+
 template <int DT, int H, int K>
 int combine_impl(const CombineArgs &a) {
   if (a.T == 0) return 0;
   constexpr int SPLIT = CombineGeometry<H * Elem<DT>::BYTES / 16>::SPLIT;
-  const int64_t waves = (int64_t)a.T * SPLIT;
-  const int blocks = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-  if (a.bias)
-    ep_combine_gather<DT, H, K, true><<<blocks, kThreads, 0, a.stream>>>(
-        (const u32x4 *)a.y, a.topk_weights, (const u32x4 *)a.bias, a.dst_slot, a.T, a.capacity,
-        (u32x4 *)a.out);
-  else
-    ep_combine_gather<DT, H, K, false><<<blocks, kThreads, 0, a.stream>>>(
-        (const u32x4 *)a.y, a.topk_weights, nullptr, a.dst_slot, a.T, a.capacity,
-        (u32x4 *)a.out);
-  return launch_status();
+  const WaveGrid g = wave_grid((int64_t)a.T * SPLIT, stream_workgroup_limit(a.stream), INT32_MAX,
+                               1, kCombineCappedThreads);
+  if (g.threads == kCombineCappedThreads) return combine_launch<DT, H, K, kCombineCappedThreads>(a, g);
+  return combine_launch<DT, H, K, kDefaultThreads>(a, g);
 }
 
 }  // namespace

@@ -23,15 +23,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2 f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-__global__ __launch_bounds__(kThreads) void ep_dispatch_compact_rows(
+__global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     const u32x4 *__restrict__ x, int64_t row_chunks, const float *__restrict__ x_scales,
     int64_t scale_cols, const int32_t *__restrict__ topk_idx,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot,
@@ -43,8 +40,9 @@ __global__ __launch_bounds__(kThreads) void ep_dispatch_compact_rows(
   const int64_t total = (int64_t)T * slices;
   const int n = __builtin_amdgcn_readfirstlane(*num_recv);
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block; gw < total;
+  const int wpb = blockDim.x / kWave;
+  const int64_t stride = (int64_t)gridDim.x * wpb;
+  for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < total;
        gw += stride) {
     const int64_t i = gw / slices;  // receive row
     const int64_t slice = gw - i * slices;
@@ -67,58 +65,58 @@ __global__ __launch_bounds__(kThreads) void ep_dispatch_compact_rows(
   }
 }
 
-// Waves [0, T*slices): receive rows back to their tokens. Waves
-// [T*slices, 2*T*slices): tokens with no unmasked entry get +0 (+ bias).
-__global__ __launch_bounds__(kThreads) void ep_combine_compact_rows(
+// out[t] chunk c = v (+ bias[t] chunk c), one binary32 add per value, RNE.
+__device__ __forceinline__ void put_row_chunk(u32x4 v, const u32x4 *__restrict__ bias, int64_t t,
+                                              int64_t row_chunks, int64_t c,
+                                              u32x4 *__restrict__ out) {
+#pragma clang fp contract(off)
+  if (bias != nullptr) {
+    const u32x4 b = bias[t * row_chunks + c];
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __uint_as_float(v[j] << 16) + __uint_as_float(b[j] << 16);
+      const float hi = __uint_as_float(v[j] & 0xffff0000u) + __uint_as_float(b[j] & 0xffff0000u);
+      r[j] = pack_bf16x2(lo, hi);
+    }
+    v = r;
+  }
+  __builtin_nontemporal_store(v, out + t * row_chunks + c);
+}
+
+// Waves [0, T*slices): (receive row, slice) back to its token. Waves
+// [T*slices, T*slices + T): one per token; a token with no unmasked entry
+// (none of its K slots valid) gets +0 (+ bias) over its whole row, the
+// others exit after one K-wide read.
+__global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
     const u32x4 *__restrict__ y, int64_t row_chunks, const u32x4 *__restrict__ bias,
     const int32_t *__restrict__ dst_slot, const int32_t *__restrict__ meta,
     const int32_t *__restrict__ num_recv, int T, int K, u32x4 *__restrict__ out) {
-#pragma clang fp contract(off)
   const int lane = lane_id();
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int64_t half = (int64_t)T * slices;
   const int n = __builtin_amdgcn_readfirstlane(*num_recv);
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block; gw < 2 * half;
-       gw += stride) {
-    const bool from_row = gw < half;
-    const int64_t r = (from_row ? gw : gw - half) / slices;
-    const int64_t slice = (from_row ? gw : gw - half) - r * slices;
-    int64_t t, src = -1;
-    if (from_row) {
+  const int wpb = blockDim.x / kWave;
+  const int64_t stride = (int64_t)gridDim.x * wpb;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < half + T; gw += stride) {
+    if (gw < half) {
+      const int64_t r = gw / slices;
+      const int64_t c = (gw - r * slices) * kWave + lane;
       if (r >= n) continue;
-      t = __builtin_amdgcn_readfirstlane(meta[r * (K + 2)]);
-      if (t < 0 || t >= T) continue;
-      src = r;
+      const int64_t t = __builtin_amdgcn_readfirstlane(meta[r * (K + 2)]);
+      if (t < 0 || t >= T || c >= row_chunks) continue;
+      put_row_chunk(__builtin_nontemporal_load(y + r * row_chunks + c), bias, t, row_chunks, c,
+                    out);
     } else {
-      t = r;
+      const int64_t t = gw - half;
       bool any = false;
       for (int k = lane; k < K; k += kWave) any |= dst_slot[t * K + k] >= 0;
       if (ballot(any) != 0) continue;  // received: written by its receive row
+      for (int64_t c = lane; c < row_chunks; c += kWave) put_row_chunk(zero, bias, t, row_chunks, c, out);
     }
-    const int64_t c = slice * kWave + lane;
-    if (c >= row_chunks) continue;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (src >= 0) v = __builtin_nontemporal_load(y + src * row_chunks + c);
-    if (bias != nullptr) {
-      const u32x4 b = bias[t * row_chunks + c];
-      u32x4 r2;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float lo = __uint_as_float(v[j] << 16) + __uint_as_float(b[j] << 16);
-        const float hi = __uint_as_float(v[j] & 0xffff0000u) + __uint_as_float(b[j] & 0xffff0000u);
-        r2[j] = pack_bf16x2(lo, hi);
-      }
-      v = r2;
-    }
-    __builtin_nontemporal_store(v, out + t * row_chunks + c);
   }
-}
-
-int64_t grid_for(int64_t waves) {
-  int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  return blocks < (1 << 22) ? blocks : (1 << 22);  // larger inputs loop
 }
 
 }  // namespace
@@ -127,7 +125,9 @@ int launch_dispatch_compact(const CompactDispatchArgs &a) {
   if (a.T == 0) return 0;
   const int64_t row_chunks = a.row_bytes / 16;
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
-  ep_dispatch_compact_rows<<<(unsigned)grid_for((int64_t)a.T * slices), kThreads, 0, a.stream>>>(
+  const WaveGrid g =  // larger inputs loop
+      wave_grid((int64_t)a.T * slices, stream_workgroup_limit(a.stream), 1 << 22);
+  ep_dispatch_compact_rows<<<g.blocks, g.threads, 0, a.stream>>>(
       (const u32x4 *)a.x, row_chunks, a.x_scales, a.scale_cols, a.topk_idx, a.topk_weights,
       a.dst_slot, a.meta, a.num_recv, a.T, a.K, (u32x4 *)a.recv_x, a.recv_scales,
       a.recv_topk_idx, a.recv_topk_weights);
@@ -138,8 +138,9 @@ int launch_combine_compact(const CompactCombineArgs &a) {
   if (a.T == 0) return 0;
   const int64_t row_chunks = a.row_bytes / 16;
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
-  ep_combine_compact_rows<<<(unsigned)grid_for(2 * (int64_t)a.T * slices), kThreads, 0,
-                            a.stream>>>((const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias,
+  const WaveGrid g =
+      wave_grid((int64_t)a.T * (slices + 1), stream_workgroup_limit(a.stream), 1 << 22);
+  ep_combine_compact_rows<<<g.blocks, g.threads, 0, a.stream>>>((const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias,
                                         a.dst_slot, a.meta, a.num_recv, a.T, a.K,
                                         (u32x4 *)a.out);
   return launch_status();

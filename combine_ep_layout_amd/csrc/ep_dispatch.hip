@@ -16,6 +16,11 @@
 // another, each written front to back; the K waves that need the same source
 // slice run on the same XCD, so x is read from HBM about once. Row bytes and
 // K are template constants.
+//
+// Under a workgroup cap (CU-limited mode) a compute unit's own memory path,
+// not HBM, is the limit, so a second kernel cuts the bytes each compute unit
+// moves: one wave per (token, slice) loads the slice once and stores it to
+// all K destinations, (K + 1) KiB per K KiB written instead of 2K KiB.
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -24,13 +29,11 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;  // 4 waves
-constexpr int kWavesPerBlock = kThreads / kWave;
-
 // Blocks run on the 8 XCDs round-robin (block b on XCD b % 8). Renumbering
 // them so that each XCD gets one contiguous eighth of the work keeps the K
 // waves that copy the same source slice on one XCD, where all but the first
-// read it from that XCD's L2. The grid is padded to a multiple of 8.
+// read it from that XCD's L2. The renumbering is a permutation only when the
+// grid is a multiple of 8: the launcher pads the grid to one.
 constexpr int kXcds = 8;
 __device__ __forceinline__ int64_t xcd_contiguous_block() {
   const int64_t nb = gridDim.x, b = blockIdx.x;
@@ -46,7 +49,7 @@ __device__ __forceinline__ int64_t xcd_contiguous_block() {
 // DT (the EP_* dtype) only names the kernel: every dtype moves bytes, so
 // instances with equal ROWB and SCB have the same body.
 template <int DT, int ROWB, int SCB, int K>
-__global__ __launch_bounds__(kThreads) void ep_dispatch_expand(
+__global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
     int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
@@ -59,10 +62,10 @@ __global__ __launch_bounds__(kThreads) void ep_dispatch_expand(
 
   const int lane = lane_id();
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  constexpr int wpb = kDefaultThreads / kWave;  // launched uncapped only
   const int64_t total = (int64_t)T * K * SLICES;
-  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t gw = xcd_contiguous_block() * kWavesPerBlock + wave_in_block; gw < total;
-       gw += stride) {
+  const int64_t stride = (int64_t)gridDim.x * wpb;
+  for (int64_t gw = xcd_contiguous_block() * wpb + wave_in_block; gw < total; gw += stride) {
     const int64_t tk = gw / SLICES;  // flat (token, k)
     const int slice = (int)(gw - tk * SLICES);
     const int64_t t = tk / K;
@@ -80,16 +83,69 @@ __global__ __launch_bounds__(kThreads) void ep_dispatch_expand(
   }
 }
 
+// One wave per (token, 1 KiB slice): the slice is loaded once and stored to
+// each of the token's K destination rows in k order (masked entries
+// skipped); slice 0 also carries the scale row and the weight of each entry.
+template <int DT, int ROWB, int SCB, int K>
+__global__ __launch_bounds__(kCappedThreads) void ep_dispatch_fanout(
+    const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
+    int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
+    float *__restrict__ expand_weights) {
+  constexpr int CH = ROWB / 16;
+  constexpr int SLICES = (CH + kWave - 1) / kWave;
+  constexpr int SCH = SCB / 16;
+  static_assert(ROWB % 16 == 0 && SCB % 16 == 0 && SCH <= kWave, "row geometry");
+  static_assert(K >= 1 && K <= kWave, "topk must fit one wavefront");
+
+  const int lane = lane_id();
+  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  constexpr int wpb = kCappedThreads / kWave;  // launched under a cap only
+  const int64_t total = (int64_t)T * SLICES;
+  const int64_t stride = (int64_t)gridDim.x * wpb;
+  for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < total; gw += stride) {
+    const int64_t t = gw / SLICES;
+    const int slice = (int)(gw - t * SLICES);
+    int my_d = -1;
+    if (lane < K) {
+      my_d = dst_slot[t * K + lane];
+      if (my_d >= capacity) my_d = -1;
+    }
+    const int i = slice * kWave + lane;
+    const bool in_row = CH % kWave == 0 || i < CH;
+    u32x4 v = {0u, 0u, 0u, 0u}, sc = {0u, 0u, 0u, 0u};
+    if (in_row) v = x[t * CH + i];
+    if (SCH > 0 && slice == 0 && lane < SCH) sc = x_scales[t * SCH + lane];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int d = read_lane(my_d, k);
+      if (d < 0) continue;
+      if (in_row) __builtin_nontemporal_store(v, expand_x + (int64_t)d * CH + i);
+      if (slice == 0) {
+        if (SCH > 0 && lane < SCH)
+          __builtin_nontemporal_store(sc, expand_scales + (int64_t)d * SCH + lane);
+        if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[t * K + k];
+      }
+    }
+  }
+}
+
 template <int DT, int ROWB, int SCB, int K>
 int dispatch_impl(const DispatchArgs &a) {
   if (a.T == 0) return 0;
   constexpr int SLICES = (ROWB / 16 + kWave - 1) / kWave;
-  const int64_t waves = (int64_t)a.T * K * SLICES;
-  int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  blocks = blocks < (1 << 24) ? blocks : (1 << 24);  // larger inputs loop
-  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
   const bool fwd_w = a.topk_weights != nullptr && a.expand_weights != nullptr;
-  ep_dispatch_expand<DT, ROWB, SCB, K><<<(unsigned)blocks, kThreads, 0, a.stream>>>(
+  const int cap = stream_workgroup_limit(a.stream);
+  if (cap > 0) {
+    const WaveGrid g = wave_grid((int64_t)a.T * SLICES, cap, 1 << 24);
+    ep_dispatch_fanout<DT, ROWB, SCB, K><<<g.blocks, kCappedThreads, 0, a.stream>>>(
+        (const u32x4 *)a.x, (const u32x4 *)a.x_scales, a.topk_weights, a.dst_slot, a.T,
+        a.capacity, (u32x4 *)a.expand_x, (u32x4 *)a.expand_scales,
+        fwd_w ? a.expand_weights : nullptr);
+    return launch_status();
+  }
+  const WaveGrid g = wave_grid((int64_t)a.T * K * SLICES, 0, 1 << 24, kXcds);
+  ep_dispatch_expand<DT, ROWB, SCB, K><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
       (const u32x4 *)a.x, (const u32x4 *)a.x_scales, a.topk_weights, a.dst_slot, a.T,
       a.capacity, (u32x4 *)a.expand_x, (u32x4 *)a.expand_scales,
       fwd_w ? a.expand_weights : nullptr);

@@ -89,6 +89,46 @@ struct CompactCombineArgs {
   hipStream_t stream;
 };
 
+// Launch geometry. By default a grid covers every unit of work with
+// 256-thread workgroups, so the hardware spreads it over all compute units.
+// A stream may carry a workgroup cap (ep_set_workgroup_limit): every kernel
+// launched on it then uses at most that many workgroups, each large enough to
+// keep one compute unit's memory pipeline busy (1024 threads for kernels
+// whose waves move 1 KiB at a time, fewer for kernels with more loads in
+// flight per wave), and its waves loop over the work, leaving the other
+// compute units free for work on other streams.
+constexpr int kDefaultThreads = 256;
+constexpr int kCappedThreads = 1024;
+
+// The cap registered for this stream handle, or 0 for none.
+int stream_workgroup_limit(hipStream_t stream);
+
+struct WaveGrid {
+  unsigned blocks;
+  int threads;
+};
+
+// Grid for `waves` independent one-wave units (at least one workgroup) under
+// the workgroup cap `cap` (0: none; read once per launch with
+// stream_workgroup_limit, so a concurrent change cannot split one launch's
+// decisions). max_blocks bounds the uncapped grid (larger inputs loop);
+// round_to, if above 1, rounds the uncapped block count up to a multiple of
+// it; capped_threads is the workgroup size under a cap (the kernel's launch
+// bound).
+inline WaveGrid wave_grid(int64_t waves, int cap, int64_t max_blocks, int round_to = 1,
+                          int capped_threads = kCappedThreads) {
+  const int threads = cap > 0 ? capped_threads : kDefaultThreads;
+  const int wpb = threads / 64;
+  int64_t blocks = (waves + wpb - 1) / wpb;
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (cap > 0) {
+    if (blocks > cap) blocks = cap;
+  } else if (round_to > 1) {
+    blocks = (blocks + round_to - 1) / round_to * round_to;
+  }
+  return {(unsigned)(blocks > 0 ? blocks : 1), threads};
+}
+
 // HIP error of the last failed launch on this thread (set by launch_status).
 hipError_t &last_hip_error();
 

@@ -219,16 +219,16 @@ __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
 // redundant scan costs O(T*K) per block, which is why larger inputs take the
 // two-launch path instead.
 template <int K, int NW>
-__global__ __launch_bounds__(kThreads) void ep_layout_fused_tiles(
+__device__ __forceinline__ void fused_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
-    int32_t *__restrict__ num_recv) {
+    int32_t *__restrict__ num_recv, const int b) {
   __shared__ int s_tmp[kWavesMax];
   const RankLds s = rank_lds(E, NW);
   int *s_pre = (int *)(g_smem + rank_lds_bytes(E, NW));  // E: entries before this tile
   int *s_all = s_pre + E;                                // E: all entries
   int *s_off = s_all + E;                                // E
-  const int tid = threadIdx.x, b = blockIdx.x;
+  const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)b * Tile<K, NW>::tokens;
   const int ntok = (int)min((int64_t)Tile<K, NW>::tokens, (int64_t)T - t0);
 
@@ -284,15 +284,34 @@ __global__ __launch_bounds__(kThreads) void ep_layout_fused_tiles(
   write_slots_and_meta<K>(t0, ntok, slot, s.tok, dst_slot, meta);
 }
 
+// Tile blockIdx.x, or with LOOP (the stream caps the workgroup count below
+// the tile count) tiles blockIdx.x, blockIdx.x + gridDim.x, ...; the barrier
+// lets the next tile reuse LDS. Without LOOP there is no loop to keep values
+// live across, which saves registers and a microsecond.
+template <int K, int NW, bool LOOP>
+__global__ __launch_bounds__(kThreads) void ep_layout_fused_tiles(
+    const int32_t *__restrict__ topk_idx, int T, int E, int A, int num_tiles,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot,
+    int32_t *__restrict__ meta, int32_t *__restrict__ num_recv) {
+  if constexpr (!LOOP) {
+    fused_tile<K, NW>(topk_idx, T, E, A, counts, offsets, dst_slot, meta, num_recv, blockIdx.x);
+  } else {
+    for (int b = blockIdx.x; b < num_tiles; b += gridDim.x) {
+      fused_tile<K, NW>(topk_idx, T, E, A, counts, offsets, dst_slot, meta, num_recv, b);
+      __syncthreads();
+    }
+  }
+}
+
 // First launch of the multi-tile path: per-tile histograms and ranks.
 // dst_slot temporarily holds (expert << kRankBits | rank-in-tile), or -1.
 template <int K, int NW>
-__global__ __launch_bounds__(kThreads) void ep_layout_tile_histogram(
+__device__ __forceinline__ void histogram_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int32_t *__restrict__ dst_slot,
-    int32_t *__restrict__ tile_counts, int32_t *__restrict__ tile_recv) {
+    int32_t *__restrict__ tile_counts, int32_t *__restrict__ tile_recv, const int b) {
   __shared__ int s_wtot[kWavesMax];
   const RankLds s = rank_lds(E, NW);
-  const int tid = threadIdx.x, b = blockIdx.x;
+  const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)b * Tile<K, NW>::tokens;
   const int ntok = (int)min((int64_t)Tile<K, NW>::tokens, (int64_t)T - t0);
 
@@ -304,20 +323,35 @@ __global__ __launch_bounds__(kThreads) void ep_layout_tile_histogram(
   if (tid == 0) tile_recv[b] = nrecv;
 }
 
-// Second launch: offsets, final slots and metadata for tile blockIdx.x.
+template <int K, int NW, bool LOOP>
+__global__ __launch_bounds__(kThreads) void ep_layout_tile_histogram(
+    const int32_t *__restrict__ topk_idx, int T, int E, int num_tiles,
+    int32_t *__restrict__ dst_slot, int32_t *__restrict__ tile_counts,
+    int32_t *__restrict__ tile_recv) {
+  if constexpr (!LOOP) {
+    histogram_tile<K, NW>(topk_idx, T, E, dst_slot, tile_counts, tile_recv, blockIdx.x);
+  } else {
+    for (int b = blockIdx.x; b < num_tiles; b += gridDim.x) {
+      histogram_tile<K, NW>(topk_idx, T, E, dst_slot, tile_counts, tile_recv, b);
+      __syncthreads();
+    }
+  }
+}
+
+// Second launch: offsets, final slots and metadata for tile b.
 template <int K, int NW>
-__global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
+__device__ __forceinline__ void assign_tile(
     int T, int E, int A, int num_tiles, const int32_t *__restrict__ tile_counts,
     const int32_t *__restrict__ tile_recv, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
-    int32_t *__restrict__ num_recv) {
+    int32_t *__restrict__ num_recv, const int b) {
   __shared__ int s_pre[kThreads];
   __shared__ int s_tot[kThreads];
   __shared__ int s_row[kThreads];
   __shared__ int s_tmp[kWavesMax];
   int *s_base = (int *)g_smem;  // E
   int *s_off = s_base + E;      // E
-  const int tid = threadIdx.x, b = blockIdx.x;
+  const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)b * Tile<K, NW>::tokens;
   const int ntok = (int)min((int64_t)Tile<K, NW>::tokens, (int64_t)T - t0);
 
@@ -388,32 +422,60 @@ __global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
   write_slots_and_meta<K>(t0, ntok, slot, s_row, dst_slot, meta);
 }
 
+template <int K, int NW, bool LOOP>
+__global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
+    int T, int E, int A, int num_tiles, const int32_t *__restrict__ tile_counts,
+    const int32_t *__restrict__ tile_recv, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
+    int32_t *__restrict__ num_recv) {
+  if constexpr (!LOOP) {
+    assign_tile<K, NW>(T, E, A, num_tiles, tile_counts, tile_recv, counts, offsets, dst_slot,
+                       meta, num_recv, blockIdx.x);
+  } else {
+    for (int b = blockIdx.x; b < num_tiles; b += gridDim.x) {
+      assign_tile<K, NW>(T, E, A, num_tiles, tile_counts, tile_recv, counts, offsets, dst_slot,
+                         meta, num_recv, b);
+      __syncthreads();
+    }
+  }
+}
+
 template <int K, int NW>
 int tiles_for(int T) {
   return (T + Tile<K, NW>::tokens - 1) / Tile<K, NW>::tokens;
 }
 
-template <int K, int NW>
-int layout_impl(const LayoutArgs &a) {
-  const int B = tiles_for<K, NW>(a.T);
+template <int K, int NW, bool LOOP>
+int layout_launch(const LayoutArgs &a, int B, unsigned G) {
   const size_t shm_rank = rank_lds_bytes(a.E, NW);
-  if (B <= 1) {
-    ep_layout_single_tile<K, NW><<<1, kThreads, shm_rank + sizeof(int) * (size_t)a.E, a.stream>>>(
-        a.topk_idx, a.T, a.E, a.A, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
-  } else if ((int64_t)a.T * K <= kFusedMaxEntries) {
-    ep_layout_fused_tiles<K, NW>
-        <<<B, kThreads, shm_rank + sizeof(int) * (size_t)(3 * a.E), a.stream>>>(
-            a.topk_idx, a.T, a.E, a.A, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
+  if ((int64_t)a.T * K <= kFusedMaxEntries) {
+    ep_layout_fused_tiles<K, NW, LOOP>
+        <<<G, kThreads, shm_rank + sizeof(int) * (size_t)(3 * a.E), a.stream>>>(
+            a.topk_idx, a.T, a.E, a.A, B, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
   } else {
     int32_t *tile_counts = (int32_t *)a.workspace;
     int32_t *tile_recv = tile_counts + (size_t)B * a.E;
-    ep_layout_tile_histogram<K, NW><<<B, kThreads, shm_rank, a.stream>>>(
-        a.topk_idx, a.T, a.E, a.dst_slot, tile_counts, tile_recv);
-    ep_layout_tile_assign<K, NW><<<B, kThreads, sizeof(int) * (size_t)(2 * a.E), a.stream>>>(
+    ep_layout_tile_histogram<K, NW, LOOP><<<G, kThreads, shm_rank, a.stream>>>(
+        a.topk_idx, a.T, a.E, B, a.dst_slot, tile_counts, tile_recv);
+    ep_layout_tile_assign<K, NW, LOOP><<<G, kThreads, sizeof(int) * (size_t)(2 * a.E), a.stream>>>(
         a.T, a.E, a.A, B, tile_counts, tile_recv, a.counts, a.offsets, a.dst_slot, a.meta,
         a.num_recv);
   }
   return launch_status();
+}
+
+template <int K, int NW>
+int layout_impl(const LayoutArgs &a) {
+  const int B = tiles_for<K, NW>(a.T);
+  if (B <= 1) {
+    const size_t shm_rank = rank_lds_bytes(a.E, NW);
+    ep_layout_single_tile<K, NW><<<1, kThreads, shm_rank + sizeof(int) * (size_t)a.E, a.stream>>>(
+        a.topk_idx, a.T, a.E, a.A, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
+    return launch_status();
+  }
+  const int cap = stream_workgroup_limit(a.stream);
+  if (cap > 0 && cap < B) return layout_launch<K, NW, true>(a, B, (unsigned)cap);
+  return layout_launch<K, NW, false>(a, B, (unsigned)B);
 }
 
 template <int K>

@@ -20,10 +20,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
-
-__global__ __launch_bounds__(kThreads) void ep_zero_padding_rows(
+__global__ __launch_bounds__(kCappedThreads) void ep_zero_padding_rows(
     u32x4 *__restrict__ expand_x, int64_t row_chunks, float *__restrict__ expand_scales,
     int64_t scale_cols, float *__restrict__ expand_weights, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, int E, int A, int64_t capacity) {
@@ -31,9 +28,10 @@ __global__ __launch_bounds__(kThreads) void ep_zero_padding_rows(
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int64_t total = (int64_t)E * (A - 1) * slices;
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t stride = (int64_t)gridDim.x * kWavesPerBlock;
+  const int wpb = blockDim.x / kWave;
+  const int64_t stride = (int64_t)gridDim.x * wpb;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block; gw < total;
+  for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < total;
        gw += stride) {
     const int64_t er = gw / slices;
     const int64_t slice = gw - er * slices;
@@ -60,10 +58,9 @@ int launch_zero_padding(const ZeroPaddingArgs &a) {
   if (a.A <= 1) return 0;  // no padding rows exist
   const int64_t row_chunks = a.row_bytes / 16;
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
-  const int64_t waves = (int64_t)a.E * (a.A - 1) * slices;
-  int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  blocks = blocks < (1 << 22) ? blocks : (1 << 22);  // larger inputs loop
-  ep_zero_padding_rows<<<(unsigned)blocks, kThreads, 0, a.stream>>>(
+  const WaveGrid g =
+      wave_grid((int64_t)a.E * (a.A - 1) * slices, stream_workgroup_limit(a.stream), 1 << 22);
+  ep_zero_padding_rows<<<g.blocks, g.threads, 0, a.stream>>>(
       (u32x4 *)a.expand_x, row_chunks, a.expand_scales, a.scale_cols, a.expand_weights, a.counts,
       a.offsets, a.E, a.A, a.capacity);
   return launch_status();

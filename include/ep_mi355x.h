@@ -239,6 +239,31 @@ int ep_zero_padding(void *expand_x, int64_t row_bytes, float *expand_scales, int
                     int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
                     void *stream);
 
+/*
+ * CU-limited mode ("MORI JIT v2" section 5.1: geometry buckets prefer the
+ * smaller workgroup count when times are close, because compute units left
+ * free overlap with the expert GEMM, and the workgroup count never exceeds the
+ * CU count; the EpCfg default of sections 3.2 and 3.5 is 64 workgroups. DeepEP overall
+ * architecture, design goals: communication on a few SMs, 4 to 64).
+ *
+ * Caps every kernel this library launches on `stream` (a hipStream_t; NULL
+ * is the null stream) at max_workgroups workgroups, each sized to keep one
+ * compute unit busy (1024 threads; 512 for combine), whose waves loop over
+ * the work; the other compute units stay free for kernels on other streams.
+ * Results are identical with and without a cap. max_workgroups = 0 removes
+ * the cap (the default: grids cover all work with 256-thread workgroups);
+ * values above the current device's compute-unit count are clamped to it.
+ * The cap is kept per stream handle, process-wide, until changed: clear it
+ * (0) before destroying the stream, since HIP may reuse the handle.
+ * Thread-safe; takes effect for launches made after it returns. Errors:
+ * EP_EINVAL for max_workgroups < 0, EP_EHIP if the compute-unit count cannot
+ * be read (no device).
+ */
+int ep_set_workgroup_limit(void *stream, int32_t max_workgroups);
+
+/* The cap in effect for `stream` (after clamping), or 0 if none. Never fails. */
+int ep_get_workgroup_limit(void *stream);
+
 /* Message for the last failed call on the calling thread ("" if none). */
 const char *ep_last_error(void);
 

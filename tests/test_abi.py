@@ -181,3 +181,10 @@ def test_compact_rejections(L):
     assert _code(B.ep_combine_compact, *cc(H=7172)) == B.EP_EINVAL
     assert _code(B.ep_combine_compact, *cc(n=None)) == B.EP_EINVAL
     assert _code(B.ep_combine_compact, *cc(b=ODD)) == B.EP_EINVAL
+
+
+def test_workgroup_limit_host_side(L):
+    assert _code(B.ep_set_workgroup_limit, FAKE, -1) == B.EP_EINVAL
+    B.ep_set_workgroup_limit(FAKE, 0)  # clearing a cap that was never set is fine
+    assert B.ep_get_workgroup_limit(FAKE) == 0
+    assert B.ep_get_workgroup_limit(None) == 0
