@@ -273,9 +273,9 @@ int ep_zero_padding(void *expand_x, int64_t row_bytes, float *expand_scales, int
                   num_experts);
     if (expert_alignment < 1)
       return fail(EP_EINVAL, "%s: expert_alignment must be >= 1 (got %d)", what, expert_alignment);
-    if (row_bytes < 16 || row_bytes % 16 != 0)
-      return fail(EP_EINVAL, "%s: row_bytes must be a positive multiple of 16 (got %lld)", what,
-                  (long long)row_bytes);
+    if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > INT32_MAX)
+      return fail(EP_EINVAL, "%s: row_bytes must be a positive multiple of 16 below 2^31 (got %lld)",
+                  what, (long long)row_bytes);
     if (capacity_rows < 0 || scale_cols < 0)
       return fail(EP_EINVAL, "%s: capacity_rows and scale_cols must be >= 0", what);
     if (!expand_x || !counts || !offsets || (scale_cols > 0 && !expand_scales))
@@ -309,9 +309,9 @@ int ep_dispatch_compact(const void *x, const float *x_scales, const int32_t *top
     else if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2) elt = 1;
     else return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
     const int64_t row_bytes = (int64_t)hidden * elt;
-    if (hidden < 1 || row_bytes % 16 != 0)
-      return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 (got %lld)", what,
-                  (long long)row_bytes);
+    if (hidden < 1 || row_bytes % 16 != 0 || row_bytes > INT32_MAX)
+      return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 below 2^31 (got %lld)",
+                  what, (long long)row_bytes);
     if ((x_scales == nullptr) != (recv_scales == nullptr))
       return fail(EP_EINVAL, "%s: x_scales and recv_scales go together", what);
     int64_t scale_cols = 0;
@@ -357,9 +357,9 @@ int ep_combine_compact(const void *expert_out, const void *bias, const int32_t *
       return fail(EP_EUNSUPPORTED, "%s: only bf16 rows are compiled for the non-expand combine",
                   what);
     if (dtype != EP_BF16) return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
-    if (hidden < 1 || ((int64_t)hidden * 2) % 16 != 0)
-      return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 (hidden %d)", what,
-                  hidden);
+    if (hidden < 1 || ((int64_t)hidden * 2) % 16 != 0 || (int64_t)hidden * 2 > INT32_MAX)
+      return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 below 2^31 (hidden %d)",
+                  what, hidden);
     if (num_tokens > 0 && (!expert_out || !dst_slot || !recv_src_metadata || !num_recv || !out))
       return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
     if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(bias, 16))

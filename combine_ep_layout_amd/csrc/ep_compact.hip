@@ -19,7 +19,6 @@
 namespace ep {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -28,6 +27,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
+// WIDE: launched over the whole chip (no workgroup cap), which selects the
+// store policy (store_row_nt).
+template <bool WIDE>
 __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     const u32x4 *__restrict__ x, int64_t row_chunks, const float *__restrict__ x_scales,
     int64_t scale_cols, const int32_t *__restrict__ topk_idx,
@@ -51,7 +53,8 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     if (t < 0 || t >= T) continue;
     const int64_t c = slice * kWave + lane;
     if (c < row_chunks)
-      __builtin_nontemporal_store(x[t * row_chunks + c], recv_x + i * row_chunks + c);
+      store_row_nt<WIDE>(x[t * row_chunks + c], recv_x + i * row_chunks, (int)(row_chunks * 16),
+                         (int)(c * 16));
     if (slice == 0) {
       if (recv_scales != nullptr)
         for (int64_t j = lane; j < scale_cols; j += kWave)
@@ -66,6 +69,7 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
 }
 
 // out[t] chunk c = v (+ bias[t] chunk c), one binary32 add per value, RNE.
+template <bool WIDE>
 __device__ __forceinline__ void put_row_chunk(u32x4 v, const u32x4 *__restrict__ bias, int64_t t,
                                               int64_t row_chunks, int64_t c,
                                               u32x4 *__restrict__ out) {
@@ -81,13 +85,14 @@ __device__ __forceinline__ void put_row_chunk(u32x4 v, const u32x4 *__restrict__
     }
     v = r;
   }
-  __builtin_nontemporal_store(v, out + t * row_chunks + c);
+  store_row_nt<WIDE>(v, out + t * row_chunks, (int)(row_chunks * 16), (int)(c * 16));
 }
 
 // Waves [0, T*slices): (receive row, slice) back to its token. Waves
 // [T*slices, T*slices + T): one per token; a token with no unmasked entry
 // (none of its K slots valid) gets +0 (+ bias) over its whole row, the
 // others exit after one K-wide read.
+template <bool WIDE>
 __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
     const u32x4 *__restrict__ y, int64_t row_chunks, const u32x4 *__restrict__ bias,
     const int32_t *__restrict__ dst_slot, const int32_t *__restrict__ meta,
@@ -107,16 +112,34 @@ __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
       if (r >= n) continue;
       const int64_t t = __builtin_amdgcn_readfirstlane(meta[r * (K + 2)]);
       if (t < 0 || t >= T || c >= row_chunks) continue;
-      put_row_chunk(__builtin_nontemporal_load(y + r * row_chunks + c), bias, t, row_chunks, c,
-                    out);
+      put_row_chunk<WIDE>(__builtin_nontemporal_load(y + r * row_chunks + c), bias, t, row_chunks, c,
+                          out);
     } else {
       const int64_t t = gw - half;
       bool any = false;
       for (int k = lane; k < K; k += kWave) any |= dst_slot[t * K + k] >= 0;
       if (ballot(any) != 0) continue;  // received: written by its receive row
-      for (int64_t c = lane; c < row_chunks; c += kWave) put_row_chunk(zero, bias, t, row_chunks, c, out);
+      for (int64_t c = lane; c < row_chunks; c += kWave)
+        put_row_chunk<WIDE>(zero, bias, t, row_chunks, c, out);
     }
   }
+}
+
+template <bool WIDE>
+int dispatch_compact_launch(const CompactDispatchArgs &a, const WaveGrid &g, int64_t row_chunks) {
+  ep_dispatch_compact_rows<WIDE><<<g.blocks, g.threads, 0, a.stream>>>(
+      (const u32x4 *)a.x, row_chunks, a.x_scales, a.scale_cols, a.topk_idx, a.topk_weights,
+      a.dst_slot, a.meta, a.num_recv, a.T, a.K, (u32x4 *)a.recv_x, a.recv_scales,
+      a.recv_topk_idx, a.recv_topk_weights);
+  return launch_status();
+}
+
+template <bool WIDE>
+int combine_compact_launch(const CompactCombineArgs &a, const WaveGrid &g, int64_t row_chunks) {
+  ep_combine_compact_rows<WIDE><<<g.blocks, g.threads, 0, a.stream>>>(
+      (const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias, a.dst_slot, a.meta, a.num_recv, a.T,
+      a.K, (u32x4 *)a.out);
+  return launch_status();
 }
 
 }  // namespace
@@ -125,25 +148,20 @@ int launch_dispatch_compact(const CompactDispatchArgs &a) {
   if (a.T == 0) return 0;
   const int64_t row_chunks = a.row_bytes / 16;
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
-  const WaveGrid g =  // larger inputs loop
-      wave_grid((int64_t)a.T * slices, stream_workgroup_limit(a.stream), 1 << 22);
-  ep_dispatch_compact_rows<<<g.blocks, g.threads, 0, a.stream>>>(
-      (const u32x4 *)a.x, row_chunks, a.x_scales, a.scale_cols, a.topk_idx, a.topk_weights,
-      a.dst_slot, a.meta, a.num_recv, a.T, a.K, (u32x4 *)a.recv_x, a.recv_scales,
-      a.recv_topk_idx, a.recv_topk_weights);
-  return launch_status();
+  const int cap = stream_workgroup_limit(a.stream);
+  const WaveGrid g = wave_grid((int64_t)a.T * slices, cap, 1 << 22);  // larger inputs loop
+  return cap > 0 ? dispatch_compact_launch<false>(a, g, row_chunks)
+                 : dispatch_compact_launch<true>(a, g, row_chunks);
 }
 
 int launch_combine_compact(const CompactCombineArgs &a) {
   if (a.T == 0) return 0;
   const int64_t row_chunks = a.row_bytes / 16;
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
-  const WaveGrid g =
-      wave_grid((int64_t)a.T * (slices + 1), stream_workgroup_limit(a.stream), 1 << 22);
-  ep_combine_compact_rows<<<g.blocks, g.threads, 0, a.stream>>>((const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias,
-                                        a.dst_slot, a.meta, a.num_recv, a.T, a.K,
-                                        (u32x4 *)a.out);
-  return launch_status();
+  const int cap = stream_workgroup_limit(a.stream);
+  const WaveGrid g = wave_grid((int64_t)a.T * (slices + 1), cap, 1 << 22);
+  return cap > 0 ? combine_compact_launch<false>(a, g, row_chunks)
+                 : combine_compact_launch<true>(a, g, row_chunks);
 }
 
 }  // namespace ep

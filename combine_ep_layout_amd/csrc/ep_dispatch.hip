@@ -9,9 +9,10 @@
 //
 // Design (MI355X): the pass is HBM-bound on its writes (read T rows, write
 // T*K rows). One wave64 moves one 1 KiB slice of one (token, k) row: a
-// 16-byte load per lane from x and one non-temporal 16-byte store per lane
-// into the expand row, whose address is wave-uniform (the slot is loaded
-// once and made scalar with readfirstlane). Waves are ordered token-major,
+// 16-byte load per lane from x and one 16-byte store per lane into the
+// expand row, whose address is wave-uniform (the slot is loaded once and made
+// scalar with readfirstlane). The store is non-temporal at device scope
+// (store_row_nt): expand rows are not read again by this pass. Waves are ordered token-major,
 // then k, then slice, so the write stream is one destination row after
 // another, each written front to back; the K waves that need the same source
 // slice run on the same XCD, so x is read from HBM about once. Row bytes and
@@ -27,7 +28,6 @@
 namespace ep {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Blocks run on the 8 XCDs round-robin (block b on XCD b % 8). Renumbering
 // them so that each XCD gets one contiguous eighth of the work keeps the K
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
     if (d < 0 || d >= capacity) continue;
     const int i = slice * kWave + lane;
     if (CH % kWave == 0 || i < CH)
-      __builtin_nontemporal_store(x[t * CH + i], expand_x + (int64_t)d * CH + i);
+      store_row_nt<true>(x[t * CH + i], expand_x + (int64_t)d * CH, ROWB, i * 16);
     if (slice == 0) {
       if (SCH > 0 && lane < SCH)
         __builtin_nontemporal_store(x_scales[t * SCH + lane],

@@ -18,8 +18,10 @@
 namespace ep {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// WIDE: launched over the whole chip (no workgroup cap), which selects the
+// store policy (store_row_nt).
+template <bool WIDE>
 __global__ __launch_bounds__(kCappedThreads) void ep_zero_padding_rows(
     u32x4 *__restrict__ expand_x, int64_t row_chunks, float *__restrict__ expand_scales,
     int64_t scale_cols, float *__restrict__ expand_weights, const int32_t *__restrict__ counts,
@@ -43,7 +45,8 @@ __global__ __launch_bounds__(kCappedThreads) void ep_zero_padding_rows(
     const int64_t row = begin + r;
     if (row >= end || row >= capacity || row < 0) continue;
     const int64_t i = slice * kWave + lane;
-    if (i < row_chunks) __builtin_nontemporal_store(zero, expand_x + row * row_chunks + i);
+    if (i < row_chunks)
+      store_row_nt<WIDE>(zero, expand_x + row * row_chunks, (int)(row_chunks * 16), (int)(i * 16));
     if (slice == 0) {
       if (expand_scales != nullptr)
         for (int64_t j = lane; j < scale_cols; j += kWave) expand_scales[row * scale_cols + j] = 0.0f;
@@ -58,11 +61,16 @@ int launch_zero_padding(const ZeroPaddingArgs &a) {
   if (a.A <= 1) return 0;  // no padding rows exist
   const int64_t row_chunks = a.row_bytes / 16;
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
-  const WaveGrid g =
-      wave_grid((int64_t)a.E * (a.A - 1) * slices, stream_workgroup_limit(a.stream), 1 << 22);
-  ep_zero_padding_rows<<<g.blocks, g.threads, 0, a.stream>>>(
-      (u32x4 *)a.expand_x, row_chunks, a.expand_scales, a.scale_cols, a.expand_weights, a.counts,
-      a.offsets, a.E, a.A, a.capacity);
+  const int cap = stream_workgroup_limit(a.stream);
+  const WaveGrid g = wave_grid((int64_t)a.E * (a.A - 1) * slices, cap, 1 << 22);
+  if (cap > 0)
+    ep_zero_padding_rows<false><<<g.blocks, g.threads, 0, a.stream>>>(
+        (u32x4 *)a.expand_x, row_chunks, a.expand_scales, a.scale_cols, a.expand_weights, a.counts,
+        a.offsets, a.E, a.A, a.capacity);
+  else
+    ep_zero_padding_rows<true><<<g.blocks, g.threads, 0, a.stream>>>(
+        (u32x4 *)a.expand_x, row_chunks, a.expand_scales, a.scale_cols, a.expand_weights, a.counts,
+        a.offsets, a.E, a.A, a.capacity);
   return launch_status();
 }
 
