@@ -10,11 +10,11 @@ C ABI on torch's current stream. Default workload: 4096 tokens, hidden 7168,
 --path non-expand times the other layout mode instead: ep_layout,
 ep_dispatch_compact (one row per received token, with its expert ids and
 router weights) and ep_combine_compact (rows back to token order).
---cold reads a 512 MB scratch buffer before every step, so no step finds
-its inputs in the 256 MB last-level cache (MALL); a read leaves only clean
-lines behind, so the step pays no write-back of the flush itself. Per-kernel
-events are then recorded on every step and `value` comes from them (the
-flush is not part of the step). Every run also times torch's copy_ of 1 GiB (16-byte
+--cold rotates several complete sets of input and output buffers (x, scale
+rows, expert outputs, expand / receive buffers, out), enough that at least
+512 MB of other traffic separates two uses of a set, so no step finds its
+rows in the 256 MB last-level cache (MALL); nothing but steps runs in the
+timed loop. Every run also times torch's copy_ of 1 GiB (16-byte
 vector loads and stores) and reports the path as a fraction of that copy.
 --workgroups L runs the step on a stream capped at L workgroups (the
 CU-limited mode); --overlap-gemm additionally times a bf16 GEMM on a second
@@ -235,7 +235,7 @@ def main():
                     help="expand: one row per (token, expert) (the default, headline path); "
                          "non-expand: one row per received token")
     ap.add_argument("--cold", action="store_true",
-                    help="evict the last-level cache (512 MB scratch read) before every step")
+                    help="rotate buffer sets so that no step finds its rows in the last-level cache")
     ap.add_argument("--workgroups", type=int, default=0,
                     help="cap every kernel of the step at this many workgroups (0: no cap)")
     ap.add_argument("--overlap-gemm", action="store_true",
@@ -287,8 +287,7 @@ def main():
         # the expert side's reduced output: one bf16 row per received token
         case.extra["y_ne"] = I.normal_bf16(w.seed, I.STREAM_Y, w.T, H_out)
         case.y = case.extra["y_ne"]
-    idx, wts, x, y = up(case.topk_idx), up(case.topk_weights), up(case.x), up(case.y)
-    xs = up(case.x_scales) if case.x_scales is not None else None
+    idx, wts = up(case.topk_idx), up(case.topk_weights)
     rowb = case.x.view(np.uint8).reshape(w.T, -1).shape[1]
     counts = torch.empty(w.E, dtype=torch.int32, device=dev)
     offsets = torch.empty(w.E + 1, dtype=torch.int32, device=dev)
@@ -298,20 +297,32 @@ def main():
     wsb = B.ep_layout_workspace_bytes(w.T, w.K, w.E)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     rows_out = w.T if non_expand else w.cap
-    expand = torch.zeros((rows_out, rowb), dtype=torch.uint8, device=dev)
-    expand_s = (torch.zeros((rows_out, scale_cols), dtype=torch.float32, device=dev)
-                if xs is not None else None)
-    recv_i = torch.empty((w.T, w.K), dtype=torch.int32, device=dev) if non_expand else None
-    recv_w = torch.empty((w.T, w.K), dtype=torch.float32, device=dev) if non_expand else None
-    out = torch.empty((w.T, H_out), dtype=torch.float32 if w.out_dtype == 1 else torch.int16,
-                      device=dev)
+
+    def buffer_set():
+        """The rows one step reads and writes (the small layout arrays are shared)."""
+        xs_d = up(case.x_scales) if case.x_scales is not None else None
+        return {
+            "x": up(case.x), "xs": xs_d, "y": up(case.y),
+            "expand": torch.zeros((rows_out, rowb), dtype=torch.uint8, device=dev),
+            "expand_s": (torch.zeros((rows_out, scale_cols), dtype=torch.float32, device=dev)
+                         if xs_d is not None else None),
+            "recv_i": torch.empty((w.T, w.K), dtype=torch.int32, device=dev) if non_expand else None,
+            "recv_w": torch.empty((w.T, w.K), dtype=torch.float32, device=dev) if non_expand else None,
+            "out": torch.empty((w.T, H_out), dtype=torch.float32 if w.out_dtype == 1 else torch.int16,
+                               device=dev),
+        }
+
+    step_bytes = sum(algorithmic_bytes(w, w.T * w.K, w.T, args.path).values())
+    nsets = 1
+    if args.cold:  # at least 512 MB of other steps' traffic between two uses of a set
+        nsets = min(32, max(2, -(-(512 << 20) // step_bytes) + 1))
+    sets = [buffer_set() for _ in range(nsets)]
     stream = torch.cuda.current_stream()
     if args.workgroups > 0:
         stream = torch.cuda.Stream()  # default priority
         B.ep_set_workgroup_limit(stream, args.workgroups)
         print(f"# workgroup cap {B.ep_get_workgroup_limit(stream)}", file=sys.stderr, flush=True)
     copy_gbps = copy_reference(torch, dev)
-    scratch = torch.ones(128 << 20, dtype=torch.int32, device=dev) if args.cold else None
     if args.copy_calibration:
         a = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -320,51 +331,52 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    def step(ev=None):
+    def step(S, ev=None):
         if ev is not None:
             ev[0].record(stream)
         B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws, wsb, stream)
         if ev is not None:
             ev[1].record(stream)
         if non_expand:
-            B.ep_dispatch_compact(x, xs, idx, wts, dst, meta, nrecv, w.T, w.H, w.K, w.dtype, expand,
-                                  expand_s, recv_i, recv_w, stream)
+            B.ep_dispatch_compact(S["x"], S["xs"], idx, wts, dst, meta, nrecv, w.T, w.H, w.K, w.dtype,
+                                  S["expand"], S["expand_s"], S["recv_i"], S["recv_w"], stream)
         else:
-            B.ep_dispatch(x, xs, None, dst, w.T, w.H, w.K, w.dtype, w.cap, expand, expand_s, None,
-                          stream)
+            B.ep_dispatch(S["x"], S["xs"], None, dst, w.T, w.H, w.K, w.dtype, w.cap, S["expand"],
+                          S["expand_s"], None, stream)
         if ev is not None:
             ev[2].record(stream)
         if non_expand:
-            B.ep_combine_compact(y, None, dst, meta, nrecv, w.T, H_out, w.K, 0, out, stream)
+            B.ep_combine_compact(S["y"], None, dst, meta, nrecv, w.T, H_out, w.K, 0, S["out"], stream)
         else:
-            B.ep_combine(y, wts, None, dst, w.T, H_out, w.K, w.out_dtype, w.cap, out, stream)
+            B.ep_combine(S["y"], wts, None, dst, w.T, H_out, w.K, w.out_dtype, w.cap, S["out"], stream)
         if ev is not None:
             ev[3].record(stream)
 
     torch.cuda.synchronize()  # inputs were written on the default stream
-    for _ in range(args.warmup):
-        if scratch is not None:
-            scratch.sum()
-        step()
-    every = 1 if args.cold else max(1, args.event_every)
+    for i in range(max(args.warmup, nsets)):
+        step(sets[i % nsets])
+    every = max(1, args.event_every)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
            for _ in range(0, args.steps, every)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if scratch is not None:
-            scratch.sum()  # reads 512 MB: evicts the 256 MB MALL; not part of the step
-        step(evs[i // every] if i % every == 0 else None)
+        step(sets[i % nsets], evs[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     us = {"layout": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3,
           "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
           "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3}
+    last = sets[(args.steps - 1) % nsets]  # every set holds the same results
+    x, y, expand, recv_i, recv_w, out = (last[k] for k in ("x", "y", "expand", "recv_i", "recv_w",
+                                                            "out"))
+    cache = ("warm" if nsets == 1 else
+             f"cold: {nsets} buffer sets rotated, "
+             f"{(nsets - 1) * step_bytes / 1e6:.0f} MB of other traffic between uses of a set")
 
-    if args.cold:  # the scratch writes are outside the step: value from the kernel events
-        ms_per_step = sum(us.values()) * 1e-3
-    overlap = overlap_gemm(torch, dev, step, ms_per_step, args.steps) if args.overlap_gemm else None
+    overlap = (overlap_gemm(torch, dev, lambda: step(sets[0]), ms_per_step, args.steps)
+               if args.overlap_gemm else None)
 
     # Validate the timed path against the oracle: layout in full, dispatch and combine sampled.
     import oracle
@@ -384,7 +396,7 @@ def main():
     if args.workgroups > 0:
         torch.cuda.synchronize()
         B.ep_set_workgroup_limit(stream, 0)
-    report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap)
+    report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap, cache)
 
 
 GEMM_SHAPE = (8192, 7168, 2048)  # M, K, N: bf16 [M, K] x [K, N], about one step's duration
@@ -477,7 +489,7 @@ def validate_expand(oracle, case, ref, expand, out, sample, xb, dev) -> bool:
     return bool(ok)
 
 
-def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=None):
+def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=None, cache="warm"):
     n_valid = int((ref["dst_slot"] >= 0).sum())
     nb = algorithmic_bytes(w, n_valid, ref["num_recv"], args.path)
     total_bytes = sum(nb.values())
@@ -489,7 +501,7 @@ def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=N
     dom_name = dom + ("_compact" if non_expand else "")
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": None if args.cold else measured_traffic(w.name, dom_name),
+                "traffic": measured_traffic(w.name, dom_name),
                 "algorithmic_bytes_per_launch": nb[dom], "avg_launch_us": round(us[dom], 2)}
     result = {
         "metric": METRIC,
@@ -510,7 +522,7 @@ def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=N
                    "dispatch_dtype": DTYPE_NAMES[w.dtype], "combine_dtype": DTYPE_NAMES[w.out_dtype],
                    "parallelism": "one GPU, all experts local", "path": args.path,
                    "workgroup_cap": args.workgroups or None,
-                   "cache": "cold (512 MB scratch read before every step)" if args.cold else "warm"},
+                   "cache": cache},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(w.T / (ms_per_step * 1e-3), 1),
         "dispatch_combine_GBps": round(dc_gbps, 1),
