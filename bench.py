@@ -36,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -92,11 +93,18 @@ def algorithmic_bytes(w, n_valid: int, n_recv: int, path: str = "expand") -> dic
     return {"layout": L, "dispatch": D, "combine": C}
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and whitespace: edits to either leave the kernels unchanged."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return re.sub(r"\s+", "", text)
+
+
 def sources_digest(path_mode: str = "expand") -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[path_mode]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -46,7 +46,8 @@ int check_topk(const char *what, int32_t T, int32_t K) {
   if (T < 0) return fail(EP_EINVAL, "%s: num_tokens must be >= 0 (got %d)", what, T);
   if (K < 1 || K > EP_MAX_TOPK)
     return fail(EP_EINVAL, "%s: topk must be in 1..%d (got %d)", what, EP_MAX_TOPK, K);
-  if ((int64_t)T * K > INT32_MAX) return fail(EP_EINVAL, "%s: num_tokens*topk overflows int32", what);
+  if ((int64_t)T * K > INT32_MAX)
+    return fail(EP_EINVAL, "%s: num_tokens*topk overflows int32", what);
   return EP_OK;
 }
 
@@ -83,7 +84,8 @@ int ep_set_workgroup_limit(void *stream, int32_t max_workgroups) {
     if (cap > 0) {  // never more workgroups than compute units
       int dev = 0, cus = 0;
       hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       if (e != hipSuccess)
         return fail(EP_EHIP, "ep_set_workgroup_limit: cannot read the compute-unit count: %s",
                     hipGetErrorString(e));
@@ -159,7 +161,8 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
     if (capacity_rows < worst)
       return fail(EP_ECAPACITY, "%s: capacity_rows %lld < worst case T*K + E*(A-1) = %lld", what,
                   (long long)capacity_rows, (long long)worst);
-    if (!counts || !offsets || !num_recv || (num_tokens > 0 && (!topk_idx || !dst_slot || !recv_src_metadata)))
+    if (!counts || !offsets || !num_recv ||
+        (num_tokens > 0 && (!topk_idx || !dst_slot || !recv_src_metadata)))
       return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
     if (!ep::has_layout(topk))
       return fail(EP_EUNSUPPORTED, "%s: topk %d has no compiled layout kernel", what, topk);
@@ -274,8 +277,9 @@ int ep_zero_padding(void *expand_x, int64_t row_bytes, float *expand_scales, int
     if (expert_alignment < 1)
       return fail(EP_EINVAL, "%s: expert_alignment must be >= 1 (got %d)", what, expert_alignment);
     if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > INT32_MAX)
-      return fail(EP_EINVAL, "%s: row_bytes must be a positive multiple of 16 below 2^31 (got %lld)",
-                  what, (long long)row_bytes);
+      return fail(EP_EINVAL,
+                  "%s: row_bytes must be a positive multiple of 16 below 2^31 (got %lld)", what,
+                  (long long)row_bytes);
     if (capacity_rows < 0 || scale_cols < 0)
       return fail(EP_EINVAL, "%s: capacity_rows and scale_cols must be >= 0", what);
     if (!expand_x || !counts || !offsets || (scale_cols > 0 && !expand_scales))
@@ -310,8 +314,9 @@ int ep_dispatch_compact(const void *x, const float *x_scales, const int32_t *top
     else return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
     const int64_t row_bytes = (int64_t)hidden * elt;
     if (hidden < 1 || row_bytes % 16 != 0 || row_bytes > INT32_MAX)
-      return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 below 2^31 (got %lld)",
-                  what, (long long)row_bytes);
+      return fail(EP_EINVAL,
+                  "%s: token bytes must be a positive multiple of 16 below 2^31 (got %lld)", what,
+                  (long long)row_bytes);
     if ((x_scales == nullptr) != (recv_scales == nullptr))
       return fail(EP_EINVAL, "%s: x_scales and recv_scales go together", what);
     int64_t scale_cols = 0;
@@ -358,8 +363,9 @@ int ep_combine_compact(const void *expert_out, const void *bias, const int32_t *
                   what);
     if (dtype != EP_BF16) return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
     if (hidden < 1 || ((int64_t)hidden * 2) % 16 != 0 || (int64_t)hidden * 2 > INT32_MAX)
-      return fail(EP_EINVAL, "%s: token bytes must be a positive multiple of 16 below 2^31 (hidden %d)",
-                  what, hidden);
+      return fail(EP_EINVAL,
+                  "%s: token bytes must be a positive multiple of 16 below 2^31 (hidden %d)", what,
+                  hidden);
     if (num_tokens > 0 && (!expert_out || !dst_slot || !recv_src_metadata || !num_recv || !out))
       return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
     if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(bias, 16))

@@ -215,7 +215,8 @@ int combine_impl(const CombineArgs &a) {
   constexpr int SPLIT = CombineGeometry<H * Elem<DT>::BYTES / 16>::SPLIT;
   const WaveGrid g = wave_grid((int64_t)a.T * SPLIT, stream_workgroup_limit(a.stream), INT32_MAX,
                                1, kCombineCappedThreads);
-  if (g.threads == kCombineCappedThreads) return combine_launch<DT, H, K, kCombineCappedThreads>(a, g);
+  if (g.threads == kCombineCappedThreads)
+    return combine_launch<DT, H, K, kCombineCappedThreads>(a, g);
   return combine_launch<DT, H, K, kDefaultThreads>(a, g);
 }
 

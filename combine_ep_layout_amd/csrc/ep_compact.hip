@@ -112,8 +112,8 @@ __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
       if (r >= n) continue;
       const int64_t t = __builtin_amdgcn_readfirstlane(meta[r * (K + 2)]);
       if (t < 0 || t >= T || c >= row_chunks) continue;
-      put_row_chunk<WIDE>(__builtin_nontemporal_load(y + r * row_chunks + c), bias, t, row_chunks, c,
-                          out);
+      const u32x4 v = __builtin_nontemporal_load(y + r * row_chunks + c);
+      put_row_chunk<WIDE>(v, bias, t, row_chunks, c, out);
     } else {
       const int64_t t = gw - half;
       bool any = false;

@@ -33,7 +33,9 @@ __device__ __forceinline__ void store_row_nt(const u32x4 &v, void *row, int row_
   }
 }
 
-__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
 
 // 64-bit ballot over the wavefront.
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
@@ -45,7 +47,9 @@ __device__ __forceinline__ int count_below(uint64_t mask) {
 }
 
 // Value of `v` held by lane `src` (src must be wave-uniform).
-__device__ __forceinline__ int read_lane(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ int read_lane(int v, int src) {
+  return __builtin_amdgcn_readlane(v, src);
+}
 __device__ __forceinline__ float read_lane(float v, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }

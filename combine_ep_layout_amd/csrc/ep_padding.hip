@@ -49,7 +49,8 @@ __global__ __launch_bounds__(kCappedThreads) void ep_zero_padding_rows(
       store_row_nt<WIDE>(zero, expand_x + row * row_chunks, (int)(row_chunks * 16), (int)(i * 16));
     if (slice == 0) {
       if (expand_scales != nullptr)
-        for (int64_t j = lane; j < scale_cols; j += kWave) expand_scales[row * scale_cols + j] = 0.0f;
+        for (int64_t j = lane; j < scale_cols; j += kWave)
+          expand_scales[row * scale_cols + j] = 0.0f;
       if (expand_weights != nullptr && lane == 0) expand_weights[row] = 0.0f;
     }
   }
