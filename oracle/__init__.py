@@ -93,6 +93,14 @@ def layout(topk_idx: np.ndarray, num_experts: int, expert_alignment: int, _lib=N
             "recv_src_metadata": meta[:n].copy(), "num_recv": n}
 
 
+def _byte_rows(a: np.ndarray, rows: int) -> np.ndarray:
+    """a as contiguous uint8 [rows, bytes per row]; the row length comes from
+    a's shape, so an array with zero rows keeps its width."""
+    a = np.ascontiguousarray(a)
+    width = int(np.prod(a.shape[1:], dtype=np.int64)) * a.itemsize if a.ndim > 1 else a.itemsize
+    return a.view(np.uint8).reshape(rows, width)
+
+
 def dispatch(x_bytes: np.ndarray, dst_slot: np.ndarray, capacity_rows: int,
              x_scales: np.ndarray = None, topk_weights: np.ndarray = None,
              expand_x: np.ndarray = None, expand_scales: np.ndarray = None,
@@ -103,9 +111,8 @@ def dispatch(x_bytes: np.ndarray, dst_slot: np.ndarray, capacity_rows: int,
     output buffers are not given they are allocated zero-filled, so padding
     rows read back as zero. Returns (expand_x, expand_scales, expand_weights).
     """
-    xb = np.ascontiguousarray(x_bytes).view(np.uint8)
-    T = xb.shape[0]
-    xb = xb.reshape(T, -1)
+    T = np.asarray(x_bytes).shape[0]
+    xb = _byte_rows(x_bytes, T)
     row_bytes = xb.shape[1]
     dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
     K = dst.shape[1]
@@ -115,7 +122,7 @@ def dispatch(x_bytes: np.ndarray, dst_slot: np.ndarray, capacity_rows: int,
     sb = 0
     xs = None
     if x_scales is not None:
-        xs = np.ascontiguousarray(x_scales).view(np.uint8).reshape(T, -1)
+        xs = _byte_rows(x_scales, T)
         sb = xs.shape[1]
         if expand_scales is None:
             expand_scales = np.zeros((cap, sb), np.uint8)
@@ -124,8 +131,8 @@ def dispatch(x_bytes: np.ndarray, dst_slot: np.ndarray, capacity_rows: int,
         w = np.ascontiguousarray(topk_weights, dtype=np.float32)
         if expand_weights is None:
             expand_weights = np.zeros(cap, np.float32)
-    ex = expand_x.view(np.uint8).reshape(cap, -1)
-    es = None if expand_scales is None else expand_scales.view(np.uint8).reshape(cap, -1)
+    ex = _byte_rows(expand_x, cap)
+    es = None if expand_scales is None else _byte_rows(expand_scales, cap)
     rc = lib(_lib).oracle_dispatch(_ptr(xb, _u8p), row_bytes, _ptr(xs, _u8p), sb, _ptr(w, _f32p),
                                _ptr(dst, _i32p), T, K, cap, _ptr(ex, _u8p), _ptr(es, _u8p),
                                _ptr(expand_weights if w is not None else None, _f32p))
@@ -139,9 +146,8 @@ def dispatch_compact(x_bytes: np.ndarray, topk_idx: np.ndarray, dst_slot: np.nda
                      topk_weights: np.ndarray = None, _lib=None):
     """Non-expand dispatch: (recv_x bytes [num_recv, row_bytes], recv_scales bytes or None,
     recv_topk_idx int32 [num_recv, K], recv_topk_weights float32 or None)."""
-    xb = np.ascontiguousarray(x_bytes).view(np.uint8)
-    T = xb.shape[0]
-    xb = xb.reshape(T, -1)
+    T = np.asarray(x_bytes).shape[0]
+    xb = _byte_rows(x_bytes, T)
     idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
     dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
     K = dst.shape[1]
@@ -150,7 +156,7 @@ def dispatch_compact(x_bytes: np.ndarray, topk_idx: np.ndarray, dst_slot: np.nda
     rx = np.zeros((n, xb.shape[1]), np.uint8)
     xs = rs = None
     if x_scales is not None:
-        xs = np.ascontiguousarray(x_scales).view(np.uint8).reshape(T, -1)
+        xs = _byte_rows(x_scales, T)
         rs = np.zeros((n, xs.shape[1]), np.uint8)
     w = None if topk_weights is None else np.ascontiguousarray(topk_weights, dtype=np.float32)
     ri = np.zeros((n, K), np.int32)
@@ -185,8 +191,8 @@ def zero_padding(expand_x: np.ndarray, counts: np.ndarray, offsets: np.ndarray,
                  expand_scales: np.ndarray = None, expand_weights: np.ndarray = None, _lib=None):
     """Zero the alignment padding rows of the expand buffers in place (and return them)."""
     cap = expand_x.shape[0]
-    ex = expand_x.view(np.uint8).reshape(cap, -1)
-    es = None if expand_scales is None else expand_scales.view(np.uint8).reshape(cap, -1)
+    ex = _byte_rows(expand_x, cap)
+    es = None if expand_scales is None else _byte_rows(expand_scales, cap)
     c = np.ascontiguousarray(counts, dtype=np.int32)
     o = np.ascontiguousarray(offsets, dtype=np.int32)
     rc = lib(_lib).oracle_zero_padding(_ptr(ex, _u8p), ex.shape[1], _ptr(es, _u8p),
