@@ -261,7 +261,8 @@ int ep_zero_padding(void *expand_x, int64_t row_bytes, float *expand_scales, int
  */
 int ep_set_workgroup_limit(void *stream, int32_t max_workgroups);
 
-/* The cap in effect for `stream` (after clamping), or 0 if none. Never fails. */
+/* The cap in effect for `stream` (after clamping), or 0 if none; EP_EHIP only if the
+ * registry's lock cannot be taken. */
 int ep_get_workgroup_limit(void *stream);
 
 /* Message for the last failed call on the calling thread ("" if none). */
