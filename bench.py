@@ -16,6 +16,9 @@ rows, expert outputs, expand / receive buffers, out), enough that at least
 rows in the 256 MB last-level cache (MALL); nothing but steps runs in the
 timed loop. Every run also times torch's copy_ of 1 GiB (16-byte
 vector loads and stores) and reports the path as a fraction of that copy.
+--graph N captures N consecutive steps in one hipGraph and times its
+replays for `value` (per-kernel times still come from the eager pass): the
+launch cost a caller pays when it captures several layers together.
 --workgroups L runs the step on a stream capped at L workgroups (the
 CU-limited mode); --overlap-gemm additionally times a bf16 GEMM on a second
 stream alone and interleaved with the steps, and reports how much of the
@@ -24,10 +27,10 @@ shorter of the two the overlap hides.
 Prints ONE JSON line. `value` is whole-step throughput: algorithmic HBM
 bytes of the three passes per step divided by the wall-clock step time
 (K steps bracketed by device synchronisation). Per-kernel times come from
-HIP events recorded on the same stream around each call, on every Nth timed
-step (--event-every, default 8: an event pair stalls the pipeline for a few
-microseconds, so recording them on every step would slow the steps they
-measure); the roofline
+HIP events recorded on the same stream around each call on every Nth timed
+step (--event-every, default 25: an instrumented step costs about 14 us
+more, so sparse events keep `value` within a fraction of a percent of an
+uninstrumented run); the roofline
 object reports the dominant kernel's algorithmic bytes over its mean event
 duration against the MI355X HBM peak (8 TB/s). The CPU baseline times the
 CPU oracle on the host (test infrastructure, never on the product path).
@@ -246,10 +249,12 @@ def main():
                     help="rotate buffer sets so that no step finds its rows in the last-level cache")
     ap.add_argument("--workgroups", type=int, default=0,
                     help="cap every kernel of the step at this many workgroups (0: no cap)")
+    ap.add_argument("--graph", type=int, default=0, metavar="N",
+                    help="time replays of a hipGraph holding N steps (0: eager launches)")
     ap.add_argument("--overlap-gemm", action="store_true",
                     help="also time a bf16 GEMM on a second stream, alone and overlapped")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=8,
+    ap.add_argument("--event-every", type=int, default=25,
                     help="record per-kernel HIP events on every Nth timed step (each event "
                          "pair costs a few microseconds of pipeline bubble)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -262,6 +267,8 @@ def main():
     if args.traffic_from:
         print(write_traffic(args.workload, *args.traffic_from, path_mode=args.path))
         return
+    if args.graph and args.workgroups:
+        raise SystemExit("--graph and --workgroups do not combine: a capture runs on its own stream")
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(every expert is local, a world of one); run with --gpus 1", file=sys.stderr)
@@ -339,7 +346,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    def step(S, ev=None):
+    def step(S, ev=None, stream=stream):
         if ev is not None:
             ev[0].record(stream)
         B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws, wsb, stream)
@@ -363,6 +370,9 @@ def main():
     torch.cuda.synchronize()  # inputs were written on the default stream
     for i in range(max(args.warmup, nsets)):
         step(sets[i % nsets])
+    # HIP events around each kernel on every Nth timed step: an instrumented
+    # step costs about 14 us more (each event drains the pipeline), so sparse
+    # events keep the wall-clock value within a fraction of a percent.
     every = max(1, args.event_every)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
            for _ in range(0, args.steps, every)]
@@ -376,6 +386,22 @@ def main():
     us = {"layout": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3,
           "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
           "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3}
+    launch = "eager"
+    if args.graph > 0:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.graph):
+                step(sets[i % nsets], stream=torch.cuda.current_stream())
+        for _ in range(3):
+            g.replay()
+        reps = max(1, args.steps // args.graph)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * args.graph)
+        launch = f"hipGraph of {args.graph} steps, {reps} replays"
     last = sets[(args.steps - 1) % nsets]  # every set holds the same results
     x, y, expand, recv_i, recv_w, out = (last[k] for k in ("x", "y", "expand", "recv_i", "recv_w",
                                                             "out"))
@@ -404,7 +430,7 @@ def main():
     if args.workgroups > 0:
         torch.cuda.synchronize()
         B.ep_set_workgroup_limit(stream, 0)
-    report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap, cache)
+    report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap, cache, launch)
 
 
 GEMM_SHAPE = (8192, 7168, 2048)  # M, K, N: bf16 [M, K] x [K, N], about one step's duration
@@ -497,7 +523,8 @@ def validate_expand(oracle, case, ref, expand, out, sample, xb, dev) -> bool:
     return bool(ok)
 
 
-def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=None, cache="warm"):
+def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=None, cache="warm",
+           launch="eager"):
     n_valid = int((ref["dst_slot"] >= 0).sum())
     nb = algorithmic_bytes(w, n_valid, ref["num_recv"], args.path)
     total_bytes = sum(nb.values())
@@ -530,7 +557,7 @@ def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=N
                    "dispatch_dtype": DTYPE_NAMES[w.dtype], "combine_dtype": DTYPE_NAMES[w.out_dtype],
                    "parallelism": "one GPU, all experts local", "path": args.path,
                    "workgroup_cap": args.workgroups or None,
-                   "cache": cache},
+                   "cache": cache, "launch": launch},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(w.T / (ms_per_step * 1e-3), 1),
         "dispatch_combine_GBps": round(dc_gbps, 1),
