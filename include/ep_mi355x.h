@@ -84,7 +84,8 @@ size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_e
  * Routing layout (DeepEP overall architecture, EPHandle fields
  * num_unaligned_recv_tokens_perpert, psum_num_recv_tokens_per_expert,
  * dst_buffer_slot_idx, recv_src_metadata, num_recv_tokens,
- * num_expanded_tokens; notify warps "count per expert, compute target slot").
+ * num_expanded_tokens; in the dispatch data-flow figure the notify warps count
+ * entries per expert and compute each entry's target slot).
  *
  * Inputs
  *   topk_idx          int32 [num_tokens, topk]: expert id of each (t, k);

@@ -59,7 +59,8 @@
 
 /*
  * Step 1, per-expert token count ([DeepEP] EPHandle
- * num_unaligned_recv_tokens_perpert; notify warps "count per expert").
+ * num_unaligned_recv_tokens_perpert; the notify warps of the dispatch
+ * data-flow figure count entries per expert).
  */
 static void count_per_expert(const int32_t *topk_idx, int64_t n_entries,
                              int32_t E, int32_t *counts) {
@@ -86,7 +87,7 @@ static void aligned_exclusive_prefix(const int32_t *counts, int32_t E,
 
 /*
  * Step 3, destination slot of every (token, k) ([DeepEP] EPHandle
- * dst_buffer_slot_idx, "notify warps: compute target slot"): walk the
+ * dst_buffer_slot_idx; the notify warps compute each target slot): walk the
  * entries in token-major order and hand out the next free row of the
  * expert's segment.
  */
