@@ -6,12 +6,15 @@ include/ep_mi355x.h). Array arguments may be anything with ``data_ptr()``
 may be a torch stream (``.cuda_stream``), a raw hipStream_t (int) or None
 for the default stream. Every step of the path runs in the library's HIP
 kernels; this module never computes anything and never falls back to
-another implementation: if the library is missing it raises.
+another implementation: if the library is missing it raises. The
+environment variable EP_MI355X_LIB names another build of the same library
+to load instead (for example the host-sanitized libep_mi355x_asan.so).
 """
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep_mi355x.so")
+LIB_PATH = (os.environ.get("EP_MI355X_LIB")
+            or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libep_mi355x.so"))
 
 EP_OK = 0
 EP_EINVAL = -1

@@ -3,6 +3,10 @@
 Every translation unit is compiled for gfx950 only, with binary32 packed
 math disabled (-packed-fp32-ops), then linked into one shared library next
 to this file. Objects go to <repo>/_build/.
+
+`python build.py --asan-host` instead builds libep_mi355x_asan.so with
+AddressSanitizer on the host code only (device code is unchanged); load it
+with the clang ASan runtime preloaded to check the C ABI's host paths.
 """
 import concurrent.futures as cf
 import os
@@ -26,9 +30,13 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-fno-gpu-rdc", "-munsafe-fp-atomics"]
 
 
-def _compile(src: str, extra=()) -> str:
+ASAN_HOST = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_LIB = os.path.join(PKG, "libep_mi355x_asan.so")
+
+
+def _compile(src: str, extra=(), tag: str = "") -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
+    obj = os.path.join(BUILD, src + tag + ".o")
     if src.endswith(".hip"):
         cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, *extra, "-c", path, "-o", obj]
     else:
@@ -39,13 +47,19 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(out: str = LIB, extra=(), jobs: int = 4, verbose: bool = False) -> str:
+def build(out: str = LIB, extra=(), jobs: int = 4, verbose: bool = False,
+          asan_host: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
+    if asan_host:
+        extra = (*extra, *ASAN_HOST)
+        out = ASAN_LIB if out == LIB else out
+    tag = ".asan" if asan_host else ""
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, extra, tag), SOURCES))
     tmp = out + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    link_extra = ["-Xarch_host", "-fsanitize=address"] if asan_host else []
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -56,4 +70,6 @@ def build(out: str = LIB, extra=(), jobs: int = 4, verbose: bool = False) -> str
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra=sys.argv[1:])
+    args = sys.argv[1:]
+    asan = "--asan-host" in args
+    build(verbose=True, extra=[a for a in args if a != "--asan-host"], asan_host=asan)
