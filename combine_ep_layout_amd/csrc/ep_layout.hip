@@ -39,6 +39,12 @@ constexpr int kRankBits = 10;  // rank inside a tile < 1024
 // through the workspace. Measured on MI355X (E=256, top-8): one launch wins
 // up to 16K entries (11.4 vs 12.8 us), two launches from 32K (12.3 vs 13.3).
 constexpr int64_t kFusedMaxEntries = 1 << 14;
+// Longest walk over tiles (loads per thread) the second launch of the
+// many-tile path does itself; beyond it a tile-scan launch runs first.
+// Measured on MI355X: without the scan 9.7 / 10.3 / 11.7 / 18.5 / 80.8 us at
+// walks of 8 / 16 / 32 / 128 / 512 tiles; with it about 12-13 us, then
+// growing slowly with the tile count (21 us at 512 tiles of 1024 experts).
+constexpr int kScanMinWalk = 64;
 
 // Waves of entries per tile for E experts: the lane masks (E x NW x 8 bytes)
 // stay within 32 KiB of LDS.
@@ -338,11 +344,23 @@ __global__ __launch_bounds__(kThreads) void ep_layout_tile_histogram(
   }
 }
 
-// Second launch: offsets, final slots and metadata for tile b.
-template <int K, int NW>
+// Per-tile prefixes computed by ep_layout_tile_scan (used when there are
+// many tiles): exclusive prefix over tiles of each expert's count, the
+// expert totals, and the same for received tokens.
+struct TileScan {
+  const int32_t *tile_base;     // [B][E]
+  const int32_t *expert_total;  // [E]
+  const int32_t *recv_base;     // [B]
+  const int32_t *recv_total;    // [1]
+};
+
+// Second launch: offsets, final slots and metadata for tile b. Without
+// SCANNED every block sums the per-tile counts of all tiles itself (P threads
+// per expert); with SCANNED it reads the prefixes of ep_layout_tile_scan.
+template <int K, int NW, bool SCANNED>
 __device__ __forceinline__ void assign_tile(
     int T, int E, int A, int num_tiles, const int32_t *__restrict__ tile_counts,
-    const int32_t *__restrict__ tile_recv, int32_t *__restrict__ counts,
+    const int32_t *__restrict__ tile_recv, const TileScan &scan, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
     int32_t *__restrict__ num_recv, const int b) {
   __shared__ int s_pre[kThreads];
@@ -357,37 +375,46 @@ __device__ __forceinline__ void assign_tile(
 
   // Every global load of the block is issued before the first barrier.
   const int packed = tid < ntok * K ? dst_slot[t0 * K + tid] : -1;
-  // Per expert: entries in tiles before b, and in all tiles. P threads share
-  // an expert so that each thread has only a few loads, all in flight.
-  const int epad = E <= 1 ? 1 : 1 << (32 - __builtin_clz((unsigned)(E - 1)));
-  const int P = kThreads / epad;
-  const int ex = tid % epad, part = tid / epad;
-  int pre = 0, tot = 0;
-  if (ex < E) {
-#pragma unroll 8
-    for (int bb = part; bb < num_tiles; bb += P) {
-      const int c = tile_counts[(int64_t)bb * E + ex];
-      tot += c;
-      pre += bb < b ? c : 0;
+  int base = 0, cnt = 0, recv_before, recv_total;
+  if constexpr (SCANNED) {
+    if (tid < E) {
+      base = scan.tile_base[(int64_t)b * E + tid];
+      cnt = scan.expert_total[tid];
     }
-  }
-  int vpre = 0, vtot = 0;
-  for (int bb = tid; bb < num_tiles; bb += kThreads) {
-    const int c = tile_recv[bb];
-    vtot += c;
-    vpre += bb < b ? c : 0;
-  }
-  s_pre[tid] = pre;
-  s_tot[tid] = tot;
-  if (tid < Tile<K, NW>::tokens) s_row[tid] = 0;
-  const int recv_before = block_sum(vpre, s_tmp);  // its barriers publish s_pre / s_tot
-  const int recv_total = block_sum(vtot, s_tmp);
-
-  int base = 0, cnt = 0;
-  if (tid < E) {
-    for (int j = 0; j < P; ++j) {
-      base += s_pre[j * epad + tid];
-      cnt += s_tot[j * epad + tid];
+    recv_before = scan.recv_base[b];
+    recv_total = *scan.recv_total;
+    if (tid < Tile<K, NW>::tokens) s_row[tid] = 0;  // published by the scan's barriers below
+  } else {
+    // Per expert: entries in tiles before b, and in all tiles. P threads share
+    // an expert so that each thread has only a few loads, all in flight.
+    const int epad = E <= 1 ? 1 : 1 << (32 - __builtin_clz((unsigned)(E - 1)));
+    const int P = kThreads / epad;
+    const int ex = tid % epad, part = tid / epad;
+    int pre = 0, tot = 0;
+    if (ex < E) {
+#pragma unroll 8
+      for (int bb = part; bb < num_tiles; bb += P) {
+        const int c = tile_counts[(int64_t)bb * E + ex];
+        tot += c;
+        pre += bb < b ? c : 0;
+      }
+    }
+    int vpre = 0, vtot = 0;
+    for (int bb = tid; bb < num_tiles; bb += kThreads) {
+      const int c = tile_recv[bb];
+      vtot += c;
+      vpre += bb < b ? c : 0;
+    }
+    s_pre[tid] = pre;
+    s_tot[tid] = tot;
+    if (tid < Tile<K, NW>::tokens) s_row[tid] = 0;
+    recv_before = block_sum(vpre, s_tmp);  // its barriers publish s_pre / s_tot
+    recv_total = block_sum(vtot, s_tmp);
+    if (tid < E) {
+      for (int j = 0; j < P; ++j) {
+        base += s_pre[j * epad + tid];
+        cnt += s_tot[j * epad + tid];
+      }
     }
   }
   const int padded = ((cnt + A - 1) / A) * A;
@@ -422,20 +449,81 @@ __device__ __forceinline__ void assign_tile(
   write_slots_and_meta<K>(t0, ntok, slot, s_row, dst_slot, meta);
 }
 
-template <int K, int NW, bool LOOP>
+template <int K, int NW, bool LOOP, bool SCANNED>
 __global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
     int T, int E, int A, int num_tiles, const int32_t *__restrict__ tile_counts,
-    const int32_t *__restrict__ tile_recv, int32_t *__restrict__ counts,
+    const int32_t *__restrict__ tile_recv, TileScan scan, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
     int32_t *__restrict__ num_recv) {
   if constexpr (!LOOP) {
-    assign_tile<K, NW>(T, E, A, num_tiles, tile_counts, tile_recv, counts, offsets, dst_slot,
-                       meta, num_recv, blockIdx.x);
+    assign_tile<K, NW, SCANNED>(T, E, A, num_tiles, tile_counts, tile_recv, scan, counts, offsets,
+                                dst_slot, meta, num_recv, blockIdx.x);
   } else {
     for (int b = blockIdx.x; b < num_tiles; b += gridDim.x) {
-      assign_tile<K, NW>(T, E, A, num_tiles, tile_counts, tile_recv, counts, offsets, dst_slot,
-                         meta, num_recv, b);
+      assign_tile<K, NW, SCANNED>(T, E, A, num_tiles, tile_counts, tile_recv, scan, counts,
+                                  offsets, dst_slot, meta, num_recv, b);
       __syncthreads();
+    }
+  }
+}
+
+// Middle launch of the many-tile path: for every expert e (one lane each, 64
+// experts per block; column E stands for the received-token counts), the
+// exclusive prefix over tiles of its per-tile count and its total. The 16
+// waves of a block split the tiles into 16 runs; each lane loads a batch of
+// its run's values before summing them, so a batch costs one load latency.
+constexpr int kScanBatch = 16;
+__global__ __launch_bounds__(kThreads) void ep_layout_tile_scan(
+    const int32_t *__restrict__ tile_counts, const int32_t *__restrict__ tile_recv, int B, int E,
+    int32_t *__restrict__ tile_base, int32_t *__restrict__ expert_total,
+    int32_t *__restrict__ recv_base, int32_t *__restrict__ recv_total) {
+  __shared__ int s_part[kWavesMax][kWave];
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int run = (B + kWavesMax - 1) / kWavesMax;  // tiles per wave
+  const int r0 = min(B, w * run), r1 = min(B, r0 + run);
+  const int ncb = (E + 1 + kWave - 1) / kWave;      // column blocks (E experts + received)
+  for (int cb = blockIdx.x; cb < ncb; cb += gridDim.x) {
+    const int c = cb * kWave + lane;
+    const bool is_expert = c < E, is_recv = c == E;
+    auto value = [&](int r) -> int {
+      if (is_expert) return tile_counts[(int64_t)r * E + c];
+      return is_recv ? tile_recv[r] : 0;
+    };
+    int sum = 0;
+    for (int r = r0; r < r1; r += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) v[j] = r + j < r1 ? value(r + j) : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) sum += v[j];
+    }
+    s_part[w][lane] = sum;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWavesMax; ++ww) {
+      const int x = s_part[ww][lane];
+      before += ww < w ? x : 0;
+      total += x;
+    }
+    __syncthreads();  // s_part is reused by the next column block
+    int acc = before;
+    for (int r = r0; r < r1; r += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) v[j] = r + j < r1 ? value(r + j) : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (r + j < r1) {
+          if (is_expert) tile_base[(int64_t)(r + j) * E + c] = acc;
+          else if (is_recv) recv_base[r + j] = acc;
+        }
+        acc += v[j];
+      }
+    }
+    if (w == 0) {
+      if (is_expert) expert_total[c] = total;
+      else if (is_recv) *recv_total = total;
     }
   }
 }
@@ -445,21 +533,47 @@ int tiles_for(int T) {
   return (T + Tile<K, NW>::tokens - 1) / Tile<K, NW>::tokens;
 }
 
+// Whether the many-tile path adds the tile-scan launch: without it, each
+// thread of the second launch walks ceil(B / P) tiles, P = 1024 / E rounded
+// up to a power of two, a chain of dependent load batches that grows with the
+// tile count (78 us at 128K entries and 1024 experts).
+inline bool use_tile_scan(int B, int E) {
+  const int epad = E <= 1 ? 1 : 1 << (32 - __builtin_clz((unsigned)(E - 1)));
+  const int P = epad >= kThreads ? 1 : kThreads / epad;
+  return (B + P - 1) / P > kScanMinWalk;
+}
+
 template <int K, int NW, bool LOOP>
-int layout_launch(const LayoutArgs &a, int B, unsigned G) {
+int layout_launch(const LayoutArgs &a, int B, unsigned G, int cap) {
   const size_t shm_rank = rank_lds_bytes(a.E, NW);
   if ((int64_t)a.T * K <= kFusedMaxEntries) {
     ep_layout_fused_tiles<K, NW, LOOP>
         <<<G, kThreads, shm_rank + sizeof(int) * (size_t)(3 * a.E), a.stream>>>(
             a.topk_idx, a.T, a.E, a.A, B, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
-  } else {
-    int32_t *tile_counts = (int32_t *)a.workspace;
-    int32_t *tile_recv = tile_counts + (size_t)B * a.E;
-    ep_layout_tile_histogram<K, NW, LOOP><<<G, kThreads, shm_rank, a.stream>>>(
-        a.topk_idx, a.T, a.E, B, a.dst_slot, tile_counts, tile_recv);
-    ep_layout_tile_assign<K, NW, LOOP><<<G, kThreads, sizeof(int) * (size_t)(2 * a.E), a.stream>>>(
-        a.T, a.E, a.A, B, tile_counts, tile_recv, a.counts, a.offsets, a.dst_slot, a.meta,
+    return launch_status();
+  }
+  int32_t *tile_counts = (int32_t *)a.workspace;
+  int32_t *tile_recv = tile_counts + (size_t)B * a.E;
+  ep_layout_tile_histogram<K, NW, LOOP><<<G, kThreads, shm_rank, a.stream>>>(
+      a.topk_idx, a.T, a.E, B, a.dst_slot, tile_counts, tile_recv);
+  const size_t shm_assign = sizeof(int) * (size_t)(2 * a.E);
+  if (use_tile_scan(B, a.E)) {
+    int32_t *tile_base = tile_recv + B;
+    int32_t *expert_total = tile_base + (size_t)B * a.E;
+    int32_t *recv_base = expert_total + a.E;
+    int32_t *recv_total = recv_base + B;
+    unsigned gs = (unsigned)((a.E + 1 + kWave - 1) / kWave);
+    if (cap > 0 && gs > (unsigned)cap) gs = (unsigned)cap;
+    ep_layout_tile_scan<<<gs, kThreads, 0, a.stream>>>(tile_counts, tile_recv, B, a.E, tile_base,
+                                                        expert_total, recv_base, recv_total);
+    const TileScan scan{tile_base, expert_total, recv_base, recv_total};
+    ep_layout_tile_assign<K, NW, LOOP, true><<<G, kThreads, shm_assign, a.stream>>>(
+        a.T, a.E, a.A, B, tile_counts, tile_recv, scan, a.counts, a.offsets, a.dst_slot, a.meta,
         a.num_recv);
+  } else {
+    ep_layout_tile_assign<K, NW, LOOP, false><<<G, kThreads, shm_assign, a.stream>>>(
+        a.T, a.E, a.A, B, tile_counts, tile_recv, TileScan{}, a.counts, a.offsets, a.dst_slot,
+        a.meta, a.num_recv);
   }
   return launch_status();
 }
@@ -474,8 +588,8 @@ int layout_impl(const LayoutArgs &a) {
     return launch_status();
   }
   const int cap = stream_workgroup_limit(a.stream);
-  if (cap > 0 && cap < B) return layout_launch<K, NW, true>(a, B, (unsigned)cap);
-  return layout_launch<K, NW, false>(a, B, (unsigned)B);
+  if (cap > 0 && cap < B) return layout_launch<K, NW, true>(a, B, (unsigned)cap, cap);
+  return layout_launch<K, NW, false>(a, B, (unsigned)B, cap);
 }
 
 template <int K>
@@ -496,7 +610,11 @@ size_t workspace_k(int T, int E) {
     default: B = tiles_for<K, 4>(T); break;
   }
   if (B <= 1 || (int64_t)T * K <= kFusedMaxEntries) return 0;
-  return (((size_t)B * E + B) * sizeof(int32_t) + 255) & ~(size_t)255;
+  // tile counts [B][E] and received tokens [B]; with the tile scan also its
+  // prefixes [B][E], expert totals [E], received prefixes [B] and total
+  const size_t ints = use_tile_scan(B, E) ? 2 * (size_t)B * E + 2 * (size_t)B + E + 1
+                                          : (size_t)B * E + B;
+  return (ints * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
 }  // namespace

@@ -72,11 +72,12 @@ extern "C" {
 /*
  * Bytes of device workspace ep_layout needs for (num_tokens, topk,
  * num_experts): per-tile expert histograms and per-tile received-token
- * counts passed between its two kernels when num_tokens*topk is above 2^14
- * (smaller inputs take one launch and need none: the result is 0). Returns 0
- * for out-of-range arguments. The workspace is scratch: its contents on entry do not matter
- * and are overwritten; two ep_layout calls in flight at once must not share
- * one workspace.
+ * counts passed between its kernels when num_tokens*topk is above 2^14
+ * (smaller inputs take one launch and need none: the result is 0), plus,
+ * when there are many tiles per expert, their per-tile prefixes and totals.
+ * Returns 0 for out-of-range arguments. The workspace is scratch: its
+ * contents on entry do not matter and are overwritten; two ep_layout calls
+ * in flight at once must not share one workspace.
  */
 size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_experts);
 
