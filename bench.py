@@ -30,7 +30,8 @@ bytes of the three passes per step divided by the wall-clock step time
 HIP events recorded on the same stream around each call on every Nth timed
 step (--event-every, default 25: an instrumented step costs about 14 us
 more, so sparse events keep `value` within a fraction of a percent of an
-uninstrumented run); the roofline
+uninstrumented run; the default 500 steps give 20 samples per kernel); the
+roofline
 object reports the dominant kernel's algorithmic bytes over its mean event
 duration against the MI355X HBM peak (8 TB/s). The CPU baseline times the
 CPU oracle on the host (test infrastructure, never on the product path).
@@ -241,7 +242,7 @@ def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 100_000, path: st
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_aligned")
     ap.add_argument("--path", choices=("expand", "non-expand"), default="expand",
