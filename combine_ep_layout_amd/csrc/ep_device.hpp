@@ -33,6 +33,16 @@ __device__ __forceinline__ void store_row_nt(const u32x4 &v, void *row, int row_
   }
 }
 
+// Waits until every vector memory operation this wave has issued is done
+// (s_waitcnt with vmcnt 0 and the expcnt and lgkmcnt fields at their maxima,
+// which leaves those two counters free; gfx9-family immediate layout:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits 15:14). A
+// kernel that loads once and then stores under several wave-uniform branches
+// calls it between the two: the compiler cannot count outstanding operations
+// across those branches and otherwise waits for the previous store before
+// each store.
+__device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ int lane_id() {
   return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }

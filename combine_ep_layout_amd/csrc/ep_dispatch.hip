@@ -18,10 +18,18 @@
 // slice run on the same XCD, so x is read from HBM about once. Row bytes and
 // K are template constants.
 //
+// When x is too large to stay in the last-level cache, the K waves that need
+// one source slice all wait on the same HBM read, and few distinct bytes of x
+// are in flight: the per-(token, k) wave order drops to about 3.3 TB/s. A
+// second kernel then has one wave load the slice once and store it to a
+// group of F of the token's entries (F = 4 for K = 8), so each wave in flight
+// carries F times the writes per read (about 5.2 TB/s at 24576 tokens, and
+// no loss on a cold x at 4096 tokens: 109 against 143 us).
+//
 // Under a workgroup cap (CU-limited mode) a compute unit's own memory path,
-// not HBM, is the limit, so a second kernel cuts the bytes each compute unit
-// moves: one wave per (token, slice) loads the slice once and stores it to
-// all K destinations, (K + 1) KiB per K KiB written instead of 2K KiB.
+// not HBM, is the limit, so the same copy runs with F = K: one wave per
+// (token, slice) loads the slice once and stores it to all K destinations,
+// (K + 1) KiB per K KiB written instead of 2K KiB.
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -83,22 +91,79 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
   }
 }
 
-// One wave per (token, 1 KiB slice): the slice is loaded once and stored to
-// each of the token's K destination rows in k order (masked entries
-// skipped); slice 0 also carries the scale row and the weight of each entry.
+// Copies slice `slice` of token t's row to the destination rows of the F
+// entries k0 .. k0 + F - 1 (masked entries skipped); slice 0 also carries
+// the scale row and each entry's router weight. Slots, slice and scale row
+// are loaded first and waited for once, so the F stores leave back to back.
+template <int ROWB, int SCB, int K, int F, bool DEVICE_SCOPE>
+__device__ __forceinline__ void copy_slice_to_group(
+    const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int64_t t,
+    int k0, int slice, int64_t capacity, u32x4 *__restrict__ expand_x,
+    u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights) {
+  constexpr int CH = ROWB / 16;
+  constexpr int SCH = SCB / 16;
+  static_assert(ROWB % 16 == 0 && SCB % 16 == 0 && SCH <= kWave, "row geometry");
+  static_assert(F >= 1 && F <= K && K % F == 0 && K <= kWave, "entry group");
+  const int lane = lane_id();
+  const int64_t tk0 = t * K + k0;
+  const int i = slice * kWave + lane;
+  const bool in_row = CH % kWave == 0 || i < CH;
+  u32x4 v = {0u, 0u, 0u, 0u}, sc = {0u, 0u, 0u, 0u};
+  if (in_row) v = x[t * CH + i];
+  if (SCH > 0 && slice == 0 && lane < SCH) sc = x_scales[t * SCH + lane];
+  // every lane reads a slot (lanes past F repeat entry k0) so that no branch
+  // separates this load from the ones above and all are in flight together
+  int my_d = dst_slot[tk0 + (lane < F ? lane : 0)];
+  wait_vector_memory();
+  if (lane >= F || my_d >= capacity) my_d = -1;
+#pragma unroll
+  for (int j = 0; j < F; ++j) {
+    const int d = read_lane(my_d, j);
+    if (d < 0) continue;
+    if (in_row) store_row_nt<DEVICE_SCOPE>(v, expand_x + (int64_t)d * CH, ROWB, i * 16);
+    if (slice == 0) {
+      if (SCH > 0 && lane < SCH)
+        __builtin_nontemporal_store(sc, expand_scales + (int64_t)d * SCH + lane);
+      if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[tk0 + j];
+    }
+  }
+}
+
+// Uncapped, x larger than the cache can hold: one wave per (token, group of
+// F entries, 1 KiB slice), ordered token-major, then group, then slice, with
+// the blocks of one XCD contiguous as in ep_dispatch_expand.
+template <int DT, int ROWB, int SCB, int K, int F>
+__global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_grouped(
+    const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
+    int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
+    float *__restrict__ expand_weights) {
+  constexpr int SLICES = (ROWB / 16 + kWave - 1) / kWave;
+  constexpr int KG = K / F;  // entry groups per token
+  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  constexpr int wpb = kDefaultThreads / kWave;
+  const int64_t total = (int64_t)T * KG * SLICES;
+  const int64_t stride = (int64_t)gridDim.x * wpb;
+  for (int64_t gw = xcd_contiguous_block() * wpb + wave_in_block; gw < total; gw += stride) {
+    const int64_t tg = gw / SLICES;  // flat (token, group)
+    const int slice = (int)(gw - tg * SLICES);
+    const int64_t t = tg / KG;
+    const int g = (int)(tg - t * KG);
+    copy_slice_to_group<ROWB, SCB, K, F, true>(x, x_scales, topk_weights, dst_slot, t, g * F,
+                                               slice, capacity, expand_x, expand_scales,
+                                               expand_weights);
+  }
+}
+
+// Under a workgroup cap: one wave per (token, 1 KiB slice), all K entries.
 template <int DT, int ROWB, int SCB, int K>
 __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_fanout(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
     int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
     float *__restrict__ expand_weights) {
-  constexpr int CH = ROWB / 16;
-  constexpr int SLICES = (CH + kWave - 1) / kWave;
-  constexpr int SCH = SCB / 16;
-  static_assert(ROWB % 16 == 0 && SCB % 16 == 0 && SCH <= kWave, "row geometry");
-  static_assert(K >= 1 && K <= kWave, "topk must fit one wavefront");
-
-  const int lane = lane_id();
+  constexpr int SLICES = (ROWB / 16 + kWave - 1) / kWave;
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   constexpr int wpb = kCappedThreads / kWave;  // launched under a cap only
   const int64_t total = (int64_t)T * SLICES;
@@ -106,49 +171,44 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_fanout(
   for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < total; gw += stride) {
     const int64_t t = gw / SLICES;
     const int slice = (int)(gw - t * SLICES);
-    int my_d = -1;
-    if (lane < K) {
-      my_d = dst_slot[t * K + lane];
-      if (my_d >= capacity) my_d = -1;
-    }
-    const int i = slice * kWave + lane;
-    const bool in_row = CH % kWave == 0 || i < CH;
-    u32x4 v = {0u, 0u, 0u, 0u}, sc = {0u, 0u, 0u, 0u};
-    if (in_row) v = x[t * CH + i];
-    if (SCH > 0 && slice == 0 && lane < SCH) sc = x_scales[t * SCH + lane];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int d = read_lane(my_d, k);
-      if (d < 0) continue;
-      if (in_row) __builtin_nontemporal_store(v, expand_x + (int64_t)d * CH + i);
-      if (slice == 0) {
-        if (SCH > 0 && lane < SCH)
-          __builtin_nontemporal_store(sc, expand_scales + (int64_t)d * SCH + lane);
-        if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[t * K + k];
-      }
-    }
+    copy_slice_to_group<ROWB, SCB, K, K, false>(x, x_scales, topk_weights, dst_slot, t, 0, slice,
+                                                capacity, expand_x, expand_scales,
+                                                expand_weights);
   }
 }
+
+// Bytes of x above which the uncapped launch uses ep_dispatch_grouped: half
+// of MI355X's 256 MiB last-level cache. Below it x, written by the kernel
+// before dispatch, is normally still cached and the per-(token, k) order is
+// fastest (87 against 95 us at 4096 tokens); above it x rarely survives
+// beside the other traffic, and past the full 256 MiB it never does.
+constexpr int64_t kCachedXBytes = int64_t(128) << 20;
 
 template <int DT, int ROWB, int SCB, int K>
 int dispatch_impl(const DispatchArgs &a) {
   if (a.T == 0) return 0;
   constexpr int SLICES = (ROWB / 16 + kWave - 1) / kWave;
+  constexpr int F = K % 4 == 0 ? 4 : K % 3 == 0 ? 3 : K % 2 == 0 ? 2 : 1;  // entries per wave
   const bool fwd_w = a.topk_weights != nullptr && a.expand_weights != nullptr;
+  const u32x4 *x = (const u32x4 *)a.x, *xs = (const u32x4 *)a.x_scales;
+  u32x4 *ex = (u32x4 *)a.expand_x, *es = (u32x4 *)a.expand_scales;
+  float *ew = fwd_w ? a.expand_weights : nullptr;
   const int cap = stream_workgroup_limit(a.stream);
   if (cap > 0) {
     const WaveGrid g = wave_grid((int64_t)a.T * SLICES, cap, 1 << 24);
     ep_dispatch_fanout<DT, ROWB, SCB, K><<<g.blocks, kCappedThreads, 0, a.stream>>>(
-        (const u32x4 *)a.x, (const u32x4 *)a.x_scales, a.topk_weights, a.dst_slot, a.T,
-        a.capacity, (u32x4 *)a.expand_x, (u32x4 *)a.expand_scales,
-        fwd_w ? a.expand_weights : nullptr);
+        x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
+    return launch_status();
+  }
+  if (F > 1 && (int64_t)a.T * ROWB > kCachedXBytes) {
+    const WaveGrid g = wave_grid((int64_t)a.T * (K / F) * SLICES, 0, 1 << 24, kXcds);
+    ep_dispatch_grouped<DT, ROWB, SCB, K, F><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+        x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
     return launch_status();
   }
   const WaveGrid g = wave_grid((int64_t)a.T * K * SLICES, 0, 1 << 24, kXcds);
   ep_dispatch_expand<DT, ROWB, SCB, K><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-      (const u32x4 *)a.x, (const u32x4 *)a.x_scales, a.topk_weights, a.dst_slot, a.T,
-      a.capacity, (u32x4 *)a.expand_x, (u32x4 *)a.expand_scales,
-      fwd_w ? a.expand_weights : nullptr);
+      x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
   return launch_status();
 }
 

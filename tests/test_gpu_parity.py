@@ -129,6 +129,37 @@ def test_ragged_shapes(T, H, E, K, A, mask, dtype, routing):
     check_combine(to_host(out, np.uint16), oracle.combine(case.y, ref["dst_slot"], None), "w=1")
 
 
+# x larger than 128 MiB: the uncapped dispatch switches to one wave per source
+# slice and group of entries (groups of 4 for K = 8 and 4, 3 for K = 6, 2 for
+# K = 2); each case sits just past that size, with masking and ragged T.
+BEYOND_CACHE = [
+    # T, H, E, K, A, mask, dtype, scales
+    (9500, 7168, 256, 8, 128, 0.02, I.BF16, False),
+    (19001, 7168, 256, 6, 1, 0.05, I.FP8_E4M3, True),
+    (16401, 2048, 64, 2, 4, 0.0, I.FP32, False),
+    (37500, 3584, 128, 4, 1, 0.01, I.FP4X2, True),
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,A,mask,dtype,scales", BEYOND_CACHE)
+def test_dispatch_x_beyond_cache(T, H, E, K, A, mask, dtype, scales):
+    w = I.custom(f"big{T}_{H}_{K}", 5000 + T, T, H, E, K, A, dtype, "uniform", scales=scales)
+    _say(f"[x beyond cache] {w}")
+    case = I.make_case(w, with_y=False, mask_frac=mask)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case, with_y=False)
+    dc.layout()
+    dc.dispatch()
+    torch.cuda.synchronize()
+    check_layout(layout_to_host(dc.lay), ref)
+    check_dispatch(dc, ref["dst_slot"])
+    # without router weights no weight slot is written
+    dc.expand_w.fill_(-5.0)
+    dc.dispatch(weights=False)
+    torch.cuda.synchronize()
+    assert bool((dc.expand_w == -5.0).all())
+
+
 def test_empty_input():
     w = I.custom("empty", 5, 0, 256, 16, 2, 4)
     lay = dev_layout(None, 0, 2, 16, 4, w.cap)
