@@ -8,18 +8,26 @@
 // (combine reduces bf16 or fp32 rows; byte dtypes are rejected upstream).
 //
 // Design (MI355X): HBM-bound (read T*K rows, write T rows, about 1 flop per
-// byte). A token's row is cut into slices of two 16-byte chunks per lane
-// (2 KiB); one wave64 owns one (token, slice), so a 14,336-byte row is
-// served by 7 waves. A wave loads its token's K slots and weights with K
-// lanes and broadcasts them with readlane, so row addresses are
-// wave-uniform; it issues all K*2 loads (16 KiB per wave) before the first
-// is consumed, then folds the K rows in k order. Many short waves keep the
-// memory system full (a long-lived wave walking a whole row stalls between
-// passes). Loads and stores are non-temporal: expert outputs are read once
-// and the output written once. Products and sums are rounded separately
-// (contraction off), so the result is a pure function of the inputs; the
-// final pack uses the hardware binary32 -> bf16 convert, which rounds to
-// nearest even.
+// byte). A wave loads its token's K slots and weights with K lanes and
+// broadcasts them with readlane, so row addresses are wave-uniform. Two
+// kernels cut the work differently:
+//   - ep_combine_stream (uncapped, at least 1024 tokens, rows of 4 to 14
+//     16-byte chunks per lane): one wave per token keeps the whole output row
+//     in binary32 and walks the K rows in k order with the next row's loads
+//     in flight. Reading each row whole is the gather order HBM serves best
+//     (measured on MI355X, pure gathers of 8 rows of 14 KiB: 85 us per 4096
+//     tokens whole-row, 89 us in 2 KiB pieces); prefill combine 92 against
+//     96 us.
+//   - ep_combine_gather (otherwise): a row is cut into slices of two 16-byte
+//     chunks per lane (2 KiB); one wave owns one (token, slice), so a
+//     14,336-byte row is served by 7 waves, and issues all K*2 loads (16 KiB)
+//     before folding. Small batches need these many short waves to fill the
+//     chip (128 tokens: 8 against 12 us for one wave per token).
+// Loads and stores are non-temporal: expert outputs are read once and the
+// output written once. Both kernels fold the same way: products and sums
+// are rounded separately (contraction off), in k order, so the result is a
+// pure function of the inputs; the final pack uses the hardware binary32 ->
+// bf16 convert, which rounds to nearest even.
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -196,6 +204,114 @@ __global__ __launch_bounds__(NT) void ep_combine_gather(
   }
 }
 
+// Row-streaming combine for rows of whole chunks per lane: one wave per token
+// holds the whole output row in binary32 (CPL chunks per lane) and walks the
+// K expert rows in k order, with the next D - 1 rows' loads in flight while
+// a row is folded. The fold is the same sequence of binary32 operations as
+// ep_combine_gather's. Rows with a negative slot are skipped; their loads
+// read another row of the token (src) so the loads stay straight-line code.
+template <int DT, int CH, int K, int D, bool ALL_VALID>
+__device__ __forceinline__ void stream_fold(const u32x4 *__restrict__ y, const int (&src)[K],
+                                            const int (&d)[K], const float (&wk)[K], int lane,
+                                            float (&acc)[CH / kWave][Elem<DT>::PER_CHUNK]) {
+#pragma clang fp contract(off)
+  constexpr int PC = Elem<DT>::PER_CHUNK;
+  constexpr int CPL = CH / kWave;
+  u32x4 buf[D][CPL];
+#pragma unroll
+  for (int r = 0; r < D; ++r)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+      buf[r][c] = __builtin_nontemporal_load(y + (int64_t)src[r] * CH + c * kWave + lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int j = 0; j < PC; ++j) acc[c][j] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {  // fixed k order
+    if (ALL_VALID || d[k] >= 0) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int j = 0; j < PC; ++j) {
+          const float p = wk[k] * Elem<DT>::get(buf[k % D][c], j);
+          acc[c][j] = acc[c][j] + p;
+        }
+    }
+    if (k + D < K) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        buf[k % D][c] = __builtin_nontemporal_load(y + (int64_t)src[k + D] * CH + c * kWave + lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Fewest tokens for ep_combine_stream: one wave per token must fill the
+// chip's 2048 wave slots at its two waves per SIMD.
+constexpr int kStreamMinTokens = 1024;
+
+template <int DT, int H, int K, bool BIAS>
+__global__ __launch_bounds__(kDefaultThreads) void ep_combine_stream(
+    const u32x4 *__restrict__ y, const float *__restrict__ topk_weights,
+    const u32x4 *__restrict__ bias, const int32_t *__restrict__ dst_slot, int T,
+    int64_t capacity, u32x4 *__restrict__ out) {
+  constexpr int CH = H * Elem<DT>::BYTES / 16;
+  constexpr int PC = Elem<DT>::PER_CHUNK;
+  constexpr int CPL = CH / kWave;
+  constexpr int D = K < 2 ? K : 2;  // rows in flight
+  static_assert(CH % kWave == 0, "whole chunks per lane");
+  const int lane = lane_id();
+  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  constexpr int wpb = kDefaultThreads / kWave;
+  const int64_t stride = (int64_t)gridDim.x * wpb;
+  for (int64_t t = (int64_t)blockIdx.x * wpb + wave_in_block; t < T; t += stride) {
+    int my_dst = -1;
+    float my_w = 0.f;
+    if (lane < K) {
+      my_dst = dst_slot[t * K + lane];
+      if (my_dst >= capacity) my_dst = -1;
+      my_w = topk_weights ? topk_weights[t * K + lane] : 1.0f;
+    }
+    const uint64_t valid = ballot(lane < K && my_dst >= 0);
+    int d[K];
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      d[k] = read_lane(my_dst, k);
+      wk[k] = read_lane(my_w, k);
+    }
+    float acc[CPL][PC];
+    if (valid == (K == 64 ? ~0ull : (1ull << K) - 1)) {
+      stream_fold<DT, CH, K, D, true>(y, d, d, wk, lane, acc);
+    } else if (valid != 0) {
+      const int any = read_lane(my_dst, __builtin_ctzll(valid));
+      int src[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) src[k] = d[k] >= 0 ? d[k] : any;
+      stream_fold<DT, CH, K, D, false>(y, src, d, wk, lane, acc);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int j = 0; j < PC; ++j) acc[c][j] = 0.0f;
+    }
+    u32x4 *o = out + t * CH;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int i = c * kWave + lane;
+      if constexpr (BIAS) {
+#pragma clang fp contract(off)
+        const u32x4 b = bias[t * CH + i];
+#pragma unroll
+        for (int j = 0; j < PC; ++j) acc[c][j] = acc[c][j] + Elem<DT>::get(b, j);
+      }
+      __builtin_nontemporal_store(Elem<DT>::put(acc[c]), o + i);
+    }
+  }
+}
+
 template <int DT, int H, int K, int NT>
 int combine_launch(const CombineArgs &a, const WaveGrid &g) {
   if (a.bias)
@@ -212,6 +328,21 @@ int combine_launch(const CombineArgs &a, const WaveGrid &g) {
 template <int DT, int H, int K>
 int combine_impl(const CombineArgs &a) {
   if (a.T == 0) return 0;
+  constexpr int CH = H * Elem<DT>::BYTES / 16;
+  if constexpr (CH % kWave == 0 && CH / kWave >= 4 && CH / kWave <= 14) {
+    if (a.T >= kStreamMinTokens && stream_workgroup_limit(a.stream) == 0) {
+      const WaveGrid g = wave_grid(a.T, 0, INT32_MAX);
+      if (a.bias)
+        ep_combine_stream<DT, H, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+            (const u32x4 *)a.y, a.topk_weights, (const u32x4 *)a.bias, a.dst_slot, a.T,
+            a.capacity, (u32x4 *)a.out);
+      else
+        ep_combine_stream<DT, H, K, false><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+            (const u32x4 *)a.y, a.topk_weights, nullptr, a.dst_slot, a.T, a.capacity,
+            (u32x4 *)a.out);
+      return launch_status();
+    }
+  }
   constexpr int SPLIT = CombineGeometry<H * Elem<DT>::BYTES / 16>::SPLIT;
   const WaveGrid g = wave_grid((int64_t)a.T * SPLIT, stream_workgroup_limit(a.stream), INT32_MAX,
                                1, kCombineCappedThreads);

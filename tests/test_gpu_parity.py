@@ -160,6 +160,50 @@ def test_dispatch_x_beyond_cache(T, H, E, K, A, mask, dtype, scales):
     assert bool((dc.expand_w == -5.0).all())
 
 
+# Combine shapes on both sides of the switch between the one-wave-per-token
+# kernel (at least 1024 tokens, rows of 4 to 14 chunks of 16 bytes per lane)
+# and the sliced kernel: masking (some tokens lose every entry), bias, K = 1
+# and 6, fp32 rows.
+ROW_STREAM = [
+    # T, H, E, K, A, mask, dtype, out_dtype
+    (1024, 7168, 256, 8, 128, 0.3, I.BF16, I.BF16),
+    (1023, 7168, 256, 8, 128, 0.3, I.BF16, I.BF16),
+    (1024, 2048, 64, 6, 1, 0.1, I.BF16, I.BF16),
+    (3000, 4096, 128, 1, 4, 0.05, I.BF16, I.BF16),
+    (1500, 1024, 32, 4, 2, 0.2, I.FP32, I.FP32),
+    (2500, 2048, 256, 2, 1, 0.6, I.FP32, I.FP32),
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,A,mask,dtype,out_dtype", ROW_STREAM)
+def test_combine_row_stream(T, H, E, K, A, mask, dtype, out_dtype):
+    w = I.custom(f"rs{T}_{H}_{K}", 7000 + T + K, T, H, E, K, A, dtype, "uniform",
+                 out_dtype=out_dtype)
+    _say(f"[combine stream] {w}")
+    case = I.make_case(w, mask_frac=mask)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case)
+    dc.layout()
+    if out_dtype == I.FP32:
+        bias_h = I.normal_f32(w.seed, 9, w.T, dc.H_out)
+    else:
+        bias_h = I.normal_bf16(w.seed, 9, w.T, dc.H_out)
+    for weights, bias in ((True, None), (True, bias_h), (False, bias_h)):
+        out = dc.combine(weights=weights, bias=None if bias is None else to_dev(bias))
+        torch.cuda.synchronize()
+        wts = case.topk_weights if weights else None
+        label = f"{w.name} weights={weights} bias={bias is not None}"
+        if out_dtype == I.FP32:
+            want = oracle.combine_f32(case.y, ref["dst_slot"], wts, bias)
+            got = to_host(out)
+            same = got.view(np.uint32) == want.view(np.uint32)
+            _say(f"combine fp32 {label}: {int(same.sum())}/{same.size} bit-exact")
+            assert same.all(), label
+        else:
+            check_combine(to_host(out, np.uint16),
+                          oracle.combine(case.y, ref["dst_slot"], wts, bias), label)
+
+
 def test_empty_input():
     w = I.custom("empty", 5, 0, 256, 16, 2, 4)
     lay = dev_layout(None, 0, 2, 16, 4, w.cap)
