@@ -10,11 +10,14 @@ C ABI on torch's current stream. Default workload: 4096 tokens, hidden 7168,
 --path non-expand times the other layout mode instead: ep_layout,
 ep_dispatch_compact (one row per received token, with its expert ids and
 router weights) and ep_combine_compact (rows back to token order).
---cold rotates several complete sets of input and output buffers (x, scale
-rows, expert outputs, expand / receive buffers, out), enough that at least
-512 MB of other traffic separates two uses of a set, so no step finds its
-rows in the 256 MB last-level cache (MALL); nothing but steps runs in the
-timed loop. Every run also times torch's copy_ of 1 GiB (16-byte
+--cold rotates several complete sets of buffers (expert outputs, expand /
+receive buffers, out), enough that at least 512 MB of other traffic separates
+two uses of a set, and separately enough copies of x (with its scale rows)
+that at least 512 MB of other x reads separate two uses of a copy. Only
+ordinary loads fill the 256 MB last-level cache (MALL); the rest of the
+step's traffic is non-temporal and leaves it alone. So rotating x among its
+own copies is what makes each step find x in HBM rather than in the MALL.
+Nothing but steps runs in the timed loop. Every run also times torch's copy_ of 1 GiB (16-byte
 vector loads and stores) and reports the path as a fraction of that copy.
 --graph N captures N consecutive steps in one hipGraph and times its
 replays for `value` (per-kernel times still come from the eager pass): the
@@ -128,10 +131,13 @@ def measured_traffic(workload: str, kernel: str):
 
 
 CALIBRATION_BYTES = 1 << 30  # fp32 elementwise negate: reads and writes this many bytes
-KERNEL_TAGS = {"dispatch": "ep_dispatch_expand", "combine": "ep_combine_gather",
-               "dispatch_compact": "ep_dispatch_compact_rows",
-               "combine_compact": "ep_combine_compact_rows",
-               "layout_histogram": "ep_layout_tile_histogram", "layout_assign": "ep_layout_tile_assign"}
+# Kernel-name fragments per pass: each pass launches one of its kernels, chosen by shape and cap.
+KERNEL_TAGS = {"dispatch": ("ep_dispatch_expand", "ep_dispatch_grouped", "ep_dispatch_fanout"),
+               "combine": ("ep_combine_stream", "ep_combine_gather"),
+               "dispatch_compact": ("ep_dispatch_compact_rows",),
+               "combine_compact": ("ep_combine_compact_rows",),
+               "layout_histogram": ("ep_layout_tile_histogram",),
+               "layout_assign": ("ep_layout_tile_assign",)}
 
 
 def _counter_means(path: str) -> dict:
@@ -142,8 +148,8 @@ def _counter_means(path: str) -> dict:
         for r in csv.DictReader(f):
             name = r.get("Kernel_Name", "")
             tag = None
-            for k, t in KERNEL_TAGS.items():
-                if t in name:
+            for k, frags in KERNEL_TAGS.items():
+                if any(f in name for f in frags):
                     tag = k
             if tag is None and "neg_kernel" in name:
                 tag = "calibration"
@@ -316,14 +322,18 @@ def main():
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     rows_out = w.T if non_expand else w.cap
 
+    def x_set():
+        """One copy of the tokens' rows and scale rows."""
+        return {"x": up(case.x),
+                "xs": up(case.x_scales) if case.x_scales is not None else None}
+
     def buffer_set():
-        """The rows one step reads and writes (the small layout arrays are shared)."""
-        xs_d = up(case.x_scales) if case.x_scales is not None else None
+        """The other rows one step reads and writes (the small layout arrays are shared)."""
         return {
-            "x": up(case.x), "xs": xs_d, "y": up(case.y),
+            "y": up(case.y),
             "expand": torch.zeros((rows_out, rowb), dtype=torch.uint8, device=dev),
             "expand_s": (torch.zeros((rows_out, scale_cols), dtype=torch.float32, device=dev)
-                         if xs_d is not None else None),
+                         if case.x_scales is not None else None),
             "recv_i": torch.empty((w.T, w.K), dtype=torch.int32, device=dev) if non_expand else None,
             "recv_w": torch.empty((w.T, w.K), dtype=torch.float32, device=dev) if non_expand else None,
             "out": torch.empty((w.T, H_out), dtype=torch.float32 if w.out_dtype == 1 else torch.int16,
@@ -331,10 +341,13 @@ def main():
         }
 
     step_bytes = sum(algorithmic_bytes(w, w.T * w.K, w.T, args.path).values())
-    nsets = 1
-    if args.cold:  # at least 512 MB of other steps' traffic between two uses of a set
+    nsets = nx = 1
+    x_bytes = case.x.nbytes + (case.x_scales.nbytes if case.x_scales is not None else 0)
+    if args.cold:  # at least 512 MB of other traffic between two uses of a set or an x copy
         nsets = min(32, max(2, -(-(512 << 20) // step_bytes) + 1))
+        nx = min(1024, max(2, -(-(512 << 20) // x_bytes) + 1))
     sets = [buffer_set() for _ in range(nsets)]
+    x_sets = [x_set() for _ in range(nx)]
     stream = torch.cuda.current_stream()
     if args.workgroups > 0:
         stream = torch.cuda.Stream()  # default priority
@@ -349,17 +362,18 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    def step(S, ev=None, stream=stream):
+    def step(i, ev=None, stream=stream):
+        S, X = sets[i % nsets], x_sets[i % nx]
         if ev is not None:
             ev[0].record(stream)
         B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws, wsb, stream)
         if ev is not None:
             ev[1].record(stream)
         if non_expand:
-            B.ep_dispatch_compact(S["x"], S["xs"], idx, wts, dst, meta, nrecv, w.T, w.H, w.K, w.dtype,
+            B.ep_dispatch_compact(X["x"], X["xs"], idx, wts, dst, meta, nrecv, w.T, w.H, w.K, w.dtype,
                                   S["expand"], S["expand_s"], S["recv_i"], S["recv_w"], stream)
         else:
-            B.ep_dispatch(S["x"], S["xs"], None, dst, w.T, w.H, w.K, w.dtype, w.cap, S["expand"],
+            B.ep_dispatch(X["x"], X["xs"], None, dst, w.T, w.H, w.K, w.dtype, w.cap, S["expand"],
                           S["expand_s"], None, stream)
         if ev is not None:
             ev[2].record(stream)
@@ -371,8 +385,8 @@ def main():
             ev[3].record(stream)
 
     torch.cuda.synchronize()  # inputs were written on the default stream
-    for i in range(max(args.warmup, nsets)):
-        step(sets[i % nsets])
+    for i in range(max(args.warmup, nsets, nx)):
+        step(i)
     # HIP events around each kernel on every Nth timed step: an instrumented
     # step costs about 14 us more (each event drains the pipeline), so sparse
     # events keep the wall-clock value within a fraction of a percent.
@@ -382,7 +396,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % nsets], evs[i // every] if i % every == 0 else None)
+        step(i, evs[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -394,7 +408,7 @@ def main():
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(args.graph):
-                step(sets[i % nsets], stream=torch.cuda.current_stream())
+                step(i, stream=torch.cuda.current_stream())
         for _ in range(3):
             g.replay()
         reps = max(1, args.steps // args.graph)
@@ -406,13 +420,14 @@ def main():
         ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * args.graph)
         launch = f"hipGraph of {args.graph} steps, {reps} replays"
     last = sets[(args.steps - 1) % nsets]  # every set holds the same results
-    x, y, expand, recv_i, recv_w, out = (last[k] for k in ("x", "y", "expand", "recv_i", "recv_w",
-                                                            "out"))
+    y, expand, recv_i, recv_w, out = (last[k] for k in ("y", "expand", "recv_i", "recv_w", "out"))
     cache = ("warm" if nsets == 1 else
              f"cold: {nsets} buffer sets rotated, "
-             f"{(nsets - 1) * step_bytes / 1e6:.0f} MB of other traffic between uses of a set")
+             f"{(nsets - 1) * step_bytes / 1e6:.0f} MB of other traffic between uses of a set; "
+             f"{nx} copies of x rotated, {(nx - 1) * x_bytes / 1e6:.0f} MB of other x reads "
+             f"between uses of a copy")
 
-    overlap = (overlap_gemm(torch, dev, lambda: step(sets[0]), ms_per_step, args.steps)
+    overlap = (overlap_gemm(torch, dev, lambda: step(0), ms_per_step, args.steps)
                if args.overlap_gemm else None)
 
     # Validate the timed path against the oracle: layout in full, dispatch and combine sampled.
