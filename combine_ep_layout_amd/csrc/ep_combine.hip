@@ -204,25 +204,36 @@ __global__ __launch_bounds__(NT) void ep_combine_gather(
   }
 }
 
+// Pieces of a row for ep_combine_stream: rows of whole chunks per lane, cut
+// into the fewest equal pieces of at most 14 chunks per lane (the registers
+// of one binary32 piece plus two rows in flight, 254 of them at 14).
+template <int CH>
+struct StreamGeometry {
+  static constexpr int ROW_CPL = CH / kWave;
+  static constexpr int PIECES = ROW_CPL > 14 ? (ROW_CPL + 13) / 14 : 1;
+  static constexpr int CPL = ROW_CPL / PIECES;  // chunks per lane per piece
+  static constexpr bool OK = CH % kWave == 0 && ROW_CPL % PIECES == 0 && CPL >= 4;
+};
+
 // Row-streaming combine for rows of whole chunks per lane: one wave per token
-// holds the whole output row in binary32 (CPL chunks per lane) and walks the
+// (per piece of at most 14 chunks per lane, for the widest fp32 rows) holds
+// its part of the output row in binary32 (CPL chunks per lane) and walks the
 // K expert rows in k order, with the next D - 1 rows' loads in flight while
 // a row is folded. The fold is the same sequence of binary32 operations as
 // ep_combine_gather's. Rows with a negative slot are skipped; their loads
 // read another row of the token (src) so the loads stay straight-line code.
-template <int DT, int CH, int K, int D, bool ALL_VALID>
+template <int DT, int CH, int CPL, int K, int D, bool ALL_VALID>
 __device__ __forceinline__ void stream_fold(const u32x4 *__restrict__ y, const int (&src)[K],
-                                            const int (&d)[K], const float (&wk)[K], int lane,
-                                            float (&acc)[CH / kWave][Elem<DT>::PER_CHUNK]) {
+                                            const int (&d)[K], const float (&wk)[K], int i0,
+                                            float (&acc)[CPL][Elem<DT>::PER_CHUNK]) {
 #pragma clang fp contract(off)
   constexpr int PC = Elem<DT>::PER_CHUNK;
-  constexpr int CPL = CH / kWave;
   u32x4 buf[D][CPL];
 #pragma unroll
   for (int r = 0; r < D; ++r)
 #pragma unroll
     for (int c = 0; c < CPL; ++c)
-      buf[r][c] = __builtin_nontemporal_load(y + (int64_t)src[r] * CH + c * kWave + lane);
+      buf[r][c] = __builtin_nontemporal_load(y + (int64_t)src[r] * CH + i0 + c * kWave);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int c = 0; c < CPL; ++c)
@@ -242,7 +253,7 @@ __device__ __forceinline__ void stream_fold(const u32x4 *__restrict__ y, const i
     if (k + D < K) {
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
-        buf[k % D][c] = __builtin_nontemporal_load(y + (int64_t)src[k + D] * CH + c * kWave + lane);
+        buf[k % D][c] = __builtin_nontemporal_load(y + (int64_t)src[k + D] * CH + i0 + c * kWave);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -259,14 +270,17 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_combine_stream(
     int64_t capacity, u32x4 *__restrict__ out) {
   constexpr int CH = H * Elem<DT>::BYTES / 16;
   constexpr int PC = Elem<DT>::PER_CHUNK;
-  constexpr int CPL = CH / kWave;
+  using Geo = StreamGeometry<CH>;
+  constexpr int CPL = Geo::CPL, PIECES = Geo::PIECES;
   constexpr int D = K < 2 ? K : 2;  // rows in flight
-  static_assert(CH % kWave == 0, "whole chunks per lane");
   const int lane = lane_id();
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   constexpr int wpb = kDefaultThreads / kWave;
   const int64_t stride = (int64_t)gridDim.x * wpb;
-  for (int64_t t = (int64_t)blockIdx.x * wpb + wave_in_block; t < T; t += stride) {
+  for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < (int64_t)T * PIECES;
+       gw += stride) {
+    const int64_t t = gw / PIECES;
+    const int i0 = (int)(gw - t * PIECES) * CPL * kWave + lane;  // this lane's first chunk
     int my_dst = -1;
     float my_w = 0.f;
     if (lane < K) {
@@ -284,13 +298,13 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_combine_stream(
     }
     float acc[CPL][PC];
     if (valid == (K == 64 ? ~0ull : (1ull << K) - 1)) {
-      stream_fold<DT, CH, K, D, true>(y, d, d, wk, lane, acc);
+      stream_fold<DT, CH, CPL, K, D, true>(y, d, d, wk, i0, acc);
     } else if (valid != 0) {
       const int any = read_lane(my_dst, __builtin_ctzll(valid));
       int src[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) src[k] = d[k] >= 0 ? d[k] : any;
-      stream_fold<DT, CH, K, D, false>(y, src, d, wk, lane, acc);
+      stream_fold<DT, CH, CPL, K, D, false>(y, src, d, wk, i0, acc);
     } else {
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_combine_stream(
     u32x4 *o = out + t * CH;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int i = c * kWave + lane;
+      const int i = i0 + c * kWave;
       if constexpr (BIAS) {
 #pragma clang fp contract(off)
         const u32x4 b = bias[t * CH + i];
@@ -329,9 +343,9 @@ template <int DT, int H, int K>
 int combine_impl(const CombineArgs &a) {
   if (a.T == 0) return 0;
   constexpr int CH = H * Elem<DT>::BYTES / 16;
-  if constexpr (CH % kWave == 0 && CH / kWave >= 4 && CH / kWave <= 14) {
+  if constexpr (StreamGeometry<CH>::OK) {
     if (a.T >= kStreamMinTokens && stream_workgroup_limit(a.stream) == 0) {
-      const WaveGrid g = wave_grid(a.T, 0, INT32_MAX);
+      const WaveGrid g = wave_grid((int64_t)a.T * StreamGeometry<CH>::PIECES, 0, INT32_MAX);
       if (a.bias)
         ep_combine_stream<DT, H, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
             (const u32x4 *)a.y, a.topk_weights, (const u32x4 *)a.bias, a.dst_slot, a.T,

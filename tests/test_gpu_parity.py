@@ -160,10 +160,10 @@ def test_dispatch_x_beyond_cache(T, H, E, K, A, mask, dtype, scales):
     assert bool((dc.expand_w == -5.0).all())
 
 
-# Combine shapes on both sides of the switch between the one-wave-per-token
-# kernel (at least 1024 tokens, rows of 4 to 14 chunks of 16 bytes per lane)
-# and the sliced kernel: masking (some tokens lose every entry), bias, K = 1
-# and 6, fp32 rows.
+# Combine shapes on both sides of the switch between the row-streaming
+# kernel (at least 1024 tokens; one wave per token, or per piece of at most 14
+# chunks of 16 bytes per lane) and the sliced kernel: masking (some tokens
+# lose every entry), bias, K = 1 and 6, fp32 rows.
 ROW_STREAM = [
     # T, H, E, K, A, mask, dtype, out_dtype
     (1024, 7168, 256, 8, 128, 0.3, I.BF16, I.BF16),
@@ -172,6 +172,10 @@ ROW_STREAM = [
     (3000, 4096, 128, 1, 4, 0.05, I.BF16, I.BF16),
     (1500, 1024, 32, 4, 2, 0.2, I.FP32, I.FP32),
     (2500, 2048, 256, 2, 1, 0.6, I.FP32, I.FP32),
+    # fp32 rows wider than one wave's registers: two pieces per token
+    (1100, 7168, 256, 8, 1, 0.1, I.BF16, I.FP32),
+    (1024, 4096, 64, 4, 1, 0.2, I.FP32, I.FP32),
+    (1000, 7168, 256, 6, 1, 0.1, I.BF16, I.FP32),
 ]
 
 
