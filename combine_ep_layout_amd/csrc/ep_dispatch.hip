@@ -200,11 +200,13 @@ int dispatch_impl(const DispatchArgs &a) {
         x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
     return launch_status();
   }
-  if (F > 1 && (int64_t)a.T * ROWB > kCachedXBytes) {
-    const WaveGrid g = wave_grid((int64_t)a.T * (K / F) * SLICES, 0, 1 << 24, kXcds);
-    ep_dispatch_grouped<DT, ROWB, SCB, K, F><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-        x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
-    return launch_status();
+  if constexpr (F > 1) {
+    if ((int64_t)a.T * ROWB > kCachedXBytes) {
+      const WaveGrid g = wave_grid((int64_t)a.T * (K / F) * SLICES, 0, 1 << 24, kXcds);
+      ep_dispatch_grouped<DT, ROWB, SCB, K, F><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+          x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
+      return launch_status();
+    }
   }
   const WaveGrid g = wave_grid((int64_t)a.T * K * SLICES, 0, 1 << 24, kXcds);
   ep_dispatch_expand<DT, ROWB, SCB, K><<<g.blocks, kDefaultThreads, 0, a.stream>>>(

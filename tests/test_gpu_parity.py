@@ -208,6 +208,54 @@ def test_combine_row_stream(T, H, E, K, A, mask, dtype, out_dtype):
                           oracle.combine(case.y, ref["dst_slot"], wts, bias), label)
 
 
+# Slots outside [0, capacity_rows) given straight to dispatch and combine are
+# skipped like masked entries: every dispatch kernel (per (token, k), grouped
+# for x beyond 128 MiB, capped fan-out) and every combine kernel (row-
+# streaming, sliced, capped).
+OUTSIDE = [
+    # T, H, K, workgroup cap, run combine
+    (2000, 7168, 8, 0, True),
+    (600, 7168, 6, 0, True),
+    (9500, 7168, 8, 0, False),
+    (2000, 2048, 8, 16, True),
+]
+
+
+@pytest.mark.parametrize("T,H,K,wg_cap,do_combine", OUTSIDE)
+def test_slots_outside_capacity_are_skipped(T, H, K, wg_cap, do_combine):
+    w = I.custom(f"oob{T}_{H}_{K}", 9100 + T, T, H, 256, K, 1, I.BF16, "uniform")
+    _say(f"[slots outside capacity] {w} workgroup cap {wg_cap}")
+    case = I.make_case(w, with_y=do_combine)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dst = ref["dst_slot"].copy()
+    pick = np.random.default_rng(9100 + T).random(dst.shape)
+    dst[pick < 0.05] = w.cap  # the first row past the buffer
+    dst[(pick >= 0.05) & (pick < 0.08)] = np.iinfo(np.int32).max
+    dst[(pick >= 0.08) & (pick < 0.10)] = -7
+    eff = np.where((dst >= 0) & (dst < w.cap), dst, -1).astype(np.int32)  # the header's meaning
+    dc = DeviceCase(case, with_y=do_combine)
+    dc.lay = {"dst_slot": to_dev(dst)}
+    s = torch.cuda.Stream()
+    try:
+        B.ep_set_workgroup_limit(s, wg_cap)
+        with torch.cuda.stream(s):
+            dc.dispatch(stream=s)
+            out = dc.combine(stream=s) if do_combine else None
+        s.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        B.ep_set_workgroup_limit(s, 0)
+    X = np.full((w.cap, dc.row_bytes), dc.sentinel, np.uint8)
+    Xw = np.full(w.cap, -5.0, np.float32)
+    oracle.dispatch(case.x, eff, w.cap, topk_weights=case.topk_weights, expand_x=X,
+                    expand_weights=Xw)
+    assert np.array_equal(to_host(dc.expand_x), X), "expand_x"
+    assert np.array_equal(to_host(dc.expand_w).view(np.uint32), Xw.view(np.uint32)), "weights"
+    if do_combine:
+        check_combine(to_host(out, np.uint16), oracle.combine(case.y, eff, case.topk_weights),
+                      w.name)
+
+
 def test_empty_input():
     w = I.custom("empty", 5, 0, 256, 16, 2, 4)
     lay = dev_layout(None, 0, 2, 16, 4, w.cap)
