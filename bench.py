@@ -254,6 +254,9 @@ def main():
     ap.add_argument("--path", choices=("expand", "non-expand"), default="expand",
                     help="expand: one row per (token, expert) (the default, headline path); "
                          "non-expand: one row per received token")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="expand path: dispatch token-major instead of in the order of the plan "
+                         "ep_layout writes (the plan is on by default)")
     ap.add_argument("--cold", action="store_true",
                     help="rotate buffer sets so that no step finds its rows in the last-level cache")
     ap.add_argument("--workgroups", type=int, default=0,
@@ -321,6 +324,8 @@ def main():
     wsb = B.ep_layout_workspace_bytes(w.T, w.K, w.E)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     rows_out = w.T if non_expand else w.cap
+    use_plan = not non_expand and not args.no_plan
+    plan = torch.empty((w.T * w.K, 2), dtype=torch.int32, device=dev) if use_plan else None
 
     def x_set():
         """One copy of the tokens' rows and scale rows."""
@@ -366,7 +371,8 @@ def main():
         S, X = sets[i % nsets], x_sets[i % nx]
         if ev is not None:
             ev[0].record(stream)
-        B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws, wsb, stream)
+        B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws, wsb, stream,
+                    dispatch_plan=plan)
         if ev is not None:
             ev[1].record(stream)
         if non_expand:
@@ -374,7 +380,7 @@ def main():
                                   S["expand"], S["expand_s"], S["recv_i"], S["recv_w"], stream)
         else:
             B.ep_dispatch(X["x"], X["xs"], None, dst, w.T, w.H, w.K, w.dtype, w.cap, S["expand"],
-                          S["expand_s"], None, stream)
+                          S["expand_s"], None, stream, dispatch_plan=plan)
         if ev is not None:
             ev[2].record(stream)
         if non_expand:
@@ -574,6 +580,7 @@ def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=N
                    "expert_alignment": w.A, "capacity_rows": w.cap, "routing": w.routing,
                    "dispatch_dtype": DTYPE_NAMES[w.dtype], "combine_dtype": DTYPE_NAMES[w.out_dtype],
                    "parallelism": "one GPU, all experts local", "path": args.path,
+                   "dispatch_plan": args.path == "expand" and not args.no_plan,
                    "workgroup_cap": args.workgroups or None,
                    "cache": cache, "launch": launch},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),

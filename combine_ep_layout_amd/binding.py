@@ -63,9 +63,11 @@ def lib(path: str = None) -> ctypes.CDLL:
     L = ctypes.CDLL(p)
     L.ep_layout_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.ep_layout_workspace_bytes.restype = _sz
-    L.ep_layout.argtypes = [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    L.ep_layout.argtypes = [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
+                            _vp]
     L.ep_layout.restype = ctypes.c_int
-    L.ep_dispatch.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp]
+    L.ep_dispatch.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
+                              _vp]
     L.ep_dispatch.restype = ctypes.c_int
     L.ep_combine.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp]
     L.ep_combine.restype = ctypes.c_int
@@ -126,18 +128,19 @@ def ep_layout_workspace_bytes(num_tokens: int, topk: int, num_experts: int) -> i
 
 def ep_layout(topk_idx, num_tokens, topk, num_experts, expert_alignment, capacity_rows,
               counts, offsets, dst_slot, recv_src_metadata, num_recv, workspace,
-              workspace_bytes, stream=None):
+              workspace_bytes, stream=None, dispatch_plan=None):
     _check(lib().ep_layout(_p(topk_idx), num_tokens, topk, num_experts, expert_alignment,
                            capacity_rows, _p(counts), _p(offsets), _p(dst_slot),
                            _p(recv_src_metadata), _p(num_recv), _p(workspace),
-                           workspace_bytes, _s(stream)))
+                           workspace_bytes, _p(dispatch_plan), _s(stream)))
 
 
 def ep_dispatch(x, x_scales, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,
-                capacity_rows, expand_x, expand_scales, expand_weights, stream=None):
+                capacity_rows, expand_x, expand_scales, expand_weights, stream=None,
+                dispatch_plan=None):
     _check(lib().ep_dispatch(_p(x), _p(x_scales), _p(topk_weights), _p(dst_slot), num_tokens,
                              hidden, topk, dtype, capacity_rows, _p(expand_x), _p(expand_scales),
-                             _p(expand_weights), _s(stream)))
+                             _p(expand_weights), _p(dispatch_plan), _s(stream)))
 
 
 def ep_combine(expert_out, topk_weights, bias, dst_slot, num_tokens, hidden, topk, dtype,

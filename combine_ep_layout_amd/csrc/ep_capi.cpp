@@ -144,7 +144,8 @@ size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_e
 int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t num_experts,
               int32_t expert_alignment, int64_t capacity_rows, int32_t *counts,
               int32_t *offsets, int32_t *dst_slot, int32_t *recv_src_metadata,
-              int32_t *num_recv, void *workspace, size_t workspace_bytes, void *stream) {
+              int32_t *num_recv, void *workspace, size_t workspace_bytes, int32_t *dispatch_plan,
+              void *stream) {
   try {
     const char *what = "ep_layout";
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
@@ -172,8 +173,11 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
                   workspace == nullptr ? (size_t)0 : workspace_bytes);
     if (need > 0 && !aligned(workspace, 16))
       return fail(EP_EINVAL, "%s: workspace must be 16-byte aligned", what);
+    if (!aligned(dispatch_plan, 8))
+      return fail(EP_EINVAL, "%s: dispatch_plan must be 8-byte aligned", what);
     ep::LayoutArgs a{topk_idx, num_tokens, topk, num_experts, expert_alignment, counts, offsets,
-                     dst_slot, recv_src_metadata, num_recv, workspace, (hipStream_t)stream};
+                     dst_slot, recv_src_metadata, num_recv, workspace, dispatch_plan,
+                     (hipStream_t)stream};
     return from_launch(ep::launch_layout(a), what);
   } catch (const std::exception &e) {
     return fail(EP_EHIP, "ep_layout: %s", e.what());
@@ -185,7 +189,7 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
 int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
                 const int32_t *dst_slot, int32_t num_tokens, int32_t hidden, int32_t topk,
                 int32_t dtype, int64_t capacity_rows, void *expand_x, float *expand_scales,
-                float *expand_weights, void *stream) {
+                float *expand_weights, const int32_t *dispatch_plan, void *stream) {
   try {
     const char *what = "ep_dispatch";
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
@@ -216,13 +220,13 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
       return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
     if (!aligned(x, 16) || !aligned(expand_x, 16) || !aligned(x_scales, 16) ||
         !aligned(expand_scales, 16) || !aligned(dst_slot, 4) || !aligned(topk_weights, 4) ||
-        !aligned(expand_weights, 4))
-      return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
+        !aligned(expand_weights, 4) || !aligned(dispatch_plan, 8))
+      return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes, the plan 8)", what);
     if (!ep::has_dispatch(hidden, topk, dtype))
       return fail(EP_EUNSUPPORTED, "%s: (hidden %d, topk %d, dtype %d) has no compiled kernel",
                   what, hidden, topk, dtype);
     ep::DispatchArgs a{x, x_scales, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,
-                       capacity_rows, expand_x, expand_scales, expand_weights,
+                       capacity_rows, expand_x, expand_scales, expand_weights, dispatch_plan,
                        (hipStream_t)stream};
     return from_launch(ep::launch_dispatch(a), what);
   } catch (const std::exception &e) {

@@ -53,15 +53,20 @@ __device__ __forceinline__ int64_t xcd_contiguous_block() {
 // store. Consecutive waves write consecutive KiB of one destination row, the
 // order in which HBM absorbs writes fastest (a wave that scatters to K rows
 // in turn is slower). The fp8 scale row and the router weight travel with
-// slice 0.
+// slice 0. PLANNED: the entries are taken in the order of the layout's
+// dispatch plan instead of token-major. Inside each tile of tokens the plan
+// lists entries by ascending slot, so consecutive entries are consecutive rows
+// of one expert's segment. Runs of about 4 rows at 128 tokens per tile make
+// HBM absorb the writes faster (prefill copy 79 against 85 us), and a tile's x
+// rows (1.8 MB) stay in the XCD's L2 for its K re-reads.
 // DT (the EP_* dtype) only names the kernel: every dtype moves bytes, so
 // instances with equal ROWB and SCB have the same body.
-template <int DT, int ROWB, int SCB, int K>
+template <int DT, int ROWB, int SCB, int K, bool PLANNED>
 __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
-    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
-    int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
-    float *__restrict__ expand_weights) {
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot,
+    const int2 *__restrict__ plan, int T, int64_t capacity, u32x4 *__restrict__ expand_x,
+    u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights) {
   constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
   constexpr int SLICES = (CH + kWave - 1) / kWave;  // 1 KiB slices per row
   constexpr int SCH = SCB / 16;                    // 16-byte chunks per scale row
@@ -74,10 +79,20 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
   const int64_t total = (int64_t)T * K * SLICES;
   const int64_t stride = (int64_t)gridDim.x * wpb;
   for (int64_t gw = xcd_contiguous_block() * wpb + wave_in_block; gw < total; gw += stride) {
-    const int64_t tk = gw / SLICES;  // flat (token, k)
-    const int slice = (int)(gw - tk * SLICES);
+    const int64_t j = gw / SLICES;  // entry index in walk order
+    const int slice = (int)(gw - j * SLICES);
+    int64_t tk;  // flat (token, k)
+    int d;
+    if constexpr (PLANNED) {
+      const int2 pe = plan[j];
+      tk = __builtin_amdgcn_readfirstlane(pe.x);
+      d = __builtin_amdgcn_readfirstlane(pe.y);
+      if (tk < 0 || tk >= (int64_t)T * K) continue;
+    } else {
+      tk = j;
+      d = __builtin_amdgcn_readfirstlane(dst_slot[tk]);
+    }
     const int64_t t = tk / K;
-    const int d = __builtin_amdgcn_readfirstlane(dst_slot[tk]);
     if (d < 0 || d >= capacity) continue;
     const int i = slice * kWave + lane;
     if (CH % kWave == 0 || i < CH)
@@ -209,8 +224,12 @@ int dispatch_impl(const DispatchArgs &a) {
     }
   }
   const WaveGrid g = wave_grid((int64_t)a.T * K * SLICES, 0, 1 << 24, kXcds);
-  ep_dispatch_expand<DT, ROWB, SCB, K><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-      x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
+  if (a.plan != nullptr)
+    ep_dispatch_expand<DT, ROWB, SCB, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+        x, xs, a.topk_weights, a.dst_slot, (const int2 *)a.plan, a.T, a.capacity, ex, es, ew);
+  else
+    ep_dispatch_expand<DT, ROWB, SCB, K, false><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+        x, xs, a.topk_weights, a.dst_slot, nullptr, a.T, a.capacity, ex, es, ew);
   return launch_status();
 }
 

@@ -24,6 +24,7 @@ struct LayoutArgs {
   int T, K, E, A;
   int32_t *counts, *offsets, *dst_slot, *meta, *num_recv;
   void *workspace;
+  int32_t *plan;  // [T*K] (entry, slot) pairs, or NULL
   hipStream_t stream;
 };
 
@@ -37,6 +38,7 @@ struct DispatchArgs {
   void *expand_x;
   float *expand_scales;
   float *expand_weights;
+  const int32_t *plan;  // [T*K] (entry, slot) pairs from ep_layout, or NULL
   hipStream_t stream;
 };
 

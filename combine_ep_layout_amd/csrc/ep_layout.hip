@@ -185,24 +185,44 @@ __device__ __forceinline__ void write_slots_and_meta(int64_t t0, int ntok, int s
   }
 }
 
+// Writes the tile's part of the dispatch plan: the tile's unmasked entries in
+// ascending slot order, each as (entry t*K + k, slot), then (-1, -1) for its
+// masked entries. Inside a tile, slots ascend with (expert, rank), so an
+// entry's place is the count of the tile's entries of lower experts (s_tb,
+// an exclusive scan over experts of the tile's counts, published by a
+// barrier) plus its rank; nvalid is the tile's count of unmasked entries.
+template <int K>
+__device__ __forceinline__ void write_plan(int64_t t0, int ntok, int e, int rank, int slot,
+                                           const int *s_tb, int nvalid,
+                                           int32_t *__restrict__ plan) {
+  const int tid = threadIdx.x;
+  if (tid < ntok * K) {
+    int2 *p = reinterpret_cast<int2 *>(plan) + t0 * K;
+    if (e >= 0) p[s_tb[e] + rank] = make_int2((int)(t0 * K) + tid, slot);
+    if (tid >= nvalid) p[tid] = make_int2(-1, -1);
+  }
+}
+
 // One launch for T*K that fits a single tile (including T = 0).
 template <int K, int NW>
 __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
-    int32_t *__restrict__ num_recv) {
-  __shared__ int s_tmp[kWavesMax];
+    int32_t *__restrict__ num_recv, int32_t *__restrict__ plan) {
+  __shared__ int s_tmp[2 * kWavesMax];
   const RankLds s = rank_lds(E, NW);
   int *s_off = (int *)(g_smem + rank_lds_bytes(E, NW));  // E
+  int *s_tb = s_off + E;                                 // E: dispatch plan
   const int tid = threadIdx.x;
 
   const EntryRank r = tile_rank<K, NW>(topk_idx, 0, T, E, s);
   const int cnt = tid < E ? s.total[tid] : 0;
   const int padded = ((cnt + A - 1) / A) * A;
-  int rows;
-  const int off = block_exclusive_scan<kThreads>(padded, s_tmp, rows);
+  int rows, tb, nvalid;
+  const int off = block_exclusive_scan2<kThreads>(padded, cnt, tb, s_tmp, rows, nvalid);
   if (tid < E) {
     s_off[tid] = off;
+    s_tb[tid] = tb;
     counts[tid] = cnt;
     offsets[tid] = off;
   }
@@ -215,6 +235,7 @@ __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
   if (tid < T) s.tok[tid] = f ? tok_rank : -1;
   __syncthreads();
   write_slots_and_meta<K>(0, T, slot, s.tok, dst_slot, meta);
+  if (plan != nullptr) write_plan<K>(0, T, r.e, r.rank, slot, s_tb, nvalid, plan);
 }
 
 // One launch for several tiles when T*K is small enough: besides ranking its
@@ -228,12 +249,13 @@ template <int K, int NW>
 __device__ __forceinline__ void fused_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
-    int32_t *__restrict__ num_recv, const int b) {
-  __shared__ int s_tmp[kWavesMax];
+    int32_t *__restrict__ num_recv, int32_t *__restrict__ plan, const int b) {
+  __shared__ int s_tmp[2 * kWavesMax];
   const RankLds s = rank_lds(E, NW);
   int *s_pre = (int *)(g_smem + rank_lds_bytes(E, NW));  // E: entries before this tile
   int *s_all = s_pre + E;                                // E: all entries
   int *s_off = s_all + E;                                // E
+  int *s_tb = s_off + E;                                 // E: dispatch plan
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)b * Tile<K, NW>::tokens;
   const int ntok = (int)min((int64_t)Tile<K, NW>::tokens, (int64_t)T - t0);
@@ -268,9 +290,13 @@ __device__ __forceinline__ void fused_tile(
   const int recv_total = block_sum(vall, s_tmp);
   const int cnt = tid < E ? s_all[tid] : 0;
   const int padded = ((cnt + A - 1) / A) * A;
-  int rows;
-  const int off = block_exclusive_scan<kThreads>(padded, s_tmp, rows);
-  if (tid < E) s_off[tid] = off;
+  const int mine = tid < E ? s.total[tid] : 0;  // this tile's count of expert tid
+  int rows, tb, nvalid;
+  const int off = block_exclusive_scan2<kThreads>(padded, mine, tb, s_tmp, rows, nvalid);
+  if (tid < E) {
+    s_off[tid] = off;
+    s_tb[tid] = tb;
+  }
   if (b == 0) {
     if (tid < E) {
       counts[tid] = cnt;
@@ -288,6 +314,7 @@ __device__ __forceinline__ void fused_tile(
   if (tid < ntok) s.tok[tid] = f ? recv_before + tok_rank : -1;
   __syncthreads();
   write_slots_and_meta<K>(t0, ntok, slot, s.tok, dst_slot, meta);
+  if (plan != nullptr) write_plan<K>(t0, ntok, r.e, r.rank, slot, s_tb, nvalid, plan);
 }
 
 // Tile blockIdx.x, or with LOOP (the stream caps the workgroup count below
@@ -298,12 +325,13 @@ template <int K, int NW, bool LOOP>
 __global__ __launch_bounds__(kThreads) void ep_layout_fused_tiles(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int num_tiles,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot,
-    int32_t *__restrict__ meta, int32_t *__restrict__ num_recv) {
+    int32_t *__restrict__ meta, int32_t *__restrict__ num_recv, int32_t *__restrict__ plan) {
   if constexpr (!LOOP) {
-    fused_tile<K, NW>(topk_idx, T, E, A, counts, offsets, dst_slot, meta, num_recv, blockIdx.x);
+    fused_tile<K, NW>(topk_idx, T, E, A, counts, offsets, dst_slot, meta, num_recv, plan,
+                      blockIdx.x);
   } else {
     for (int b = blockIdx.x; b < num_tiles; b += gridDim.x) {
-      fused_tile<K, NW>(topk_idx, T, E, A, counts, offsets, dst_slot, meta, num_recv, b);
+      fused_tile<K, NW>(topk_idx, T, E, A, counts, offsets, dst_slot, meta, num_recv, plan, b);
       __syncthreads();
     }
   }
@@ -362,19 +390,21 @@ __device__ __forceinline__ void assign_tile(
     int T, int E, int A, int num_tiles, const int32_t *__restrict__ tile_counts,
     const int32_t *__restrict__ tile_recv, const TileScan &scan, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
-    int32_t *__restrict__ num_recv, const int b) {
+    int32_t *__restrict__ num_recv, int32_t *__restrict__ plan, const int b) {
   __shared__ int s_pre[kThreads];
   __shared__ int s_tot[kThreads];
   __shared__ int s_row[kThreads];
-  __shared__ int s_tmp[kWavesMax];
+  __shared__ int s_tmp[2 * kWavesMax];
   int *s_base = (int *)g_smem;  // E
   int *s_off = s_base + E;      // E
+  int *s_tb = s_off + E;        // E: dispatch plan
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)b * Tile<K, NW>::tokens;
   const int ntok = (int)min((int64_t)Tile<K, NW>::tokens, (int64_t)T - t0);
 
   // Every global load of the block is issued before the first barrier.
   const int packed = tid < ntok * K ? dst_slot[t0 * K + tid] : -1;
+  const int mine = plan != nullptr && tid < E ? tile_counts[(int64_t)b * E + tid] : 0;
   int base = 0, cnt = 0, recv_before, recv_total;
   if constexpr (SCANNED) {
     if (tid < E) {
@@ -418,11 +448,12 @@ __device__ __forceinline__ void assign_tile(
     }
   }
   const int padded = ((cnt + A - 1) / A) * A;
-  int rows;
-  const int off = block_exclusive_scan<kThreads>(padded, s_tmp, rows);
+  int rows, tb, nvalid;
+  const int off = block_exclusive_scan2<kThreads>(padded, mine, tb, s_tmp, rows, nvalid);
   if (tid < E) {
     s_base[tid] = base;
     s_off[tid] = off;
+    s_tb[tid] = tb;
   }
   if (b == 0) {
     if (tid < E) {
@@ -447,6 +478,11 @@ __device__ __forceinline__ void assign_tile(
   if (tid < ntok) s_row[tid] = f ? recv_before + tok_rank : -1;
   __syncthreads();
   write_slots_and_meta<K>(t0, ntok, slot, s_row, dst_slot, meta);
+  if (plan != nullptr) {
+    const int e = packed >= 0 ? packed >> kRankBits : -1;
+    const int rank = packed & ((1 << kRankBits) - 1);
+    write_plan<K>(t0, ntok, e, rank, slot, s_tb, nvalid, plan);
+  }
 }
 
 template <int K, int NW, bool LOOP, bool SCANNED>
@@ -454,14 +490,14 @@ __global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
     int T, int E, int A, int num_tiles, const int32_t *__restrict__ tile_counts,
     const int32_t *__restrict__ tile_recv, TileScan scan, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
-    int32_t *__restrict__ num_recv) {
+    int32_t *__restrict__ num_recv, int32_t *__restrict__ plan) {
   if constexpr (!LOOP) {
     assign_tile<K, NW, SCANNED>(T, E, A, num_tiles, tile_counts, tile_recv, scan, counts, offsets,
-                                dst_slot, meta, num_recv, blockIdx.x);
+                                dst_slot, meta, num_recv, plan, blockIdx.x);
   } else {
     for (int b = blockIdx.x; b < num_tiles; b += gridDim.x) {
       assign_tile<K, NW, SCANNED>(T, E, A, num_tiles, tile_counts, tile_recv, scan, counts,
-                                  offsets, dst_slot, meta, num_recv, b);
+                                  offsets, dst_slot, meta, num_recv, plan, b);
       __syncthreads();
     }
   }
@@ -548,15 +584,16 @@ int layout_launch(const LayoutArgs &a, int B, unsigned G, int cap) {
   const size_t shm_rank = rank_lds_bytes(a.E, NW);
   if ((int64_t)a.T * K <= kFusedMaxEntries) {
     ep_layout_fused_tiles<K, NW, LOOP>
-        <<<G, kThreads, shm_rank + sizeof(int) * (size_t)(3 * a.E), a.stream>>>(
-            a.topk_idx, a.T, a.E, a.A, B, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
+        <<<G, kThreads, shm_rank + sizeof(int) * (size_t)(4 * a.E), a.stream>>>(
+            a.topk_idx, a.T, a.E, a.A, B, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv,
+            a.plan);
     return launch_status();
   }
   int32_t *tile_counts = (int32_t *)a.workspace;
   int32_t *tile_recv = tile_counts + (size_t)B * a.E;
   ep_layout_tile_histogram<K, NW, LOOP><<<G, kThreads, shm_rank, a.stream>>>(
       a.topk_idx, a.T, a.E, B, a.dst_slot, tile_counts, tile_recv);
-  const size_t shm_assign = sizeof(int) * (size_t)(2 * a.E);
+  const size_t shm_assign = sizeof(int) * (size_t)(3 * a.E);
   if (use_tile_scan(B, a.E)) {
     int32_t *tile_base = tile_recv + B;
     int32_t *expert_total = tile_base + (size_t)B * a.E;
@@ -569,11 +606,11 @@ int layout_launch(const LayoutArgs &a, int B, unsigned G, int cap) {
     const TileScan scan{tile_base, expert_total, recv_base, recv_total};
     ep_layout_tile_assign<K, NW, LOOP, true><<<G, kThreads, shm_assign, a.stream>>>(
         a.T, a.E, a.A, B, tile_counts, tile_recv, scan, a.counts, a.offsets, a.dst_slot, a.meta,
-        a.num_recv);
+        a.num_recv, a.plan);
   } else {
     ep_layout_tile_assign<K, NW, LOOP, false><<<G, kThreads, shm_assign, a.stream>>>(
         a.T, a.E, a.A, B, tile_counts, tile_recv, TileScan{}, a.counts, a.offsets, a.dst_slot,
-        a.meta, a.num_recv);
+        a.meta, a.num_recv, a.plan);
   }
   return launch_status();
 }
@@ -583,8 +620,10 @@ int layout_impl(const LayoutArgs &a) {
   const int B = tiles_for<K, NW>(a.T);
   if (B <= 1) {
     const size_t shm_rank = rank_lds_bytes(a.E, NW);
-    ep_layout_single_tile<K, NW><<<1, kThreads, shm_rank + sizeof(int) * (size_t)a.E, a.stream>>>(
-        a.topk_idx, a.T, a.E, a.A, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv);
+    ep_layout_single_tile<K, NW>
+        <<<1, kThreads, shm_rank + sizeof(int) * (size_t)(2 * a.E), a.stream>>>(
+            a.topk_idx, a.T, a.E, a.A, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv,
+            a.plan);
     return launch_status();
   }
   const int cap = stream_workgroup_limit(a.stream);

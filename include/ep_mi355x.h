@@ -113,12 +113,23 @@ size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_e
  *                     Rows i >= *num_recv are left untouched.
  *   num_recv          int32 [1]: number of such tokens (stays on the device)
  *   workspace         device scratch of >= ep_layout_workspace_bytes(T, K, E)
+ *   dispatch_plan     optional (NULL: not written), int32 [T*K, 2], 8-byte
+ *                     aligned: the order in which ep_dispatch copies rows
+ *                     fastest. The entries are cut into tiles of whole tokens,
+ *                     floor(W / K) tokens each, where W = 1024 for E <= 256,
+ *                     512 for E <= 512 and 256 above. Each tile's span
+ *                     lists its unmasked entries by ascending slot as
+ *                     (t*K + k, dst_slot[t, k]), then (-1, -1) once per
+ *                     masked entry. This array is not part of the pages'
+ *                     handle: it is a gfx950-specific write-order aid, and
+ *                     every other output is the same with or without it.
  * Results are a pure function of the inputs (no atomics whose order matters).
  */
 int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t num_experts,
               int32_t expert_alignment, int64_t capacity_rows, int32_t *counts,
               int32_t *offsets, int32_t *dst_slot, int32_t *recv_src_metadata,
-              int32_t *num_recv, void *workspace, size_t workspace_bytes, void *stream);
+              int32_t *num_recv, void *workspace, size_t workspace_bytes,
+              int32_t *dispatch_plan, void *stream);
 
 /*
  * Dispatch in the expand layout (DeepEP overall architecture, dispatch copy
@@ -143,6 +154,12 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
  *   expand_x        [capacity_rows, hidden] of the same element type as x
  *   expand_scales   fp32 [capacity_rows, S], given exactly when x_scales is
  *   expand_weights  fp32 [capacity_rows] or NULL
+ *   dispatch_plan   optional (NULL: token-major order): the plan ep_layout
+ *                   wrote in the same call as dst_slot. It changes only the
+ *                   order of the copies, never their result. Entries of the
+ *                   plan outside [0, T*K) and slots outside
+ *                   [0, capacity_rows) are skipped. A plan that does not
+ *                   match dst_slot copies what the plan says.
  * Errors: EP_EINVAL for a NULL required pointer, misalignment, row bytes
  * not a multiple of 16, scales for bf16 / fp32 or only one scale pointer;
  * EP_EUNSUPPORTED for (hidden, topk, dtype) outside the compiled set.
@@ -150,7 +167,7 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
 int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
                 const int32_t *dst_slot, int32_t num_tokens, int32_t hidden, int32_t topk,
                 int32_t dtype, int64_t capacity_rows, void *expand_x, float *expand_scales,
-                float *expand_weights, void *stream);
+                float *expand_weights, const int32_t *dispatch_plan, void *stream);
 
 /*
  * Gather combine (DeepEP overall architecture, combine reduce epilogue

@@ -26,8 +26,9 @@ def to_host(t: torch.Tensor, dtype=None) -> np.ndarray:
     return a
 
 
-def dev_layout(idx_d: torch.Tensor, T: int, K: int, E: int, A: int, cap: int, stream=None):
-    """Run ep_layout; returns a dict of device tensors."""
+def dev_layout(idx_d: torch.Tensor, T: int, K: int, E: int, A: int, cap: int, stream=None,
+               plan: bool = False):
+    """Run ep_layout; returns a dict of device tensors (with the dispatch plan if asked)."""
     counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
     offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
     dst = torch.full((max(T, 1), K), -7, dtype=torch.int32, device=DEV)
@@ -35,10 +36,14 @@ def dev_layout(idx_d: torch.Tensor, T: int, K: int, E: int, A: int, cap: int, st
     nrecv = torch.full((1,), -7, dtype=torch.int32, device=DEV)
     wsb = B.ep_layout_workspace_bytes(T, K, E)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+    pl = torch.full((max(T * K, 1), 2), -9, dtype=torch.int32, device=DEV) if plan else None
     B.ep_layout(idx_d if T else None, T, K, E, A, cap, counts, offsets, dst if T else None,
-                meta if T else None, nrecv, ws, wsb, stream)
-    return {"counts": counts, "offsets": offsets, "dst_slot": dst[:T], "meta": meta[:T],
-            "num_recv": nrecv}
+                meta if T else None, nrecv, ws, wsb, stream, dispatch_plan=pl)
+    out = {"counts": counts, "offsets": offsets, "dst_slot": dst[:T], "meta": meta[:T],
+           "num_recv": nrecv}
+    if plan:
+        out["plan"] = pl[:T * K]
+    return out
 
 
 def layout_to_host(d):
@@ -74,16 +79,17 @@ class DeviceCase:
             self.out = torch.full((max(w.T, 1), self.H_out), 0x7FC1, dtype=torch.int16, device=DEV)
         self.sentinel = sentinel
 
-    def layout(self, stream=None):
+    def layout(self, stream=None, plan=False):
         w = self.w
-        self.lay = dev_layout(self.idx, w.T, w.K, w.E, w.A, w.cap, stream)
+        self.lay = dev_layout(self.idx, w.T, w.K, w.E, w.A, w.cap, stream, plan=plan)
         return self.lay
 
-    def dispatch(self, stream=None, weights=True):
+    def dispatch(self, stream=None, weights=True, plan=False):
         w = self.w
         B.ep_dispatch(self.x, self.xs, self.wts if weights else None, self.lay["dst_slot"], w.T,
                       w.H, w.K, w.dtype, w.cap, self.expand_x, self.expand_s,
-                      self.expand_w if weights else None, stream)
+                      self.expand_w if weights else None, stream,
+                      dispatch_plan=self.lay["plan"] if plan else None)
 
     def combine(self, y=None, weights=True, bias=None, stream=None):
         w = self.w

@@ -101,6 +101,10 @@ def test_layout_rejections(L):
     assert _code(B.ep_layout, *lay(idx=None)) == B.EP_EINVAL
     assert _code(B.ep_layout, *lay(counts=None)) == B.EP_EINVAL
     assert _code(B.ep_layout, *lay(T=1 << 28, cap=1 << 40)) == B.EP_EINVAL  # T*K overflows int32
+    plan_4 = FAKE + 4  # (entry, slot) pairs need 8-byte alignment
+    with pytest.raises(B.EpError) as ei:
+        B.ep_layout(*lay(), dispatch_plan=plan_4)
+    assert ei.value.code == B.EP_EINVAL and "dispatch_plan" in str(ei.value)
 
 
 def disp(x=FAKE, xs=None, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280, X=FAKE, Xs=None):
@@ -123,6 +127,9 @@ def test_dispatch_rejections(L):
     assert _code(B.ep_dispatch, *disp(X=None)) == B.EP_EINVAL
     assert _code(B.ep_dispatch, *disp(cap=-1)) == B.EP_EINVAL
     assert _code(B.ep_dispatch, *disp(K=5)) == B.EP_EUNSUPPORTED
+    with pytest.raises(B.EpError) as ei:
+        B.ep_dispatch(*disp(), dispatch_plan=FAKE + 4)
+    assert ei.value.code == B.EP_EINVAL and "plan" in str(ei.value)
 
 
 def comb(y=FAKE, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280, out=FAKE, bias=None):

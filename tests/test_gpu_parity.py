@@ -256,6 +256,62 @@ def test_slots_outside_capacity_are_skipped(T, H, K, wg_cap, do_combine):
                       w.name)
 
 
+def expected_plan(dst, E, K):
+    """The dispatch plan the header specifies, from the oracle's slots: per tile
+    of floor(W / K) tokens, the unmasked entries by ascending slot as (entry,
+    slot), then (-1, -1) once per masked entry."""
+    T = dst.shape[0]
+    W = 1024 if E <= 256 else (512 if E <= 512 else 256)
+    tokens = W // K
+    flat = dst.reshape(-1)
+    out = np.full((T * K, 2), -1, np.int32)
+    for t0 in range(0, T, tokens):
+        lo, hi = t0 * K, min(T, t0 + tokens) * K
+        seg = flat[lo:hi]
+        valid = np.nonzero(seg >= 0)[0]
+        order = valid[np.argsort(seg[valid], kind="stable")]
+        out[lo:lo + order.size, 0] = lo + order
+        out[lo:lo + order.size, 1] = seg[order]
+    return out
+
+
+PLANS = [
+    # T, H, E, K, A, mask, workgroup cap: every layout launch shape, capped loops
+    (100, 7168, 256, 8, 128, 0.1, 0),     # one tile
+    (1500, 2048, 256, 8, 4, 0.05, 0),     # single launch, several tiles
+    (4096, 7168, 256, 8, 128, 0.0, 0),    # two launches (the prefill shape)
+    (20000, 256, 1024, 8, 4, 0.05, 0),    # with the tile-scan launch, 32-token tiles
+    (3000, 1024, 300, 6, 3, 0.1, 0),      # 85-token tiles
+    (5000, 512, 16, 1, 1, 0.2, 0),        # K = 1
+    (4096, 7168, 256, 8, 128, 0.02, 3),   # capped: tiles loop; dispatch ignores the plan
+    (1500, 2048, 256, 8, 4, 0.05, 5),
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,A,mask,wg_cap", PLANS)
+def test_dispatch_plan(T, H, E, K, A, mask, wg_cap):
+    w = I.custom(f"plan{T}_{E}_{K}", 9300 + T + E, T, H, E, K, A, I.BF16, "uniform")
+    _say(f"[dispatch plan] {w} workgroup cap {wg_cap}")
+    case = I.make_case(w, with_y=False, mask_frac=mask)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case, with_y=False)
+    s = torch.cuda.Stream()
+    try:
+        B.ep_set_workgroup_limit(s, wg_cap)
+        with torch.cuda.stream(s):
+            dc.layout(stream=s, plan=True)
+            dc.dispatch(stream=s, plan=True)
+        s.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        B.ep_set_workgroup_limit(s, 0)
+    check_layout(layout_to_host(dc.lay), ref)  # the plan changes no other output
+    got = to_host(dc.lay["plan"])
+    want = expected_plan(ref["dst_slot"], w.E, w.K)
+    assert np.array_equal(got, want), f"plan differs at {int(np.argmax((got != want).any(1)))}"
+    check_dispatch(dc, ref["dst_slot"])
+
+
 def test_empty_input():
     w = I.custom("empty", 5, 0, 256, 16, 2, 4)
     lay = dev_layout(None, 0, 2, 16, 4, w.cap)
