@@ -130,6 +130,12 @@ def measured_traffic(workload: str, kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+# Expand payload from which the step asks ep_layout for the dispatch plan.
+# Measured on MI355X: prefill (470 MB of rows) gains 3.6 us per step; at
+# 117-120 MB (mori_default, fp4x2 prefill) and below the plan's layout cost
+# (about 0.1-0.4 us) cancels or exceeds the gain.
+PLAN_MIN_BYTES = 256 << 20
+
 CALIBRATION_BYTES = 1 << 30  # fp32 elementwise negate: reads and writes this many bytes
 # Kernel-name fragments per pass: each pass launches one of its kernels, chosen by shape and cap.
 KERNEL_TAGS = {"dispatch": ("ep_dispatch_expand", "ep_dispatch_grouped", "ep_dispatch_fanout"),
@@ -255,8 +261,8 @@ def main():
                     help="expand: one row per (token, expert) (the default, headline path); "
                          "non-expand: one row per received token")
     ap.add_argument("--no-plan", action="store_true",
-                    help="expand path: dispatch token-major instead of in the order of the plan "
-                         "ep_layout writes (the plan is on by default)")
+                    help="expand path: never ask ep_layout for the dispatch plan (by default it is "
+                         "used when the expand rows total at least PLAN_MIN_BYTES)")
     ap.add_argument("--cold", action="store_true",
                     help="rotate buffer sets so that no step finds its rows in the last-level cache")
     ap.add_argument("--workgroups", type=int, default=0,
@@ -324,7 +330,8 @@ def main():
     wsb = B.ep_layout_workspace_bytes(w.T, w.K, w.E)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     rows_out = w.T if non_expand else w.cap
-    use_plan = not non_expand and not args.no_plan
+    use_plan = (not non_expand and not args.no_plan
+                and w.T * w.K * case.x.view(np.uint8).reshape(w.T, -1).shape[1] >= PLAN_MIN_BYTES)
     plan = torch.empty((w.T * w.K, 2), dtype=torch.int32, device=dev) if use_plan else None
 
     def x_set():
@@ -454,7 +461,8 @@ def main():
     if args.workgroups > 0:
         torch.cuda.synchronize()
         B.ep_set_workgroup_limit(stream, 0)
-    report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap, cache, launch)
+    report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap, cache, launch,
+           use_plan)
 
 
 GEMM_SHAPE = (8192, 7168, 2048)  # M, K, N: bf16 [M, K] x [K, N], about one step's duration
@@ -548,7 +556,7 @@ def validate_expand(oracle, case, ref, expand, out, sample, xb, dev) -> bool:
 
 
 def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=None, cache="warm",
-           launch="eager"):
+           launch="eager", plan_used=False):
     n_valid = int((ref["dst_slot"] >= 0).sum())
     nb = algorithmic_bytes(w, n_valid, ref["num_recv"], args.path)
     total_bytes = sum(nb.values())
@@ -580,7 +588,7 @@ def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=N
                    "expert_alignment": w.A, "capacity_rows": w.cap, "routing": w.routing,
                    "dispatch_dtype": DTYPE_NAMES[w.dtype], "combine_dtype": DTYPE_NAMES[w.out_dtype],
                    "parallelism": "one GPU, all experts local", "path": args.path,
-                   "dispatch_plan": args.path == "expand" and not args.no_plan,
+                   "dispatch_plan": plan_used,
                    "workgroup_cap": args.workgroups or None,
                    "cache": cache, "launch": launch},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -98,13 +98,11 @@ template <int K, int NW>
 __device__ EntryRank tile_rank(const int32_t *__restrict__ topk_idx, int64_t t0, int ntok, int E,
                                const RankLds &s) {
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  // the id load is issued first, so that its latency overlaps the LDS clearing
+  const int v = tid < ntok * K ? topk_idx[t0 * K + tid] : -1;
   for (int i = tid; i < E * NW; i += kThreads) s.mask[i] = 0;
   if (tid < Tile<K, NW>::tokens) s.tok[tid] = 0;
-  int e = -1;
-  if (tid < ntok * K) {
-    const int v = topk_idx[t0 * K + tid];
-    e = (v >= 0 && v < E) ? v : -1;
-  }
+  const int e = (v >= 0 && v < E) ? v : -1;
   __syncthreads();
   if (e >= 0) {
     __hip_atomic_fetch_or(&s.mask[e * NW + w], 1ull << lane, __ATOMIC_RELAXED,

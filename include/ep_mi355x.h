@@ -123,6 +123,10 @@ size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_e
  *                     masked entry. This array is not part of the pages'
  *                     handle: it is a gfx950-specific write-order aid, and
  *                     every other output is the same with or without it.
+ *                     Measured on MI355X it pays for large expand buffers
+ *                     (prefill with 470 MB of rows: dispatch 87 -> 83 us for
+ *                     0.1 us more layout). At 120 MB of rows and below it
+ *                     gains about what it costs the layout (0.1-0.4 us).
  * Results are a pure function of the inputs (no atomics whose order matters).
  */
 int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t num_experts,
