@@ -223,3 +223,28 @@ def check_combine_compact(y_bits, dst, meta, num_recv, out_bits, bias_bits=None)
     # two binary32 roundings of a sum of two bf16 values (the first is exact) then bf16 rounding
     bound = 0.5 * bf16_ulp(out) + U32 * np.abs(exact)
     assert np.all(np.abs(out - exact) <= bound), "bias add outside half a bf16 ulp"
+
+
+# --------------------------------------------------------------------------
+# Dispatch plan
+# --------------------------------------------------------------------------
+
+def dispatch_plan(dst, E, K):
+    """The dispatch plan ep_layout writes, as include/ep_mi355x.h defines it,
+    computed from the oracle's slots: per tile of floor(W / K) tokens (W =
+    1024, 512 or 256 for E up to 256, 512, 1024), the unmasked entries by
+    ascending slot as (entry, slot), then (-1, -1) once per masked entry. The
+    plan is the library's write-order aid, not part of the pages' method."""
+    T = dst.shape[0]
+    W = 1024 if E <= 256 else (512 if E <= 512 else 256)
+    tokens = W // K
+    flat = dst.reshape(-1)
+    out = np.full((T * K, 2), -1, np.int32)
+    for t0 in range(0, T, tokens):
+        lo, hi = t0 * K, min(T, t0 + tokens) * K
+        seg = flat[lo:hi]
+        valid = np.nonzero(seg >= 0)[0]
+        order = valid[np.argsort(seg[valid], kind="stable")]
+        out[lo:lo + order.size, 0] = lo + order
+        out[lo:lo + order.size, 1] = seg[order]
+    return out

@@ -256,25 +256,6 @@ def test_slots_outside_capacity_are_skipped(T, H, K, wg_cap, do_combine):
                       w.name)
 
 
-def expected_plan(dst, E, K):
-    """The dispatch plan the header specifies, from the oracle's slots: per tile
-    of floor(W / K) tokens, the unmasked entries by ascending slot as (entry,
-    slot), then (-1, -1) once per masked entry."""
-    T = dst.shape[0]
-    W = 1024 if E <= 256 else (512 if E <= 512 else 256)
-    tokens = W // K
-    flat = dst.reshape(-1)
-    out = np.full((T * K, 2), -1, np.int32)
-    for t0 in range(0, T, tokens):
-        lo, hi = t0 * K, min(T, t0 + tokens) * K
-        seg = flat[lo:hi]
-        valid = np.nonzero(seg >= 0)[0]
-        order = valid[np.argsort(seg[valid], kind="stable")]
-        out[lo:lo + order.size, 0] = lo + order
-        out[lo:lo + order.size, 1] = seg[order]
-    return out
-
-
 PLANS = [
     # T, H, E, K, A, mask, workgroup cap: every layout launch shape, capped loops
     (100, 7168, 256, 8, 128, 0.1, 0),     # one tile
@@ -307,7 +288,7 @@ def test_dispatch_plan(T, H, E, K, A, mask, wg_cap):
         B.ep_set_workgroup_limit(s, 0)
     check_layout(layout_to_host(dc.lay), ref)  # the plan changes no other output
     got = to_host(dc.lay["plan"])
-    want = expected_plan(ref["dst_slot"], w.E, w.K)
+    want = pins.dispatch_plan(ref["dst_slot"], w.E, w.K)
     assert np.array_equal(got, want), f"plan differs at {int(np.argmax((got != want).any(1)))}"
     check_dispatch(dc, ref["dst_slot"])
 

@@ -3,7 +3,8 @@
 Each case draws a compiled (hidden, topk, dtype), a token count, an expert
 count up to 1024, an alignment, a masking fraction, out-of-range ids, an
 optional bias and an optional workgroup cap, then runs layout, dispatch,
-combine (and, for bf16, the non-expand pair) through the C ABI. Bar as in
+combine (and, for bf16, the non-expand pair) through the C ABI; even seeds
+also ask the layout for the dispatch plan and dispatch through it. Bar as in
 the other parity tests: everything bit-exact except bf16 combine (<= 1 ulp).
 """
 import numpy as np
@@ -51,13 +52,14 @@ def test_random_shape(seed):
                  "uniform", out_dtype=out_dtype, scales=c["scales"])
     case = I.make_case(w, mask_frac=c["mask"])
     case.topk_idx[::11, 0] = w.E + 1  # some ids outside [0, E): masked
+    plan = seed % 2 == 0
     s = torch.cuda.Stream()
     try:
         B.ep_set_workgroup_limit(s, c["cap"])
         with torch.cuda.stream(s):
             dc = DeviceCase(case)
-            lay = dc.layout(stream=s)
-            dc.dispatch(stream=s)
+            lay = dc.layout(stream=s, plan=plan)
+            dc.dispatch(stream=s, plan=plan)
             bias = None
             if c["bias"]:
                 bias_host = (I.normal_f32(w.seed, 9, w.T, dc.H_out) if out_dtype == I.FP32
@@ -75,6 +77,8 @@ def test_random_shape(seed):
         assert np.array_equal(got[k], ref[k]), k
     assert got["num_recv"] == ref["num_recv"]
     assert np.array_equal(got["recv_src_metadata"], ref["recv_src_metadata"])
+    if plan:
+        assert np.array_equal(to_host(lay["plan"]), pins.dispatch_plan(ref["dst_slot"], w.E, w.K))
 
     X = np.full((w.cap, dc.row_bytes), dc.sentinel, np.uint8)
     Xs = (np.full((w.cap, case.x_scales.shape[1]), -3.0, np.float32)
