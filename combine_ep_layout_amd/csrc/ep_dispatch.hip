@@ -12,11 +12,12 @@
 // 16-byte load per lane from x and one 16-byte store per lane into the
 // expand row, whose address is wave-uniform (the slot is loaded once and made
 // scalar with readfirstlane). The store is non-temporal at device scope
-// (store_row_nt): expand rows are not read again by this pass. Waves are ordered token-major,
-// then k, then slice, so the write stream is one destination row after
-// another, each written front to back; the K waves that need the same source
-// slice run on the same XCD, so x is read from HBM about once. Row bytes and
-// K are template constants.
+// (store_row_nt): expand rows are not read again by this pass. Waves are
+// ordered token-major, then k, then slice, or, given the layout's dispatch
+// plan, by ascending slot within each tile of tokens, then slice; either way
+// each destination row is written front to back by consecutive waves, and
+// the K waves that need the same source slice run on the same XCD, so x is
+// read from HBM about once. Row bytes and K are template constants.
 //
 // When x is too large to stay in the last-level cache, the K waves that need
 // one source slice all wait on the same HBM read, and few distinct bytes of x

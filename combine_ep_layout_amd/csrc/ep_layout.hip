@@ -25,6 +25,9 @@
 // A single tile (small T*K) runs both halves in one launch with no
 // workspace; so do up to 2^14 entries, with every block also scanning all
 // entries (see ep_layout_fused_tiles). Results do not depend on scheduling.
+// On request the last launch also writes the dispatch plan: each tile's
+// entries in slot order, the order in which dispatch writes expand rows
+// fastest (write_plan).
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
