@@ -28,7 +28,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // WIDE: launched over the whole chip (no workgroup cap), which selects the
-// store policy (store_row_nt).
+// store policy: the receive rows and combine's output rows (one row per
+// token, 59 MB at prefill) are stored at device scope and kept
+// (RowStore::kDevice); under a cap, non-temporally.
 template <bool WIDE>
 __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     const u32x4 *__restrict__ x, int64_t row_chunks, const float *__restrict__ x_scales,
@@ -53,7 +55,9 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     if (t < 0 || t >= T) continue;
     const int64_t c = slice * kWave + lane;
     if (c < row_chunks)
-      store_row_nt<WIDE>(x[t * row_chunks + c], recv_x + i * row_chunks, (int)(row_chunks * 16),
+      store_row<WIDE ? RowStore::kDevice : RowStore::kNt>(x[t * row_chunks + c],
+                                                          recv_x + i * row_chunks,
+                                                          (int)(row_chunks * 16),
                          (int)(c * 16));
     if (slice == 0) {
       if (recv_scales != nullptr)
@@ -85,7 +89,8 @@ __device__ __forceinline__ void put_row_chunk(u32x4 v, const u32x4 *__restrict__
     }
     v = r;
   }
-  store_row_nt<WIDE>(v, out + t * row_chunks, (int)(row_chunks * 16), (int)(c * 16));
+  store_row<WIDE ? RowStore::kDevice : RowStore::kNt>(v, out + t * row_chunks,
+                                                      (int)(row_chunks * 16), (int)(c * 16));
 }
 
 // Waves [0, T*slices): (receive row, slice) back to its token. Waves

@@ -10,26 +10,37 @@ constexpr int kWave = 64;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Cache policy of a row store.
+//   kNt:       non-temporal (global_store ... nt).
+//   kNtDevice: non-temporal at device scope (gfx950 `nt sc1`): the line is
+//              written towards memory without being kept in this XCD's L2.
+//   kDevice:   device scope, kept (`sc1` alone).
+// Measured on MI355X with the whole chip storing: dispatch's expand rows
+// (470 MB at prefill, more than the 256 MB last-level cache) are fastest with
+// kNtDevice (87.5 against 91.7 us with kNt, about 160 us with kDevice or plain
+// stores); combine's output rows (59 MB, which fit that cache) are fastest
+// with kDevice (86.9 against 91.6 us with kNt, 90.3 with kNtDevice, 93.4
+// plain). Under a workgroup cap device scope is much slower (fan-out dispatch
+// 183 against 115 us on 64 workgroups) or no better, so capped launches use
+// kNt.
+enum class RowStore { kNt, kNtDevice, kDevice };
+
 // Stores 16 bytes at byte offset `off` of a row of `row_bytes` bytes that
-// starts at `row` (wave-uniform), non-temporal. DEVICE_SCOPE adds device
-// scope (the gfx950 `nt sc1` policy: the line is written towards memory
-// without being kept in this XCD's L2), through a buffer resource built from
-// the row pointer, so the offset stays small however large the buffer is and
-// a lane past the row's end writes nothing. Measured on MI355X: with the
-// whole chip storing, device scope is faster (prefill dispatch 87.5 against
-// 91.7 us with `nt` alone; about 160 us without `nt`); under a workgroup cap
-// it is much slower (fan-out dispatch 183 against 115 us on 64 workgroups),
-// so capped launches use `nt` alone.
-template <bool DEVICE_SCOPE>
-__device__ __forceinline__ void store_row_nt(const u32x4 &v, void *row, int row_bytes, int off) {
-  if constexpr (DEVICE_SCOPE) {
-    constexpr int kNtSc1 = 2 | 16;               // cache-policy bits: nt, sc1
+// starts at `row` (wave-uniform) with policy P. The two device-scope policies
+// go through a buffer resource built from the row pointer, so the offset
+// stays small however large the buffer is and a lane past the row's end
+// writes nothing.
+template <RowStore P>
+__device__ __forceinline__ void store_row(const u32x4 &v, void *row, int row_bytes, int off) {
+  if constexpr (P == RowStore::kNt) {
+    __builtin_nontemporal_store(v, (u32x4 *)((char *)row + off));
+  } else {
+    constexpr int kNt = 2, kSc1 = 16;            // cache-policy bits of a buffer store
     constexpr int kRawBufferFlags = 0x00020000;  // buffer descriptor word 3 for gfx9-family parts
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, kRawBufferFlags);
-    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, kNtSc1);
-  } else {
-    __builtin_nontemporal_store(v, (u32x4 *)((char *)row + off));
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0,
+                                           P == RowStore::kNtDevice ? kNt | kSc1 : kSc1);
   }
 }
 

@@ -12,7 +12,7 @@
 // 16-byte load per lane from x and one 16-byte store per lane into the
 // expand row, whose address is wave-uniform (the slot is loaded once and made
 // scalar with readfirstlane). The store is non-temporal at device scope
-// (store_row_nt): expand rows are not read again by this pass. Waves are
+// (RowStore::kNtDevice): expand rows are not read again by this pass. Waves are
 // ordered token-major, then k, then slice, or, given the layout's dispatch
 // plan, by ascending slot within each tile of tokens, then slice; either way
 // each destination row is written front to back by consecutive waves, and
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
     if (d < 0 || d >= capacity) continue;
     const int i = slice * kWave + lane;
     if (CH % kWave == 0 || i < CH)
-      store_row_nt<true>(x[t * CH + i], expand_x + (int64_t)d * CH, ROWB, i * 16);
+      store_row<RowStore::kNtDevice>(x[t * CH + i], expand_x + (int64_t)d * CH, ROWB, i * 16);
     if (slice == 0) {
       if (SCH > 0 && lane < SCH)
         __builtin_nontemporal_store(x_scales[t * SCH + lane],
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
 // entries k0 .. k0 + F - 1 (masked entries skipped); slice 0 also carries
 // the scale row and each entry's router weight. Slots, slice and scale row
 // are loaded first and waited for once, so the F stores leave back to back.
-template <int ROWB, int SCB, int K, int F, bool DEVICE_SCOPE>
+template <int ROWB, int SCB, int K, int F, RowStore P>
 __device__ __forceinline__ void copy_slice_to_group(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int64_t t,
@@ -137,7 +137,7 @@ __device__ __forceinline__ void copy_slice_to_group(
   for (int j = 0; j < F; ++j) {
     const int d = read_lane(my_d, j);
     if (d < 0) continue;
-    if (in_row) store_row_nt<DEVICE_SCOPE>(v, expand_x + (int64_t)d * CH, ROWB, i * 16);
+    if (in_row) store_row<P>(v, expand_x + (int64_t)d * CH, ROWB, i * 16);
     if (slice == 0) {
       if (SCH > 0 && lane < SCH)
         __builtin_nontemporal_store(sc, expand_scales + (int64_t)d * SCH + lane);
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_grouped(
     const int slice = (int)(gw - tg * SLICES);
     const int64_t t = tg / KG;
     const int g = (int)(tg - t * KG);
-    copy_slice_to_group<ROWB, SCB, K, F, true>(x, x_scales, topk_weights, dst_slot, t, g * F,
+    copy_slice_to_group<ROWB, SCB, K, F, RowStore::kNtDevice>(x, x_scales, topk_weights, dst_slot, t, g * F,
                                                slice, capacity, expand_x, expand_scales,
                                                expand_weights);
   }
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_fanout(
   for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < total; gw += stride) {
     const int64_t t = gw / SLICES;
     const int slice = (int)(gw - t * SLICES);
-    copy_slice_to_group<ROWB, SCB, K, K, false>(x, x_scales, topk_weights, dst_slot, t, 0, slice,
+    copy_slice_to_group<ROWB, SCB, K, K, RowStore::kNt>(x, x_scales, topk_weights, dst_slot, t, 0, slice,
                                                 capacity, expand_x, expand_scales,
                                                 expand_weights);
   }

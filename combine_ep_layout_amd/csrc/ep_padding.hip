@@ -20,7 +20,8 @@ namespace {
 
 
 // WIDE: launched over the whole chip (no workgroup cap), which selects the
-// store policy (store_row_nt).
+// store policy: non-temporal at device scope like dispatch's rows
+// (RowStore::kNtDevice); under a cap, non-temporal.
 template <bool WIDE>
 __global__ __launch_bounds__(kCappedThreads) void ep_zero_padding_rows(
     u32x4 *__restrict__ expand_x, int64_t row_chunks, float *__restrict__ expand_scales,
@@ -46,7 +47,8 @@ __global__ __launch_bounds__(kCappedThreads) void ep_zero_padding_rows(
     if (row >= end || row >= capacity || row < 0) continue;
     const int64_t i = slice * kWave + lane;
     if (i < row_chunks)
-      store_row_nt<WIDE>(zero, expand_x + row * row_chunks, (int)(row_chunks * 16), (int)(i * 16));
+      store_row<WIDE ? RowStore::kNtDevice : RowStore::kNt>(zero, expand_x + row * row_chunks,
+                                                             (int)(row_chunks * 16), (int)(i * 16));
     if (slice == 0) {
       if (expand_scales != nullptr)
         for (int64_t j = lane; j < scale_cols; j += kWave)
