@@ -257,21 +257,23 @@ def test_slots_outside_capacity_are_skipped(T, H, K, wg_cap, do_combine):
 
 
 PLANS = [
-    # T, H, E, K, A, mask, workgroup cap: every layout launch shape, capped loops
-    (100, 7168, 256, 8, 128, 0.1, 0),     # one tile
-    (1500, 2048, 256, 8, 4, 0.05, 0),     # single launch, several tiles
-    (4096, 7168, 256, 8, 128, 0.0, 0),    # two launches (the prefill shape)
-    (20000, 256, 1024, 8, 4, 0.05, 0),    # with the tile-scan launch, 32-token tiles
-    (3000, 1024, 300, 6, 3, 0.1, 0),      # 85-token tiles
-    (5000, 512, 16, 1, 1, 0.2, 0),        # K = 1
-    (4096, 7168, 256, 8, 128, 0.02, 3),   # capped: tiles loop; dispatch ignores the plan
-    (1500, 2048, 256, 8, 4, 0.05, 5),
+    # T, H, E, K, A, mask, workgroup cap, dtype: every layout launch shape, capped loops
+    (100, 7168, 256, 8, 128, 0.1, 0, I.BF16),     # one tile
+    (1500, 2048, 256, 8, 4, 0.05, 0, I.BF16),     # single launch, several tiles
+    (4096, 7168, 256, 8, 128, 0.0, 0, I.BF16),    # two launches (the prefill shape)
+    (20000, 256, 1024, 8, 4, 0.05, 0, I.BF16),    # with the tile-scan launch, 32-token tiles
+    (3000, 1024, 300, 6, 3, 0.1, 0, I.BF16),      # 85-token tiles
+    (5000, 512, 16, 1, 1, 0.2, 0, I.BF16),        # K = 1
+    (4096, 7168, 256, 8, 128, 0.02, 3, I.BF16),   # capped: tiles loop; dispatch ignores the plan
+    (1500, 2048, 256, 8, 4, 0.05, 5, I.BF16),
+    (2048, 7168, 256, 8, 1, 0.05, 0, I.FP8_E4M3),  # scale rows ride with the planned walk
+    (1024, 3584, 64, 6, 16, 0.1, 0, I.FP4X2),
 ]
 
 
-@pytest.mark.parametrize("T,H,E,K,A,mask,wg_cap", PLANS)
-def test_dispatch_plan(T, H, E, K, A, mask, wg_cap):
-    w = I.custom(f"plan{T}_{E}_{K}", 9300 + T + E, T, H, E, K, A, I.BF16, "uniform")
+@pytest.mark.parametrize("T,H,E,K,A,mask,wg_cap,dtype", PLANS)
+def test_dispatch_plan(T, H, E, K, A, mask, wg_cap, dtype):
+    w = I.custom(f"plan{T}_{E}_{K}", 9300 + T + E, T, H, E, K, A, dtype, "uniform")
     _say(f"[dispatch plan] {w} workgroup cap {wg_cap}")
     case = I.make_case(w, with_y=False, mask_frac=mask)
     ref = oracle.layout(case.topk_idx, w.E, w.A)
