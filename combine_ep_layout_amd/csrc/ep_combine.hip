@@ -348,8 +348,9 @@ template <int DT, int H, int K>
 int combine_impl(const CombineArgs &a) {
   if (a.T == 0) return 0;
   constexpr int CH = H * Elem<DT>::BYTES / 16;
+  const int cap = stream_workgroup_limit(a.stream);  // read once per launch
   if constexpr (StreamGeometry<CH>::OK) {
-    if (a.T >= kStreamMinTokens && stream_workgroup_limit(a.stream) == 0) {
+    if (a.T >= kStreamMinTokens && cap == 0) {
       const WaveGrid g = wave_grid((int64_t)a.T * StreamGeometry<CH>::PIECES, 0, INT32_MAX);
       if (a.bias)
         ep_combine_stream<DT, H, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
@@ -363,8 +364,7 @@ int combine_impl(const CombineArgs &a) {
     }
   }
   constexpr int SPLIT = CombineGeometry<H * Elem<DT>::BYTES / 16>::SPLIT;
-  const WaveGrid g = wave_grid((int64_t)a.T * SPLIT, stream_workgroup_limit(a.stream), INT32_MAX,
-                               1, kCombineCappedThreads);
+  const WaveGrid g = wave_grid((int64_t)a.T * SPLIT, cap, INT32_MAX, 1, kCombineCappedThreads);
   if (g.threads == kCombineCappedThreads)
     return combine_launch<DT, H, K, kCombineCappedThreads>(a, g);
   return combine_launch<DT, H, K, kDefaultThreads>(a, g);
