@@ -136,6 +136,13 @@ def measured_traffic(workload: str, kernel: str):
 # (about 0.1-0.4 us) cancels or exceeds the gain.
 PLAN_MIN_BYTES = 256 << 20
 
+def one_layout_tile(T: int, K: int, E: int) -> bool:
+    """Whether ep_layout_dispatch runs as one launch: T*K fits one layout tile
+    of floor(W / K) tokens, W = 1024, 512 or 256 for E up to 256, 512, 1024."""
+    W = 1024 if E <= 256 else (512 if E <= 512 else 256)
+    return T <= W // K
+
+
 CALIBRATION_BYTES = 1 << 30  # fp32 elementwise negate: reads and writes this many bytes
 # Kernel-name fragments per pass: each pass launches one of its kernels, chosen by shape and cap.
 KERNEL_TAGS = {"dispatch": ("ep_dispatch_expand", "ep_dispatch_grouped", "ep_dispatch_fanout"),
@@ -263,6 +270,9 @@ def main():
     ap.add_argument("--no-plan", action="store_true",
                     help="expand path: never ask ep_layout for the dispatch plan (by default it is "
                          "used when the expand rows total at least PLAN_MIN_BYTES)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="expand path: call ep_layout and ep_dispatch separately even when the "
+                         "batch fits one layout tile (by default ep_layout_dispatch is used then)")
     ap.add_argument("--cold", action="store_true",
                     help="rotate buffer sets so that no step finds its rows in the last-level cache")
     ap.add_argument("--workgroups", type=int, default=0,
@@ -332,6 +342,7 @@ def main():
     rows_out = w.T if non_expand else w.cap
     use_plan = (not non_expand and not args.no_plan
                 and w.T * w.K * case.x.view(np.uint8).reshape(w.T, -1).shape[1] >= PLAN_MIN_BYTES)
+    fused = not non_expand and not args.no_fused and one_layout_tile(w.T, w.K, w.E)
     plan = torch.empty((w.T * w.K, 2), dtype=torch.int32, device=dev) if use_plan else None
 
     def x_set():
@@ -378,14 +389,19 @@ def main():
         S, X = sets[i % nsets], x_sets[i % nx]
         if ev is not None:
             ev[0].record(stream)
-        B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws, wsb, stream,
-                    dispatch_plan=plan)
+        if fused:  # one launch; its time is reported as dispatch's, layout's as zero
+            B.ep_layout_dispatch(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv,
+                                 ws, wsb, X["x"], X["xs"], None, w.H, w.dtype, S["expand"],
+                                 S["expand_s"], None, stream)
+        else:
+            B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws, wsb,
+                        stream, dispatch_plan=plan)
         if ev is not None:
             ev[1].record(stream)
         if non_expand:
             B.ep_dispatch_compact(X["x"], X["xs"], idx, wts, dst, meta, nrecv, w.T, w.H, w.K, w.dtype,
                                   S["expand"], S["expand_s"], S["recv_i"], S["recv_w"], stream)
-        else:
+        elif not fused:
             B.ep_dispatch(X["x"], X["xs"], None, dst, w.T, w.H, w.K, w.dtype, w.cap, S["expand"],
                           S["expand_s"], None, stream, dispatch_plan=plan)
         if ev is not None:
@@ -416,6 +432,8 @@ def main():
     us = {"layout": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3,
           "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
           "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3}
+    if fused:  # layout ran inside the dispatch launch
+        us = {"layout": 0.0, "dispatch": us["layout"] + us["dispatch"], "combine": us["combine"]}
     launch = "eager"
     if args.graph > 0:
         g = torch.cuda.CUDAGraph()
@@ -462,7 +480,7 @@ def main():
         torch.cuda.synchronize()
         B.ep_set_workgroup_limit(stream, 0)
     report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap, cache, launch,
-           use_plan)
+           use_plan, fused)
 
 
 GEMM_SHAPE = (8192, 7168, 2048)  # M, K, N: bf16 [M, K] x [K, N], about one step's duration
@@ -556,7 +574,7 @@ def validate_expand(oracle, case, ref, expand, out, sample, xb, dev) -> bool:
 
 
 def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=None, cache="warm",
-           launch="eager", plan_used=False):
+           launch="eager", plan_used=False, fused=False):
     n_valid = int((ref["dst_slot"] >= 0).sum())
     nb = algorithmic_bytes(w, n_valid, ref["num_recv"], args.path)
     total_bytes = sum(nb.values())
@@ -589,6 +607,7 @@ def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=N
                    "dispatch_dtype": DTYPE_NAMES[w.dtype], "combine_dtype": DTYPE_NAMES[w.out_dtype],
                    "parallelism": "one GPU, all experts local", "path": args.path,
                    "dispatch_plan": plan_used,
+                   "layout_dispatch": "one launch (ep_layout_dispatch)" if fused else "two launches",
                    "workgroup_cap": args.workgroups or None,
                    "cache": cache, "launch": launch},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),

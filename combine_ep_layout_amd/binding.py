@@ -30,7 +30,8 @@ EP_FP4X2 = 3
 EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 64
 
-SYMBOLS = ("ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_combine",
+SYMBOLS = ("ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_dispatch",
+           "ep_combine",
            "ep_dispatch_compact", "ep_combine_compact", "ep_zero_padding", "ep_set_workgroup_limit",
            "ep_get_workgroup_limit", "ep_last_error", "ep_supported")
 
@@ -69,6 +70,9 @@ def lib(path: str = None) -> ctypes.CDLL:
     L.ep_dispatch.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
                               _vp]
     L.ep_dispatch.restype = ctypes.c_int
+    L.ep_layout_dispatch.argtypes = [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _sz, _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp]
+    L.ep_layout_dispatch.restype = ctypes.c_int
     L.ep_combine.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp]
     L.ep_combine.restype = ctypes.c_int
     L.ep_dispatch_compact.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -141,6 +145,18 @@ def ep_dispatch(x, x_scales, topk_weights, dst_slot, num_tokens, hidden, topk, d
     _check(lib().ep_dispatch(_p(x), _p(x_scales), _p(topk_weights), _p(dst_slot), num_tokens,
                              hidden, topk, dtype, capacity_rows, _p(expand_x), _p(expand_scales),
                              _p(expand_weights), _p(dispatch_plan), _s(stream)))
+
+
+def ep_layout_dispatch(topk_idx, num_tokens, topk, num_experts, expert_alignment, capacity_rows,
+                       counts, offsets, dst_slot, recv_src_metadata, num_recv, workspace,
+                       workspace_bytes, x, x_scales, topk_weights, hidden, dtype, expand_x,
+                       expand_scales, expand_weights, stream=None):
+    _check(lib().ep_layout_dispatch(_p(topk_idx), num_tokens, topk, num_experts, expert_alignment,
+                                    capacity_rows, _p(counts), _p(offsets), _p(dst_slot),
+                                    _p(recv_src_metadata), _p(num_recv), _p(workspace),
+                                    workspace_bytes, _p(x), _p(x_scales), _p(topk_weights), hidden,
+                                    dtype, _p(expand_x), _p(expand_scales), _p(expand_weights),
+                                    _s(stream)))
 
 
 def ep_combine(expert_out, topk_weights, bias, dst_slot, num_tokens, hidden, topk, dtype,

@@ -141,6 +141,92 @@ size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_e
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks of ep_layout's arguments (shared with ep_layout_dispatch).
+int check_layout(const char *what, const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
+                 int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
+                 const int32_t *counts, const int32_t *offsets, const int32_t *dst_slot,
+                 const int32_t *recv_src_metadata, const int32_t *num_recv, const void *workspace,
+                 size_t workspace_bytes) {
+  if (int rc = check_topk(what, num_tokens, topk)) return rc;
+  if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
+    return fail(EP_EINVAL, "%s: num_experts must be in 1..%d (got %d)", what, EP_MAX_EXPERTS,
+                num_experts);
+  if (expert_alignment < 1)
+    return fail(EP_EINVAL, "%s: expert_alignment must be >= 1 (got %d)", what, expert_alignment);
+  const int64_t worst =
+      (int64_t)num_tokens * topk + (int64_t)num_experts * (expert_alignment - 1);
+  if (worst > INT32_MAX)
+    return fail(EP_EINVAL, "%s: worst-case expand rows %lld overflow int32", what,
+                (long long)worst);
+  if (capacity_rows < worst)
+    return fail(EP_ECAPACITY, "%s: capacity_rows %lld < worst case T*K + E*(A-1) = %lld", what,
+                (long long)capacity_rows, (long long)worst);
+  if (!counts || !offsets || !num_recv ||
+      (num_tokens > 0 && (!topk_idx || !dst_slot || !recv_src_metadata)))
+    return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
+  if (!ep::has_layout(topk))
+    return fail(EP_EUNSUPPORTED, "%s: topk %d has no compiled layout kernel", what, topk);
+  const size_t need = ep::layout_workspace(num_tokens, topk, num_experts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(EP_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", what, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(EP_EINVAL, "%s: workspace must be 16-byte aligned", what);
+  return EP_OK;
+}
+
+// Checks of ep_dispatch's arguments (shared with ep_layout_dispatch); on
+// success *row_bytes receives the bytes of one token row.
+int check_dispatch(const char *what, const void *x, const float *x_scales,
+                   const float *topk_weights, const int32_t *dst_slot, int32_t num_tokens,
+                   int32_t hidden, int32_t topk, int32_t dtype, int64_t capacity_rows,
+                   const void *expand_x, const float *expand_scales, const float *expand_weights,
+                   int64_t *row_bytes) {
+  if (int rc = check_topk(what, num_tokens, topk)) return rc;
+  if (hidden < 1) return fail(EP_EINVAL, "%s: hidden must be >= 1 (got %d)", what, hidden);
+  if (capacity_rows < 0) return fail(EP_EINVAL, "%s: capacity_rows must be >= 0", what);
+  // Bytes per hidden unit: hidden counts elements, except for fp4x2 where it
+  // counts bytes (two e2m1 values per byte, as the caller packs them).
+  int elt;
+  if (dtype == EP_BF16) elt = 2;
+  else if (dtype == EP_FP32) elt = 4;
+  else if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2) elt = 1;
+  else return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
+  if (((int64_t)hidden * elt) % 16 != 0)
+    return fail(EP_EINVAL, "%s: token bytes (%lld) must be a multiple of 16", what,
+                (long long)hidden * elt);
+  const bool byte_dtype = dtype == EP_FP8_E4M3 || dtype == EP_FP4X2;
+  if ((x_scales == nullptr) != (expand_scales == nullptr))
+    return fail(EP_EINVAL, "%s: x_scales and expand_scales go together", what);
+  if (x_scales != nullptr) {
+    if (!byte_dtype)
+      return fail(EP_EINVAL, "%s: scale rows travel only with fp8 / fp4x2 rows", what);
+    const int64_t elems = dtype == EP_FP4X2 ? 2 * (int64_t)hidden : hidden;
+    if (elems % 128 != 0)
+      return fail(EP_EINVAL, "%s: scales need a multiple of 128 elements per row (got %lld)",
+                  what, (long long)elems);
+  }
+  if (num_tokens > 0 && (!x || !dst_slot || !expand_x))
+    return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
+  if (!aligned(x, 16) || !aligned(expand_x, 16) || !aligned(x_scales, 16) ||
+      !aligned(expand_scales, 16) || !aligned(dst_slot, 4) || !aligned(topk_weights, 4) ||
+      !aligned(expand_weights, 4))
+    return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
+  if (!ep::has_dispatch(hidden, topk, dtype))
+    return fail(EP_EUNSUPPORTED, "%s: (hidden %d, topk %d, dtype %d) has no compiled kernel",
+                what, hidden, topk, dtype);
+  *row_bytes = (int64_t)hidden * elt;
+  return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t num_experts,
               int32_t expert_alignment, int64_t capacity_rows, int32_t *counts,
               int32_t *offsets, int32_t *dst_slot, int32_t *recv_src_metadata,
@@ -148,31 +234,10 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
               void *stream) {
   try {
     const char *what = "ep_layout";
-    if (int rc = check_topk(what, num_tokens, topk)) return rc;
-    if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
-      return fail(EP_EINVAL, "%s: num_experts must be in 1..%d (got %d)", what, EP_MAX_EXPERTS,
-                  num_experts);
-    if (expert_alignment < 1)
-      return fail(EP_EINVAL, "%s: expert_alignment must be >= 1 (got %d)", what, expert_alignment);
-    const int64_t worst =
-        (int64_t)num_tokens * topk + (int64_t)num_experts * (expert_alignment - 1);
-    if (worst > INT32_MAX)
-      return fail(EP_EINVAL, "%s: worst-case expand rows %lld overflow int32", what,
-                  (long long)worst);
-    if (capacity_rows < worst)
-      return fail(EP_ECAPACITY, "%s: capacity_rows %lld < worst case T*K + E*(A-1) = %lld", what,
-                  (long long)capacity_rows, (long long)worst);
-    if (!counts || !offsets || !num_recv ||
-        (num_tokens > 0 && (!topk_idx || !dst_slot || !recv_src_metadata)))
-      return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
-    if (!ep::has_layout(topk))
-      return fail(EP_EUNSUPPORTED, "%s: topk %d has no compiled layout kernel", what, topk);
-    const size_t need = ep::layout_workspace(num_tokens, topk, num_experts);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
-      return fail(EP_EINVAL, "%s: workspace of %zu bytes needed (got %zu)", what, need,
-                  workspace == nullptr ? (size_t)0 : workspace_bytes);
-    if (need > 0 && !aligned(workspace, 16))
-      return fail(EP_EINVAL, "%s: workspace must be 16-byte aligned", what);
+    if (int rc = check_layout(what, topk_idx, num_tokens, topk, num_experts, expert_alignment,
+                              capacity_rows, counts, offsets, dst_slot, recv_src_metadata,
+                              num_recv, workspace, workspace_bytes))
+      return rc;
     if (!aligned(dispatch_plan, 8))
       return fail(EP_EINVAL, "%s: dispatch_plan must be 8-byte aligned", what);
     ep::LayoutArgs a{topk_idx, num_tokens, topk, num_experts, expert_alignment, counts, offsets,
@@ -192,39 +257,13 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
                 float *expand_weights, const int32_t *dispatch_plan, void *stream) {
   try {
     const char *what = "ep_dispatch";
-    if (int rc = check_topk(what, num_tokens, topk)) return rc;
-    if (hidden < 1) return fail(EP_EINVAL, "%s: hidden must be >= 1 (got %d)", what, hidden);
-    if (capacity_rows < 0) return fail(EP_EINVAL, "%s: capacity_rows must be >= 0", what);
-    // Bytes per hidden unit: hidden counts elements, except for fp4x2 where it
-    // counts bytes (two e2m1 values per byte, as the caller packs them).
-    int elt;
-    if (dtype == EP_BF16) elt = 2;
-    else if (dtype == EP_FP32) elt = 4;
-    else if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2) elt = 1;
-    else return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
-    if (((int64_t)hidden * elt) % 16 != 0)
-      return fail(EP_EINVAL, "%s: token bytes (%lld) must be a multiple of 16", what,
-                  (long long)hidden * elt);
-    const bool byte_dtype = dtype == EP_FP8_E4M3 || dtype == EP_FP4X2;
-    if ((x_scales == nullptr) != (expand_scales == nullptr))
-      return fail(EP_EINVAL, "%s: x_scales and expand_scales go together", what);
-    if (x_scales != nullptr) {
-      if (!byte_dtype)
-        return fail(EP_EINVAL, "%s: scale rows travel only with fp8 / fp4x2 rows", what);
-      const int64_t elems = dtype == EP_FP4X2 ? 2 * (int64_t)hidden : hidden;
-      if (elems % 128 != 0)
-        return fail(EP_EINVAL, "%s: scales need a multiple of 128 elements per row (got %lld)",
-                    what, (long long)elems);
-    }
-    if (num_tokens > 0 && (!x || !dst_slot || !expand_x))
-      return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
-    if (!aligned(x, 16) || !aligned(expand_x, 16) || !aligned(x_scales, 16) ||
-        !aligned(expand_scales, 16) || !aligned(dst_slot, 4) || !aligned(topk_weights, 4) ||
-        !aligned(expand_weights, 4) || !aligned(dispatch_plan, 8))
+    int64_t row_bytes = 0;
+    if (int rc = check_dispatch(what, x, x_scales, topk_weights, dst_slot, num_tokens, hidden,
+                                topk, dtype, capacity_rows, expand_x, expand_scales,
+                                expand_weights, &row_bytes))
+      return rc;
+    if (!aligned(dispatch_plan, 8))
       return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes, the plan 8)", what);
-    if (!ep::has_dispatch(hidden, topk, dtype))
-      return fail(EP_EUNSUPPORTED, "%s: (hidden %d, topk %d, dtype %d) has no compiled kernel",
-                  what, hidden, topk, dtype);
     ep::DispatchArgs a{x, x_scales, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,
                        capacity_rows, expand_x, expand_scales, expand_weights, dispatch_plan,
                        (hipStream_t)stream};
@@ -233,6 +272,46 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
     return fail(EP_EHIP, "ep_dispatch: %s", e.what());
   } catch (...) {
     return fail(EP_EHIP, "ep_dispatch: unknown exception");
+  }
+}
+
+int ep_layout_dispatch(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
+                       int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
+                       int32_t *counts, int32_t *offsets, int32_t *dst_slot,
+                       int32_t *recv_src_metadata, int32_t *num_recv, void *workspace,
+                       size_t workspace_bytes, const void *x, const float *x_scales,
+                       const float *topk_weights, int32_t hidden, int32_t dtype, void *expand_x,
+                       float *expand_scales, float *expand_weights, void *stream) {
+  try {
+    const char *what = "ep_layout_dispatch";
+    if (int rc = check_layout(what, topk_idx, num_tokens, topk, num_experts, expert_alignment,
+                              capacity_rows, counts, offsets, dst_slot, recv_src_metadata,
+                              num_recv, workspace, workspace_bytes))
+      return rc;
+    int64_t row_bytes = 0;
+    if (int rc = check_dispatch(what, x, x_scales, topk_weights, dst_slot, num_tokens, hidden,
+                                topk, dtype, capacity_rows, expand_x, expand_scales,
+                                expand_weights, &row_bytes))
+      return rc;
+    ep::LayoutArgs l{topk_idx, num_tokens, topk, num_experts, expert_alignment, counts, offsets,
+                     dst_slot, recv_src_metadata, num_recv, workspace, nullptr,
+                     (hipStream_t)stream};
+    ep::DispatchArgs d{x, x_scales, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,
+                       capacity_rows, expand_x, expand_scales, expand_weights, nullptr,
+                       (hipStream_t)stream};
+    if (num_tokens > 0) {
+      const int64_t elems = dtype == EP_FP4X2 ? 2 * (int64_t)hidden : hidden;
+      const int scale_chunks = x_scales != nullptr ? (int)(elems / 128 * 4 / 16) : 0;
+      const int rc = ep::launch_layout_dispatch(l, d, (int)(row_bytes / 16), scale_chunks);
+      if (rc != -3) return from_launch(rc, what);
+    }
+    // more than one tile (or nothing to copy): the two launches of ep_layout and ep_dispatch
+    if (int rc = from_launch(ep::launch_layout(l), what)) return rc;
+    return from_launch(ep::launch_dispatch(d), what);
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_layout_dispatch: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_layout_dispatch: unknown exception");
   }
 }
 

@@ -147,6 +147,11 @@ inline int launch_status() {
 int launch_layout(const LayoutArgs &a);
 size_t layout_workspace(int T, int K, int E);
 int launch_dispatch(const DispatchArgs &a);
+// Layout and dispatch in one launch when T*K fits one layout tile; -3 when it
+// does not (the caller then launches them separately). Row and scale-row
+// widths in 16-byte chunks.
+int launch_layout_dispatch(const LayoutArgs &l, const DispatchArgs &d, int row_chunks,
+                           int scale_chunks);
 int launch_combine(const CombineArgs &a);
 int launch_zero_padding(const ZeroPaddingArgs &a);
 int launch_dispatch_compact(const CompactDispatchArgs &a);

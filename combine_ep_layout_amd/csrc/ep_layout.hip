@@ -28,6 +28,8 @@
 // On request the last launch also writes the dispatch plan: each tile's
 // entries in slot order, the order in which dispatch writes expand rows
 // fastest (write_plan).
+#include <type_traits>
+
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -237,6 +239,81 @@ __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
   __syncthreads();
   write_slots_and_meta<K>(0, T, slot, s.tok, dst_slot, meta);
   if (plan != nullptr) write_plan<K>(0, T, r.e, r.rank, slot, s_tb, nvalid, plan);
+}
+
+// Layout and dispatch in one launch for a batch that fits one tile (a
+// decode step, say), after the dispatch kernels of the DeepEP page, whose
+// notify warps compute the slots inside dispatch. Every workgroup ranks all
+// entries in its own LDS exactly as ep_layout_single_tile does, and
+// workgroup 0 also writes the layout's outputs. Each workgroup then copies
+// its share of (entry, 1 KiB slice) units token-major, with the slots read
+// from its own LDS. The ranking is repeated per workgroup, a few microseconds
+// of LDS work in parallel. That costs less than a second launch and the
+// round trip of dst_slot through memory. Row and scale-row widths are run-time
+// values (16-byte chunks). WIDE: launched uncapped, which selects the device-
+// scope non-temporal row store, as ep_dispatch_expand uses.
+template <int K, int NW, bool WIDE>
+__global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
+    const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
+    int32_t *__restrict__ num_recv, const u32x4 *__restrict__ x, int row_chunks,
+    const u32x4 *__restrict__ x_scales, int scale_chunks, const float *__restrict__ topk_weights,
+    int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
+    float *__restrict__ expand_weights) {
+  __shared__ int s_tmp[kWavesMax];
+  const RankLds s = rank_lds(E, NW);
+  int *s_off = (int *)(g_smem + rank_lds_bytes(E, NW));  // E
+  int *s_slot = s_off + E;                               // kThreads: slot of entry tid
+  const int tid = threadIdx.x;
+
+  const EntryRank r = tile_rank<K, NW>(topk_idx, 0, T, E, s);
+  const int cnt = tid < E ? s.total[tid] : 0;
+  const int padded = ((cnt + A - 1) / A) * A;
+  int rows;
+  const int off = block_exclusive_scan<kThreads>(padded, s_tmp, rows);
+  if (tid < E) s_off[tid] = off;
+  __syncthreads();
+  const int slot = r.e >= 0 ? s_off[r.e] + r.rank : -1;
+  s_slot[tid] = slot;
+  if (blockIdx.x == 0) {  // the layout's outputs, as ep_layout_single_tile writes them
+    if (tid < E) {
+      counts[tid] = cnt;
+      offsets[tid] = off;
+    }
+    if (tid == 0) offsets[E] = rows;
+    const bool f = tid < T && s.tok[tid] != 0;
+    int nrecv;
+    const int tok_rank = block_flag_rank(f, s_tmp, nrecv);
+    if (tid == 0) *num_recv = nrecv;
+    if (tid < T) s.tok[tid] = f ? tok_rank : -1;
+    __syncthreads();
+    write_slots_and_meta<K>(0, T, slot, s.tok, dst_slot, meta);
+  }
+  __syncthreads();  // publishes s_slot
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int slices = (row_chunks + kWave - 1) / kWave;
+  const int64_t units = (int64_t)T * K * slices;
+  const int64_t stride = (int64_t)gridDim.x * kWavesMax;
+  for (int64_t u = (int64_t)blockIdx.x * kWavesMax + wave; u < units; u += stride) {
+    const int j = (int)(u / slices);  // entry t*K + k
+    const int slice = (int)(u - (int64_t)j * slices);
+    const int d = __builtin_amdgcn_readfirstlane(s_slot[j]);
+    if (d < 0 || d >= capacity) continue;
+    const int64_t t = j / K;
+    const int c = slice * kWave + lane;
+    if (c < row_chunks)
+      store_row<WIDE ? RowStore::kNtDevice : RowStore::kNt>(
+          x[t * row_chunks + c], expand_x + (int64_t)d * row_chunks, row_chunks * 16, c * 16);
+    if (slice == 0) {
+      if (x_scales != nullptr)
+        for (int q = lane; q < scale_chunks; q += kWave)
+          __builtin_nontemporal_store(x_scales[t * scale_chunks + q],
+                                      expand_scales + (int64_t)d * scale_chunks + q);
+      if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[j];
+    }
+  }
 }
 
 // One launch for several tiles when T*K is small enough: besides ranking its
@@ -641,6 +718,49 @@ int layout_k(const LayoutArgs &a) {
   }
 }
 
+// Most workgroups of the fused layout + dispatch launch, one per compute
+// unit: each repeats the ranking, so more only add LDS work. Measured on
+// MI355X (decode step, 128 tokens, top-8, hidden 7168, with combine): 13.5 /
+// 12.1 / 12.8 / 17.5 us per step at 128 / 256 / 512 / 1024 workgroups, against
+// 15.8 with layout and dispatch launched separately.
+constexpr int kFusedDispatchMaxBlocks = 256;
+
+template <int K, int NW>
+int layout_dispatch_impl(const LayoutArgs &l, const DispatchArgs &d, int row_chunks,
+                         int scale_chunks) {
+  if (tiles_for<K, NW>(l.T) > 1) return -3;  // more than one tile: not fused
+  const int cap = stream_workgroup_limit(l.stream);
+  const int64_t slices = (row_chunks + kWave - 1) / kWave;
+  const int64_t units = (int64_t)l.T * K * slices;
+  int64_t blocks = (units + kWavesMax - 1) / kWavesMax;
+  if (blocks > kFusedDispatchMaxBlocks) blocks = kFusedDispatchMaxBlocks;
+  if (cap > 0 && blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  const size_t shm = rank_lds_bytes(l.E, NW) + sizeof(int) * ((size_t)l.E + kThreads);
+  const bool fwd_w = d.topk_weights != nullptr && d.expand_weights != nullptr;
+  auto go = [&](auto wide) {
+    ep_layout_dispatch_tile<K, NW, decltype(wide)::value>
+        <<<(unsigned)blocks, kThreads, shm, l.stream>>>(
+            l.topk_idx, l.T, l.E, l.A, l.counts, l.offsets, l.dst_slot, l.meta, l.num_recv,
+            (const u32x4 *)d.x, row_chunks, (const u32x4 *)d.x_scales, scale_chunks,
+            d.topk_weights, d.capacity, (u32x4 *)d.expand_x, (u32x4 *)d.expand_scales,
+            fwd_w ? d.expand_weights : nullptr);
+  };
+  if (cap > 0) go(std::false_type{});
+  else go(std::true_type{});
+  return launch_status();
+}
+
+template <int K>
+int layout_dispatch_k(const LayoutArgs &l, const DispatchArgs &d, int row_chunks,
+                      int scale_chunks) {
+  switch (tile_waves(l.E)) {
+    case 16: return layout_dispatch_impl<K, 16>(l, d, row_chunks, scale_chunks);
+    case 8: return layout_dispatch_impl<K, 8>(l, d, row_chunks, scale_chunks);
+    default: return layout_dispatch_impl<K, 4>(l, d, row_chunks, scale_chunks);
+  }
+}
+
 template <int K>
 size_t workspace_k(int T, int E) {
   int B;
@@ -665,6 +785,15 @@ size_t workspace_k(int T, int E) {
 
 int launch_layout(const LayoutArgs &a) {
   switch (a.K) { EP_FOR_EACH_TOPK(EP_LAYOUT_CASE) default: return -2; }
+}
+
+#define EP_LAYOUT_DISPATCH_CASE(K) \
+  case K:                          \
+    return layout_dispatch_k<K>(l, d, row_chunks, scale_chunks);
+
+int launch_layout_dispatch(const LayoutArgs &l, const DispatchArgs &d, int row_chunks,
+                           int scale_chunks) {
+  switch (l.K) { EP_FOR_EACH_TOPK(EP_LAYOUT_DISPATCH_CASE) default: return -2; }
 }
 
 #define EP_WS_CASE(K) \

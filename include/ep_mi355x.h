@@ -174,6 +174,28 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
                 float *expand_weights, const int32_t *dispatch_plan, void *stream);
 
 /*
+ * Layout and dispatch in one call (the DeepEP overall-architecture page,
+ * dispatch data-flow figure: the dispatch kernel's notify warps count per
+ * expert and compute each token's target slot before the copy epilogue
+ * moves the data). It produces everything ep_layout and ep_dispatch produce,
+ * with the same arguments, meanings, checks and errors as those two calls
+ * (the dispatch arguments take their slots from this layout). When T*K fits
+ * one layout tile (the floor(W / K) tokens of ep_layout's dispatch_plan,
+ * W = 1024, 512 or 256 by num_experts: a decode step, say) it runs as a
+ * single launch. Every workgroup ranks all entries itself and workgroup 0
+ * writes the layout's outputs, which saves a launch and the trip of dst_slot
+ * through memory. Larger batches run the two launches of ep_layout and
+ * ep_dispatch (token-major, no plan). Results are identical either way.
+ */
+int ep_layout_dispatch(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
+                       int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
+                       int32_t *counts, int32_t *offsets, int32_t *dst_slot,
+                       int32_t *recv_src_metadata, int32_t *num_recv, void *workspace,
+                       size_t workspace_bytes, const void *x, const float *x_scales,
+                       const float *topk_weights, int32_t hidden, int32_t dtype, void *expand_x,
+                       float *expand_scales, float *expand_weights, void *stream);
+
+/*
  * Gather combine (DeepEP overall architecture, combine reduce epilogue
  * weighting expert outputs by topk_weights and adding a bias; "MORI JIT v2",
  * section 3.7: combine reduces bf16 or fp32 rows, writes the same type, and

@@ -84,6 +84,26 @@ class DeviceCase:
         self.lay = dev_layout(self.idx, w.T, w.K, w.E, w.A, w.cap, stream, plan=plan)
         return self.lay
 
+    def layout_dispatch(self, stream=None, weights=True):
+        """ep_layout_dispatch: the layout's outputs and the expand buffer in one call."""
+        w = self.w
+        T, K, E = w.T, w.K, w.E
+        counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+        offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+        dst = torch.full((max(T, 1), K), -7, dtype=torch.int32, device=DEV)
+        meta = torch.full((max(T, 1), K + 2), -7, dtype=torch.int32, device=DEV)
+        nrecv = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+        wsb = B.ep_layout_workspace_bytes(T, K, E)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+        B.ep_layout_dispatch(self.idx if T else None, T, K, E, w.A, w.cap, counts, offsets,
+                             dst if T else None, meta if T else None, nrecv, ws, wsb,
+                             self.x if T else None, self.xs, self.wts if weights else None, w.H,
+                             w.dtype, self.expand_x, self.expand_s,
+                             self.expand_w if weights else None, stream)
+        self.lay = {"counts": counts, "offsets": offsets, "dst_slot": dst[:T], "meta": meta[:T],
+                    "num_recv": nrecv}
+        return self.lay
+
     def dispatch(self, stream=None, weights=True, plan=False):
         w = self.w
         B.ep_dispatch(self.x, self.xs, self.wts if weights else None, self.lay["dst_slot"], w.T,

@@ -132,6 +132,27 @@ def test_dispatch_rejections(L):
     assert ei.value.code == B.EP_EINVAL and "plan" in str(ei.value)
 
 
+def lay_disp(T=128, K=8, E=256, A=1, cap=1024, x=FAKE, xs=None, H=7168, dt=B.EP_BF16, X=FAKE,
+             Xs=None):
+    return (FAKE, T, K, E, A, cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, x, xs, None, H, dt,
+            X, Xs, None)
+
+
+def test_layout_dispatch_rejections(L):
+    """The fused call applies ep_layout's and ep_dispatch's checks (nothing is launched)."""
+    assert _code(B.ep_layout_dispatch, *lay_disp(K=0)) == B.EP_EINVAL
+    assert _code(B.ep_layout_dispatch, *lay_disp(E=1025)) == B.EP_EINVAL
+    assert _code(B.ep_layout_dispatch, *lay_disp(cap=1023)) == B.EP_ECAPACITY
+    assert _code(B.ep_layout_dispatch, *lay_disp(K=3, cap=1 << 20)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_layout_dispatch, *lay_disp(H=7169)) == B.EP_EINVAL
+    assert _code(B.ep_layout_dispatch, *lay_disp(H=7000)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_layout_dispatch, *lay_disp(dt=9)) == B.EP_EINVAL
+    assert _code(B.ep_layout_dispatch, *lay_disp(xs=FAKE, Xs=FAKE)) == B.EP_EINVAL  # bf16 scales
+    assert _code(B.ep_layout_dispatch, *lay_disp(x=ODD)) == B.EP_EINVAL
+    assert _code(B.ep_layout_dispatch, *lay_disp(X=None)) == B.EP_EINVAL
+    assert "ep_layout_dispatch" in B.ep_last_error()
+
+
 def comb(y=FAKE, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280, out=FAKE, bias=None):
     return (y, None, bias, dst, T, H, K, dt, cap, out)
 

@@ -105,3 +105,13 @@ def test_cpu_baseline_record(path):
     r = bench.cpu_baseline(case, budget_s=0.5, max_reps=2, path=path)
     assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "GB/s"
     assert r["value"] > 0 and "tiny" in r["sample"]
+
+
+@pytest.mark.parametrize("T,K,E,one", [(128, 8, 256, True), (129, 8, 256, False), (64, 2, 16, True),
+                                       (170, 6, 64, True), (171, 6, 64, False),
+                                       (64, 8, 300, True), (65, 8, 300, False),
+                                       (32, 8, 1024, True), (33, 8, 1024, False)])
+def test_one_layout_tile_follows_the_tile_rule(T, K, E, one):
+    """The step fuses layout and dispatch exactly when T*K fits one layout tile
+    (floor(W / K) tokens, W by expert count, as the header states)."""
+    assert bench.one_layout_tile(T, K, E) == one

@@ -295,6 +295,55 @@ def test_dispatch_plan(T, H, E, K, A, mask, wg_cap, dtype):
     check_dispatch(dc, ref["dst_slot"])
 
 
+FUSED = [
+    # T, H, E, K, A, mask, dtype, scales, routing, workgroup cap: one tile fuses layout and
+    # dispatch into one launch; larger batches fall back to two
+    (128, 7168, 256, 8, 1, 0.0, I.BF16, False, "zipf", 0),       # the decode shape
+    (64, 256, 16, 2, 1, 0.0, I.BF16, False, "uniform", 0),       # tiny
+    (100, 7168, 256, 8, 128, 0.1, I.FP8_E4M3, True, "uniform", 0),
+    (100, 3584, 128, 8, 4, 0.05, I.FP4X2, True, "uniform", 0),
+    (50, 1024, 32, 4, 2, 0.2, I.FP32, False, "uniform", 0),
+    (170, 2048, 64, 6, 4, 0.1, I.BF16, False, "uniform", 0),     # 1020 entries, K = 6
+    (64, 512, 300, 8, 1, 0.0, I.BF16, False, "uniform", 0),      # 512-entry tile
+    (32, 512, 1024, 8, 3, 0.1, I.BF16, False, "uniform", 0),     # 256-entry tile
+    (128, 7168, 256, 8, 1, 0.1, I.BF16, False, "zipf", 3),       # capped
+    (4096, 7168, 256, 8, 128, 0.02, I.BF16, False, "uniform", 0),  # several tiles: two launches
+    (300, 1024, 64, 8, 1, 0.0, I.BF16, False, "uniform", 0),     # 2400 entries: two launches
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,A,mask,dtype,scales,routing,wg_cap", FUSED)
+def test_layout_dispatch(T, H, E, K, A, mask, dtype, scales, routing, wg_cap):
+    w = I.custom(f"fused{T}_{E}_{K}", 9500 + T + E, T, H, E, K, A, dtype, routing,
+                 scales=scales)
+    _say(f"[layout + dispatch] {w} workgroup cap {wg_cap}")
+    case = I.make_case(w, with_y=False, mask_frac=mask)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case, with_y=False)
+    s = torch.cuda.Stream()
+    try:
+        B.ep_set_workgroup_limit(s, wg_cap)
+        with torch.cuda.stream(s):
+            dc.layout_dispatch(stream=s)
+        s.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        B.ep_set_workgroup_limit(s, 0)
+    check_layout(layout_to_host(dc.lay), ref)
+    check_dispatch(dc, ref["dst_slot"])
+
+
+def test_layout_dispatch_empty():
+    w = I.custom("fused_empty", 9499, 0, 7168, 256, 8, 1)
+    case = I.make_case(w, with_y=False)
+    dc = DeviceCase(case, with_y=False)
+    dc.layout_dispatch()
+    torch.cuda.synchronize()
+    got = layout_to_host(dc.lay)
+    assert np.all(got["counts"] == 0) and np.all(got["offsets"] == 0) and got["num_recv"] == 0
+    assert np.all(to_host(dc.expand_x) == dc.sentinel)
+
+
 def test_empty_input():
     w = I.custom("empty", 5, 0, 256, 16, 2, 4)
     lay = dev_layout(None, 0, 2, 16, 4, w.cap)
