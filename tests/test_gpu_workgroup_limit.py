@@ -55,6 +55,7 @@ CASES = [
     ("single tile, one workgroup", 100, 2048, 64, 8, 1, I.BF16, 0.0, 1),
     ("fp8 with scales", 2048, 7168, 256, 8, 1, I.FP8_E4M3, 0.0, 32),
     ("fp32 rows, fp32 combine", 777, 256, 32, 6, 4, I.FP32, 0.3, 3),
+    ("fp32 rows of 28 chunks per lane, pieces", 1200, 7168, 64, 8, 1, I.FP32, 0.1, 16),
     ("tile-scan layout, tiles loop", 20000, 256, 1024, 8, 4, I.BF16, 0.05, 6),
 ]
 
