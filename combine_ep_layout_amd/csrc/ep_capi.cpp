@@ -301,6 +301,7 @@ int ep_layout_dispatch(const int32_t *topk_idx, int32_t num_tokens, int32_t topk
                        (hipStream_t)stream};
     if (num_tokens > 0) {
       const int64_t elems = dtype == EP_FP4X2 ? 2 * (int64_t)hidden : hidden;
+      // whole 16-byte chunks: every compiled byte-row width is a multiple of 512 elements
       const int scale_chunks = x_scales != nullptr ? (int)(elems / 128 * 4 / 16) : 0;
       const int rc = ep::launch_layout_dispatch(l, d, (int)(row_bytes / 16), scale_chunks);
       if (rc != -3) return from_launch(rc, what);

@@ -333,6 +333,32 @@ def test_layout_dispatch(T, H, E, K, A, mask, dtype, scales, routing, wg_cap):
     check_dispatch(dc, ref["dst_slot"])
 
 
+@pytest.mark.parametrize("T,H,E,K,dtype,scales", [
+    (128, 7168, 256, 8, I.BF16, False),     # the decode shape
+    (100, 7168, 256, 8, I.FP8_E4M3, True),  # scale rows travel, weights do not
+    (3, 512, 16, 1, I.BF16, False),         # 3 units for thousands of waves
+    (1, 7168, 64, 8, I.BF16, False),        # one token
+])
+def test_layout_dispatch_without_weights(T, H, E, K, dtype, scales):
+    """Without router weights to forward the expand weights stay untouched."""
+    w = I.custom(f"fused_nw{T}_{K}", 9600 + T + K, T, H, E, K, 1, dtype, "uniform", scales=scales)
+    _say(f"[layout + dispatch, no weights] {w}")
+    case = I.make_case(w, with_y=False, mask_frac=0.1 if T > 1 else 0.0)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case, with_y=False)
+    dc.layout_dispatch(weights=False)
+    torch.cuda.synchronize()
+    check_layout(layout_to_host(dc.lay), ref)
+    got = to_host(dc.expand_x)
+    xb = case.x.view(np.uint8).reshape(w.T, -1)
+    pins.check_dispatch(xb, ref["dst_slot"], np.full_like(got, dc.sentinel), got)
+    assert np.all(to_host(dc.expand_w) == -5.0), "expand_weights untouched"
+    if dc.expand_s is not None:
+        gs = to_host(dc.expand_s)
+        pins.check_dispatch(case.x_scales.view(np.uint8).reshape(w.T, -1), ref["dst_slot"],
+                            np.full_like(gs, -3.0).view(np.uint8), gs.view(np.uint8))
+
+
 def test_layout_dispatch_empty():
     w = I.custom("fused_empty", 9499, 0, 7168, 256, 8, 1)
     case = I.make_case(w, with_y=False)
