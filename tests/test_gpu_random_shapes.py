@@ -4,8 +4,10 @@ Each case draws a compiled (hidden, topk, dtype), a token count, an expert
 count up to 1024, an alignment, a masking fraction, out-of-range ids, an
 optional bias and an optional workgroup cap, then runs layout, dispatch,
 combine (and, for bf16, the non-expand pair) through the C ABI; even seeds
-also ask the layout for the dispatch plan and dispatch through it. Bar as in
-the other parity tests: everything bit-exact except bf16 combine (<= 1 ulp).
+also ask the layout for the dispatch plan and dispatch through it. A second
+sweep draws batches that fit one layout tile and runs ep_layout_dispatch (one
+launch), with or without router weights and scale rows. Bar as in the other
+parity tests: everything bit-exact except bf16 combine (<= 1 ulp).
 """
 import numpy as np
 import pytest
@@ -43,7 +45,7 @@ def draw(seed):
     return dict(dtype=dtype, H=H, K=K, E=E, T=T, A=A, mask=mask, bias=bias, cap=cap, scales=scales)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_shape(seed):
     c = draw(seed)
     print(f"random case {seed}: {c}", flush=True)
@@ -117,3 +119,59 @@ def test_random_shape(seed):
         want2 = oracle.combine_compact(case.y[:max(n, 1)], ref["dst_slot"], ref["recv_src_metadata"],
                                        n, bias_h)
         assert pins.bf16_ulp_distance(to_host(out2, np.uint16), want2).max() <= 1
+
+
+def draw_one_tile(seed):
+    g = np.random.default_rng([seed, 777])
+    dtype = int(g.choice([I.BF16, I.BF16, I.FP32, I.FP8_E4M3, I.FP4X2]))
+    H = int(g.choice(HIDDEN[dtype]))
+    K = int(g.choice(TOPK))
+    E = max(K, int(g.choice([K, 16, 64, 256, 300, 1024])))
+    entries = 1024 if E <= 256 else (512 if E <= 512 else 256)  # one layout tile
+    T = int(g.integers(1, entries // K + 1))
+    A = int(g.choice([1, 2, 16, 128]))
+    mask = float(g.choice([0.0, 0.1, 0.5])) if T > 1 else 0.0
+    scales = bool(g.integers(0, 2)) and dtype in (I.FP8_E4M3, I.FP4X2)
+    weights = bool(g.integers(0, 2))
+    cap = int(g.choice([0, 0, 0, 1, 5, 64]))
+    return dict(dtype=dtype, H=H, K=K, E=E, T=T, A=A, mask=mask, scales=scales, weights=weights,
+                cap=cap)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_one_tile_layout_dispatch(seed):
+    c = draw_one_tile(seed)
+    print(f"one-tile case {seed}: {c}", flush=True)
+    w = I.custom(f"rndf{seed}", 7000 + seed, c["T"], c["H"], c["E"], c["K"], c["A"], c["dtype"],
+                 "uniform", scales=c["scales"])
+    case = I.make_case(w, with_y=False, mask_frac=c["mask"])
+    case.topk_idx[::11, 0] = w.E + 1  # some ids outside [0, E): masked
+    dc = DeviceCase(case, with_y=False)
+    s = torch.cuda.Stream()
+    try:
+        B.ep_set_workgroup_limit(s, c["cap"])
+        with torch.cuda.stream(s):
+            dc.layout_dispatch(stream=s, weights=c["weights"])
+        s.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        B.ep_set_workgroup_limit(s, 0)
+
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    got = layout_to_host(dc.lay)
+    for k in ("counts", "offsets", "dst_slot"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert got["num_recv"] == ref["num_recv"]
+    assert np.array_equal(got["recv_src_metadata"], ref["recv_src_metadata"])
+
+    X = np.full((w.cap, dc.row_bytes), dc.sentinel, np.uint8)
+    Xs = (np.full((w.cap, case.x_scales.shape[1]), -3.0, np.float32)
+          if case.x_scales is not None else None)
+    Xw = np.full(w.cap, -5.0, np.float32)
+    oracle.dispatch(case.x, ref["dst_slot"], w.cap, x_scales=case.x_scales,
+                    topk_weights=case.topk_weights if c["weights"] else None, expand_x=X,
+                    expand_scales=Xs, expand_weights=Xw)
+    assert np.array_equal(to_host(dc.expand_x), X), "expand_x"
+    assert np.array_equal(to_host(dc.expand_w).view(np.uint32), Xw.view(np.uint32)), "weights"
+    if Xs is not None:
+        assert np.array_equal(to_host(dc.expand_s).view(np.uint32), Xs.view(np.uint32)), "scales"
