@@ -75,21 +75,35 @@ __device__ __forceinline__ float read_lane(float v, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront.
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+// Inclusive prefix sum within each row of 16 lanes, in registers: DPP row
+// shifts by 1, 2, 4 and 8 lanes (a lane whose source falls outside its row
+// adds 0).
+__device__ __forceinline__ int row_inclusive_scan(int x) {
+  constexpr int kRowShr = 0x110;  // DPP control row_shr:n is kRowShr + n
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 1, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 2, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 4, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 8, 0xF, 0xF, false);
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: row scans, then
+// each lane adds the totals of the rows below its own (last lane of each
+// row, read with readlane). No LDS traffic, unlike lane shuffles.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x = row_inclusive_scan(x);
+  const int lane = lane_id();
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
+// Sum over the 64 lanes of a wavefront (the same value in every lane).
 __device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  x = row_inclusive_scan(x);
+  return __builtin_amdgcn_readlane(x, 15) + __builtin_amdgcn_readlane(x, 31) +
+         __builtin_amdgcn_readlane(x, 47) + __builtin_amdgcn_readlane(x, 63);
 }
 
 // Exclusive prefix sum of one value per thread over a block of NT threads.

@@ -146,6 +146,28 @@ __device__ __forceinline__ int block_sum(int v, int *s_wtot) {
   return tot;
 }
 
+// Sums of two ints per thread over the block, sharing one barrier round.
+// s_wtot holds 2 * kWavesMax ints.
+__device__ __forceinline__ void block_sum2(int a, int b, int *s_wtot, int &sum_a, int &sum_b) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if (lane == 0) {
+    s_wtot[w] = a;
+    s_wtot[kWavesMax + w] = b;
+  }
+  __syncthreads();
+  int ta = 0, tb = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWavesMax; ++ww) {
+    ta += s_wtot[ww];
+    tb += s_wtot[kWavesMax + ww];
+  }
+  __syncthreads();
+  sum_a = ta;
+  sum_b = tb;
+}
+
 // Number of threads below the caller (in thread order) whose flag is set;
 // `total` receives the block-wide count.
 __device__ __forceinline__ int block_flag_rank(bool f, int *s_wtot, int &total) {
@@ -364,8 +386,8 @@ __device__ __forceinline__ void fused_tile(
     vall += any ? 1 : 0;
     vpre += (any && before) ? 1 : 0;
   }
-  const int recv_before = block_sum(vpre, s_tmp);  // its barriers publish the histograms
-  const int recv_total = block_sum(vall, s_tmp);
+  int recv_before, recv_total;
+  block_sum2(vpre, vall, s_tmp, recv_before, recv_total);  // its barriers publish the histograms
   const int cnt = tid < E ? s_all[tid] : 0;
   const int padded = ((cnt + A - 1) / A) * A;
   const int mine = tid < E ? s.total[tid] : 0;  // this tile's count of expert tid
@@ -516,8 +538,7 @@ __device__ __forceinline__ void assign_tile(
     s_pre[tid] = pre;
     s_tot[tid] = tot;
     if (tid < Tile<K, NW>::tokens) s_row[tid] = 0;
-    recv_before = block_sum(vpre, s_tmp);  // its barriers publish s_pre / s_tot
-    recv_total = block_sum(vtot, s_tmp);
+    block_sum2(vpre, vtot, s_tmp, recv_before, recv_total);  // its barriers publish s_pre / s_tot
     if (tid < E) {
       for (int j = 0; j < P; ++j) {
         base += s_pre[j * epad + tid];
