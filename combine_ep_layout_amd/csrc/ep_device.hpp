@@ -106,61 +106,4 @@ __device__ __forceinline__ int wave_sum(int x) {
          __builtin_amdgcn_readlane(x, 47) + __builtin_amdgcn_readlane(x, 63);
 }
 
-// Exclusive prefix sum of one value per thread over a block of NT threads.
-// `s_tmp` holds NT/64 ints of LDS. Returns the exclusive prefix; `total`
-// receives the block-wide sum. Contains barriers: call from every thread.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int *s_tmp, int &total) {
-  constexpr int NW = NT / kWave;
-  static_assert(NW <= kWave, "block too large for a two-level scan");
-  const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
-  const int inc = wave_inclusive_scan(v);
-  if (lane == kWave - 1) s_tmp[w] = inc;
-  __syncthreads();
-  if (w == 0) {
-    int s = lane < NW ? s_tmp[lane] : 0;
-    s = wave_inclusive_scan(s);
-    if (lane < NW) s_tmp[lane] = s;
-  }
-  __syncthreads();
-  const int before = w ? s_tmp[w - 1] : 0;
-  total = s_tmp[NW - 1];
-  __syncthreads();
-  return before + inc - v;
-}
-
-// Two exclusive prefix sums at once (v and u, one value each per thread),
-// sharing the barriers of one scan. `s_tmp` holds 2 * NT/64 ints of LDS.
-// Returns v's exclusive prefix; u_excl receives u's; the totals go to v_total
-// and u_total. Contains barriers: call from every thread.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan2(int v, int u, int &u_excl, int *s_tmp,
-                                                     int &v_total, int &u_total) {
-  constexpr int NW = NT / kWave;
-  static_assert(NW >= 2 && NW <= kWave, "block size for a two-level scan of two values");
-  const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
-  const int inc_v = wave_inclusive_scan(v);
-  const int inc_u = wave_inclusive_scan(u);
-  if (lane == kWave - 1) {
-    s_tmp[w] = inc_v;
-    s_tmp[NW + w] = inc_u;
-  }
-  __syncthreads();
-  if (w < 2) {  // wave 0 scans the v totals, wave 1 the u totals
-    int s = lane < NW ? s_tmp[w * NW + lane] : 0;
-    s = wave_inclusive_scan(s);
-    if (lane < NW) s_tmp[w * NW + lane] = s;
-  }
-  __syncthreads();
-  const int before_v = w ? s_tmp[w - 1] : 0;
-  const int before_u = w ? s_tmp[NW + w - 1] : 0;
-  v_total = s_tmp[NW - 1];
-  u_total = s_tmp[2 * NW - 1];
-  __syncthreads();
-  u_excl = before_u + inc_u - u;
-  return before_v + inc_v - v;
-}
-
 }  // namespace ep

@@ -133,57 +133,62 @@ __device__ EntryRank tile_rank(const int32_t *__restrict__ topk_idx, int64_t t0,
   return {e, rank};
 }
 
-// Sum of one int per thread over the block (deterministic: fixed tree).
-__device__ __forceinline__ int block_sum(int v, int *s_wtot) {
-  const int lane = lane_id(), w = threadIdx.x / kWave;
+// Block-wide reductions split around a barrier that the caller places, so
+// that several of them, and other LDS writes, share one barrier. Each
+// *_publish writes one int per wave into its own LDS array (kWavesMax ints);
+// after the barrier the matching *_collect reads all of them. Such an array
+// is not written again until every thread has passed a later barrier.
+
+// Sum over the block: the wave's sum of v.
+__device__ __forceinline__ void sum_publish(int v, int *s_w) {
   v = wave_sum(v);
-  if (lane == 0) s_wtot[w] = v;
-  __syncthreads();
-  int tot = 0;
+  if (lane_id() == 0) s_w[threadIdx.x / kWave] = v;
+}
+__device__ __forceinline__ int sum_collect(const int *s_w) {
+  int t = 0;
 #pragma unroll
-  for (int ww = 0; ww < kWavesMax; ++ww) tot += s_wtot[ww];
-  __syncthreads();
-  return tot;
+  for (int ww = 0; ww < kWavesMax; ++ww) t += s_w[ww];
+  return t;
 }
 
-// Sums of two ints per thread over the block, sharing one barrier round.
-// s_wtot holds 2 * kWavesMax ints.
-__device__ __forceinline__ void block_sum2(int a, int b, int *s_wtot, int &sum_a, int &sum_b) {
-  const int lane = lane_id(), w = threadIdx.x / kWave;
-  a = wave_sum(a);
-  b = wave_sum(b);
-  if (lane == 0) {
-    s_wtot[w] = a;
-    s_wtot[kWavesMax + w] = b;
-  }
-  __syncthreads();
-  int ta = 0, tb = 0;
+// Exclusive prefix of v over the block in thread order: publish returns the
+// inclusive prefix within the wave; collect adds the totals of earlier waves
+// and gives the block total.
+__device__ __forceinline__ int scan_publish(int v, int *s_w) {
+  const int inc = wave_inclusive_scan(v);
+  if (lane_id() == kWave - 1) s_w[threadIdx.x / kWave] = inc;
+  return inc;
+}
+__device__ __forceinline__ int scan_collect(int inc, int v, const int *s_w, int &total) {
+  const int w = threadIdx.x / kWave;
+  int before = 0, t = 0;
 #pragma unroll
   for (int ww = 0; ww < kWavesMax; ++ww) {
-    ta += s_wtot[ww];
-    tb += s_wtot[kWavesMax + ww];
+    const int x = s_w[ww];
+    before += ww < w ? x : 0;
+    t += x;
   }
-  __syncthreads();
-  sum_a = ta;
-  sum_b = tb;
+  total = t;
+  return before + inc - v;
 }
 
-// Number of threads below the caller (in thread order) whose flag is set;
-// `total` receives the block-wide count.
-__device__ __forceinline__ int block_flag_rank(bool f, int *s_wtot, int &total) {
-  const int lane = lane_id(), w = threadIdx.x / kWave;
+// Rank of a set flag among the block's set flags (those of lower threads);
+// collect also gives the block's count.
+__device__ __forceinline__ uint64_t flag_publish(bool f, int *s_w) {
   const uint64_t bits = ballot(f);
-  if (lane == 0) s_wtot[w] = __popcll(bits);
-  __syncthreads();
-  int before = 0, tot = 0;
+  if (lane_id() == 0) s_w[threadIdx.x / kWave] = __popcll(bits);
+  return bits;
+}
+__device__ __forceinline__ int flag_collect(uint64_t bits, const int *s_w, int &total) {
+  const int w = threadIdx.x / kWave;
+  int before = 0, t = 0;
 #pragma unroll
   for (int ww = 0; ww < kWavesMax; ++ww) {
-    const int c = s_wtot[ww];
+    const int c = s_w[ww];
     before += ww < w ? c : 0;
-    tot += c;
+    t += c;
   }
-  total = tot;
-  __syncthreads();
+  total = t;
   return before + count_below(bits);
 }
 
@@ -234,7 +239,8 @@ __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
     int32_t *__restrict__ num_recv, int32_t *__restrict__ plan) {
-  __shared__ int s_tmp[2 * kWavesMax];
+  __shared__ int s_scan[2 * kWavesMax];
+  __shared__ int s_flag[kWavesMax];
   const RankLds s = rank_lds(E, NW);
   int *s_off = (int *)(g_smem + rank_lds_bytes(E, NW));  // E
   int *s_tb = s_off + E;                                 // E: dispatch plan
@@ -243,22 +249,28 @@ __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
   const EntryRank r = tile_rank<K, NW>(topk_idx, 0, T, E, s);
   const int cnt = tid < E ? s.total[tid] : 0;
   const int padded = ((cnt + A - 1) / A) * A;
-  int rows, tb, nvalid;
-  const int off = block_exclusive_scan2<kThreads>(padded, cnt, tb, s_tmp, rows, nvalid);
+  const int inc_off = scan_publish(padded, s_scan);
+  const int inc_tb = scan_publish(cnt, s_scan + kWavesMax);
+  const bool f = tid < T && s.tok[tid] != 0;  // only thread tid reads or writes s.tok[tid] here
+  const uint64_t fbits = flag_publish(f, s_flag);
+  __syncthreads();
+  int rows, nvalid, nrecv;
+  const int off = scan_collect(inc_off, padded, s_scan, rows);
+  const int tb = scan_collect(inc_tb, cnt, s_scan + kWavesMax, nvalid);
+  const int tok_rank = flag_collect(fbits, s_flag, nrecv);
   if (tid < E) {
     s_off[tid] = off;
     s_tb[tid] = tb;
     counts[tid] = cnt;
     offsets[tid] = off;
   }
-  if (tid == 0) offsets[E] = rows;
-  const bool f = tid < T && s.tok[tid] != 0;
-  int nrecv;
-  const int tok_rank = block_flag_rank(f, s_tmp, nrecv);  // barriers publish s_off too
-  if (tid == 0) *num_recv = nrecv;
-  const int slot = r.e >= 0 ? s_off[r.e] + r.rank : -1;
+  if (tid == 0) {
+    offsets[E] = rows;
+    *num_recv = nrecv;
+  }
   if (tid < T) s.tok[tid] = f ? tok_rank : -1;
-  __syncthreads();
+  __syncthreads();  // publishes s_off, s_tb and the receive rows
+  const int slot = r.e >= 0 ? s_off[r.e] + r.rank : -1;
   write_slots_and_meta<K>(0, T, slot, s.tok, dst_slot, meta);
   if (plan != nullptr) write_plan<K>(0, T, r.e, r.rank, slot, s_tb, nvalid, plan);
 }
@@ -282,7 +294,8 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
     const u32x4 *__restrict__ x_scales, int scale_chunks, const float *__restrict__ topk_weights,
     int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
     float *__restrict__ expand_weights) {
-  __shared__ int s_tmp[kWavesMax];
+  __shared__ int s_scan[kWavesMax];
+  __shared__ int s_flag[kWavesMax];
   const RankLds s = rank_lds(E, NW);
   int *s_off = (int *)(g_smem + rank_lds_bytes(E, NW));  // E
   int *s_slot = s_off + E;                               // kThreads: slot of entry tid
@@ -291,26 +304,29 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
   const EntryRank r = tile_rank<K, NW>(topk_idx, 0, T, E, s);
   const int cnt = tid < E ? s.total[tid] : 0;
   const int padded = ((cnt + A - 1) / A) * A;
-  int rows;
-  const int off = block_exclusive_scan<kThreads>(padded, s_tmp, rows);
-  if (tid < E) s_off[tid] = off;
+  const int inc_off = scan_publish(padded, s_scan);
+  const bool f = tid < T && s.tok[tid] != 0;  // only thread tid reads or writes s.tok[tid] here
+  const uint64_t fbits = flag_publish(f, s_flag);
   __syncthreads();
-  const int slot = r.e >= 0 ? s_off[r.e] + r.rank : -1;
-  s_slot[tid] = slot;
+  int rows, nrecv;
+  const int off = scan_collect(inc_off, padded, s_scan, rows);
+  const int tok_rank = flag_collect(fbits, s_flag, nrecv);
+  if (tid < E) s_off[tid] = off;
   if (blockIdx.x == 0) {  // the layout's outputs, as ep_layout_single_tile writes them
     if (tid < E) {
       counts[tid] = cnt;
       offsets[tid] = off;
     }
-    if (tid == 0) offsets[E] = rows;
-    const bool f = tid < T && s.tok[tid] != 0;
-    int nrecv;
-    const int tok_rank = block_flag_rank(f, s_tmp, nrecv);
-    if (tid == 0) *num_recv = nrecv;
+    if (tid == 0) {
+      offsets[E] = rows;
+      *num_recv = nrecv;
+    }
     if (tid < T) s.tok[tid] = f ? tok_rank : -1;
-    __syncthreads();
-    write_slots_and_meta<K>(0, T, slot, s.tok, dst_slot, meta);
   }
+  __syncthreads();  // publishes s_off (and in workgroup 0 the receive rows)
+  const int slot = r.e >= 0 ? s_off[r.e] + r.rank : -1;
+  s_slot[tid] = slot;
+  if (blockIdx.x == 0) write_slots_and_meta<K>(0, T, slot, s.tok, dst_slot, meta);
   __syncthreads();  // publishes s_slot
 
   const int lane = lane_id();
@@ -350,7 +366,9 @@ __device__ __forceinline__ void fused_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
     int32_t *__restrict__ num_recv, int32_t *__restrict__ plan, const int b) {
-  __shared__ int s_tmp[2 * kWavesMax];
+  __shared__ int s_sum[2 * kWavesMax];
+  __shared__ int s_scan[2 * kWavesMax];
+  __shared__ int s_flag[kWavesMax];
   const RankLds s = rank_lds(E, NW);
   int *s_pre = (int *)(g_smem + rank_lds_bytes(E, NW));  // E: entries before this tile
   int *s_all = s_pre + E;                                // E: all entries
@@ -386,13 +404,25 @@ __device__ __forceinline__ void fused_tile(
     vall += any ? 1 : 0;
     vpre += (any && before) ? 1 : 0;
   }
-  int recv_before, recv_total;
-  block_sum2(vpre, vall, s_tmp, recv_before, recv_total);  // its barriers publish the histograms
+  sum_publish(vpre, s_sum);
+  sum_publish(vall, s_sum + kWavesMax);
+  const bool f = tid < ntok && s.tok[tid] != 0;  // only thread tid reads or writes s.tok[tid] here
+  const uint64_t fbits = flag_publish(f, s_flag);
+  __syncthreads();  // publishes the histograms, the wave sums and the flag counts
+  const int recv_before = sum_collect(s_sum);
+  const int recv_total = sum_collect(s_sum + kWavesMax);
+  int nflag;
+  const int tok_rank = flag_collect(fbits, s_flag, nflag);
   const int cnt = tid < E ? s_all[tid] : 0;
   const int padded = ((cnt + A - 1) / A) * A;
   const int mine = tid < E ? s.total[tid] : 0;  // this tile's count of expert tid
-  int rows, tb, nvalid;
-  const int off = block_exclusive_scan2<kThreads>(padded, mine, tb, s_tmp, rows, nvalid);
+  const int inc_off = scan_publish(padded, s_scan);
+  const int inc_tb = scan_publish(mine, s_scan + kWavesMax);
+  if (tid < ntok) s.tok[tid] = f ? recv_before + tok_rank : -1;
+  __syncthreads();
+  int rows, nvalid;
+  const int off = scan_collect(inc_off, padded, s_scan, rows);
+  const int tb = scan_collect(inc_tb, mine, s_scan + kWavesMax, nvalid);
   if (tid < E) {
     s_off[tid] = off;
     s_tb[tid] = tb;
@@ -407,12 +437,8 @@ __device__ __forceinline__ void fused_tile(
       *num_recv = recv_total;
     }
   }
-  const bool f = tid < ntok && s.tok[tid] != 0;
-  int nflag;
-  const int tok_rank = block_flag_rank(f, s_tmp, nflag);  // barriers publish s_off
+  __syncthreads();  // publishes s_off and s_tb
   const int slot = r.e >= 0 ? s_off[r.e] + s_pre[r.e] + r.rank : -1;
-  if (tid < ntok) s.tok[tid] = f ? recv_before + tok_rank : -1;
-  __syncthreads();
   write_slots_and_meta<K>(t0, ntok, slot, s.tok, dst_slot, meta);
   if (plan != nullptr) write_plan<K>(t0, ntok, r.e, r.rank, slot, s_tb, nvalid, plan);
 }
@@ -443,7 +469,7 @@ template <int K, int NW>
 __device__ __forceinline__ void histogram_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int32_t *__restrict__ dst_slot,
     int32_t *__restrict__ tile_counts, int32_t *__restrict__ tile_recv, const int b) {
-  __shared__ int s_wtot[kWavesMax];
+  __shared__ int s_flag[kWavesMax];
   const RankLds s = rank_lds(E, NW);
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)b * Tile<K, NW>::tokens;
@@ -452,9 +478,9 @@ __device__ __forceinline__ void histogram_tile(
   const EntryRank r = tile_rank<K, NW>(topk_idx, t0, ntok, E, s);
   if (tid < ntok * K) dst_slot[t0 * K + tid] = r.e >= 0 ? (r.e << kRankBits) | r.rank : -1;
   for (int ex = tid; ex < E; ex += kThreads) tile_counts[(int64_t)b * E + ex] = s.total[ex];
-  const bool f = tid < ntok && s.tok[tid] != 0;
-  const int nrecv = block_sum(f ? 1 : 0, s_wtot);
-  if (tid == 0) tile_recv[b] = nrecv;
+  flag_publish(tid < ntok && s.tok[tid] != 0, s_flag);
+  __syncthreads();
+  if (tid == 0) tile_recv[b] = sum_collect(s_flag);
 }
 
 template <int K, int NW, bool LOOP>
@@ -494,7 +520,9 @@ __device__ __forceinline__ void assign_tile(
   __shared__ int s_pre[kThreads];
   __shared__ int s_tot[kThreads];
   __shared__ int s_row[kThreads];
-  __shared__ int s_tmp[2 * kWavesMax];
+  __shared__ int s_sum[2 * kWavesMax];
+  __shared__ int s_scan[2 * kWavesMax];
+  __shared__ int s_flag[kWavesMax];
   int *s_base = (int *)g_smem;  // E
   int *s_off = s_base + E;      // E
   int *s_tb = s_off + E;        // E: dispatch plan
@@ -505,7 +533,10 @@ __device__ __forceinline__ void assign_tile(
   // Every global load of the block is issued before the first barrier.
   const int packed = tid < ntok * K ? dst_slot[t0 * K + tid] : -1;
   const int mine = plan != nullptr && tid < E ? tile_counts[(int64_t)b * E + tid] : 0;
-  int base = 0, cnt = 0, recv_before, recv_total;
+  // P threads share an expert when the block sums the tile counts itself.
+  const int epad = E <= 1 ? 1 : 1 << (32 - __builtin_clz((unsigned)(E - 1)));
+  const int P = kThreads / epad;
+  int base = 0, cnt = 0, recv_before = 0, recv_total = 0;
   if constexpr (SCANNED) {
     if (tid < E) {
       base = scan.tile_base[(int64_t)b * E + tid];
@@ -513,12 +544,9 @@ __device__ __forceinline__ void assign_tile(
     }
     recv_before = scan.recv_base[b];
     recv_total = *scan.recv_total;
-    if (tid < Tile<K, NW>::tokens) s_row[tid] = 0;  // published by the scan's barriers below
   } else {
     // Per expert: entries in tiles before b, and in all tiles. P threads share
     // an expert so that each thread has only a few loads, all in flight.
-    const int epad = E <= 1 ? 1 : 1 << (32 - __builtin_clz((unsigned)(E - 1)));
-    const int P = kThreads / epad;
     const int ex = tid % epad, part = tid / epad;
     int pre = 0, tot = 0;
     if (ex < E) {
@@ -537,8 +565,14 @@ __device__ __forceinline__ void assign_tile(
     }
     s_pre[tid] = pre;
     s_tot[tid] = tot;
-    if (tid < Tile<K, NW>::tokens) s_row[tid] = 0;
-    block_sum2(vpre, vtot, s_tmp, recv_before, recv_total);  // its barriers publish s_pre / s_tot
+    sum_publish(vpre, s_sum);
+    sum_publish(vtot, s_sum + kWavesMax);
+  }
+  if (tid < Tile<K, NW>::tokens) s_row[tid] = 0;
+  __syncthreads();  // publishes the partial sums and the cleared token flags
+  if constexpr (!SCANNED) {
+    recv_before = sum_collect(s_sum);
+    recv_total = sum_collect(s_sum + kWavesMax);
     if (tid < E) {
       for (int j = 0; j < P; ++j) {
         base += s_pre[j * epad + tid];
@@ -546,9 +580,14 @@ __device__ __forceinline__ void assign_tile(
       }
     }
   }
+  if (packed >= 0) s_row[tid / K] = 1;  // every writer stores the same value
   const int padded = ((cnt + A - 1) / A) * A;
-  int rows, tb, nvalid;
-  const int off = block_exclusive_scan2<kThreads>(padded, mine, tb, s_tmp, rows, nvalid);
+  const int inc_off = scan_publish(padded, s_scan);
+  const int inc_tb = scan_publish(mine, s_scan + kWavesMax);
+  __syncthreads();  // publishes the wave scans and the token flags
+  int rows, nvalid;
+  const int off = scan_collect(inc_off, padded, s_scan, rows);
+  const int tb = scan_collect(inc_tb, mine, s_scan + kWavesMax, nvalid);
   if (tid < E) {
     s_base[tid] = base;
     s_off[tid] = off;
@@ -564,18 +603,18 @@ __device__ __forceinline__ void assign_tile(
       *num_recv = recv_total;
     }
   }
-  if (packed >= 0) s_row[tid / K] = 1;
-  __syncthreads();
+  const bool f = tid < ntok && s_row[tid] != 0;  // only thread tid reads or writes s_row[tid] now
+  const uint64_t fbits = flag_publish(f, s_flag);
+  __syncthreads();  // publishes s_base, s_off, s_tb and the flag counts
+  int nflag;
+  const int tok_rank = flag_collect(fbits, s_flag, nflag);
   int slot = -1;
   if (packed >= 0) {
     const int e = packed >> kRankBits;
     slot = s_off[e] + s_base[e] + (packed & ((1 << kRankBits) - 1));
   }
-  const bool f = tid < ntok && s_row[tid] != 0;
-  int nflag;
-  const int tok_rank = block_flag_rank(f, s_tmp, nflag);
   if (tid < ntok) s_row[tid] = f ? recv_before + tok_rank : -1;
-  __syncthreads();
+  __syncthreads();  // publishes the receive rows
   write_slots_and_meta<K>(t0, ntok, slot, s_row, dst_slot, meta);
   if (plan != nullptr) {
     const int e = packed >= 0 ? packed >> kRankBits : -1;
