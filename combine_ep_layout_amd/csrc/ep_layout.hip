@@ -13,11 +13,13 @@
 // Design (MI355X): entries are cut into tiles of whole tokens (up to 1024
 // entries: 16, 8 or 4 wave64s of entries as E grows), one 1024-thread
 // workgroup per tile, one entry per thread.
-//   1. Every entry ORs its lane bit into an LDS word mask[e][wave] (the
+//   1. Every entry ORs its lane bit into an LDS word mask[wave][e] (the
 //      result of an OR does not depend on the order of the ORs). For each
 //      expert, a pass over its wave words gives the entries of that expert in
 //      earlier waves; an entry's rank in the tile is that base plus the
-//      popcount of its own wave word below its lane (mbcnt).
+//      popcount of its own wave word below its lane (mbcnt). The words are
+//      stored wave-major, so the pass (one thread per expert) reads
+//      consecutive words across lanes, free of LDS bank conflicts.
 //   2. A tile's per-expert totals go to the workspace. A second launch
 //      reduces, per expert, the totals of earlier tiles (prefix) and of all
 //      tiles (count), pads each count to the alignment, scans over experts,
@@ -110,7 +112,7 @@ __device__ EntryRank tile_rank(const int32_t *__restrict__ topk_idx, int64_t t0,
   const int e = (v >= 0 && v < E) ? v : -1;
   __syncthreads();
   if (e >= 0) {
-    __hip_atomic_fetch_or(&s.mask[e * NW + w], 1ull << lane, __ATOMIC_RELAXED,
+    __hip_atomic_fetch_or(&s.mask[w * E + e], 1ull << lane, __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_WORKGROUP);
     s.tok[tid / K] = 1;  // every writer stores the same value
   }
@@ -118,18 +120,18 @@ __device__ EntryRank tile_rank(const int32_t *__restrict__ topk_idx, int64_t t0,
   for (int ex = tid; ex < E; ex += kThreads) {
     uint64_t m[NW];
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) m[ww] = s.mask[ex * NW + ww];
+    for (int ww = 0; ww < NW; ++ww) m[ww] = s.mask[ww * E + ex];
     int run = 0;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      s.wbase[ex * NW + ww] = (uint16_t)run;
+      s.wbase[ww * E + ex] = (uint16_t)run;
       run += __popcll(m[ww]);
     }
     s.total[ex] = run;
   }
   __syncthreads();
   int rank = 0;
-  if (e >= 0) rank = s.wbase[e * NW + w] + count_below(s.mask[e * NW + w]);
+  if (e >= 0) rank = s.wbase[w * E + e] + count_below(s.mask[w * E + e]);
   return {e, rank};
 }
 
