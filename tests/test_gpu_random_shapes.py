@@ -6,8 +6,9 @@ optional bias and an optional workgroup cap, then runs layout, dispatch,
 combine (and, for bf16, the non-expand pair) through the C ABI; even seeds
 also ask the layout for the dispatch plan and dispatch through it. A second
 sweep draws batches that fit one layout tile and runs ep_layout_dispatch (one
-launch), with or without router weights and scale rows. Bar as in the other
-parity tests: everything bit-exact except bf16 combine (<= 1 ulp).
+launch), with or without router weights and scale rows. A third draws large
+layouts alone (up to 70K tokens, every launch path of the layout). Bar as in
+the other parity tests: everything bit-exact except bf16 combine (<= 1 ulp).
 """
 import numpy as np
 import pytest
@@ -22,7 +23,7 @@ import oracle  # noqa: E402
 from combine_ep_layout_amd import binding as B  # noqa: E402
 from combine_ep_layout_amd import inputs as I  # noqa: E402
 from tests import pins  # noqa: E402
-from tests.gpu_util import DEV, DeviceCase, layout_to_host, to_dev, to_host  # noqa: E402
+from tests.gpu_util import DEV, DeviceCase, dev_layout, layout_to_host, to_dev, to_host  # noqa: E402
 
 HIDDEN = {I.BF16: [256, 512, 1024, 2048, 4096, 7168], I.FP32: [256, 512, 1024, 2048],
           I.FP8_E4M3: [512, 1024, 2048, 7168], I.FP4X2: [256, 512, 1024, 3584]}
@@ -175,3 +176,40 @@ def test_random_one_tile_layout_dispatch(seed):
     assert np.array_equal(to_host(dc.expand_w).view(np.uint32), Xw.view(np.uint32)), "weights"
     if Xs is not None:
         assert np.array_equal(to_host(dc.expand_s).view(np.uint32), Xs.view(np.uint32)), "scales"
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_large_layout(seed):
+    g = np.random.default_rng([seed, 31337])
+    K = int(g.choice(TOPK))
+    E = max(K, int(g.choice([8, 64, 256, 300, 512, 777, 1024])))
+    T = int(g.choice([int(g.integers(1, 3000)), int(g.integers(3000, 70000))]))
+    A = int(g.choice([1, 4, 128]))
+    mask = float(g.choice([0.0, 0.05, 0.5]))
+    cap = int(g.choice([0, 0, 0, 1, 7, 33, 200]))
+    plan = bool(g.integers(0, 2))
+    print(f"large layout {seed}: T={T} K={K} E={E} A={A} mask={mask} cap={cap} plan={plan}",
+          flush=True)
+    if T * E <= 10_000_000:  # distinct experts per token
+        idx = np.argsort(g.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    else:  # repeats allowed: each entry still gets its own row
+        idx = g.integers(0, E, (T, K)).astype(np.int32)
+    idx[g.random((T, K)) < mask] = -1
+    idx[::13, 0] = E + 3  # outside [0, E): masked
+    ref = oracle.layout(idx, E, A)
+    s = torch.cuda.Stream()
+    try:
+        B.ep_set_workgroup_limit(s, cap)
+        with torch.cuda.stream(s):
+            lay = dev_layout(to_dev(idx), T, K, E, A, T * K + E * (A - 1), plan=plan, stream=s)
+        s.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        B.ep_set_workgroup_limit(s, 0)
+    got = layout_to_host(lay)
+    for k in ("counts", "offsets", "dst_slot"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert got["num_recv"] == ref["num_recv"]
+    assert np.array_equal(got["recv_src_metadata"], ref["recv_src_metadata"])
+    if plan:
+        assert np.array_equal(to_host(lay["plan"]), pins.dispatch_plan(ref["dst_slot"], E, K))
