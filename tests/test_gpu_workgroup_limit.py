@@ -140,3 +140,60 @@ def test_capped_non_expand_matches_oracle(capped_stream, cap):
     assert np.array_equal(to_host(recv_w)[:n].view(np.uint32), rw.view(np.uint32))
     want = oracle.combine_compact(y, ref["dst_slot"], ref["recv_src_metadata"], n, bias)
     assert pins.bf16_ulp_distance(to_host(out, np.uint16), want).max() <= 1
+
+
+def test_two_host_threads_two_streams_two_caps():
+    """Two host threads call the library at the same time, each on its own
+    stream with its own workgroup cap (none and 64) and its own buffers; the
+    caps are per stream and every call's state is its own, so both end with
+    the oracle's results."""
+    import threading
+    runs = []
+    for i, (T, cap) in enumerate([(3000, 0), (2000, 64)]):
+        w = I.custom(f"threads{i}", 9700 + i, T, 2048, 64, 8, 4)
+        case = I.make_case(w, mask_frac=0.1)
+        runs.append({"w": w, "case": case, "dc": DeviceCase(case), "cap": cap,
+                     "stream": torch.cuda.Stream()})
+    torch.cuda.synchronize()
+    errors = []
+
+    def drive(r):
+        s = r["stream"]
+        try:
+            B.ep_set_workgroup_limit(s, r["cap"])  # raises EpError on failure
+            assert B.ep_get_workgroup_limit(s) == r["cap"]
+            with torch.cuda.stream(s):
+                for _ in range(10):
+                    r["lay"] = r["dc"].layout(stream=s, plan=True)
+                    r["dc"].dispatch(stream=s, plan=True)
+                    r["out"] = r["dc"].combine(stream=s)
+            s.synchronize()
+        except Exception as e:  # reported below, on the test's own thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=drive, args=(r,)) for r in runs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for r in runs:
+        B.ep_set_workgroup_limit(r["stream"], 0)
+    assert not errors, errors
+
+    for r in runs:
+        w, case, dc = r["w"], r["case"], r["dc"]
+        _say(f"thread run: T={w.T} cap={r['cap']}")
+        ref = oracle.layout(case.topk_idx, w.E, w.A)
+        got = layout_to_host(r["lay"])
+        for k in ("counts", "offsets", "dst_slot"):
+            assert np.array_equal(got[k], ref[k]), k
+        assert np.array_equal(got["recv_src_metadata"], ref["recv_src_metadata"])
+        ex = np.full((w.cap, dc.row_bytes), dc.sentinel, np.uint8)
+        ew = np.full((w.cap,), -5.0, np.float32)
+        oracle.dispatch(case.x, ref["dst_slot"], w.cap, topk_weights=case.topk_weights,
+                        expand_x=ex, expand_weights=ew)
+        assert np.array_equal(to_host(dc.expand_x), ex), "expand_x"
+        assert np.array_equal(to_host(dc.expand_w).view(np.uint32), ew.view(np.uint32))
+        want = oracle.combine(case.y, ref["dst_slot"], case.topk_weights)
+        assert pins.bf16_ulp_distance(to_host(r["out"], np.uint16), want).max() <= 1
