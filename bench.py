@@ -271,8 +271,9 @@ def main():
                     help="expand path: never ask ep_layout for the dispatch plan (by default it is "
                          "used when the expand rows total at least PLAN_MIN_BYTES)")
     ap.add_argument("--no-fused", action="store_true",
-                    help="expand path: call ep_layout and ep_dispatch separately even when the "
-                         "batch fits one layout tile (by default ep_layout_dispatch is used then)")
+                    help="call ep_layout and ep_dispatch (ep_dispatch_compact) separately even "
+                         "when the batch fits one layout tile (by default ep_layout_dispatch "
+                         "(ep_layout_dispatch_compact) is used then)")
     ap.add_argument("--cold", action="store_true",
                     help="rotate buffer sets so that no step finds its rows in the last-level cache")
     ap.add_argument("--workgroups", type=int, default=0,
@@ -342,7 +343,7 @@ def main():
     rows_out = w.T if non_expand else w.cap
     use_plan = (not non_expand and not args.no_plan
                 and w.T * w.K * case.x.view(np.uint8).reshape(w.T, -1).shape[1] >= PLAN_MIN_BYTES)
-    fused = not non_expand and not args.no_fused and one_layout_tile(w.T, w.K, w.E)
+    fused = not args.no_fused and one_layout_tile(w.T, w.K, w.E)
     plan = torch.empty((w.T * w.K, 2), dtype=torch.int32, device=dev) if use_plan else None
 
     def x_set():
@@ -389,7 +390,12 @@ def main():
         S, X = sets[i % nsets], x_sets[i % nx]
         if ev is not None:
             ev[0].record(stream)
-        if fused:  # one launch; its time is reported as dispatch's, layout's as zero
+        if fused and non_expand:  # one launch; its time is reported as dispatch's, layout's as zero
+            B.ep_layout_dispatch_compact(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta,
+                                         nrecv, ws, wsb, X["x"], X["xs"], wts, w.H, w.dtype,
+                                         S["expand"], S["expand_s"], S["recv_i"], S["recv_w"],
+                                         stream)
+        elif fused:
             B.ep_layout_dispatch(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv,
                                  ws, wsb, X["x"], X["xs"], None, w.H, w.dtype, S["expand"],
                                  S["expand_s"], None, stream)
@@ -398,10 +404,10 @@ def main():
                         stream, dispatch_plan=plan)
         if ev is not None:
             ev[1].record(stream)
-        if non_expand:
+        if non_expand and not fused:
             B.ep_dispatch_compact(X["x"], X["xs"], idx, wts, dst, meta, nrecv, w.T, w.H, w.K, w.dtype,
                                   S["expand"], S["expand_s"], S["recv_i"], S["recv_w"], stream)
-        elif not fused:
+        elif not non_expand and not fused:
             B.ep_dispatch(X["x"], X["xs"], None, dst, w.T, w.H, w.K, w.dtype, w.cap, S["expand"],
                           S["expand_s"], None, stream, dispatch_plan=plan)
         if ev is not None:
@@ -607,7 +613,9 @@ def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=N
                    "dispatch_dtype": DTYPE_NAMES[w.dtype], "combine_dtype": DTYPE_NAMES[w.out_dtype],
                    "parallelism": "one GPU, all experts local", "path": args.path,
                    "dispatch_plan": plan_used,
-                   "layout_dispatch": "one launch (ep_layout_dispatch)" if fused else "two launches",
+                   "layout_dispatch": (("one launch (ep_layout_dispatch_compact)" if non_expand
+                                        else "one launch (ep_layout_dispatch)")
+                                       if fused else "separate launches"),
                    "workgroup_cap": args.workgroups or None,
                    "cache": cache, "launch": launch},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -32,7 +32,8 @@ EP_MAX_TOPK = 64
 
 SYMBOLS = ("ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_dispatch",
            "ep_combine",
-           "ep_dispatch_compact", "ep_combine_compact", "ep_zero_padding", "ep_set_workgroup_limit",
+           "ep_dispatch_compact", "ep_layout_dispatch_compact", "ep_combine_compact",
+           "ep_zero_padding", "ep_set_workgroup_limit",
            "ep_get_workgroup_limit", "ep_last_error", "ep_supported")
 
 
@@ -78,6 +79,10 @@ def lib(path: str = None) -> ctypes.CDLL:
     L.ep_dispatch_compact.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                       _vp, _vp, _vp, _vp, _vp]
     L.ep_dispatch_compact.restype = ctypes.c_int
+    L.ep_layout_dispatch_compact.argtypes = [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
+                                             _vp, _vp, _sz, _vp, _vp, _vp, _i32, _i32, _vp, _vp,
+                                             _vp, _vp, _vp]
+    L.ep_layout_dispatch_compact.restype = ctypes.c_int
     L.ep_combine_compact.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]
     L.ep_combine_compact.restype = ctypes.c_int
     L.ep_set_workgroup_limit.argtypes = [_vp, _i32]
@@ -179,6 +184,18 @@ def ep_dispatch_compact(x, x_scales, topk_idx, topk_weights, dst_slot, recv_src_
                                      _p(dst_slot), _p(recv_src_metadata), _p(num_recv), num_tokens,
                                      hidden, topk, dtype, _p(recv_x), _p(recv_scales),
                                      _p(recv_topk_idx), _p(recv_topk_weights), _s(stream)))
+
+
+def ep_layout_dispatch_compact(topk_idx, num_tokens, topk, num_experts, expert_alignment,
+                               capacity_rows, counts, offsets, dst_slot, recv_src_metadata,
+                               num_recv, workspace, workspace_bytes, x, x_scales, topk_weights,
+                               hidden, dtype, recv_x, recv_scales, recv_topk_idx,
+                               recv_topk_weights, stream=None):
+    _check(lib().ep_layout_dispatch_compact(
+        _p(topk_idx), num_tokens, topk, num_experts, expert_alignment, capacity_rows, _p(counts),
+        _p(offsets), _p(dst_slot), _p(recv_src_metadata), _p(num_recv), _p(workspace),
+        workspace_bytes, _p(x), _p(x_scales), _p(topk_weights), hidden, dtype, _p(recv_x),
+        _p(recv_scales), _p(recv_topk_idx), _p(recv_topk_weights), _s(stream)))
 
 
 def ep_combine_compact(expert_out, bias, dst_slot, recv_src_metadata, num_recv, num_tokens, hidden,

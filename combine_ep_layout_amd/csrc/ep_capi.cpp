@@ -223,6 +223,48 @@ int check_dispatch(const char *what, const void *x, const float *x_scales,
   return EP_OK;
 }
 
+// The checks of the non-expand dispatch's own arguments (the layout's outputs
+// it reads are checked by the caller). Sets the row bytes and scale columns.
+int check_dispatch_compact(const char *what, const void *x, const float *x_scales,
+                           const int32_t *topk_idx, const float *topk_weights, int32_t num_tokens,
+                           int32_t hidden, int32_t topk, int32_t dtype, const void *recv_x,
+                           const float *recv_scales, const int32_t *recv_topk_idx,
+                           const float *recv_topk_weights, int64_t *row_bytes,
+                           int64_t *scale_cols) {
+  if (int rc = check_topk(what, num_tokens, topk)) return rc;
+  int elt;
+  if (dtype == EP_BF16) elt = 2;
+  else if (dtype == EP_FP32) elt = 4;
+  else if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2) elt = 1;
+  else return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
+  const int64_t rb = (int64_t)hidden * elt;
+  if (hidden < 1 || rb % 16 != 0 || rb > INT32_MAX)
+    return fail(EP_EINVAL,
+                "%s: token bytes must be a positive multiple of 16 below 2^31 (got %lld)", what,
+                (long long)rb);
+  if ((x_scales == nullptr) != (recv_scales == nullptr))
+    return fail(EP_EINVAL, "%s: x_scales and recv_scales go together", what);
+  int64_t sc = 0;
+  if (x_scales != nullptr) {
+    if (dtype != EP_FP8_E4M3 && dtype != EP_FP4X2)
+      return fail(EP_EINVAL, "%s: scale rows travel only with fp8 / fp4x2 rows", what);
+    const int64_t values = dtype == EP_FP4X2 ? 2 * (int64_t)hidden : hidden;
+    if (values % 128 != 0)
+      return fail(EP_EINVAL, "%s: scales need a multiple of 128 values per row", what);
+    sc = values / 128;
+  }
+  if (num_tokens > 0 && (!x || !topk_idx || !recv_x || !recv_topk_idx))
+    return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
+  if (topk_weights != nullptr && recv_topk_weights == nullptr)
+    return fail(EP_EINVAL, "%s: topk_weights given without recv_topk_weights", what);
+  if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(x_scales, 4) ||
+      !aligned(recv_scales, 4) || !aligned(topk_weights, 4) || !aligned(recv_topk_weights, 4))
+    return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
+  *row_bytes = rb;
+  *scale_cols = sc;
+  return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,36 +432,13 @@ int ep_dispatch_compact(const void *x, const float *x_scales, const int32_t *top
                         float *recv_topk_weights, void *stream) {
   try {
     const char *what = "ep_dispatch_compact";
-    if (int rc = check_topk(what, num_tokens, topk)) return rc;
-    int elt;
-    if (dtype == EP_BF16) elt = 2;
-    else if (dtype == EP_FP32) elt = 4;
-    else if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2) elt = 1;
-    else return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
-    const int64_t row_bytes = (int64_t)hidden * elt;
-    if (hidden < 1 || row_bytes % 16 != 0 || row_bytes > INT32_MAX)
-      return fail(EP_EINVAL,
-                  "%s: token bytes must be a positive multiple of 16 below 2^31 (got %lld)", what,
-                  (long long)row_bytes);
-    if ((x_scales == nullptr) != (recv_scales == nullptr))
-      return fail(EP_EINVAL, "%s: x_scales and recv_scales go together", what);
-    int64_t scale_cols = 0;
-    if (x_scales != nullptr) {
-      if (dtype != EP_FP8_E4M3 && dtype != EP_FP4X2)
-        return fail(EP_EINVAL, "%s: scale rows travel only with fp8 / fp4x2 rows", what);
-      const int64_t values = dtype == EP_FP4X2 ? 2 * (int64_t)hidden : hidden;
-      if (values % 128 != 0)
-        return fail(EP_EINVAL, "%s: scales need a multiple of 128 values per row", what);
-      scale_cols = values / 128;
-    }
-    if (num_tokens > 0 && (!x || !topk_idx || !dst_slot || !recv_src_metadata || !num_recv ||
-                           !recv_x || !recv_topk_idx))
+    int64_t row_bytes = 0, scale_cols = 0;
+    if (int rc = check_dispatch_compact(what, x, x_scales, topk_idx, topk_weights, num_tokens,
+                                        hidden, topk, dtype, recv_x, recv_scales, recv_topk_idx,
+                                        recv_topk_weights, &row_bytes, &scale_cols))
+      return rc;
+    if (num_tokens > 0 && (!dst_slot || !recv_src_metadata || !num_recv))
       return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
-    if (topk_weights != nullptr && recv_topk_weights == nullptr)
-      return fail(EP_EINVAL, "%s: topk_weights given without recv_topk_weights", what);
-    if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(x_scales, 4) ||
-        !aligned(recv_scales, 4) || !aligned(topk_weights, 4) || !aligned(recv_topk_weights, 4))
-      return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
     ep::CompactDispatchArgs a{x, row_bytes, x_scales, scale_cols, topk_idx,
                               recv_topk_weights ? topk_weights : nullptr, dst_slot,
                               recv_src_metadata, num_recv, num_tokens, topk, recv_x,
@@ -430,6 +449,47 @@ int ep_dispatch_compact(const void *x, const float *x_scales, const int32_t *top
     return fail(EP_EHIP, "ep_dispatch_compact: %s", e.what());
   } catch (...) {
     return fail(EP_EHIP, "ep_dispatch_compact: unknown exception");
+  }
+}
+
+int ep_layout_dispatch_compact(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
+                               int32_t num_experts, int32_t expert_alignment,
+                               int64_t capacity_rows, int32_t *counts, int32_t *offsets,
+                               int32_t *dst_slot, int32_t *recv_src_metadata, int32_t *num_recv,
+                               void *workspace, size_t workspace_bytes, const void *x,
+                               const float *x_scales, const float *topk_weights, int32_t hidden,
+                               int32_t dtype, void *recv_x, float *recv_scales,
+                               int32_t *recv_topk_idx, float *recv_topk_weights, void *stream) {
+  try {
+    const char *what = "ep_layout_dispatch_compact";
+    if (int rc = check_layout(what, topk_idx, num_tokens, topk, num_experts, expert_alignment,
+                              capacity_rows, counts, offsets, dst_slot, recv_src_metadata,
+                              num_recv, workspace, workspace_bytes))
+      return rc;
+    int64_t row_bytes = 0, scale_cols = 0;
+    if (int rc = check_dispatch_compact(what, x, x_scales, topk_idx, topk_weights, num_tokens,
+                                        hidden, topk, dtype, recv_x, recv_scales, recv_topk_idx,
+                                        recv_topk_weights, &row_bytes, &scale_cols))
+      return rc;
+    ep::LayoutArgs l{topk_idx, num_tokens, topk, num_experts, expert_alignment, counts, offsets,
+                     dst_slot, recv_src_metadata, num_recv, workspace, nullptr,
+                     (hipStream_t)stream};
+    ep::CompactDispatchArgs d{x, row_bytes, x_scales, scale_cols, topk_idx,
+                              recv_topk_weights ? topk_weights : nullptr, dst_slot,
+                              recv_src_metadata, num_recv, num_tokens, topk, recv_x,
+                              recv_scales, recv_topk_idx,
+                              topk_weights ? recv_topk_weights : nullptr, (hipStream_t)stream};
+    if (num_tokens > 0) {
+      const int rc = ep::launch_layout_dispatch_compact(l, d);
+      if (rc != -3) return from_launch(rc, what);
+    }
+    // more than one tile (or no tokens): the launches of ep_layout and ep_dispatch_compact
+    if (int rc = from_launch(ep::launch_layout(l), what)) return rc;
+    return from_launch(ep::launch_dispatch_compact(d), what);
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_layout_dispatch_compact: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_layout_dispatch_compact: unknown exception");
   }
 }
 

@@ -155,6 +155,10 @@ int launch_layout_dispatch(const LayoutArgs &l, const DispatchArgs &d, int row_c
 int launch_combine(const CombineArgs &a);
 int launch_zero_padding(const ZeroPaddingArgs &a);
 int launch_dispatch_compact(const CompactDispatchArgs &a);
+// Layout and non-expand dispatch in one launch when T*K fits one layout tile;
+// -3 when it does not. The dispatch arguments' dst_slot, meta and num_recv
+// are the layout's outputs.
+int launch_layout_dispatch_compact(const LayoutArgs &l, const CompactDispatchArgs &d);
 int launch_combine_compact(const CompactCombineArgs &a);
 
 bool has_layout(int K);

@@ -356,6 +356,84 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
   }
 }
 
+// Layout and non-expand dispatch in one launch for a batch that fits one
+// tile, as ep_layout_dispatch_tile does for the expand buffer: every
+// workgroup ranks the entries and the received tokens in its own LDS and
+// workgroup 0 writes the layout's outputs; then each workgroup copies its
+// share of (token, 1 KiB slice) units of the received tokens to their
+// receive rows, with the rows, ids and weights ep_dispatch_compact writes
+// (an entry has a slot exactly when its id lies in [0, E)). WIDE: launched
+// uncapped, which keeps the received rows at device scope, as
+// ep_dispatch_compact does.
+template <int K, int NW, bool WIDE>
+__global__ __launch_bounds__(kThreads) void ep_layout_dispatch_compact_tile(
+    const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
+    int32_t *__restrict__ num_recv, const u32x4 *__restrict__ x, int row_chunks,
+    const float *__restrict__ x_scales, int scale_cols, const float *__restrict__ topk_weights,
+    u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales,
+    int32_t *__restrict__ recv_topk_idx, float *__restrict__ recv_topk_weights) {
+  __shared__ int s_scan[kWavesMax];
+  __shared__ int s_flag[kWavesMax];
+  const RankLds s = rank_lds(E, NW);
+  int *s_off = (int *)(g_smem + rank_lds_bytes(E, NW));  // E
+  const int tid = threadIdx.x;
+
+  const EntryRank r = tile_rank<K, NW>(topk_idx, 0, T, E, s);
+  const int cnt = tid < E ? s.total[tid] : 0;
+  const int padded = ((cnt + A - 1) / A) * A;
+  const int inc_off = scan_publish(padded, s_scan);
+  const bool f = tid < T && s.tok[tid] != 0;  // only thread tid reads or writes s.tok[tid] here
+  const uint64_t fbits = flag_publish(f, s_flag);
+  __syncthreads();
+  int rows, nrecv;
+  const int off = scan_collect(inc_off, padded, s_scan, rows);
+  const int tok_rank = flag_collect(fbits, s_flag, nrecv);
+  if (tid < T) s.tok[tid] = f ? tok_rank : -1;
+  if (blockIdx.x == 0) {  // the layout's outputs, as ep_layout_single_tile writes them
+    if (tid < E) {
+      s_off[tid] = off;
+      counts[tid] = cnt;
+      offsets[tid] = off;
+    }
+    if (tid == 0) {
+      offsets[E] = rows;
+      *num_recv = nrecv;
+    }
+  }
+  __syncthreads();  // publishes the receive rows (and in workgroup 0 s_off)
+  if (blockIdx.x == 0)
+    write_slots_and_meta<K>(0, T, r.e >= 0 ? s_off[r.e] + r.rank : -1, s.tok, dst_slot, meta);
+
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int slices = (row_chunks + kWave - 1) / kWave;
+  const int64_t units = (int64_t)T * slices;
+  const int64_t stride = (int64_t)gridDim.x * kWavesMax;
+  for (int64_t u = (int64_t)blockIdx.x * kWavesMax + wave; u < units; u += stride) {
+    const int t = (int)(u / slices);
+    const int slice = (int)(u - (int64_t)t * slices);
+    const int i = __builtin_amdgcn_readfirstlane(s.tok[t]);  // receive row, or -1
+    if (i < 0) continue;
+    const int c = slice * kWave + lane;
+    if (c < row_chunks)
+      store_row<WIDE ? RowStore::kDevice : RowStore::kNt>(
+          x[(int64_t)t * row_chunks + c], recv_x + (int64_t)i * row_chunks, row_chunks * 16,
+          c * 16);
+    if (slice == 0) {
+      if (recv_scales != nullptr)
+        for (int j = lane; j < scale_cols; j += kWave)
+          recv_scales[(int64_t)i * scale_cols + j] = x_scales[(int64_t)t * scale_cols + j];
+      for (int k = lane; k < K; k += kWave) {
+        const int64_t tk = (int64_t)t * K + k;
+        const int id = topk_idx[tk];
+        recv_topk_idx[(int64_t)i * K + k] = id >= 0 && id < E ? id : -1;
+        if (recv_topk_weights != nullptr) recv_topk_weights[(int64_t)i * K + k] = topk_weights[tk];
+      }
+    }
+  }
+}
+
 // One launch for several tiles when T*K is small enough: besides ranking its
 // own tile, every block streams all of topk_idx (from L2) into LDS integer
 // histograms of the entries before its tile and of all entries, and counts
@@ -813,6 +891,39 @@ int layout_dispatch_impl(const LayoutArgs &l, const DispatchArgs &d, int row_chu
   return launch_status();
 }
 
+template <int K, int NW>
+int layout_dispatch_compact_impl(const LayoutArgs &l, const CompactDispatchArgs &d) {
+  if (tiles_for<K, NW>(l.T) > 1) return -3;  // more than one tile: not fused
+  const int cap = stream_workgroup_limit(l.stream);
+  const int row_chunks = (int)(d.row_bytes / 16);
+  const int64_t slices = (row_chunks + kWave - 1) / kWave;
+  const int64_t units = (int64_t)l.T * slices;
+  int64_t blocks = (units + kWavesMax - 1) / kWavesMax;
+  if (blocks > kFusedDispatchMaxBlocks) blocks = kFusedDispatchMaxBlocks;
+  if (cap > 0 && blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  const size_t shm = rank_lds_bytes(l.E, NW) + sizeof(int) * (size_t)l.E;
+  auto go = [&](auto wide) {
+    ep_layout_dispatch_compact_tile<K, NW, decltype(wide)::value>
+        <<<(unsigned)blocks, kThreads, shm, l.stream>>>(
+            l.topk_idx, l.T, l.E, l.A, l.counts, l.offsets, l.dst_slot, l.meta, l.num_recv,
+            (const u32x4 *)d.x, row_chunks, d.x_scales, (int)d.scale_cols, d.topk_weights,
+            (u32x4 *)d.recv_x, d.recv_scales, d.recv_topk_idx, d.recv_topk_weights);
+  };
+  if (cap > 0) go(std::false_type{});
+  else go(std::true_type{});
+  return launch_status();
+}
+
+template <int K>
+int layout_dispatch_compact_k(const LayoutArgs &l, const CompactDispatchArgs &d) {
+  switch (tile_waves(l.E)) {
+    case 16: return layout_dispatch_compact_impl<K, 16>(l, d);
+    case 8: return layout_dispatch_compact_impl<K, 8>(l, d);
+    default: return layout_dispatch_compact_impl<K, 4>(l, d);
+  }
+}
+
 template <int K>
 int layout_dispatch_k(const LayoutArgs &l, const DispatchArgs &d, int row_chunks,
                       int scale_chunks) {
@@ -856,6 +967,14 @@ int launch_layout(const LayoutArgs &a) {
 int launch_layout_dispatch(const LayoutArgs &l, const DispatchArgs &d, int row_chunks,
                            int scale_chunks) {
   switch (l.K) { EP_FOR_EACH_TOPK(EP_LAYOUT_DISPATCH_CASE) default: return -2; }
+}
+
+#define EP_LAYOUT_DISPATCH_COMPACT_CASE(K) \
+  case K:                                  \
+    return layout_dispatch_compact_k<K>(l, d);
+
+int launch_layout_dispatch_compact(const LayoutArgs &l, const CompactDispatchArgs &d) {
+  switch (l.K) { EP_FOR_EACH_TOPK(EP_LAYOUT_DISPATCH_COMPACT_CASE) default: return -2; }
 }
 
 #define EP_WS_CASE(K) \

@@ -248,6 +248,29 @@ int ep_dispatch_compact(const void *x, const float *x_scales, const int32_t *top
                         float *recv_topk_weights, void *stream);
 
 /*
+ * Layout and non-expand dispatch in one call (the DeepEP overall-architecture
+ * page: EPHandle do_expand = false, with the dispatch kernel's notify warps
+ * computing the layout before its copy epilogue writes recv_x, recv_topk_idx
+ * and recv_topk_weights). It produces everything ep_layout and
+ * ep_dispatch_compact produce, with the same arguments, meanings, checks and
+ * errors as those two calls (the dispatch reads this layout's dst_slot,
+ * recv_src_metadata and num_recv). When T*K fits one layout tile (the
+ * floor(W / K) tokens of ep_layout's dispatch_plan: a decode step, say) it
+ * runs as a single launch in which every workgroup ranks the entries and the
+ * received tokens itself and workgroup 0 writes the layout's outputs; larger
+ * batches run the launches of ep_layout and ep_dispatch_compact. Results are
+ * identical either way.
+ */
+int ep_layout_dispatch_compact(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
+                               int32_t num_experts, int32_t expert_alignment,
+                               int64_t capacity_rows, int32_t *counts, int32_t *offsets,
+                               int32_t *dst_slot, int32_t *recv_src_metadata, int32_t *num_recv,
+                               void *workspace, size_t workspace_bytes, const void *x,
+                               const float *x_scales, const float *topk_weights, int32_t hidden,
+                               int32_t dtype, void *recv_x, float *recv_scales,
+                               int32_t *recv_topk_idx, float *recv_topk_weights, void *stream);
+
+/*
  * Non-expand combine (DeepEP overall architecture: combine reduce epilogue
  * with bias, do_expand = false). The expert side returns one row per
  * received token with that token's experts already reduced, so in a world

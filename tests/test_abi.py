@@ -153,6 +153,31 @@ def test_layout_dispatch_rejections(L):
     assert "ep_layout_dispatch" in B.ep_last_error()
 
 
+def lay_disp_c(T=128, K=8, E=256, A=1, cap=1024, x=FAKE, xs=None, w=None, H=7168, dt=B.EP_BF16,
+               rx=FAKE, rs=None, ri=FAKE, rw=None):
+    return (FAKE, T, K, E, A, cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, x, xs, w, H, dt,
+            rx, rs, ri, rw)
+
+
+def test_layout_dispatch_compact_rejections(L):
+    """The fused non-expand call applies ep_layout's and ep_dispatch_compact's checks
+    (nothing is launched)."""
+    f = B.ep_layout_dispatch_compact
+    assert _code(f, *lay_disp_c(K=0)) == B.EP_EINVAL
+    assert _code(f, *lay_disp_c(E=1025)) == B.EP_EINVAL
+    assert _code(f, *lay_disp_c(cap=1023)) == B.EP_ECAPACITY
+    assert _code(f, *lay_disp_c(K=3, cap=1 << 20)) == B.EP_EUNSUPPORTED
+    assert _code(f, *lay_disp_c(H=7169)) == B.EP_EINVAL  # 14,338 bytes per row
+    assert _code(f, *lay_disp_c(dt=9)) == B.EP_EINVAL
+    assert _code(f, *lay_disp_c(xs=FAKE, rs=FAKE)) == B.EP_EINVAL  # scales with bf16 rows
+    assert _code(f, *lay_disp_c(dt=B.EP_FP8_E4M3, xs=FAKE)) == B.EP_EINVAL  # scales go together
+    assert _code(f, *lay_disp_c(x=ODD)) == B.EP_EINVAL
+    assert _code(f, *lay_disp_c(rx=None)) == B.EP_EINVAL
+    assert _code(f, *lay_disp_c(ri=None)) == B.EP_EINVAL
+    assert _code(f, *lay_disp_c(w=FAKE)) == B.EP_EINVAL  # weights without recv_topk_weights
+    assert "ep_layout_dispatch_compact" in B.ep_last_error()
+
+
 def comb(y=FAKE, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280, out=FAKE, bias=None):
     return (y, None, bias, dst, T, H, K, dt, cap, out)
 

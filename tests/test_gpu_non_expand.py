@@ -145,3 +145,82 @@ def test_round_trip_returns_x():
     got = to_host(out, np.uint16)
     recv = (ref["dst_slot"] >= 0).any(axis=1)
     assert np.array_equal(got[recv], case.x[recv]) and np.all(got[~recv] == 0)
+
+
+FUSED = [
+    # T, H, E, K, A, mask, dtype, scales, routing, workgroup cap: one tile runs layout and the
+    # non-expand dispatch as one launch; larger batches fall back to two launches
+    (128, 7168, 256, 8, 1, 0.0, I.BF16, False, "zipf", 0),       # the decode shape
+    (64, 256, 16, 2, 1, 0.2, I.BF16, False, "uniform", 0),       # tiny, with masking
+    (100, 7168, 256, 8, 128, 0.1, I.FP8_E4M3, True, "uniform", 0),
+    (100, 3584, 128, 8, 4, 0.05, I.FP4X2, True, "uniform", 0),
+    (50, 1024, 32, 4, 2, 0.2, I.FP32, False, "uniform", 0),
+    (170, 2048, 64, 6, 4, 0.1, I.BF16, False, "uniform", 0),     # 1020 entries, K = 6
+    (64, 512, 300, 8, 1, 0.0, I.BF16, False, "uniform", 0),      # 512-entry tile
+    (32, 512, 1024, 8, 3, 0.5, I.BF16, False, "uniform", 0),     # 256-entry tile
+    (1, 7168, 64, 8, 1, 0.0, I.BF16, False, "uniform", 0),       # one token
+    (128, 7168, 256, 8, 1, 0.1, I.BF16, False, "zipf", 3),       # capped
+    (3000, 2048, 256, 8, 16, 0.05, I.BF16, False, "uniform", 0),  # several tiles: two launches
+]
+
+
+@pytest.mark.parametrize("weights", [True, False])
+@pytest.mark.parametrize("T,H,E,K,A,mask,dtype,scales,routing,cap", FUSED)
+def test_layout_dispatch_compact(T, H, E, K, A, mask, dtype, scales, routing, cap, weights):
+    """ep_layout_dispatch_compact produces what ep_layout and ep_dispatch_compact produce."""
+    w = I.custom(f"nefused{T}_{E}_{K}", 9800 + T + E, T, H, E, K, A, dtype, routing,
+                 scales=scales)
+    _say(f"[layout + non-expand dispatch] {w} cap {cap} weights {weights}")
+    case = I.make_case(w, with_y=False, mask_frac=mask)
+    case.topk_idx[::7, 0] = w.E + 5  # ids outside [0, E) are masked like -1
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    n = ref["num_recv"]
+    idx_d, wts_d, x_d = to_dev(case.topk_idx), to_dev(case.topk_weights), to_dev(case.x)
+    xs_d = to_dev(case.x_scales) if case.x_scales is not None else None
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    dst = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+    meta = torch.full((T, K + 2), -7, dtype=torch.int32, device=DEV)
+    nrecv = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    wsb = B.ep_layout_workspace_bytes(T, K, E)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+    row_bytes = H * ELT[dtype]
+    recv_x = torch.full((T, row_bytes), 0x5A, dtype=torch.uint8, device=DEV)
+    recv_s = (torch.full((T, case.x_scales.shape[1]), -3.0, dtype=torch.float32, device=DEV)
+              if xs_d is not None else None)
+    recv_i = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
+    recv_w = torch.full((T, K), -5.0, dtype=torch.float32, device=DEV) if weights else None
+    s = torch.cuda.Stream()
+    try:
+        B.ep_set_workgroup_limit(s, cap)
+        with torch.cuda.stream(s):
+            B.ep_layout_dispatch_compact(idx_d, T, K, E, A, w.cap, counts, offsets, dst, meta,
+                                         nrecv, ws, wsb, x_d, xs_d, wts_d if weights else None,
+                                         H, dtype, recv_x, recv_s, recv_i, recv_w, s)
+        s.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        B.ep_set_workgroup_limit(s, 0)
+
+    got = layout_to_host({"counts": counts, "offsets": offsets, "dst_slot": dst, "meta": meta,
+                          "num_recv": nrecv})
+    for k in ("counts", "offsets", "dst_slot"):
+        assert np.array_equal(got[k], ref[k]), k
+    assert got["num_recv"] == n
+    assert np.array_equal(got["recv_src_metadata"], ref["recv_src_metadata"])
+    rx, rs, ri, rw = oracle.dispatch_compact(case.x, case.topk_idx, ref["dst_slot"],
+                                             ref["recv_src_metadata"], n, case.x_scales,
+                                             case.topk_weights if weights else None)
+    gx, gi = to_host(recv_x), to_host(recv_i)
+    assert np.array_equal(gx[:n], rx), "recv_x"
+    assert np.all(gx[n:] == 0x5A), "rows past num_recv were written"
+    assert np.array_equal(gi[:n], ri), "recv_topk_idx"
+    assert np.all(gi[n:] == -7)
+    if recv_s is not None:
+        gs = to_host(recv_s)
+        assert np.array_equal(gs[:n].view(np.uint8), rs), "recv_scales"
+        assert np.all(gs[n:] == -3.0)
+    if weights:
+        gw = to_host(recv_w)
+        assert np.array_equal(gw[:n].view(np.uint32), rw.view(np.uint32)), "recv_topk_weights"
+        assert np.all(gw[n:] == -5.0)
