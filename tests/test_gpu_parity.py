@@ -601,6 +601,68 @@ def test_graph_capture_replay(name):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("path", ["expand", "non-expand"])
+def test_graph_capture_replay_one_launch_calls(path):
+    """A decode step through the one-launch layout + dispatch calls (ep_layout_dispatch, or
+    ep_layout_dispatch_compact) and combine, captured into one HIP graph; every replay, with
+    eager steps in between, matches eager."""
+    w = I.WORKLOADS["decode_zipf"]
+    case = I.make_case(w)
+    dev = "cuda:0"
+    T, K, E, H = w.T, w.K, w.E, w.H
+    idx, wts, x = to_dev(case.topk_idx), to_dev(case.topk_weights), to_dev(case.x)
+    y = to_dev(case.y) if path == "expand" else to_dev(case.y[:T])
+    counts = torch.zeros(E, dtype=torch.int32, device=dev)
+    offs = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+    dst = torch.zeros((T, K), dtype=torch.int32, device=dev)
+    meta = torch.zeros((T, K + 2), dtype=torch.int32, device=dev)
+    nrecv = torch.zeros(1, dtype=torch.int32, device=dev)
+    wsb = B.ep_layout_workspace_bytes(T, K, E)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
+    rows = w.cap if path == "expand" else T
+    X = torch.zeros((rows, H), dtype=torch.int16, device=dev)
+    Xw = torch.zeros((rows,), dtype=torch.float32, device=dev)
+    recv_i = torch.zeros((T, K), dtype=torch.int32, device=dev)
+    recv_w = torch.zeros((T, K), dtype=torch.float32, device=dev)
+    out = torch.zeros((T, H), dtype=torch.int16, device=dev)
+
+    def step(stream):
+        if path == "expand":
+            B.ep_layout_dispatch(idx, T, K, E, w.A, w.cap, counts, offs, dst, meta, nrecv, ws, wsb,
+                                 x, None, wts, H, B.EP_BF16, X, None, Xw, stream)
+            B.ep_combine(y, wts, None, dst, T, H, K, B.EP_BF16, w.cap, out, stream)
+        else:
+            B.ep_layout_dispatch_compact(idx, T, K, E, w.A, w.cap, counts, offs, dst, meta, nrecv,
+                                         ws, wsb, x, None, wts, H, B.EP_BF16, X, None, recv_i,
+                                         recv_w, stream)
+            B.ep_combine_compact(y, None, dst, meta, nrecv, T, H, K, B.EP_BF16, out, stream)
+
+    step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    outs = (counts, offs, dst, meta, nrecv, X, Xw, recv_i, recv_w, out)
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for r in range(4):
+        for t in outs:
+            t.zero_()  # a fill kernel outside the graph, so every replay must rewrite everything
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), f"replay {r} differs from eager"
+        step(torch.cuda.current_stream())  # eager work between replays
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("T,H,E,K,A,dtype", [(4096, 256, 256, 8, 128, I.BF16),
                                               (700, 512, 64, 4, 16, I.FP8_E4M3),
                                               (300, 1024, 16, 2, 1, I.BF16)])
