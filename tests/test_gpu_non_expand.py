@@ -224,3 +224,21 @@ def test_layout_dispatch_compact(T, H, E, K, A, mask, dtype, scales, routing, ca
         gw = to_host(recv_w)
         assert np.array_equal(gw[:n].view(np.uint32), rw.view(np.uint32)), "recv_topk_weights"
         assert np.all(gw[n:] == -5.0)
+
+
+def test_layout_dispatch_compact_empty():
+    """No tokens: the layout's outputs are zero and no received row is written."""
+    E, K, H = 256, 8, 7168
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    nrecv = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    recv_x = torch.full((4, 2 * H), 0x5A, dtype=torch.uint8, device=DEV)
+    recv_i = torch.full((4, K), -7, dtype=torch.int32, device=DEV)
+    B.ep_layout_dispatch_compact(None, 0, K, E, 1, 0, counts, offsets, None, None, nrecv, ws,
+                                 B.ep_layout_workspace_bytes(0, K, E), None, None, None, H,
+                                 B.EP_BF16, recv_x, None, recv_i, None)
+    torch.cuda.synchronize()
+    assert np.all(to_host(counts) == 0) and np.all(to_host(offsets) == 0)
+    assert int(nrecv.item()) == 0
+    assert np.all(to_host(recv_x) == 0x5A) and np.all(to_host(recv_i) == -7)
