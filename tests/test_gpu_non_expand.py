@@ -191,6 +191,7 @@ def test_layout_dispatch_compact(T, H, E, K, A, mask, dtype, scales, routing, ca
     recv_i = torch.full((T, K), -7, dtype=torch.int32, device=DEV)
     recv_w = torch.full((T, K), -5.0, dtype=torch.float32, device=DEV) if weights else None
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())  # the inputs and buffers were written there
     try:
         B.ep_set_workgroup_limit(s, cap)
         with torch.cuda.stream(s):

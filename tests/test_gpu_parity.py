@@ -236,6 +236,7 @@ def test_slots_outside_capacity_are_skipped(T, H, K, wg_cap, do_combine):
     dc = DeviceCase(case, with_y=do_combine)
     dc.lay = {"dst_slot": to_dev(dst)}
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())  # the inputs and buffers were written there
     try:
         B.ep_set_workgroup_limit(s, wg_cap)
         with torch.cuda.stream(s):
@@ -279,6 +280,7 @@ def test_dispatch_plan(T, H, E, K, A, mask, wg_cap, dtype):
     ref = oracle.layout(case.topk_idx, w.E, w.A)
     dc = DeviceCase(case, with_y=False)
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())  # the inputs and buffers were written there
     try:
         B.ep_set_workgroup_limit(s, wg_cap)
         with torch.cuda.stream(s):
@@ -321,6 +323,7 @@ def test_layout_dispatch(T, H, E, K, A, mask, dtype, scales, routing, wg_cap):
     ref = oracle.layout(case.topk_idx, w.E, w.A)
     dc = DeviceCase(case, with_y=False)
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())  # the inputs and buffers were written there
     try:
         B.ep_set_workgroup_limit(s, wg_cap)
         with torch.cuda.stream(s):

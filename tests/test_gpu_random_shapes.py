@@ -149,6 +149,7 @@ def test_random_one_tile_layout_dispatch(seed):
     case.topk_idx[::11, 0] = w.E + 1  # some ids outside [0, E): masked
     dc = DeviceCase(case, with_y=False)
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())  # the inputs and buffers were written there
     try:
         B.ep_set_workgroup_limit(s, c["cap"])
         with torch.cuda.stream(s):
