@@ -309,8 +309,16 @@ FUSED = [
     (64, 512, 300, 8, 1, 0.0, I.BF16, False, "uniform", 0),      # 512-entry tile
     (32, 512, 1024, 8, 3, 0.1, I.BF16, False, "uniform", 0),     # 256-entry tile
     (128, 7168, 256, 8, 1, 0.1, I.BF16, False, "zipf", 3),       # capped
-    (4096, 7168, 256, 8, 128, 0.02, I.BF16, False, "uniform", 0),  # several tiles: two launches
-    (300, 1024, 64, 8, 1, 0.0, I.BF16, False, "uniform", 0),     # 2400 entries: two launches
+    (4096, 7168, 256, 8, 128, 0.02, I.BF16, False, "uniform", 0),  # 32K entries: two launches
+    (300, 1024, 64, 8, 1, 0.0, I.BF16, False, "uniform", 0),     # 3 tiles: two launches
+    (1024, 7168, 64, 8, 1, 0.0, I.BF16, False, "uniform", 0),    # the MORI default shape, 8 tiles
+    (2048, 7168, 256, 8, 128, 0.1, I.FP8_E4M3, True, "uniform", 0),  # 16 tiles, scale rows
+    (1000, 3584, 128, 8, 4, 0.05, I.FP4X2, True, "uniform", 0),
+    (700, 1024, 32, 4, 2, 0.2, I.FP32, False, "uniform", 0),
+    (2700, 512, 64, 6, 4, 0.1, I.BF16, False, "uniform", 0),     # 16,200 entries, K = 6
+    (900, 512, 300, 8, 1, 0.3, I.BF16, False, "uniform", 0),     # 512-entry tiles
+    (1500, 512, 1024, 8, 3, 0.1, I.BF16, False, "uniform", 0),   # 256-entry tiles: 47 tiles
+    (1024, 7168, 64, 8, 1, 0.1, I.BF16, False, "uniform", 7),    # capped
 ]
 
 
@@ -341,6 +349,8 @@ def test_layout_dispatch(T, H, E, K, A, mask, dtype, scales, routing, wg_cap):
     (100, 7168, 256, 8, I.FP8_E4M3, True),  # scale rows travel, weights do not
     (3, 512, 16, 1, I.BF16, False),         # 3 units for thousands of waves
     (1, 7168, 64, 8, I.BF16, False),        # one token
+    (1024, 7168, 64, 8, I.BF16, False),     # 8 tiles: two launches
+    (2048, 7168, 256, 8, I.FP8_E4M3, True),  # 16 tiles, scale rows
 ])
 def test_layout_dispatch_without_weights(T, H, E, K, dtype, scales):
     """Without router weights to forward the expand weights stay untouched."""
