@@ -10,6 +10,10 @@ C ABI on torch's current stream. Default workload: 4096 tokens, hidden 7168,
 --path non-expand times the other layout mode instead: ep_layout,
 ep_dispatch_compact (one row per received token, with its expert ids and
 router weights) and ep_combine_compact (rows back to token order).
+A batch that fits one layout tile (a decode step) calls ep_layout_dispatch
+(ep_layout_dispatch_compact) instead of the first two calls: one launch;
+--no-fused keeps them apart. Batches of at least 256 MiB of expand rows ask
+the layout for the dispatch plan and dispatch by it (--no-plan: token-major).
 --cold rotates several complete sets of buffers (expert outputs, expand /
 receive buffers, out), enough that at least 512 MB of other traffic separates
 two uses of a set, and separately enough copies of x (with its scale rows)
