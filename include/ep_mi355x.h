@@ -12,6 +12,13 @@
  *                weight them by the router weights, sum in binary32 in k
  *                order, store in the rows' type
  *
+ * and around them: ep_layout_dispatch (layout + dispatch in one launch for a
+ * one-tile batch), the non-expand mode (ep_dispatch_compact,
+ * ep_combine_compact, ep_layout_dispatch_compact: one row per received
+ * token), ep_zero_padding (zero the alignment rows), the CU-limited mode
+ * (ep_set_workgroup_limit / ep_get_workgroup_limit) and the helpers
+ * ep_layout_workspace_bytes, ep_supported and ep_last_error.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All array arguments are DEVICE pointers owned by the caller; the library
