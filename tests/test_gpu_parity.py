@@ -463,6 +463,60 @@ def test_combine_hand_worked_on_gpu():
         assert np.all(got[:, exp.shape[1]:] == 0)
 
 
+def _golden_combine_case(c, fp32):
+    """Rows, slots, weights and expected output of one hand-worked combine case."""
+    if fp32:
+        return (np.array(c["y_rows"], np.float32), np.array(c["dst_slot"], np.int32),
+                None if c["topk_weights"] is None else np.array(c["topk_weights"], np.float32),
+                np.array(c["out"], np.float32))
+    hx = lambda rows: np.array([[int(v, 16) for v in r] for r in rows], np.uint16)  # noqa: E731
+    return (hx(c["y_rows_hex"]), np.array(c["dst_slot"], np.int32),
+            None if c["topk_weights"] is None else np.array(c["topk_weights"], np.float32),
+            hx(c["out_hex"]))
+
+
+@pytest.mark.parametrize("T,wg_cap", [(5, 0), (1024, 0), (1030, 64)],
+                         ids=["sliced_gather", "row_stream", "capped_gather"])
+@pytest.mark.parametrize("fp32", [False, True], ids=["bf16", "fp32"])
+def test_combine_hand_worked_every_kernel(T, wg_cap, fp32):
+    """Every hand-worked combine case (k order, product rounded before the add,
+    ties, masking, unit weights) through each combine kernel at hidden 7168:
+    a case's channels are repeated across the row and its tokens over T tokens,
+    so 5 tokens take the sliced gather, 1024 the row stream and a capped stream
+    the gather in 1024-thread workgroups. Expected values are the hand-worked
+    ones, bit for bit (both types)."""
+    data = json.load(open(os.path.join(GOLDEN, "combine_worked_examples.json")))
+    H, dtype = 7168, (B.EP_FP32 if fp32 else B.EP_BF16)
+    s = torch.cuda.Stream()
+    try:
+        B.ep_set_workgroup_limit(s, wg_cap)
+        for c in data["combine_f32" if fp32 else "combine"]:
+            rows0, dst0, w0, exp0 = _golden_combine_case(c, fp32)
+            while not B.ep_supported(2, H, dst0.shape[1], dtype):  # pad with masked entries
+                dst0 = np.concatenate([dst0, np.full((dst0.shape[0], 1), -1, np.int32)], axis=1)
+                if w0 is not None:
+                    w0 = np.concatenate([w0, np.zeros((w0.shape[0], 1), np.float32)], axis=1)
+            reps = H // rows0.shape[1]
+            rows = np.tile(rows0, (1, reps))
+            tok = np.arange(T) % dst0.shape[0]  # token t repeats hand-worked token t mod T0
+            dst, K = dst0[tok], dst0.shape[1]
+            wts = None if w0 is None else to_dev(w0[tok])
+            _say(f"[golden combine] {c['name']} T={T} K={K} cap={wg_cap} fp32={fp32}")
+            out = (torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda:0") if fp32
+                   else torch.full((T, H), 0x7FC1, dtype=torch.int16, device="cuda:0"))
+            y_d, dst_d = to_dev(rows), to_dev(dst)
+            torch.cuda.synchronize()  # buffers were filled on the default stream
+            B.ep_combine(y_d, wts, None, dst_d, T, H, K, dtype, rows.shape[0], out, s)
+            s.synchronize()
+            got = to_host(out).view(np.uint32) if fp32 else to_host(out, np.uint16)
+            exp = np.tile(exp0, (1, reps))[tok]
+            exp = exp.view(np.uint32) if fp32 else exp
+            assert np.array_equal(got, exp), c["name"]
+    finally:
+        torch.cuda.synchronize()
+        B.ep_set_workgroup_limit(s, 0)
+
+
 def test_combine_rounding_ties_and_specials():
     """Sums that land exactly on bf16 ties, overflow, infinities and NaNs."""
     H, T, K = 1024, 64, 2

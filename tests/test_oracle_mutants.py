@@ -65,6 +65,13 @@ MUTANTS = {
                           "recv_topk_idx[(int64_t)i * K + k] = topk_idx[tk];"),
     "compact_combine_unreceived_kept": ("    int32_t i = any ? row_of[t] : -1;", "    int32_t i = row_of[t] >= 0 ? row_of[t] : 0;"),
     "compact_combine_bias_dropped": ("        acc = acc + bf16_bits_to_float(bias[(int64_t)t * H + h]);\n", ""),
+    "combine_reverse_k": ("      for (int32_t k = 0; k < K; ++k) {\n        if (d[k] < 0) continue;\n        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float v",
+                          "      for (int32_t k = K - 1; k >= 0; --k) {\n        if (d[k] < 0) continue;\n        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float v"),
+    "combine_f32_reverse_k": ("      for (int32_t k = 0; k < K; ++k) {\n        if (d[k] < 0) continue;\n        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod",
+                              "      for (int32_t k = K - 1; k >= 0; --k) {\n        if (d[k] < 0) continue;\n        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod"),
+    "combine_fma": ("        float prod = w * v;\n        acc = acc + prod;", "        acc = __builtin_fmaf(w, v, acc);"),
+    "combine_f32_fma": ("        float prod = w * y[(int64_t)d[k] * H + h];\n        acc = acc + prod;",
+                        "        acc = __builtin_fmaf(w, y[(int64_t)d[k] * H + h], acc);"),
     "combine_f32_weight_k0": ("        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod",
                               "        float w = topk_weights ? topk_weights[(int64_t)t * K] : 1.0f;\n        float prod"),
 }
