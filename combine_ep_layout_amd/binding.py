@@ -29,12 +29,13 @@ EP_FP4X2 = 3
 
 EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 64
+EP_LAYOUT_SCRATCH_BYTES = 8 << 20
 
 SYMBOLS = ("ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_dispatch",
            "ep_combine",
            "ep_dispatch_compact", "ep_layout_dispatch_compact", "ep_combine_compact",
            "ep_zero_padding", "ep_set_workgroup_limit",
-           "ep_get_workgroup_limit", "ep_last_error", "ep_supported")
+           "ep_get_workgroup_limit", "ep_last_error", "ep_supported", "ep_layout_noalloc")
 
 
 class EpError(RuntimeError):
@@ -68,6 +69,9 @@ def lib(path: str = None) -> ctypes.CDLL:
     L.ep_layout.argtypes = [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
                             _vp]
     L.ep_layout.restype = ctypes.c_int
+    L.ep_layout_noalloc.argtypes = [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp]
+    L.ep_layout_noalloc.restype = ctypes.c_int
     L.ep_dispatch.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
                               _vp]
     L.ep_dispatch.restype = ctypes.c_int
@@ -142,6 +146,15 @@ def ep_layout(topk_idx, num_tokens, topk, num_experts, expert_alignment, capacit
                            capacity_rows, _p(counts), _p(offsets), _p(dst_slot),
                            _p(recv_src_metadata), _p(num_recv), _p(workspace),
                            workspace_bytes, _p(dispatch_plan), _s(stream)))
+
+
+def ep_layout_noalloc(topk_idx, num_tokens, topk, num_experts, expert_alignment, capacity_rows,
+                      counts, offsets, dst_slot, recv_src_metadata, num_recv, stream=None,
+                      dispatch_plan=None):
+    _check(lib().ep_layout_noalloc(_p(topk_idx), num_tokens, topk, num_experts, expert_alignment,
+                                   capacity_rows, _p(counts), _p(offsets), _p(dst_slot),
+                                   _p(recv_src_metadata), _p(num_recv), _p(dispatch_plan),
+                                   _s(stream)))
 
 
 def ep_dispatch(x, x_scales, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,

@@ -293,6 +293,55 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
   }
 }
 
+int ep_layout_noalloc(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
+                      int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
+                      int32_t *counts, int32_t *offsets, int32_t *dst_slot,
+                      int32_t *recv_src_metadata, int32_t *num_recv, int32_t *dispatch_plan,
+                      void *stream) {
+  try {
+    const char *what = "ep_layout_noalloc";
+    if (int rc = check_topk(what, num_tokens, topk)) return rc;
+    if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
+      return fail(EP_EINVAL, "%s: num_experts must be in 1..%d (got %d)", what, EP_MAX_EXPERTS,
+                  num_experts);
+    const size_t need = ep::layout_workspace(num_tokens, topk, num_experts);
+    if (need > (size_t)EP_LAYOUT_SCRATCH_BYTES)
+      return fail(EP_EINVAL,
+                  "%s: %d tokens x top-%d over %d experts need %zu bytes of layout scratch, "
+                  "above the fixed %zu (use ep_layout with a workspace)",
+                  what, num_tokens, topk, num_experts, need, (size_t)EP_LAYOUT_SCRATCH_BYTES);
+    void *scratch = nullptr;
+    if (need > 0) {  // the arguments are checked in full below, before any launch
+      int dev = -1, stream_dev = -1;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipStreamGetDevice((hipStream_t)stream, &stream_dev);
+      if (e != hipSuccess)
+        return fail(EP_EHIP, "%s: cannot read the current device: %s", what, hipGetErrorString(e));
+      if (stream_dev != dev)
+        return fail(EP_EINVAL, "%s: the stream belongs to device %d, the current device is %d",
+                    what, stream_dev, dev);
+      e = ep::layout_scratch(dev, &scratch);
+      if (e != hipSuccess)
+        return fail(EP_EHIP, "%s: cannot resolve device %d's layout scratch: %s", what, dev,
+                    hipGetErrorString(e));
+    }
+    if (int rc = check_layout(what, topk_idx, num_tokens, topk, num_experts, expert_alignment,
+                              capacity_rows, counts, offsets, dst_slot, recv_src_metadata,
+                              num_recv, scratch, need))
+      return rc;
+    if (!aligned(dispatch_plan, 8))
+      return fail(EP_EINVAL, "%s: dispatch_plan must be 8-byte aligned", what);
+    ep::LayoutArgs a{topk_idx, num_tokens, topk, num_experts, expert_alignment, counts, offsets,
+                     dst_slot, recv_src_metadata, num_recv, scratch, dispatch_plan,
+                     (hipStream_t)stream};
+    return from_launch(ep::launch_layout(a), what);
+  } catch (const std::exception &e) {
+    return fail(EP_EHIP, "ep_layout_noalloc: %s", e.what());
+  } catch (...) {
+    return fail(EP_EHIP, "ep_layout_noalloc: unknown exception");
+  }
+}
+
 int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
                 const int32_t *dst_slot, int32_t num_tokens, int32_t hidden, int32_t topk,
                 int32_t dtype, int64_t capacity_rows, void *expand_x, float *expand_scales,

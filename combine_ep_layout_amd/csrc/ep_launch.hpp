@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ep_mi355x.h"
+
 // The compiled shape set. Shapes are template constants of the kernels, so
 // loops over a row and over k unroll completely; anything outside these
 // lists is rejected by the capability gate in the C ABI.
@@ -146,6 +148,10 @@ inline int launch_status() {
 // launch, -2 if the shape has no compiled kernel.
 int launch_layout(const LayoutArgs &a);
 size_t layout_workspace(int T, int K, int E);
+// Device address of `device`'s copy of the library's fixed layout scratch
+// (EP_LAYOUT_SCRATCH_BYTES), resolved on the first call for that device; the
+// device must be current. Used by ep_layout_noalloc in place of a workspace.
+hipError_t layout_scratch(int device, void **ptr);
 int launch_dispatch(const DispatchArgs &a);
 // Layout and dispatch in one launch when T*K fits one layout tile; -3 when it
 // does not (the caller then launches them separately). Row and scale-row

@@ -30,6 +30,7 @@
 // On request the last launch also writes the dispatch plan: each tile's
 // entries in slot order, the order in which dispatch writes expand rows
 // fastest (write_plan).
+#include <mutex>
 #include <type_traits>
 
 #include "ep_device.hpp"
@@ -983,6 +984,40 @@ int launch_layout_dispatch_compact(const LayoutArgs &l, const CompactDispatchArg
 
 size_t layout_workspace(int T, int K, int E) {
   switch (K) { EP_FOR_EACH_TOPK(EP_WS_CASE) default: return 0; }
+}
+
+}  // namespace ep
+
+// Fixed device scratch for ep_layout_noalloc: the workspace of the many-tile
+// launches (per-tile histograms, received-token counts and tile-scan
+// prefixes) for callers that cannot allocate one. Every GPU holds its own
+// copy for the life of the process; every call on one GPU shares it, so two
+// such calls in flight on one GPU at once race. Nothing in it needs to start
+// at zero: each launch writes every word it later reads.
+static __device__ __align__(256) unsigned char scratch[EP_LAYOUT_SCRATCH_BYTES];
+
+namespace ep {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (guarded)
+}  // namespace
+
+// Device address of the current device's `scratch`, looked up on the first
+// call on each device, with that device current. The host-side name of the
+// array is only a registration handle: kernels must be given this address.
+hipError_t layout_scratch(int device, void **ptr) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 }  // namespace ep

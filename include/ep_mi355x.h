@@ -17,7 +17,8 @@
  * ep_combine_compact, ep_layout_dispatch_compact: one row per received
  * token), ep_zero_padding (zero the alignment rows), the CU-limited mode
  * (ep_set_workgroup_limit / ep_get_workgroup_limit) and the helpers
- * ep_layout_workspace_bytes, ep_supported and ep_last_error.
+ * ep_layout_workspace_bytes, ep_supported and ep_last_error; ep_layout_noalloc
+ * runs ep_layout on a fixed scratch array for callers that cannot allocate.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -141,6 +142,42 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
               int32_t *offsets, int32_t *dst_slot, int32_t *recv_src_metadata,
               int32_t *num_recv, void *workspace, size_t workspace_bytes,
               int32_t *dispatch_plan, void *stream);
+
+/*
+ * Bytes of the library's fixed layout scratch, one copy per GPU (8 MiB):
+ * the largest ep_layout_workspace_bytes() that ep_layout_noalloc accepts. It
+ * covers batches of up to 4,176,896 (token, k) entries at 256 experts
+ * (522,112 tokens at top-8), 1,046,016 at 512 and 261,632 at 1024; batches
+ * of at most 2^14 entries need no scratch at all.
+ */
+#define EP_LAYOUT_SCRATCH_BYTES 8388608 /* 8 MiB */
+
+/*
+ * ep_layout without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, outputs, checks and errors as
+ * ep_layout; the workspace is instead a fixed device array of
+ * EP_LAYOUT_SCRATCH_BYTES inside the library, one copy per GPU, kept until
+ * the process ends. The call allocates nothing: on the first call on a GPU it
+ * looks up that GPU's copy (with the GPU current), then only enqueues kernels.
+ *
+ * Extra rules:
+ * - `stream` must belong to the current device (EP_EINVAL otherwise).
+ * - ep_layout_workspace_bytes(num_tokens, topk, num_experts) must not exceed
+ *   EP_LAYOUT_SCRATCH_BYTES (EP_EINVAL, with the sizes in the message).
+ * - Every call on one GPU shares that GPU's scratch and nothing in it is
+ *   cleared between calls (no word needs to start at zero): two calls in
+ *   flight at once on one GPU (on different streams, or overlapping graph
+ *   replays) race and may return wrong results. Calls on one stream are
+ *   ordered and safe.
+ * - The first call on a GPU fails with EP_EHIP if the runtime cannot resolve
+ *   the scratch address; a failed lookup is retried on the next call.
+ */
+int ep_layout_noalloc(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
+                      int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
+                      int32_t *counts, int32_t *offsets, int32_t *dst_slot,
+                      int32_t *recv_src_metadata, int32_t *num_recv, int32_t *dispatch_plan,
+                      void *stream);
 
 /*
  * Dispatch in the expand layout (DeepEP overall architecture, dispatch copy

@@ -241,3 +241,19 @@ def test_workgroup_limit_host_side(L):
     B.ep_set_workgroup_limit(FAKE, 0)  # clearing a cap that was never set is fine
     assert B.ep_get_workgroup_limit(FAKE) == 0
     assert B.ep_get_workgroup_limit(None) == 0
+
+
+def test_layout_noalloc_host_rejections(L):
+    """Checks that ep_layout_noalloc makes before touching any device."""
+    def na(T=64, K=2, E=16, A=1, cap=128, idx=FAKE, counts=FAKE):
+        return (idx, T, K, E, A, cap, counts, FAKE, FAKE, FAKE, FAKE)
+    assert _code(B.ep_layout_noalloc, *na(T=-1)) == B.EP_EINVAL
+    assert _code(B.ep_layout_noalloc, *na(K=65)) == B.EP_EINVAL
+    assert _code(B.ep_layout_noalloc, *na(E=1025)) == B.EP_EINVAL
+    assert _code(B.ep_layout_noalloc, *na(cap=127)) == B.EP_ECAPACITY  # one tile: no scratch
+    assert _code(B.ep_layout_noalloc, *na(counts=None)) == B.EP_EINVAL
+    T, K, E = 40000, 8, 1024  # 10 MB of workspace, above the fixed 8 MiB
+    assert B.ep_layout_workspace_bytes(T, K, E) > B.EP_LAYOUT_SCRATCH_BYTES
+    with pytest.raises(B.EpError) as ei:
+        B.ep_layout_noalloc(*na(T=T, K=K, E=E, cap=T * K))
+    assert ei.value.code == B.EP_EINVAL and "scratch" in str(ei.value)
