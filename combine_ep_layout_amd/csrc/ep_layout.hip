@@ -30,6 +30,7 @@
 // On request the last launch also writes the dispatch plan: each tile's
 // entries in slot order, the order in which dispatch writes expand rows
 // fastest (write_plan).
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -278,6 +279,88 @@ __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
   if (plan != nullptr) write_plan<K>(0, T, r.e, r.rank, slot, s_tb, nvalid, plan);
 }
 
+// Copies one (entry j, 1 KiB slice) unit of the fused layout + dispatch
+// launch to expand row d; slice 0 also carries the scale row and the weight.
+// v is the lane's chunk of the row slice, already loaded.
+template <bool WIDE>
+__device__ __forceinline__ void copy_unit(const u32x4 &v, int64_t t, int j, int slice, int d,
+                                          int row_chunks, const u32x4 *__restrict__ x_scales,
+                                          int scale_chunks, const float *__restrict__ topk_weights,
+                                          u32x4 *__restrict__ expand_x,
+                                          u32x4 *__restrict__ expand_scales,
+                                          float *__restrict__ expand_weights) {
+  const int lane = lane_id();
+  const int c = slice * kWave + lane;
+  if (c < row_chunks)
+    store_row<WIDE ? RowStore::kNtDevice : RowStore::kNt>(
+        v, expand_x + (int64_t)d * row_chunks, row_chunks * 16, c * 16);
+  if (slice == 0) {
+    if (x_scales != nullptr)
+      for (int q = lane; q < scale_chunks; q += kWave)
+        __builtin_nontemporal_store(x_scales[t * scale_chunks + q],
+                                    expand_scales + (int64_t)d * scale_chunks + q);
+    if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[j];
+  }
+}
+
+// The copy workgroups of the fused launch when expert_alignment is 1
+// (COUNTED): no ranking at all. Without alignment padding an entry's slot is
+// the number of unmasked entries whose key (expert id, entry index) is
+// smaller than its own: the entries of lower experts (the expert's offset)
+// plus the earlier entries of its own expert (its rank). The workgroup
+// stages the T*K keys in LDS once (a masked entry gets the largest key);
+// each lane then holds 16 of them, and a wave counts, for each entry it
+// copies, the keys below that entry's key and sums the count over the wave.
+// The wave's first row slice is loaded before the keys are staged, so the
+// two load latencies overlap. Workgroup 0 writes the layout's outputs and
+// copies nothing; workgroups 1.. share the (entry, slice) units.
+template <int K, bool WIDE>
+__device__ __forceinline__ void copy_counted(
+    const int32_t *__restrict__ topk_idx, int T, int E, const u32x4 *__restrict__ x,
+    int row_chunks, const u32x4 *__restrict__ x_scales, int scale_chunks,
+    const float *__restrict__ topk_weights, int64_t capacity, u32x4 *__restrict__ expand_x,
+    u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights) {
+  constexpr int kNoKey = 0x7fffffff;
+  int *s_key = (int *)g_smem;  // kThreads keys
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n = T * K;  // <= kThreads (one tile)
+  const int slices = (row_chunks + kWave - 1) / kWave;
+  const int64_t units = (int64_t)n * slices;
+  const int64_t stride = (int64_t)(gridDim.x - 1) * kWavesMax;
+  int64_t u = (int64_t)(blockIdx.x - 1) * kWavesMax + wave;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (u < units) {
+    const int j = (int)(u / slices);
+    const int c = (int)(u - (int64_t)j * slices) * kWave + lane;
+    if (c < row_chunks) v = x[(int64_t)(j / K) * row_chunks + c];
+  }
+  const int id = tid < n ? topk_idx[tid] : -1;
+  s_key[tid] = (id >= 0 && id < E) ? (id << kRankBits) | tid : kNoKey;
+  __syncthreads();
+  int key[kWavesMax];  // entries q * 64 + lane
+#pragma unroll
+  for (int q = 0; q < kWavesMax; ++q) key[q] = s_key[q * kWave + lane];
+  for (bool first = true; u < units; u += stride, first = false) {
+    const int j = (int)(u / slices);
+    const int slice = (int)(u - (int64_t)j * slices);
+    const int kj = __builtin_amdgcn_readfirstlane(s_key[j]);
+    if (kj == kNoKey) continue;  // masked: no slot
+    int below = 0;
+#pragma unroll
+    for (int q = 0; q < kWavesMax; ++q) below += key[q] < kj ? 1 : 0;
+    const int d = __builtin_amdgcn_readfirstlane(wave_sum(below));
+    if (d >= capacity) continue;
+    const int64_t t = j / K;
+    if (!first) {
+      const int c = slice * kWave + lane;
+      if (c < row_chunks) v = x[t * row_chunks + c];
+    }
+    copy_unit<WIDE>(v, t, j, slice, d, row_chunks, x_scales, scale_chunks, topk_weights,
+                    expand_x, expand_scales, expand_weights);
+  }
+}
+
 // Layout and dispatch in one launch for a batch that fits one tile (a
 // decode step, say), after the dispatch kernels of the DeepEP page, whose
 // notify warps compute the slots inside dispatch. Every workgroup ranks all
@@ -286,10 +369,13 @@ __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
 // its share of (entry, 1 KiB slice) units token-major, with the slots read
 // from its own LDS. The ranking is repeated per workgroup, a few microseconds
 // of LDS work in parallel. That costs less than a second launch and the
-// round trip of dst_slot through memory. Row and scale-row widths are run-time
-// values (16-byte chunks). WIDE: launched uncapped, which selects the device-
-// scope non-temporal row store, as ep_dispatch_expand uses.
-template <int K, int NW, bool WIDE>
+// round trip of dst_slot through memory. COUNTED (expert_alignment 1,
+// uncapped): only workgroup 0 ranks, to write the layout's outputs, and the
+// other workgroups find their entries' slots by counting keys
+// (copy_counted). Row and scale-row widths are run-time values (16-byte
+// chunks). WIDE: launched uncapped, which selects the device-scope
+// non-temporal row store, as ep_dispatch_expand uses.
+template <int K, int NW, bool WIDE, bool COUNTED>
 __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
@@ -297,6 +383,11 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
     const u32x4 *__restrict__ x_scales, int scale_chunks, const float *__restrict__ topk_weights,
     int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
     float *__restrict__ expand_weights) {
+  if (COUNTED && blockIdx.x != 0) {
+    copy_counted<K, WIDE>(topk_idx, T, E, x, row_chunks, x_scales, scale_chunks, topk_weights,
+                          capacity, expand_x, expand_scales, expand_weights);
+    return;
+  }
   __shared__ int s_scan[kWavesMax];
   __shared__ int s_flag[kWavesMax];
   const RankLds s = rank_lds(E, NW);
@@ -328,8 +419,9 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
   }
   __syncthreads();  // publishes s_off (and in workgroup 0 the receive rows)
   const int slot = r.e >= 0 ? s_off[r.e] + r.rank : -1;
-  s_slot[tid] = slot;
   if (blockIdx.x == 0) write_slots_and_meta<K>(0, T, slot, s.tok, dst_slot, meta);
+  if (COUNTED) return;  // workgroup 0 copies nothing
+  s_slot[tid] = slot;
   __syncthreads();  // publishes s_slot
 
   const int lane = lane_id();
@@ -344,16 +436,10 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
     if (d < 0 || d >= capacity) continue;
     const int64_t t = j / K;
     const int c = slice * kWave + lane;
-    if (c < row_chunks)
-      store_row<WIDE ? RowStore::kNtDevice : RowStore::kNt>(
-          x[t * row_chunks + c], expand_x + (int64_t)d * row_chunks, row_chunks * 16, c * 16);
-    if (slice == 0) {
-      if (x_scales != nullptr)
-        for (int q = lane; q < scale_chunks; q += kWave)
-          __builtin_nontemporal_store(x_scales[t * scale_chunks + q],
-                                      expand_scales + (int64_t)d * scale_chunks + q);
-      if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[j];
-    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (c < row_chunks) v = x[t * row_chunks + c];
+    copy_unit<WIDE>(v, t, j, slice, d, row_chunks, x_scales, scale_chunks, topk_weights,
+                    expand_x, expand_scales, expand_weights);
   }
 }
 
@@ -879,16 +965,18 @@ int layout_dispatch_impl(const LayoutArgs &l, const DispatchArgs &d, int row_chu
   if (blocks < 1) blocks = 1;
   const size_t shm = rank_lds_bytes(l.E, NW) + sizeof(int) * ((size_t)l.E + kThreads);
   const bool fwd_w = d.topk_weights != nullptr && d.expand_weights != nullptr;
-  auto go = [&](auto wide) {
-    ep_layout_dispatch_tile<K, NW, decltype(wide)::value>
-        <<<(unsigned)blocks, kThreads, shm, l.stream>>>(
+  auto go = [&](auto wide, auto counted, int64_t grid) {
+    ep_layout_dispatch_tile<K, NW, decltype(wide)::value, decltype(counted)::value>
+        <<<(unsigned)grid, kThreads, shm, l.stream>>>(
             l.topk_idx, l.T, l.E, l.A, l.counts, l.offsets, l.dst_slot, l.meta, l.num_recv,
             (const u32x4 *)d.x, row_chunks, (const u32x4 *)d.x_scales, scale_chunks,
             d.topk_weights, d.capacity, (u32x4 *)d.expand_x, (u32x4 *)d.expand_scales,
             fwd_w ? d.expand_weights : nullptr);
   };
-  if (cap > 0) go(std::false_type{});
-  else go(std::true_type{});
+  if (cap > 0) go(std::false_type{}, std::false_type{}, blocks);
+  else if (l.A == 1)  // workgroup 0 lays out, the others copy
+    go(std::true_type{}, std::true_type{}, (units > 0 ? std::min<int64_t>(blocks, kFusedDispatchMaxBlocks - 1) : 0) + 1);
+  else go(std::true_type{}, std::false_type{}, blocks);
   return launch_status();
 }
 

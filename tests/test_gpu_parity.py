@@ -319,6 +319,16 @@ FUSED = [
     (900, 512, 300, 8, 1, 0.3, I.BF16, False, "uniform", 0),     # 512-entry tiles
     (1500, 512, 1024, 8, 3, 0.1, I.BF16, False, "uniform", 0),   # 256-entry tiles: 47 tiles
     (1024, 7168, 64, 8, 1, 0.1, I.BF16, False, "uniform", 7),    # capped
+    # expert_alignment 1, uncapped: the copy workgroups count keys instead of ranking
+    (128, 7168, 256, 8, 1, 0.3, I.BF16, False, "zipf", 0),       # decode shape, masked entries
+    (100, 7168, 256, 8, 1, 0.1, I.FP8_E4M3, True, "uniform", 0),  # scale rows
+    (100, 3584, 128, 8, 1, 0.05, I.FP4X2, True, "uniform", 0),
+    (170, 2048, 64, 6, 1, 0.2, I.BF16, False, "uniform", 0),     # 1020 entries, K = 6
+    (50, 1024, 32, 4, 1, 0.5, I.FP32, False, "uniform", 0),
+    (64, 512, 300, 8, 1, 0.2, I.BF16, False, "uniform", 0),      # 512-entry tile, masked
+    (32, 512, 1024, 8, 1, 0.1, I.BF16, False, "uniform", 0),     # 256-entry tile
+    (1, 7168, 16, 2, 1, 0.0, I.BF16, False, "uniform", 0),       # one token
+    (3, 256, 16, 1, 1, 0.0, I.BF16, False, "uniform", 0),        # 3 units, K = 1
 ]
 
 
@@ -409,6 +419,23 @@ def test_out_of_range_and_duplicate_ids():
     check_layout(layout_to_host(dc.lay), ref)
     check_dispatch(dc, ref["dst_slot"])
     check_combine(to_host(out, np.uint16), oracle.combine(case.y, ref["dst_slot"], case.topk_weights))
+
+
+@pytest.mark.parametrize("A", [1, 3])
+def test_layout_dispatch_out_of_range_and_duplicate_ids(A):
+    """The one-launch layout + dispatch with negative, out-of-range and repeated expert
+    ids in one tile (alignment 1: the copy workgroups count keys; 3: they rank)."""
+    T, H, E, K = 200, 256, 12, 4
+    idx = np.random.default_rng(19).integers(-3, E + 4, (T, K)).astype(np.int32)
+    w = I.custom(f"odd_fused{A}", 78, T, H, E, K, A)
+    case = I.make_case(w, with_y=False)
+    case.topk_idx = idx
+    ref = oracle.layout(idx, E, A)
+    dc = DeviceCase(case, with_y=False)
+    dc.layout_dispatch()
+    torch.cuda.synchronize()
+    check_layout(layout_to_host(dc.lay), ref)
+    check_dispatch(dc, ref["dst_slot"])
 
 
 def test_identity_expert_round_trip_full_size():
