@@ -14,15 +14,19 @@ A batch that fits one layout tile (a decode step) calls ep_layout_dispatch
 (ep_layout_dispatch_compact) instead of the first two calls: one launch;
 --no-fused keeps them apart. Batches of at least 256 MiB of expand rows ask
 the layout for the dispatch plan and dispatch by it (--no-plan: token-major).
---cold rotates several complete sets of buffers (expert outputs, expand /
-receive buffers, out), enough that at least 512 MB of other traffic separates
-two uses of a set, and separately enough copies of x (with its scale rows)
-that at least 512 MB of other x reads separate two uses of a copy. Only
-ordinary loads fill the 256 MB last-level cache (MALL); the rest of the
-step's traffic is non-temporal and leaves it alone. So rotating x among its
-own copies is what makes each step find x in HBM rather than in the MALL.
-Nothing but steps runs in the timed loop. Every run also times torch's copy_ of 1 GiB (16-byte
-vector loads and stores) and reports the path as a fraction of that copy.
+Each run times two cache modes (--cache both, the default; --cache warm or
+--cache cold, or --cold, times one). Warm: steps back to back on one buffer
+set, so x, read by the step before, is still in the 256 MB last-level cache
+(MALL), as when the router GEMM has just touched it. Cold: the step rotates
+several complete sets of buffers (expert outputs, expand / receive buffers,
+out), enough that at least 512 MB of other traffic separates two uses of a
+set, and separately enough copies of x (with its scale rows) that at least
+512 MB of other x reads separate two uses of a copy. Only ordinary loads fill
+the MALL; the rest of the step's traffic is non-temporal and leaves it alone,
+so rotating x among its own copies is what makes each step find x in HBM.
+Nothing but steps runs in the timed loop. Every run also times torch's copy_
+of 1 GiB (16-byte vector loads and stores) and reports the path as a
+fraction of that copy.
 --graph N captures N consecutive steps in one hipGraph and times its
 replays for `value` (per-kernel times still come from the eager pass): the
 launch cost a caller pays when it captures several layers together.
@@ -31,17 +35,20 @@ CU-limited mode); --overlap-gemm additionally times a bf16 GEMM on a second
 stream alone and interleaved with the steps, and reports how much of the
 shorter of the two the overlap hides.
 
-Prints ONE JSON line. `value` is whole-step throughput: algorithmic HBM
-bytes of the three passes per step divided by the wall-clock step time
-(K steps bracketed by device synchronisation). Per-kernel times come from
-HIP events recorded on the same stream around each call on every Nth timed
-step (--event-every, default 25: an instrumented step costs about 14 us
-more, so sparse events keep `value` within a fraction of a percent of an
-uninstrumented run; the default 500 steps give 20 samples per kernel); the
-roofline
-object reports the dominant kernel's algorithmic bytes over its mean event
-duration against the MI355X HBM peak (8 TB/s). The CPU baseline times the
-CPU oracle on the host (test infrastructure, never on the product path).
+Prints ONE JSON line: the first mode's figures at the top level, the other
+mode's in an object named after it ("cold" by default). `value` is
+whole-step throughput: algorithmic HBM bytes of the three passes per step
+divided by the wall-clock step time (K steps bracketed by device
+synchronisation, no events inside). Per-kernel times come right after the
+timed loop: each pass is launched --event-steps times back to back (default
+50, at least 20) on the same stream and buffer rotation between two HIP
+events, and kernel_us is the mean per launch (an event drains the pipeline,
+about 3 us, so events around each single launch would read several
+microseconds above the kernel's own duration as rocprofv3 reports it). The
+roofline object reports the dominant kernel's algorithmic bytes over that
+mean against the MI355X HBM peak (8 TB/s). The CPU baseline times the CPU oracle on the host, on one
+thread and on all host threads (test infrastructure, never on the product
+path).
 """
 import argparse
 import hashlib
@@ -212,54 +219,120 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, path_mode: str 
     return path
 
 
-def cpu_baseline(case, budget_s: float = 10.0, max_reps: int = 100_000, path: str = "expand"):
-    """Time the CPU oracle (as it stands) on the same workload on the host: whole
-    steps, repeated until budget_s seconds of CPU work (at least two runs)."""
+def host_threads() -> int:
+    """Threads the CPU baseline may use: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS when the host sets it (a share of a larger machine)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _ranges(T: int, n: int):
+    """n contiguous token ranges covering [0, T)."""
+    cuts = [T * i // n for i in range(n + 1)]
+    return [(cuts[i], cuts[i + 1]) for i in range(n) if cuts[i + 1] > cuts[i]]
+
+
+def cpu_baseline(case, budget_s: float = 8.0, max_reps: int = 100_000, path: str = "expand"):
+    """Time the CPU oracle (as it stands) on the same workload on the host.
+
+    Two figures, each whole steps repeated until budget_s seconds (at least two
+    runs), median: one host thread; and all host threads, where the layout
+    stays one sequential call and dispatch and combine are split over
+    contiguous token ranges, one per thread, each thread calling the same
+    oracle functions on its range (ctypes releases the interpreter lock
+    during the C calls). Per-token arithmetic is unchanged, so the results
+    are the same; only the wall time differs.
+    """
+    import concurrent.futures as cf
+
     import oracle
 
     w = case.w
+    n_threads = host_threads()
+    pool = cf.ThreadPoolExecutor(max_workers=n_threads) if n_threads > 1 else None
+
+    def split(fn, parts):
+        if pool is None or len(parts) == 1:
+            for a, b in parts:
+                fn(a, b)
+        else:
+            list(pool.map(lambda r: fn(*r), parts))
+
     if path == "non-expand":
-        _, _, H_out, _ = geometry(w)
         y = case.extra["y_ne"]
+
+        def one_step(parts):
+            lay = oracle.layout(case.topk_idx, w.E, w.A)
+            meta, n = lay["recv_src_metadata"], lay["num_recv"]
+            def disp(a, b):  # received rows are in token order: a token range is a row range
+                i0, i1 = np.searchsorted(meta[:, 0], [a, b])
+                oracle.dispatch_compact(case.x, case.topk_idx, lay["dst_slot"], meta[i0:i1],
+                                        i1 - i0, case.x_scales, case.topk_weights)
+
+            def comb(a, b):  # the range's received rows, token column taken relative to a
+                i0, i1 = np.searchsorted(meta[:, 0], [a, b])
+                m = meta[i0:i1].copy()
+                m[:, 0] -= a
+                oracle.combine_compact(y[i0:i1], lay["dst_slot"][a:b], m, i1 - i0)
+
+            split(disp, parts)
+            split(comb, parts)
+            return lay
+        label = "non-expand (layout + dispatch_compact + combine_compact)"
+    else:
+        rowb = case.x.view(np.uint8).reshape(w.T, -1).shape[1]
+        expand = np.zeros((w.cap, rowb), np.uint8)
+        expand_s = (np.zeros((w.cap, case.x_scales.shape[1] * 4), np.uint8)
+                    if case.x_scales is not None else None)
+
+        def one_step(parts):
+            lay = oracle.layout(case.topk_idx, w.E, w.A)
+            dst = lay["dst_slot"]
+
+            def disp(a, b):
+                oracle.dispatch(case.x[a:b], dst[a:b], w.cap,
+                                x_scales=None if case.x_scales is None else case.x_scales[a:b],
+                                expand_x=expand, expand_scales=expand_s)
+
+            def comb(a, b):
+                if w.out_dtype == 1:
+                    oracle.combine_f32(case.y, dst[a:b], case.topk_weights[a:b])
+                else:
+                    oracle.combine(case.y, dst[a:b], case.topk_weights[a:b])
+
+            split(disp, parts)
+            split(comb, parts)
+            return lay
+        label = "(layout + dispatch + combine)"
+
+    def timed(parts):
         times = []
         t_start = time.perf_counter()
+        lay = None
         while len(times) < max_reps and (len(times) < 2 or time.perf_counter() - t_start < budget_s):
             t0 = time.perf_counter()
-            lay = oracle.layout(case.topk_idx, w.E, w.A)
-            oracle.dispatch_compact(case.x, case.topk_idx, lay["dst_slot"], lay["recv_src_metadata"],
-                                    lay["num_recv"], case.x_scales, case.topk_weights)
-            oracle.combine_compact(y, lay["dst_slot"], lay["recv_src_metadata"], lay["num_recv"])
+            lay = one_step(parts)
             times.append(time.perf_counter() - t0)
-        b = algorithmic_bytes(w, int((lay["dst_slot"] >= 0).sum()), lay["num_recv"], path)
-        sec = float(np.median(times))
-        return {"value": round(sum(b.values()) / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
-                "kind": "oracle", "seconds_per_step": round(sec, 4),
-                "sample": f"the full {w.name} workload, non-expand (layout + dispatch_compact + "
-                          f"combine_compact), {len(times)} single-threaded runs in "
-                          f"{sum(times):.1f} s, median"}
-    rowb = case.x.view(np.uint8).reshape(w.T, -1).shape[1]
-    expand = np.zeros((w.cap, rowb), np.uint8)
-    expand_s = (np.zeros((w.cap, case.x_scales.shape[1] * 4), np.uint8)
-                if case.x_scales is not None else None)
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < max_reps and (len(times) < 2 or time.perf_counter() - t_start < budget_s):
-        t0 = time.perf_counter()
-        lay = oracle.layout(case.topk_idx, w.E, w.A)
-        oracle.dispatch(case.x, lay["dst_slot"], w.cap, x_scales=case.x_scales,
-                        expand_x=expand, expand_scales=expand_s)
-        if w.out_dtype == 1:
-            oracle.combine_f32(case.y, lay["dst_slot"], case.topk_weights)
-        else:
-            oracle.combine(case.y, lay["dst_slot"], case.topk_weights)
-        times.append(time.perf_counter() - t0)
+        return float(np.median(times)), len(times), sum(times), lay
+
+    sec1, n1, tot1, lay = timed([(0, w.T)])
+    secn, nn, totn, _ = timed(_ranges(w.T, n_threads)) if n_threads > 1 else (sec1, n1, tot1, lay)
+    if pool is not None:
+        pool.shutdown()
     n_valid = int((lay["dst_slot"] >= 0).sum())
-    b = algorithmic_bytes(w, n_valid, lay["num_recv"])
-    sec = float(np.median(times))
-    return {"value": round(sum(b.values()) / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seconds_per_step": round(sec, 4),
-            "sample": f"the full {w.name} workload (layout + dispatch + combine), "
-                      f"{len(times)} single-threaded runs in {sum(times):.1f} s, median"}
+    b = sum(algorithmic_bytes(w, n_valid, lay["num_recv"], path).values())
+    return {"value": round(b / secn / 1e9, 3), "unit": "GB/s", "cores": n_threads,
+            "kind": "oracle", "seconds_per_step": round(secn, 4),
+            "single_thread": {"value": round(b / sec1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                              "seconds_per_step": round(sec1, 4)},
+            "host_cpus": os.cpu_count(),
+            "sample": f"the full {w.name} workload {label}: {n1} single-threaded steps in "
+                      f"{tot1:.1f} s and {nn} steps on {n_threads} threads in {totn:.1f} s, "
+                      f"medians; the layout runs on one thread, dispatch and combine are "
+                      f"split over {n_threads} contiguous token ranges"}
 
 
 def main():
@@ -278,8 +351,11 @@ def main():
                     help="call ep_layout and ep_dispatch (ep_dispatch_compact) separately even "
                          "when the batch fits one layout tile (by default ep_layout_dispatch "
                          "(ep_layout_dispatch_compact) is used then)")
-    ap.add_argument("--cold", action="store_true",
-                    help="rotate buffer sets so that no step finds its rows in the last-level cache")
+    ap.add_argument("--cache", choices=("both", "warm", "cold"), default="both",
+                    help="warm: steps back to back on one buffer set; cold: rotate buffer sets "
+                         "and copies of x so that no step finds its rows in the last-level "
+                         "cache; both (default): the warm line with a `cold` object beside it")
+    ap.add_argument("--cold", action="store_true", help="same as --cache cold")
     ap.add_argument("--workgroups", type=int, default=0,
                     help="cap every kernel of the step at this many workgroups (0: no cap)")
     ap.add_argument("--graph", type=int, default=0, metavar="N",
@@ -287,9 +363,9 @@ def main():
     ap.add_argument("--overlap-gemm", action="store_true",
                     help="also time a bf16 GEMM on a second stream, alone and overlapped")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=25,
-                    help="record per-kernel HIP events on every Nth timed step (each event "
-                         "pair costs a few microseconds of pipeline bubble)")
+    ap.add_argument("--event-steps", type=int, default=50,
+                    help="launches of each pass timed back to back between two HIP events after "
+                         "the timed loop, for the per-kernel times (at least 20)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB fp32 negate first (a plain streaming kernel of known size "
                          "for scaling hardware byte counters)")
@@ -369,13 +445,7 @@ def main():
         }
 
     step_bytes = sum(algorithmic_bytes(w, w.T * w.K, w.T, args.path).values())
-    nsets = nx = 1
     x_bytes = case.x.nbytes + (case.x_scales.nbytes if case.x_scales is not None else 0)
-    if args.cold:  # at least 512 MB of other traffic between two uses of a set or an x copy
-        nsets = min(32, max(2, -(-(512 << 20) // step_bytes) + 1))
-        nx = min(1024, max(2, -(-(512 << 20) // x_bytes) + 1))
-    sets = [buffer_set() for _ in range(nsets)]
-    x_sets = [x_set() for _ in range(nx)]
     stream = torch.cuda.current_stream()
     if args.workgroups > 0:
         stream = torch.cuda.Stream()  # default priority
@@ -390,107 +460,143 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    def step(i, ev=None, stream=stream):
-        S, X = sets[i % nsets], x_sets[i % nx]
-        if ev is not None:
-            ev[0].record(stream)
-        if fused and non_expand:  # one launch; its time is reported as dispatch's, layout's as zero
-            B.ep_layout_dispatch_compact(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta,
-                                         nrecv, ws, wsb, X["x"], X["xs"], wts, w.H, w.dtype,
-                                         S["expand"], S["expand_s"], S["recv_i"], S["recv_w"],
-                                         stream)
-        elif fused:
-            B.ep_layout_dispatch(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv,
-                                 ws, wsb, X["x"], X["xs"], None, w.H, w.dtype, S["expand"],
-                                 S["expand_s"], None, stream)
-        else:
-            B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws, wsb,
-                        stream, dispatch_plan=plan)
-        if ev is not None:
-            ev[1].record(stream)
-        if non_expand and not fused:
-            B.ep_dispatch_compact(X["x"], X["xs"], idx, wts, dst, meta, nrecv, w.T, w.H, w.K, w.dtype,
-                                  S["expand"], S["expand_s"], S["recv_i"], S["recv_w"], stream)
-        elif not non_expand and not fused:
-            B.ep_dispatch(X["x"], X["xs"], None, dst, w.T, w.H, w.K, w.dtype, w.cap, S["expand"],
-                          S["expand_s"], None, stream, dispatch_plan=plan)
-        if ev is not None:
-            ev[2].record(stream)
-        if non_expand:
-            B.ep_combine_compact(S["y"], None, dst, meta, nrecv, w.T, H_out, w.K, 0, S["out"], stream)
-        else:
-            B.ep_combine(S["y"], wts, None, dst, w.T, H_out, w.K, w.out_dtype, w.cap, S["out"], stream)
-        if ev is not None:
-            ev[3].record(stream)
-
-    torch.cuda.synchronize()  # inputs were written on the default stream
-    for i in range(max(args.warmup, nsets, nx)):
-        step(i)
-    # HIP events around each kernel on every Nth timed step: an instrumented
-    # step costs about 14 us more (each event drains the pipeline), so sparse
-    # events keep the wall-clock value within a fraction of a percent.
-    every = max(1, args.event_every)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
-           for _ in range(0, args.steps, every)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i // every] if i % every == 0 else None)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    us = {"layout": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3,
-          "dispatch": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3,
-          "combine": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3}
-    if fused:  # layout ran inside the dispatch launch
-        us = {"layout": 0.0, "dispatch": us["layout"] + us["dispatch"], "combine": us["combine"]}
-    launch = "eager"
-    if args.graph > 0:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(args.graph):
-                step(i, stream=torch.cuda.current_stream())
-        for _ in range(3):
-            g.replay()
-        reps = max(1, args.steps // args.graph)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * args.graph)
-        launch = f"hipGraph of {args.graph} steps, {reps} replays"
-    last = sets[(args.steps - 1) % nsets]  # every set holds the same results
-    y, expand, recv_i, recv_w, out = (last[k] for k in ("y", "expand", "recv_i", "recv_w", "out"))
-    cache = ("warm" if nsets == 1 else
-             f"cold: {nsets} buffer sets rotated, "
-             f"{(nsets - 1) * step_bytes / 1e6:.0f} MB of other traffic between uses of a set; "
-             f"{nx} copies of x rotated, {(nx - 1) * x_bytes / 1e6:.0f} MB of other x reads "
-             f"between uses of a copy")
-
-    overlap = (overlap_gemm(torch, dev, lambda: step(0), ms_per_step, args.steps)
-               if args.overlap_gemm else None)
-
-    # Validate the timed path against the oracle: layout in full, dispatch and combine sampled.
     import oracle
     ref = oracle.layout(case.topk_idx, w.E, w.A)
-    got_dst = dst.cpu().numpy()
-    ok = (np.array_equal(got_dst, ref["dst_slot"]) and np.array_equal(offsets.cpu().numpy(), ref["offsets"])
-          and np.array_equal(counts.cpu().numpy(), ref["counts"]) and int(nrecv.item()) == ref["num_recv"])
     sample = np.random.default_rng(0).choice(w.T, size=min(w.T, 256), replace=False)
     xb = case.x.view(np.uint8).reshape(w.T, -1)
-    if non_expand:
-        ok = ok and validate_non_expand(oracle, case, ref, expand, recv_i, recv_w, out, sample)
-    else:
-        ok = ok and validate_expand(oracle, case, ref, expand, out, sample, xb, dev)
-    if not ok:
-        print("bench: GPU results do not match the oracle; refusing to report", file=sys.stderr)
-        sys.exit(1)
+
+    def run_mode(cold: bool, first: bool) -> dict:
+        """Warm-up, the K timed steps, then the instrumented pass; validates the results."""
+        nsets = nx = 1
+        if cold:  # at least 512 MB of other traffic between two uses of a set or an x copy
+            nsets = min(32, max(2, -(-(512 << 20) // step_bytes) + 1))
+            nx = min(1024, max(2, -(-(512 << 20) // x_bytes) + 1))
+        sets = [buffer_set() for _ in range(nsets)]
+        x_sets = [x_set() for _ in range(nx)]
+
+        def run_layout(i, stream=stream):
+            S, X = sets[i % nsets], x_sets[i % nx]
+            if fused and non_expand:  # one launch; its time is reported as dispatch's
+                B.ep_layout_dispatch_compact(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst,
+                                             meta, nrecv, ws, wsb, X["x"], X["xs"], wts, w.H,
+                                             w.dtype, S["expand"], S["expand_s"], S["recv_i"],
+                                             S["recv_w"], stream)
+            elif fused:
+                B.ep_layout_dispatch(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta,
+                                     nrecv, ws, wsb, X["x"], X["xs"], None, w.H, w.dtype,
+                                     S["expand"], S["expand_s"], None, stream)
+            else:
+                B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws,
+                            wsb, stream, dispatch_plan=plan)
+
+        def run_dispatch(i, stream=stream):
+            S, X = sets[i % nsets], x_sets[i % nx]
+            if non_expand and not fused:
+                B.ep_dispatch_compact(X["x"], X["xs"], idx, wts, dst, meta, nrecv, w.T, w.H, w.K,
+                                      w.dtype, S["expand"], S["expand_s"], S["recv_i"],
+                                      S["recv_w"], stream)
+            elif not non_expand and not fused:
+                B.ep_dispatch(X["x"], X["xs"], None, dst, w.T, w.H, w.K, w.dtype, w.cap,
+                              S["expand"], S["expand_s"], None, stream, dispatch_plan=plan)
+
+        def run_combine(i, stream=stream):
+            S = sets[i % nsets]
+            if non_expand:
+                B.ep_combine_compact(S["y"], None, dst, meta, nrecv, w.T, H_out, w.K, 0, S["out"],
+                                     stream)
+            else:
+                B.ep_combine(S["y"], wts, None, dst, w.T, H_out, w.K, w.out_dtype, w.cap, S["out"],
+                             stream)
+
+        def step(i, stream=stream):
+            run_layout(i, stream)
+            run_dispatch(i, stream)
+            run_combine(i, stream)
+
+        torch.cuda.synchronize()  # inputs were written on the default stream
+        for i in range(max(args.warmup, nsets, nx)):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):  # the timed region: steps only, no events
+            step(i)
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        # Per-kernel times: right after the timed loop, each pass is launched
+        # n_ev times back to back on the same stream, with the step's buffer
+        # rotation, between two HIP events (an event drains the pipeline, about
+        # 3 us each, so events around single launches would read several
+        # microseconds above the kernel's own duration). The mean per launch is
+        # the kernel's average launch duration.
+        n_ev = max(20, args.event_steps)
+        us = {}
+        for name, fn in (("layout", run_layout), ("dispatch", run_dispatch),
+                         ("combine", run_combine)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for j in range(n_ev):
+                fn(args.steps + j)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us[name] = e0.elapsed_time(e1) * 1e3 / n_ev
+        if fused:  # layout ran inside the dispatch launch
+            us = {"layout": 0.0, "dispatch": us["layout"], "combine": us["combine"]}
+        launch = "eager"
+        if first and args.graph > 0:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(args.graph):
+                    step(i, stream=torch.cuda.current_stream())
+            for _ in range(3):
+                g.replay()
+            reps = max(1, args.steps // args.graph)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * args.graph)
+            launch = f"hipGraph of {args.graph} steps, {reps} replays"
+        overlap = (overlap_gemm(torch, dev, lambda: step(0), ms_per_step, args.steps)
+                   if first and args.overlap_gemm else None)
+        torch.cuda.synchronize()
+        # Validate this mode's results against the oracle: layout in full,
+        # dispatch and combine on sampled tokens (every set holds the same rows).
+        last = sets[(args.steps + n_ev - 1) % nsets]
+        ok = (np.array_equal(dst.cpu().numpy(), ref["dst_slot"])
+              and np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+              and np.array_equal(counts.cpu().numpy(), ref["counts"])
+              and int(nrecv.item()) == ref["num_recv"])
+        if non_expand:
+            ok = ok and validate_non_expand(oracle, case, ref, last["expand"], last["recv_i"],
+                                            last["recv_w"], last["out"], sample)
+        else:
+            ok = ok and validate_expand(oracle, case, ref, last["expand"], last["out"], sample, xb,
+                                        dev)
+        if not ok:
+            print("bench: GPU results do not match the oracle; refusing to report", file=sys.stderr)
+            sys.exit(1)
+        cache = ("warm: one buffer set, steps back to back" if nsets == 1 else
+                 f"cold: {nsets} buffer sets rotated, "
+                 f"{(nsets - 1) * step_bytes / 1e6:.0f} MB of other traffic between uses of a set; "
+                 f"{nx} copies of x rotated, {(nx - 1) * x_bytes / 1e6:.0f} MB of other x reads "
+                 f"between uses of a copy")
+        del sets, x_sets, last
+        torch.cuda.empty_cache()
+        return {"ms_per_step": ms_per_step, "us": us, "event_steps": n_ev,
+                "launch": launch, "overlap": overlap, "cache": cache}
+
+    modes = ["cold"] if args.cold or args.cache == "cold" else \
+        ["warm"] if args.cache == "warm" else ["warm", "cold"]
+    runs = {}
+    for m in modes:
+        print(f"# {m} pass: {args.warmup} warm-up steps, {args.steps} timed steps, then "
+              f"{max(20, args.event_steps)} instrumented steps", file=sys.stderr, flush=True)
+        runs[m] = run_mode(m == "cold", m == modes[0])
     if args.workgroups > 0:
         torch.cuda.synchronize()
         B.ep_set_workgroup_limit(stream, 0)
-    report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap, cache, launch,
-           use_plan, fused)
+    report(args, w, case, ref, runs, modes, copy_gbps, non_expand, use_plan, fused)
 
 
 GEMM_SHAPE = (8192, 7168, 2048)  # M, K, N: bf16 [M, K] x [K, N], about one step's duration
@@ -583,12 +689,12 @@ def validate_expand(oracle, case, ref, expand, out, sample, xb, dev) -> bool:
     return bool(ok)
 
 
-def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=None, cache="warm",
-           launch="eager", plan_used=False, fused=False):
-    n_valid = int((ref["dst_slot"] >= 0).sum())
-    nb = algorithmic_bytes(w, n_valid, ref["num_recv"], args.path)
+def mode_figures(w, nb, run, non_expand, workload) -> dict:
+    """Throughput, per-kernel times and the dominant kernel's roofline of one cache mode."""
     total_bytes = sum(nb.values())
-    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    ms = run["ms_per_step"]
+    us = run["us"]
+    value = total_bytes / (ms * 1e-3) / 1e9
     dc_us = us["dispatch"] + us["combine"]
     dc_gbps = (nb["dispatch"] + nb["combine"]) / (dc_us * 1e-6) / 1e9
     dom = max(("dispatch", "combine"), key=lambda k: us[k])
@@ -596,16 +702,32 @@ def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=N
     dom_name = dom + ("_compact" if non_expand else "")
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(w.name, dom_name),
-                "algorithmic_bytes_per_launch": nb[dom], "avg_launch_us": round(us[dom], 2)}
+                "traffic": measured_traffic(workload, dom_name),
+                "algorithmic_bytes_per_launch": nb[dom], "avg_launch_us": round(us[dom], 2),
+                "samples": run["event_steps"]}
+    return {"value": round(value, 1), "ms_per_step": round(ms, 4),
+            "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+            "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+            "dispatch_combine_GBps": round(dc_gbps, 1),
+            "dispatch_combine_pct_of_peak": round(100 * dc_gbps / HBM_PEAK_GBPS, 2),
+            "dispatch_combine_tokens_per_s": round(w.T / (dc_us * 1e-6), 1),
+            "kernel_us": {k: round(v, 2) for k, v in us.items()},
+            "roofline": roofline}
+
+
+def report(args, w, case, ref, runs, modes, copy_gbps, non_expand, plan_used=False, fused=False):
+    n_valid = int((ref["dst_slot"] >= 0).sum())
+    nb = algorithmic_bytes(w, n_valid, ref["num_recv"], args.path)
+    main_run = runs[modes[0]]
+    fig = mode_figures(w, nb, main_run, non_expand, w.name)
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": fig["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": fig["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -621,19 +743,22 @@ def report(args, w, case, ref, us, ms_per_step, copy_gbps, non_expand, overlap=N
                                         else "one launch (ep_layout_dispatch)")
                                        if fused else "separate launches"),
                    "workgroup_cap": args.workgroups or None,
-                   "cache": cache, "launch": launch},
-        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "tokens_per_s": round(w.T / (ms_per_step * 1e-3), 1),
-        "dispatch_combine_GBps": round(dc_gbps, 1),
-        "dispatch_combine_pct_of_peak": round(100 * dc_gbps / HBM_PEAK_GBPS, 2),
-        "dispatch_combine_tokens_per_s": round(w.T / (dc_us * 1e-6), 1),
+                   "cache": main_run["cache"], "launch": main_run["launch"]},
+        **{k: fig[k] for k in ("pct_of_peak", "tokens_per_s", "dispatch_combine_GBps",
+                               "dispatch_combine_pct_of_peak", "dispatch_combine_tokens_per_s")},
         "copy_reference_GBps": round(copy_gbps, 1),
-        "dispatch_combine_pct_of_copy": round(100 * dc_gbps / copy_gbps, 2),
-        "kernel_us": {k: round(v, 2) for k, v in us.items()},
+        "dispatch_combine_pct_of_copy": round(100 * fig["dispatch_combine_GBps"] / copy_gbps, 2),
+        "kernel_us": fig["kernel_us"],
+        "kernel_timing": f"HIP events around {main_run['event_steps']} back-to-back launches of "
+                         f"each pass, run right after the timed loop; mean per launch",
         "algorithmic_bytes": nb,
-        **({"overlap": overlap} if overlap else {}),
-        "roofline": roofline,
+        **({"overlap": main_run["overlap"]} if main_run["overlap"] else {}),
+        "roofline": fig["roofline"],
     }
+    for m in modes[1:]:
+        sub = mode_figures(w, nb, runs[m], non_expand, w.name)
+        sub["roofline"]["traffic"] = None  # counters are taken on the warm loop only
+        result[m] = {**sub, "cache": runs[m]["cache"]}
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(case, path=args.path)

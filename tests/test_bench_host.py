@@ -103,8 +103,25 @@ def test_cpu_baseline_record(path):
     if path == "non-expand":
         case.extra["y_ne"] = I.normal_bf16(w.seed, I.STREAM_Y, w.T, w.H)
     r = bench.cpu_baseline(case, budget_s=0.5, max_reps=2, path=path)
-    assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "GB/s"
+    assert r["kind"] == "oracle" and r["cores"] == bench.host_threads() and r["unit"] == "GB/s"
     assert r["value"] > 0 and "tiny" in r["sample"]
+    assert r["single_thread"]["cores"] == 1 and r["single_thread"]["value"] > 0
+
+
+@pytest.mark.parametrize("T,n", [(0, 4), (1, 8), (7, 3), (64, 64), (4096, 16), (1000, 7)])
+def test_token_ranges_cover_every_token_once(T, n):
+    """The all-threads CPU baseline splits the tokens into contiguous ranges: together
+    they must cover every token exactly once, in order, with no empty range."""
+    parts = bench._ranges(T, n)
+    assert len(parts) <= n and all(b > a for a, b in parts)
+    assert [t for a, b in parts for t in range(a, b)] == list(range(T))
+
+
+def test_host_threads_respects_omp_cap(monkeypatch):
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.host_threads() == 1
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.host_threads() >= 1
 
 
 @pytest.mark.parametrize("T,K,E,one", [(128, 8, 256, True), (129, 8, 256, False), (64, 2, 16, True),
