@@ -50,6 +50,10 @@ def lib(path: str = None):
         L.oracle_combine_compact.argtypes = [_u16p, ctypes.c_int32, _u16p, _i32p, _i32p, ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_int32, _u16p]
         L.oracle_combine_compact.restype = ctypes.c_int
+        L.oracle_combine_compact_f32.argtypes = [_f32p, ctypes.c_int32, _f32p, _i32p, _i32p,
+                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 _f32p]
+        L.oracle_combine_compact_f32.restype = ctypes.c_int
         L.oracle_zero_padding.argtypes = [_u8p, ctypes.c_int64, _u8p, ctypes.c_int64, _f32p, _i32p,
                                           _i32p, ctypes.c_int32, ctypes.c_int64]
         L.oracle_zero_padding.restype = ctypes.c_int
@@ -184,6 +188,24 @@ def combine_compact(y_bf16_bits: np.ndarray, dst_slot: np.ndarray, recv_src_meta
                                           _ptr(meta, _i32p), int(num_recv), T, K, _ptr(out, _u16p))
     if rc != 0:
         raise ValueError("oracle_combine_compact rejected its arguments")
+    return out
+
+
+def combine_compact_f32(y: np.ndarray, dst_slot: np.ndarray, recv_src_metadata: np.ndarray,
+                        num_recv: int, bias: np.ndarray = None, _lib=None):
+    """Non-expand combine of fp32 rows [>= num_recv, H] back to token order [T, H] (+ bias)."""
+    yf = np.ascontiguousarray(y, dtype=np.float32)
+    H = yf.shape[1]
+    dst = np.ascontiguousarray(dst_slot, dtype=np.int32)
+    T, K = dst.shape
+    meta = np.ascontiguousarray(recv_src_metadata, dtype=np.int32).reshape(-1, K + 2)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.empty((T, H), np.float32)
+    rc = lib(_lib).oracle_combine_compact_f32(_ptr(yf, _f32p), H, _ptr(b, _f32p), _ptr(dst, _i32p),
+                                              _ptr(meta, _i32p), int(num_recv), T, K,
+                                              _ptr(out, _f32p))
+    if rc != 0:
+        raise ValueError("oracle_combine_compact_f32 rejected its arguments")
     return out
 
 

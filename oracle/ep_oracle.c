@@ -276,6 +276,44 @@ int oracle_combine_compact(const uint16_t *y, int32_t H, const uint16_t *bias,
 }
 
 /*
+ * The same non-expand combine for binary32 rows ("MORI JIT v2", section 3.7:
+ * combine takes bf16 or fp32 rows and writes the same type): for the token t
+ * of receive row i, out[t] = y[i] + bias[t] in binary32 (one rounded add per
+ * value); a token with no unmasked entry gets +0.0 + bias[t]; without a bias,
+ * out[t] = y[i] value for value, or +0.0. y is fp32 [>= num_recv, H], bias
+ * fp32 [T, H] or NULL, out fp32 [T, H].
+ */
+int oracle_combine_compact_f32(const float *y, int32_t H, const float *bias,
+                               const int32_t *dst_slot, const int32_t *meta, int32_t num_recv,
+                               int32_t T, int32_t K, float *out) {
+  if (num_recv < 0 || num_recv > T || K < 1 || H < 0) return -1;
+  /* receive row of each token, from the metadata's token column */
+  int32_t *recv_row = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  for (int32_t t = 0; t < T; ++t) recv_row[t] = -1;
+  for (int32_t i = 0; i < num_recv; ++i) {
+    int32_t t = meta[(int64_t)i * (K + 2)];
+    if (t < 0 || t >= T) {
+      free(recv_row);
+      return -1;
+    }
+    recv_row[t] = i;
+  }
+  for (int32_t t = 0; t < T; ++t) {
+    int received = 0;
+    for (int32_t k = 0; k < K; ++k)
+      if (dst_slot[(int64_t)t * K + k] >= 0) received = 1;
+    const float *row = received && recv_row[t] >= 0 ? y + (int64_t)recv_row[t] * H : NULL;
+    for (int32_t h = 0; h < H; ++h) {
+      float v = row ? row[h] : 0.0f;
+      if (bias) v = v + bias[(int64_t)t * H + h];
+      out[(int64_t)t * H + h] = v;
+    }
+  }
+  free(recv_row);
+  return 0;
+}
+
+/*
  * Optional clean-up of the expand layout: the alignment padding rows of each
  * expert segment, [offsets[e] + counts[e], offsets[e+1]), are set to zero in
  * expand_x (and in expand_scales / expand_weights when given), so a consumer

@@ -225,6 +225,27 @@ def check_combine_compact(y_bits, dst, meta, num_recv, out_bits, bias_bits=None)
     assert np.all(np.abs(out - exact) <= bound), "bias add outside half a bf16 ulp"
 
 
+def check_combine_compact_f32(y, dst, meta, num_recv, out, bias=None):
+    """Binary32 rows: out[t] = y[row of t] (+ bias) with one binary32 rounding;
+    +0 (+ bias) for unreceived tokens. The sum is evaluated in float64, where
+    the sum of two binary32 values of similar size is exact."""
+    T = dst.shape[0]
+    row_of = np.full(T, -1)
+    row_of[np.asarray(meta)[:num_recv, 0]] = np.arange(num_recv)
+    recv = (dst >= 0).any(axis=1)
+    assert np.array_equal(recv, row_of >= 0), "exactly the tokens with an unmasked entry are received"
+    y = np.asarray(y, np.float32)
+    got = np.where(recv[:, None], y[np.maximum(row_of, 0)], np.float32(0.0)).astype(np.float32)
+    if bias is None:
+        assert np.array_equal(out.view(np.uint32), got.view(np.uint32)), \
+            "without a bias rows come back bit for bit (+0 for unreceived tokens)"
+        return
+    exact = got.astype(np.float64) + np.asarray(bias, np.float64)
+    ulp = np.spacing(np.abs(out).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(out.astype(np.float64) - exact) <= 0.5 * ulp + 2.0 ** -53 * np.abs(exact)), \
+        "bias add outside half a binary32 ulp"
+
+
 # --------------------------------------------------------------------------
 # Dispatch plan
 # --------------------------------------------------------------------------

@@ -136,6 +136,14 @@ def test_non_expand_hand_worked(oracle_mod):
         out = oracle_mod.combine_compact(h(c["y_hex"]), lay["dst_slot"], lay["recv_src_metadata"],
                                          lay["num_recv"])
         assert np.array_equal(out, h(c["out_no_bias_hex"]))
+        f = lambda rows: np.array(rows, np.float32).view(np.uint32)  # noqa: E731
+        out = oracle_mod.combine_compact_f32(np.array(c["y_f32"], np.float32), lay["dst_slot"],
+                                             lay["recv_src_metadata"], lay["num_recv"],
+                                             np.array(c["bias_f32"], np.float32))
+        assert np.array_equal(out.view(np.uint32), f(c["out_f32_bias"]))
+        out = oracle_mod.combine_compact_f32(np.array(c["y_f32"], np.float32), lay["dst_slot"],
+                                             lay["recv_src_metadata"], lay["num_recv"])
+        assert np.array_equal(out.view(np.uint32), f(c["out_f32_no_bias"]))
 
 
 @pytest.mark.parametrize("mask", [0.0, 0.4])
@@ -158,3 +166,7 @@ def test_non_expand_pins(oracle_mod, mask):
     y = I.normal_bf16(w.seed, 4, max(n, 1), w.H)
     out = oracle_mod.combine_compact(y, dst, meta, n, bias)
     pins.check_combine_compact(y, dst, meta, n, out, bias)
+    yf, bf = I.normal_f32(w.seed, 4, max(n, 1), w.H), I.normal_f32(w.seed, 9, w.T, w.H)
+    pins.check_combine_compact_f32(yf, dst, meta, n, oracle_mod.combine_compact_f32(yf, dst, meta, n))
+    pins.check_combine_compact_f32(yf, dst, meta, n,
+                                   oracle_mod.combine_compact_f32(yf, dst, meta, n, bf), bf)

@@ -72,6 +72,12 @@ MUTANTS = {
     "combine_fma": ("        float prod = w * v;\n        acc = acc + prod;", "        acc = __builtin_fmaf(w, v, acc);"),
     "combine_f32_fma": ("        float prod = w * y[(int64_t)d[k] * H + h];\n        acc = acc + prod;",
                         "        acc = __builtin_fmaf(w, y[(int64_t)d[k] * H + h], acc);"),
+    "compact_f32_bias_dropped": ("      if (bias) v = v + bias[(int64_t)t * H + h];\n", ""),
+    "compact_f32_unreceived_kept": ("const float *row = received && recv_row[t] >= 0 ? y + (int64_t)recv_row[t] * H : NULL;",
+                                    "const float *row = y + (int64_t)(recv_row[t] >= 0 ? recv_row[t] : 0) * H;"),
+    "compact_f32_bias_first": ("      float v = row ? row[h] : 0.0f;\n      if (bias) v = v + bias[(int64_t)t * H + h];",
+                               "      float v = bias ? bias[(int64_t)t * H + h] : 0.0f;\n      if (row) v = v + row[h];"),
+    "compact_f32_row_zero": ("float v = row ? row[h] : 0.0f;", "float v = row ? row[0] : 0.0f;"),
     "combine_f32_weight_k0": ("        float w = topk_weights ? topk_weights[(int64_t)t * K + k] : 1.0f;\n        float prod",
                               "        float w = topk_weights ? topk_weights[(int64_t)t * K] : 1.0f;\n        float prod"),
 }
@@ -200,6 +206,12 @@ def _run_pins(libpath):
             assert np.array_equal(out, h(c["out_bias_hex"]))
             out = oracle.combine_compact(h(c["y_hex"]), dst_, meta_, c["num_recv"], _lib=libpath)
             assert np.array_equal(out, h(c["out_no_bias_hex"]))
+            f = lambda rows: np.array(rows, np.float32)  # noqa: E731
+            out = oracle.combine_compact_f32(f(c["y_f32"]), dst_, meta_, c["num_recv"], f(c["bias_f32"]),
+                                             _lib=libpath)
+            assert np.array_equal(out.view(np.uint32), f(c["out_f32_bias"]).view(np.uint32))
+            out = oracle.combine_compact_f32(f(c["y_f32"]), dst_, meta_, c["num_recv"], _lib=libpath)
+            assert np.array_equal(out.view(np.uint32), f(c["out_f32_no_bias"]).view(np.uint32))
 
     def combine_f32_pins():
         for c in comb_gold["combine_f32"]:
