@@ -551,11 +551,10 @@ int ep_combine_compact(const void *expert_out, const void *bias, const int32_t *
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
     if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2)
       return fail(EP_EINVAL, "%s: combine adds its input; byte dtype %d is rejected", what, dtype);
-    if (dtype == EP_FP32)
-      return fail(EP_EUNSUPPORTED, "%s: only bf16 rows are compiled for the non-expand combine",
-                  what);
-    if (dtype != EP_BF16) return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
-    if (hidden < 1 || ((int64_t)hidden * 2) % 16 != 0 || (int64_t)hidden * 2 > INT32_MAX)
+    if (dtype != EP_BF16 && dtype != EP_FP32)
+      return fail(EP_EINVAL, "%s: unknown dtype %d", what, dtype);
+    const int64_t elt = dtype == EP_FP32 ? 4 : 2;
+    if (hidden < 1 || ((int64_t)hidden * elt) % 16 != 0 || (int64_t)hidden * elt > INT32_MAX)
       return fail(EP_EINVAL,
                   "%s: token bytes must be a positive multiple of 16 below 2^31 (hidden %d)", what,
                   hidden);
@@ -563,8 +562,9 @@ int ep_combine_compact(const void *expert_out, const void *bias, const int32_t *
       return fail(EP_EINVAL, "%s: a required pointer is NULL", what);
     if (!aligned(expert_out, 16) || !aligned(out, 16) || !aligned(bias, 16))
       return fail(EP_EINVAL, "%s: misaligned pointer (rows need 16 bytes)", what);
-    ep::CompactCombineArgs a{expert_out, (int64_t)hidden * 2, bias, dst_slot, recv_src_metadata,
-                             num_recv, num_tokens, topk, out, (hipStream_t)stream};
+    ep::CompactCombineArgs a{expert_out, (int64_t)hidden * elt, bias, dst_slot,
+                             recv_src_metadata, num_recv, num_tokens, topk, out,
+                             (hipStream_t)stream, dtype == EP_FP32};
     return from_launch(ep::launch_combine_compact(a), what);
   } catch (const std::exception &e) {
     return fail(EP_EHIP, "ep_combine_compact: %s", e.what());

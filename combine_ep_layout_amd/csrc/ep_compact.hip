@@ -72,8 +72,10 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
   }
 }
 
-// out[t] chunk c = v (+ bias[t] chunk c), one binary32 add per value, RNE.
-template <bool WIDE>
+// out[t] chunk c = v (+ bias[t] chunk c), one binary32 add per value; bf16
+// rows (FP32 false) are widened exactly and the sum rounded back to bf16
+// (round to nearest even), binary32 rows keep the sum as it is.
+template <bool WIDE, bool FP32>
 __device__ __forceinline__ void put_row_chunk(u32x4 v, const u32x4 *__restrict__ bias, int64_t t,
                                               int64_t row_chunks, int64_t c,
                                               u32x4 *__restrict__ out) {
@@ -83,9 +85,14 @@ __device__ __forceinline__ void put_row_chunk(u32x4 v, const u32x4 *__restrict__
     u32x4 r;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float lo = __uint_as_float(v[j] << 16) + __uint_as_float(b[j] << 16);
-      const float hi = __uint_as_float(v[j] & 0xffff0000u) + __uint_as_float(b[j] & 0xffff0000u);
-      r[j] = pack_bf16x2(lo, hi);
+      if constexpr (FP32) {
+        r[j] = __float_as_uint(__uint_as_float(v[j]) + __uint_as_float(b[j]));
+      } else {
+        const float lo = __uint_as_float(v[j] << 16) + __uint_as_float(b[j] << 16);
+        const float hi =
+            __uint_as_float(v[j] & 0xffff0000u) + __uint_as_float(b[j] & 0xffff0000u);
+        r[j] = pack_bf16x2(lo, hi);
+      }
     }
     v = r;
   }
@@ -97,7 +104,7 @@ __device__ __forceinline__ void put_row_chunk(u32x4 v, const u32x4 *__restrict__
 // [T*slices, T*slices + T): one per token; a token with no unmasked entry
 // (none of its K slots valid) gets +0 (+ bias) over its whole row, the
 // others exit after one K-wide read.
-template <bool WIDE>
+template <bool WIDE, bool FP32>
 __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
     const u32x4 *__restrict__ y, int64_t row_chunks, const u32x4 *__restrict__ bias,
     const int32_t *__restrict__ dst_slot, const int32_t *__restrict__ meta,
@@ -118,14 +125,14 @@ __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
       const int64_t t = __builtin_amdgcn_readfirstlane(meta[r * (K + 2)]);
       if (t < 0 || t >= T || c >= row_chunks) continue;
       const u32x4 v = __builtin_nontemporal_load(y + r * row_chunks + c);
-      put_row_chunk<WIDE>(v, bias, t, row_chunks, c, out);
+      put_row_chunk<WIDE, FP32>(v, bias, t, row_chunks, c, out);
     } else {
       const int64_t t = gw - half;
       bool any = false;
       for (int k = lane; k < K; k += kWave) any |= dst_slot[t * K + k] >= 0;
       if (ballot(any) != 0) continue;  // received: written by its receive row
       for (int64_t c = lane; c < row_chunks; c += kWave)
-        put_row_chunk<WIDE>(zero, bias, t, row_chunks, c, out);
+        put_row_chunk<WIDE, FP32>(zero, bias, t, row_chunks, c, out);
     }
   }
 }
@@ -139,9 +146,9 @@ int dispatch_compact_launch(const CompactDispatchArgs &a, const WaveGrid &g, int
   return launch_status();
 }
 
-template <bool WIDE>
+template <bool WIDE, bool FP32>
 int combine_compact_launch(const CompactCombineArgs &a, const WaveGrid &g, int64_t row_chunks) {
-  ep_combine_compact_rows<WIDE><<<g.blocks, g.threads, 0, a.stream>>>(
+  ep_combine_compact_rows<WIDE, FP32><<<g.blocks, g.threads, 0, a.stream>>>(
       (const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias, a.dst_slot, a.meta, a.num_recv, a.T,
       a.K, (u32x4 *)a.out);
   return launch_status();
@@ -165,8 +172,11 @@ int launch_combine_compact(const CompactCombineArgs &a) {
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int cap = stream_workgroup_limit(a.stream);
   const WaveGrid g = wave_grid((int64_t)a.T * (slices + 1), cap, 1 << 22);
-  return cap > 0 ? combine_compact_launch<false>(a, g, row_chunks)
-                 : combine_compact_launch<true>(a, g, row_chunks);
+  if (a.fp32)
+    return cap > 0 ? combine_compact_launch<false, true>(a, g, row_chunks)
+                   : combine_compact_launch<true, true>(a, g, row_chunks);
+  return cap > 0 ? combine_compact_launch<false, false>(a, g, row_chunks)
+                 : combine_compact_launch<true, false>(a, g, row_chunks);
 }
 
 }  // namespace ep

@@ -91,6 +91,7 @@ struct CompactCombineArgs {
   int T, K;
   void *out;
   hipStream_t stream;
+  bool fp32 = false;  // binary32 rows (else bf16)
 };
 
 // Launch geometry. By default a grid covers every unit of work with

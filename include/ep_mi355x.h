@@ -319,12 +319,15 @@ int ep_layout_dispatch_compact(const int32_t *topk_idx, int32_t num_tokens, int3
  * with bias, do_expand = false). The expert side returns one row per
  * received token with that token's experts already reduced, so in a world
  * of one combine only puts rows back in token order and adds the bias:
- *   out[t] = bf16(float(expert_out[i]) + float(bias[t]))  for t = recv_src_metadata[i][0]
- *   out[t] = bf16(+0.0 + float(bias[t]))                   for a token with no unmasked entry
- * (without a bias: the row's bits, or +0). expert_out bf16 [T, hidden] (rows
- * >= *num_recv are not read), bias bf16 [T, hidden] or NULL, out bf16
- * [T, hidden], every row written. Errors: EP_EINVAL (byte dtypes rejected),
- * EP_EUNSUPPORTED for fp32 rows.
+ *   out[t] = float(expert_out[i]) + float(bias[t])  for t = recv_src_metadata[i][0]
+ *   out[t] = +0.0 + float(bias[t])                   for a token with no unmasked entry
+ * in binary32, one rounded add per value, stored in the rows' type (bf16:
+ * round to nearest even; fp32: as is); without a bias, the row's bits, or
+ * +0. dtype EP_BF16 or EP_FP32 ("MORI JIT v2" section 3.7: combine takes bf16
+ * or fp32 rows and writes the same type). expert_out [T, hidden] (rows
+ * >= *num_recv are not read), bias [T, hidden] of the same type or NULL, out
+ * [T, hidden] of the same type, every row written. Errors: EP_EINVAL (byte
+ * dtypes and unknown dtypes rejected, NULL or misaligned pointers).
  */
 int ep_combine_compact(const void *expert_out, const void *bias, const int32_t *dst_slot,
                        const int32_t *recv_src_metadata, const int32_t *num_recv,

@@ -230,8 +230,9 @@ def test_compact_rejections(L):
         a.update(kw)
         return tuple(a.values())
     assert _code(B.ep_combine_compact, *cc(dt=B.EP_FP8_E4M3)) == B.EP_EINVAL
-    assert _code(B.ep_combine_compact, *cc(dt=B.EP_FP32)) == B.EP_EUNSUPPORTED
+    assert _code(B.ep_combine_compact, *cc(dt=7)) == B.EP_EINVAL
     assert _code(B.ep_combine_compact, *cc(H=7172)) == B.EP_EINVAL
+    assert _code(B.ep_combine_compact, *cc(H=7170, dt=B.EP_FP32)) == B.EP_EINVAL  # 28,680 bytes
     assert _code(B.ep_combine_compact, *cc(n=None)) == B.EP_EINVAL
     assert _code(B.ep_combine_compact, *cc(b=ODD)) == B.EP_EINVAL
 

@@ -30,7 +30,7 @@ def _say(msg):
 
 
 def _run(w: I.Workload, mask: float = 0.0, weights: bool = True, bias: bool = True,
-         oob_every: int = 0):
+         oob_every: int = 0, combine_fp32: bool = False):
     """Layout -> non-expand dispatch -> non-expand combine on the GPU, each checked."""
     _say(f"non-expand {w.name}: T={w.T} H={w.H} E={w.E} K={w.K} A={w.A} dtype={w.dtype} "
          f"mask={mask} weights={weights} bias={bias}")
@@ -75,8 +75,21 @@ def _run(w: I.Workload, mask: float = 0.0, weights: bool = True, bias: bool = Tr
         assert np.array_equal(gw[:n].view(np.uint32), rw.view(np.uint32)), "recv_topk_weights"
         assert np.all(gw[n:] == -5.0)
 
-    # combine: the expert side hands back one bf16 row per received token
     H_out = 2 * w.H if w.dtype == I.FP4X2 else w.H
+    if combine_fp32:  # the expert side hands back one binary32 row per received token
+        y = I.normal_f32(w.seed, 4, rows, H_out)
+        b = I.normal_f32(w.seed, 9, rows, H_out)[:T] if bias else None
+        out = torch.full((rows, H_out), float("nan"), dtype=torch.float32, device=DEV)
+        B.ep_combine_compact(to_dev(y), to_dev(b) if bias else None, lay["dst_slot"], lay["meta"],
+                             lay["num_recv"], T, H_out, K, B.EP_FP32, out)
+        torch.cuda.synchronize()
+        got = to_host(out)[:T]
+        want = oracle.combine_compact_f32(y, ref["dst_slot"], ref["recv_src_metadata"], n, b)
+        same = got.view(np.uint32) == want.view(np.uint32)
+        _say(f"  num_recv={n} fp32 combine bit-exact {int(same.sum())}/{same.size}")
+        assert same.all(), "fp32 non-expand combine differs from the oracle"
+        return case, ref, recv_x, n
+    # combine: the expert side hands back one bf16 row per received token
     y = I.normal_bf16(w.seed, 4, rows, H_out)
     b = I.normal_bf16(w.seed, 9, rows, H_out)[:T] if bias else None
     out = torch.full((rows, H_out), 0x7FC1, dtype=torch.int16, device=DEV)
@@ -117,6 +130,21 @@ RAGGED = [
 def test_ragged_shapes(T, H, E, K, A, dtype, mask, weights, bias):
     w = I.custom(f"ne_{T}_{H}_{K}", 500 + T, T, H, E, K, A, dtype)
     _run(w, mask=mask, weights=weights, bias=bias, oob_every=5)
+
+
+FP32_COMBINE = [
+    # T, H, E, K, A, dtype, mask, bias: binary32 rows through the non-expand combine
+    (4096, 7168, 256, 8, 128, I.BF16, 0.0, True),    # the prefill shape, 28 KiB rows
+    (333, 520, 32, 4, 16, I.BF16, 0.3, True),         # 130 chunks per row: a two-chunk tail slice
+    (777, 1024, 256, 8, 1, I.FP8_E4M3, 0.9, False),   # many tokens receive nothing; no bias
+    (1, 256, 8, 1, 1, I.BF16, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,A,dtype,mask,bias", FP32_COMBINE)
+def test_combine_fp32_rows(T, H, E, K, A, dtype, mask, bias):
+    w = I.custom(f"ne32_{T}_{H}", 900 + T, T, H, E, K, A, dtype)
+    _run(w, mask=mask, bias=bias, oob_every=7, combine_fp32=True)
 
 
 def test_nothing_received():

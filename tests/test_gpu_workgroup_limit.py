@@ -140,6 +140,16 @@ def test_capped_non_expand_matches_oracle(capped_stream, cap):
     assert np.array_equal(to_host(recv_w)[:n].view(np.uint32), rw.view(np.uint32))
     want = oracle.combine_compact(y, ref["dst_slot"], ref["recv_src_metadata"], n, bias)
     assert pins.bf16_ulp_distance(to_host(out, np.uint16), want).max() <= 1
+    # binary32 rows under the same cap
+    yf, bf = I.normal_f32(w.seed, 4, w.T, w.H), I.normal_f32(w.seed, 9, w.T, w.H)
+    yf_d, bf_d = to_dev(yf), to_dev(bf)
+    out32 = torch.empty((w.T, w.H), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    B.ep_combine_compact(yf_d, bf_d, lay["dst_slot"], lay["meta"], lay["num_recv"], w.T, w.H, w.K,
+                         B.EP_FP32, out32, s)
+    s.synchronize()
+    want32 = oracle.combine_compact_f32(yf, ref["dst_slot"], ref["recv_src_metadata"], n, bf)
+    assert np.array_equal(to_host(out32).view(np.uint32), want32.view(np.uint32))
 
 
 def test_two_host_threads_two_streams_two_caps():
