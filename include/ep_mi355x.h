@@ -196,7 +196,14 @@ int ep_layout_noalloc(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
  *                   EP_FP8_E4M3: e4m3 bytes [T, hidden];
  *                   EP_FP4X2: packed e2m1 pairs, [T, hidden] bytes (2*hidden values)
  *   x_scales        fp32 [T, S] with S = values per row / 128, or NULL; only for
- *                   fp8 and fp4x2 (values per row a multiple of 128)
+ *                   fp8 and fp4x2 (values per row a multiple of 128). The
+ *                   scale rows are optional for both byte dtypes, fp8
+ *                   included: the payload travels as bytes either way ("MORI
+ *                   JIT v2" section 3.7; its HIP backend moves fp8 rows with
+ *                   no scales), so fp8 with x_scales = NULL is accepted and
+ *                   moves the rows alone, and the multiple-of-128 rule
+ *                   applies only when scales are given. A stricter contract,
+ *                   fp8 always with scales, is left to the caller.
  *   topk_weights    fp32 [T, K] or NULL
  *   dst_slot        int32 [T, K], as produced by ep_layout
  *   expand_x        [capacity_rows, hidden] of the same element type as x

@@ -111,6 +111,18 @@ def disp(x=FAKE, xs=None, dst=FAKE, T=4096, H=7168, K=8, dt=B.EP_BF16, cap=65280
     return (x, xs, None, dst, T, H, K, dt, cap, X, Xs, None)
 
 
+def test_fp8_without_scales_passes_the_checks(L):
+    """fp8 rows may travel without scale rows (the header's reading: the payload is
+    bytes either way): a NULL x_scales passes every argument check, and so does a
+    hidden size that is not a multiple of 128 then. An uncompiled topk (3) stops
+    each call at the capability gate, after those checks and before any launch."""
+    for H in (7168, 7184):
+        assert _code(B.ep_dispatch, *disp(dt=B.EP_FP8_E4M3, H=H, K=3)) == B.EP_EUNSUPPORTED
+    # with scale rows, hidden must be a multiple of 128 values
+    assert _code(B.ep_dispatch, *disp(dt=B.EP_FP8_E4M3, H=7184, K=3, xs=FAKE, Xs=FAKE)) == \
+        B.EP_EINVAL
+
+
 def test_dispatch_rejections(L):
     assert _code(B.ep_dispatch, *disp(H=7169)) == B.EP_EINVAL           # 16-byte rows
     assert _code(B.ep_dispatch, *disp(H=7000)) == B.EP_EUNSUPPORTED     # aligned but not compiled
