@@ -67,10 +67,10 @@ def lib(path: str = None) -> ctypes.CDLL:
     L.ep_layout_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.ep_layout_workspace_bytes.restype = _sz
     L.ep_layout.argtypes = [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
-                            _vp]
+                            _vp, _sz, _vp]
     L.ep_layout.restype = ctypes.c_int
     L.ep_layout_noalloc.argtypes = [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp,
-                                    _vp, _vp]
+                                    _vp, _vp, _sz, _vp]
     L.ep_layout_noalloc.restype = ctypes.c_int
     L.ep_dispatch.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
                               _vp]
@@ -139,22 +139,31 @@ def ep_layout_workspace_bytes(num_tokens: int, topk: int, num_experts: int) -> i
     return int(lib().ep_layout_workspace_bytes(num_tokens, topk, num_experts))
 
 
+def _nbytes(a, nbytes):
+    """Byte count of an optional read-ahead region: given, else the tensor's own size."""
+    if a is None:
+        return 0
+    return int(a.nbytes) if nbytes is None else int(nbytes)
+
+
 def ep_layout(topk_idx, num_tokens, topk, num_experts, expert_alignment, capacity_rows,
               counts, offsets, dst_slot, recv_src_metadata, num_recv, workspace,
-              workspace_bytes, stream=None, dispatch_plan=None):
+              workspace_bytes, stream=None, dispatch_plan=None, prefetch=None,
+              prefetch_bytes=None):
     _check(lib().ep_layout(_p(topk_idx), num_tokens, topk, num_experts, expert_alignment,
                            capacity_rows, _p(counts), _p(offsets), _p(dst_slot),
                            _p(recv_src_metadata), _p(num_recv), _p(workspace),
-                           workspace_bytes, _p(dispatch_plan), _s(stream)))
+                           workspace_bytes, _p(dispatch_plan), _p(prefetch),
+                           _nbytes(prefetch, prefetch_bytes), _s(stream)))
 
 
 def ep_layout_noalloc(topk_idx, num_tokens, topk, num_experts, expert_alignment, capacity_rows,
                       counts, offsets, dst_slot, recv_src_metadata, num_recv, stream=None,
-                      dispatch_plan=None):
+                      dispatch_plan=None, prefetch=None, prefetch_bytes=None):
     _check(lib().ep_layout_noalloc(_p(topk_idx), num_tokens, topk, num_experts, expert_alignment,
                                    capacity_rows, _p(counts), _p(offsets), _p(dst_slot),
                                    _p(recv_src_metadata), _p(num_recv), _p(dispatch_plan),
-                                   _s(stream)))
+                                   _p(prefetch), _nbytes(prefetch, prefetch_bytes), _s(stream)))
 
 
 def ep_dispatch(x, x_scales, topk_weights, dst_slot, num_tokens, hidden, topk, dtype,

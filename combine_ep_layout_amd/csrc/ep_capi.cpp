@@ -145,6 +145,15 @@ size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_e
 
 namespace {
 
+// The optional read-ahead region of ep_layout: NULL with 0 bytes, or a
+// 4-byte aligned pointer (the layout reads 4-byte words of it).
+int check_prefetch(const char *what, const void *prefetch, size_t prefetch_bytes) {
+  if (prefetch == nullptr && prefetch_bytes != 0)
+    return fail(EP_EINVAL, "%s: prefetch is NULL but prefetch_bytes is %zu", what, prefetch_bytes);
+  if (!aligned(prefetch, 4)) return fail(EP_EINVAL, "%s: prefetch must be 4-byte aligned", what);
+  return EP_OK;
+}
+
 // Checks of ep_layout's arguments (shared with ep_layout_dispatch).
 int check_layout(const char *what, const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
                  int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
@@ -273,7 +282,7 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
               int32_t expert_alignment, int64_t capacity_rows, int32_t *counts,
               int32_t *offsets, int32_t *dst_slot, int32_t *recv_src_metadata,
               int32_t *num_recv, void *workspace, size_t workspace_bytes, int32_t *dispatch_plan,
-              void *stream) {
+              const void *prefetch, size_t prefetch_bytes, void *stream) {
   try {
     const char *what = "ep_layout";
     if (int rc = check_layout(what, topk_idx, num_tokens, topk, num_experts, expert_alignment,
@@ -282,9 +291,10 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
       return rc;
     if (!aligned(dispatch_plan, 8))
       return fail(EP_EINVAL, "%s: dispatch_plan must be 8-byte aligned", what);
+    if (int rc = check_prefetch(what, prefetch, prefetch_bytes)) return rc;
     ep::LayoutArgs a{topk_idx, num_tokens, topk, num_experts, expert_alignment, counts, offsets,
                      dst_slot, recv_src_metadata, num_recv, workspace, dispatch_plan,
-                     (hipStream_t)stream};
+                     (hipStream_t)stream, prefetch, (int64_t)prefetch_bytes};
     return from_launch(ep::launch_layout(a), what);
   } catch (const std::exception &e) {
     return fail(EP_EHIP, "ep_layout: %s", e.what());
@@ -297,7 +307,7 @@ int ep_layout_noalloc(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
                       int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
                       int32_t *counts, int32_t *offsets, int32_t *dst_slot,
                       int32_t *recv_src_metadata, int32_t *num_recv, int32_t *dispatch_plan,
-                      void *stream) {
+                      const void *prefetch, size_t prefetch_bytes, void *stream) {
   try {
     const char *what = "ep_layout_noalloc";
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
@@ -331,9 +341,10 @@ int ep_layout_noalloc(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
       return rc;
     if (!aligned(dispatch_plan, 8))
       return fail(EP_EINVAL, "%s: dispatch_plan must be 8-byte aligned", what);
+    if (int rc = check_prefetch(what, prefetch, prefetch_bytes)) return rc;
     ep::LayoutArgs a{topk_idx, num_tokens, topk, num_experts, expert_alignment, counts, offsets,
                      dst_slot, recv_src_metadata, num_recv, scratch, dispatch_plan,
-                     (hipStream_t)stream};
+                     (hipStream_t)stream, prefetch, (int64_t)prefetch_bytes};
     return from_launch(ep::launch_layout(a), what);
   } catch (const std::exception &e) {
     return fail(EP_EHIP, "ep_layout_noalloc: %s", e.what());

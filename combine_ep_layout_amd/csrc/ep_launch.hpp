@@ -28,6 +28,8 @@ struct LayoutArgs {
   void *workspace;
   int32_t *plan;  // [T*K] (entry, slot) pairs, or NULL
   hipStream_t stream;
+  const void *prefetch = nullptr;  // memory to read ahead into the last-level cache, or NULL
+  int64_t prefetch_bytes = 0;
 };
 
 struct DispatchArgs {

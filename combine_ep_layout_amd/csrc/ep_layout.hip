@@ -101,6 +101,40 @@ __device__ __forceinline__ RankLds rank_lds(int E, int NW) {
   return s;
 }
 
+// Optional read-ahead of memory the caller reads next (the token rows, before
+// dispatch). The layout's launches leave most of the chip idle; workgroups
+// added after the layout's own read one 4-byte word of every 128-byte line of
+// their share with ordinary loads, which pulls those lines into the
+// last-level cache while the layout runs. The words are only kept alive, never
+// used. Measured on MI355X (prefill, 58.7 MB of rows evicted from the cache):
+// with the rows read ahead, dispatch takes about as long as with the rows
+// cached (a burst of reads while the layout runs costs far less than the same
+// reads interleaved with dispatch's writes).
+struct Prefetch {
+  const uint32_t *p;  // NULL: none
+  int64_t l0, l1;     // this launch's share, in 128-byte lines from p
+  int blocks;         // workgroups given to it, after the layout's own
+};
+
+__device__ __forceinline__ void prefetch_share(const Prefetch &pf, int q) {
+  constexpr int kDepth = 8;  // loads in flight per lane
+  const int lane = lane_id();
+  const int64_t w = (int64_t)q * kWavesMax + threadIdx.x / kWave;
+  const int64_t nw = (int64_t)pf.blocks * kWavesMax;
+  // groups of 64 lines, one per load instruction: wave w takes groups w, w + nw, ...
+  const int64_t groups = (pf.l1 - pf.l0 + kWave - 1) / kWave;
+  for (int64_t g0 = w; g0 < groups; g0 += nw * kDepth) {
+    uint32_t v[kDepth];
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      const int64_t l = pf.l0 + (g0 + j * nw) * kWave + lane;
+      v[j] = l < pf.l1 ? pf.p[l * 32] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) asm volatile("" ::"v"(v[j]));
+  }
+}
+
 // Step 1. Also leaves s.tok[j] = 1 for every token j of the tile with an
 // unmasked entry (0 otherwise) and s.total[e] = entries of expert e.
 template <int K, int NW>
@@ -242,7 +276,11 @@ template <int K, int NW>
 __global__ __launch_bounds__(kThreads) void ep_layout_single_tile(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
-    int32_t *__restrict__ num_recv, int32_t *__restrict__ plan) {
+    int32_t *__restrict__ num_recv, int32_t *__restrict__ plan, Prefetch pf) {
+  if (blockIdx.x >= 1) {  // read-ahead workgroups
+    prefetch_share(pf, blockIdx.x - 1);
+    return;
+  }
   __shared__ int s_scan[2 * kWavesMax];
   __shared__ int s_flag[kWavesMax];
   const RankLds s = rank_lds(E, NW);
@@ -311,9 +349,10 @@ __device__ __forceinline__ void copy_unit(const u32x4 &v, int64_t t, int j, int 
 // stages the T*K keys in LDS once (a masked entry gets the largest key);
 // each lane then holds 16 of them, and a wave counts, for each entry it
 // copies, the keys below that entry's key and sums the count over the wave.
-// The wave's first row slice is loaded before the keys are staged, so the
-// two load latencies overlap. Workgroup 0 writes the layout's outputs and
-// copies nothing; workgroups 1.. share the (entry, slice) units.
+// The row slices of a wave's first kPre units are loaded before the keys are
+// staged, so their latencies overlap each other and the key load. Workgroup
+// 0 writes the layout's outputs and copies nothing; workgroups 1.. share the
+// (entry, slice) units.
 template <int K, bool WIDE>
 __device__ __forceinline__ void copy_counted(
     const int32_t *__restrict__ topk_idx, int T, int E, const u32x4 *__restrict__ x,
@@ -321,6 +360,7 @@ __device__ __forceinline__ void copy_counted(
     const float *__restrict__ topk_weights, int64_t capacity, u32x4 *__restrict__ expand_x,
     u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights) {
   constexpr int kNoKey = 0x7fffffff;
+  constexpr int kPre = 4;  // units per wave whose row slices load before the keys
   int *s_key = (int *)g_smem;  // kThreads keys
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -328,37 +368,42 @@ __device__ __forceinline__ void copy_counted(
   const int slices = (row_chunks + kWave - 1) / kWave;
   const int64_t units = (int64_t)n * slices;
   const int64_t stride = (int64_t)(gridDim.x - 1) * kWavesMax;
-  int64_t u = (int64_t)(blockIdx.x - 1) * kWavesMax + wave;
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (u < units) {
-    const int j = (int)(u / slices);
-    const int c = (int)(u - (int64_t)j * slices) * kWave + lane;
-    if (c < row_chunks) v = x[(int64_t)(j / K) * row_chunks + c];
-  }
+  const int64_t u0 = (int64_t)(blockIdx.x - 1) * kWavesMax + wave;
+  auto load = [&](int64_t u) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (u < units) {
+      const int j = (int)(u / slices);
+      const int c = (int)(u - (int64_t)j * slices) * kWave + lane;
+      if (c < row_chunks) v = x[(int64_t)(j / K) * row_chunks + c];
+    }
+    return v;
+  };
+  u32x4 pre[kPre];
+#pragma unroll
+  for (int p = 0; p < kPre; ++p) pre[p] = load(u0 + p * stride);
   const int id = tid < n ? topk_idx[tid] : -1;
   s_key[tid] = (id >= 0 && id < E) ? (id << kRankBits) | tid : kNoKey;
   __syncthreads();
   int key[kWavesMax];  // entries q * 64 + lane
 #pragma unroll
   for (int q = 0; q < kWavesMax; ++q) key[q] = s_key[q * kWave + lane];
-  for (bool first = true; u < units; u += stride, first = false) {
+  auto copy = [&](int64_t u, const u32x4 &v) {
     const int j = (int)(u / slices);
     const int slice = (int)(u - (int64_t)j * slices);
     const int kj = __builtin_amdgcn_readfirstlane(s_key[j]);
-    if (kj == kNoKey) continue;  // masked: no slot
+    if (kj == kNoKey) return;  // masked: no slot
     int below = 0;
 #pragma unroll
     for (int q = 0; q < kWavesMax; ++q) below += key[q] < kj ? 1 : 0;
     const int d = __builtin_amdgcn_readfirstlane(wave_sum(below));
-    if (d >= capacity) continue;
-    const int64_t t = j / K;
-    if (!first) {
-      const int c = slice * kWave + lane;
-      if (c < row_chunks) v = x[t * row_chunks + c];
-    }
-    copy_unit<WIDE>(v, t, j, slice, d, row_chunks, x_scales, scale_chunks, topk_weights,
+    if (d >= capacity) return;
+    copy_unit<WIDE>(v, j / K, j, slice, d, row_chunks, x_scales, scale_chunks, topk_weights,
                     expand_x, expand_scales, expand_weights);
-  }
+  };
+#pragma unroll
+  for (int p = 0; p < kPre; ++p)
+    if (u0 + p * stride < units) copy(u0 + p * stride, pre[p]);
+  for (int64_t u = u0 + kPre * stride; u < units; u += stride) copy(u, load(u));
 }
 
 // Layout and dispatch in one launch for a batch that fits one tile (a
@@ -618,8 +663,13 @@ template <int K, int NW, bool LOOP>
 __global__ __launch_bounds__(kThreads) void ep_layout_fused_tiles(
     const int32_t *__restrict__ topk_idx, int T, int E, int A, int num_tiles,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot,
-    int32_t *__restrict__ meta, int32_t *__restrict__ num_recv, int32_t *__restrict__ plan) {
+    int32_t *__restrict__ meta, int32_t *__restrict__ num_recv, int32_t *__restrict__ plan,
+    Prefetch pf) {
   if constexpr (!LOOP) {
+    if ((int)blockIdx.x >= num_tiles) {  // read-ahead workgroups
+      prefetch_share(pf, blockIdx.x - num_tiles);
+      return;
+    }
     fused_tile<K, NW>(topk_idx, T, E, A, counts, offsets, dst_slot, meta, num_recv, plan,
                       blockIdx.x);
   } else {
@@ -654,8 +704,12 @@ template <int K, int NW, bool LOOP>
 __global__ __launch_bounds__(kThreads) void ep_layout_tile_histogram(
     const int32_t *__restrict__ topk_idx, int T, int E, int num_tiles,
     int32_t *__restrict__ dst_slot, int32_t *__restrict__ tile_counts,
-    int32_t *__restrict__ tile_recv) {
+    int32_t *__restrict__ tile_recv, Prefetch pf) {
   if constexpr (!LOOP) {
+    if ((int)blockIdx.x >= num_tiles) {  // read-ahead workgroups
+      prefetch_share(pf, blockIdx.x - num_tiles);
+      return;
+    }
     histogram_tile<K, NW>(topk_idx, T, E, dst_slot, tile_counts, tile_recv, blockIdx.x);
   } else {
     for (int b = blockIdx.x; b < num_tiles; b += gridDim.x) {
@@ -795,8 +849,12 @@ __global__ __launch_bounds__(kThreads) void ep_layout_tile_assign(
     int T, int E, int A, int num_tiles, const int32_t *__restrict__ tile_counts,
     const int32_t *__restrict__ tile_recv, TileScan scan, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ dst_slot, int32_t *__restrict__ meta,
-    int32_t *__restrict__ num_recv, int32_t *__restrict__ plan) {
+    int32_t *__restrict__ num_recv, int32_t *__restrict__ plan, Prefetch pf) {
   if constexpr (!LOOP) {
+    if ((int)blockIdx.x >= num_tiles) {  // read-ahead workgroups
+      prefetch_share(pf, blockIdx.x - num_tiles);
+      return;
+    }
     assign_tile<K, NW, SCANNED>(T, E, A, num_tiles, tile_counts, tile_recv, scan, counts, offsets,
                                 dst_slot, meta, num_recv, plan, blockIdx.x);
   } else {
@@ -884,20 +942,49 @@ inline bool use_tile_scan(int B, int E) {
   return (B + P - 1) / P > kScanMinWalk;
 }
 
+// Most bytes the read-ahead covers: half of MI355X's 256 MiB last-level cache
+// (dispatch's other traffic streams past it); larger token buffers never
+// stay cached, and dispatch handles them with its grouped kernel.
+constexpr int64_t kPrefetchMaxBytes = int64_t(128) << 20;
+// Read-ahead workgroups per launch: one compute unit's memory path moves far
+// less than HBM can (about 33-54 GB/s measured on MI355X), so the read-ahead
+// is spread over most of the chip, at least 1024 lines (one load per lane of
+// each of 16 waves) per workgroup.
+constexpr int kPrefetchMaxBlocks = 224;
+constexpr int64_t kPrefetchMinLinesPerBlock = int64_t(kWavesMax) * kWave;
+
+// The read-ahead share [part, part + 1) of `parts` of a launch: nothing
+// under a workgroup cap (the extra workgroups would exceed it).
+inline Prefetch prefetch_part(const LayoutArgs &a, int cap, int part, int parts) {
+  Prefetch pf{nullptr, 0, 0, 0};
+  if (a.prefetch == nullptr || cap > 0) return pf;
+  const int64_t lines = std::min<int64_t>(a.prefetch_bytes, kPrefetchMaxBytes) / 128;
+  pf.p = (const uint32_t *)a.prefetch;
+  pf.l0 = lines * part / parts;
+  pf.l1 = lines * (part + 1) / parts;
+  pf.blocks = (int)std::min<int64_t>((pf.l1 - pf.l0 + kPrefetchMinLinesPerBlock - 1) /
+                                         kPrefetchMinLinesPerBlock, kPrefetchMaxBlocks);
+  return pf;
+}
+
 template <int K, int NW, bool LOOP>
 int layout_launch(const LayoutArgs &a, int B, unsigned G, int cap) {
   const size_t shm_rank = rank_lds_bytes(a.E, NW);
   if ((int64_t)a.T * K <= kFusedMaxEntries) {
+    const Prefetch pf = LOOP ? Prefetch{nullptr, 0, 0, 0} : prefetch_part(a, cap, 0, 1);
     ep_layout_fused_tiles<K, NW, LOOP>
-        <<<G, kThreads, shm_rank + sizeof(int) * (size_t)(4 * a.E), a.stream>>>(
+        <<<G + pf.blocks, kThreads, shm_rank + sizeof(int) * (size_t)(4 * a.E), a.stream>>>(
             a.topk_idx, a.T, a.E, a.A, B, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv,
-            a.plan);
+            a.plan, pf);
     return launch_status();
   }
+  // the read-ahead is split between the first and the last launch
+  const Prefetch pf0 = LOOP ? Prefetch{nullptr, 0, 0, 0} : prefetch_part(a, cap, 0, 2);
+  const Prefetch pf1 = LOOP ? Prefetch{nullptr, 0, 0, 0} : prefetch_part(a, cap, 1, 2);
   int32_t *tile_counts = (int32_t *)a.workspace;
   int32_t *tile_recv = tile_counts + (size_t)B * a.E;
-  ep_layout_tile_histogram<K, NW, LOOP><<<G, kThreads, shm_rank, a.stream>>>(
-      a.topk_idx, a.T, a.E, B, a.dst_slot, tile_counts, tile_recv);
+  ep_layout_tile_histogram<K, NW, LOOP><<<G + pf0.blocks, kThreads, shm_rank, a.stream>>>(
+      a.topk_idx, a.T, a.E, B, a.dst_slot, tile_counts, tile_recv, pf0);
   const size_t shm_assign = sizeof(int) * (size_t)(3 * a.E);
   if (use_tile_scan(B, a.E)) {
     int32_t *tile_base = tile_recv + B;
@@ -909,13 +996,14 @@ int layout_launch(const LayoutArgs &a, int B, unsigned G, int cap) {
     ep_layout_tile_scan<<<gs, kThreads, 0, a.stream>>>(tile_counts, tile_recv, B, a.E, tile_base,
                                                         expert_total, recv_base, recv_total);
     const TileScan scan{tile_base, expert_total, recv_base, recv_total};
-    ep_layout_tile_assign<K, NW, LOOP, true><<<G, kThreads, shm_assign, a.stream>>>(
+    ep_layout_tile_assign<K, NW, LOOP, true><<<G + pf1.blocks, kThreads, shm_assign, a.stream>>>(
         a.T, a.E, a.A, B, tile_counts, tile_recv, scan, a.counts, a.offsets, a.dst_slot, a.meta,
-        a.num_recv, a.plan);
+        a.num_recv, a.plan, pf1);
   } else {
-    ep_layout_tile_assign<K, NW, LOOP, false><<<G, kThreads, shm_assign, a.stream>>>(
-        a.T, a.E, a.A, B, tile_counts, tile_recv, TileScan{}, a.counts, a.offsets, a.dst_slot,
-        a.meta, a.num_recv, a.plan);
+    ep_layout_tile_assign<K, NW, LOOP, false>
+        <<<G + pf1.blocks, kThreads, shm_assign, a.stream>>>(
+            a.T, a.E, a.A, B, tile_counts, tile_recv, TileScan{}, a.counts, a.offsets,
+            a.dst_slot, a.meta, a.num_recv, a.plan, pf1);
   }
   return launch_status();
 }
@@ -923,15 +1011,16 @@ int layout_launch(const LayoutArgs &a, int B, unsigned G, int cap) {
 template <int K, int NW>
 int layout_impl(const LayoutArgs &a) {
   const int B = tiles_for<K, NW>(a.T);
+  const int cap = stream_workgroup_limit(a.stream);
   if (B <= 1) {
     const size_t shm_rank = rank_lds_bytes(a.E, NW);
+    const Prefetch pf = prefetch_part(a, cap, 0, 1);
     ep_layout_single_tile<K, NW>
-        <<<1, kThreads, shm_rank + sizeof(int) * (size_t)(2 * a.E), a.stream>>>(
+        <<<1 + pf.blocks, kThreads, shm_rank + sizeof(int) * (size_t)(2 * a.E), a.stream>>>(
             a.topk_idx, a.T, a.E, a.A, a.counts, a.offsets, a.dst_slot, a.meta, a.num_recv,
-            a.plan);
+            a.plan, pf);
     return launch_status();
   }
-  const int cap = stream_workgroup_limit(a.stream);
   if (cap > 0 && cap < B) return layout_launch<K, NW, true>(a, B, (unsigned)cap, cap);
   return layout_launch<K, NW, false>(a, B, (unsigned)B, cap);
 }

@@ -135,13 +135,32 @@ size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_e
  *                     (prefill with 470 MB of rows: dispatch 87 -> 83 us for
  *                     0.1 us more layout). At 120 MB of rows and below it
  *                     gains about what it costs the layout (0.1-0.4 us).
+ *   prefetch,         optional read-ahead (NULL and 0: none): device memory
+ *   prefetch_bytes    the caller reads next, typically the token rows x
+ *                     (and their scale rows) that ep_dispatch copies. The
+ *                     layout leaves most compute units idle; workgroups
+ *                     added to its launches read one 4-byte word of every
+ *                     128-byte line of the first min(prefetch_bytes, 128 MiB)
+ *                     bytes with ordinary loads, which brings those lines
+ *                     into the last-level cache while the layout runs. It
+ *                     reads only inside [prefetch, prefetch + prefetch_bytes),
+ *                     writes nothing there and changes no result. Ignored
+ *                     under a workgroup cap. The pointer must be 4-byte
+ *                     aligned; NULL with nonzero bytes is EP_EINVAL.
+ *                     Measured on MI355X (prefill step, 4096 tokens of
+ *                     hidden 7168, 58.7 MB of rows): with the rows not in the
+ *                     cache the step takes 184 us with the read-ahead against
+ *                     197 us without; with the rows cached, 177 against 173
+ *                     us (the reads then only add work). Worth asking for
+ *                     when x was produced long before dispatch.
  * Results are a pure function of the inputs (no atomics whose order matters).
  */
 int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t num_experts,
               int32_t expert_alignment, int64_t capacity_rows, int32_t *counts,
               int32_t *offsets, int32_t *dst_slot, int32_t *recv_src_metadata,
               int32_t *num_recv, void *workspace, size_t workspace_bytes,
-              int32_t *dispatch_plan, void *stream);
+              int32_t *dispatch_plan, const void *prefetch, size_t prefetch_bytes,
+              void *stream);
 
 /*
  * Bytes of the library's fixed layout scratch, one copy per GPU (8 MiB):
@@ -177,7 +196,7 @@ int ep_layout_noalloc(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
                       int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,
                       int32_t *counts, int32_t *offsets, int32_t *dst_slot,
                       int32_t *recv_src_metadata, int32_t *num_recv, int32_t *dispatch_plan,
-                      void *stream);
+                      const void *prefetch, size_t prefetch_bytes, void *stream);
 
 /*
  * Dispatch in the expand layout (DeepEP overall architecture, dispatch copy
@@ -233,10 +252,13 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
  * (the dispatch arguments take their slots from this layout). When T*K fits
  * one layout tile (the floor(W / K) tokens of ep_layout's dispatch_plan,
  * W = 1024, 512 or 256 by num_experts: a decode step, say) it runs as a
- * single launch. Every workgroup ranks all entries itself and workgroup 0
- * writes the layout's outputs, which saves a launch and the trip of dst_slot
- * through memory. Larger batches run the two launches of ep_layout and
- * ep_dispatch (token-major, no plan). Results are identical either way.
+ * single launch: workgroup 0 ranks all entries and writes the layout's
+ * outputs, and the copying workgroups find their entries' slots in their own
+ * LDS (with expert_alignment 1 and no workgroup cap, by counting the entries
+ * whose (expert id, entry index) is smaller; otherwise by ranking all entries
+ * as workgroup 0 does). This saves a launch and the trip of dst_slot through
+ * memory. Larger batches run the launches of ep_layout and ep_dispatch
+ * (token-major, no plan, no read-ahead). Results are identical either way.
  */
 int ep_layout_dispatch(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
                        int32_t num_experts, int32_t expert_alignment, int64_t capacity_rows,

@@ -27,7 +27,7 @@ def to_host(t: torch.Tensor, dtype=None) -> np.ndarray:
 
 
 def dev_layout(idx_d: torch.Tensor, T: int, K: int, E: int, A: int, cap: int, stream=None,
-               plan: bool = False):
+               plan: bool = False, prefetch=None):
     """Run ep_layout; returns a dict of device tensors (with the dispatch plan if asked)."""
     counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
     offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
@@ -38,7 +38,7 @@ def dev_layout(idx_d: torch.Tensor, T: int, K: int, E: int, A: int, cap: int, st
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
     pl = torch.full((max(T * K, 1), 2), -9, dtype=torch.int32, device=DEV) if plan else None
     B.ep_layout(idx_d if T else None, T, K, E, A, cap, counts, offsets, dst if T else None,
-                meta if T else None, nrecv, ws, wsb, stream, dispatch_plan=pl)
+                meta if T else None, nrecv, ws, wsb, stream, dispatch_plan=pl, prefetch=prefetch)
     out = {"counts": counts, "offsets": offsets, "dst_slot": dst[:T], "meta": meta[:T],
            "num_recv": nrecv}
     if plan:

@@ -101,6 +101,13 @@ def test_layout_rejections(L):
     assert _code(B.ep_layout, *lay(idx=None)) == B.EP_EINVAL
     assert _code(B.ep_layout, *lay(counts=None)) == B.EP_EINVAL
     assert _code(B.ep_layout, *lay(T=1 << 28, cap=1 << 40)) == B.EP_EINVAL  # T*K overflows int32
+    with pytest.raises(B.EpError) as ei:  # a read-ahead region needs a pointer
+        B.ep_layout(*lay(), prefetch=0, prefetch_bytes=1 << 20)
+    assert ei.value.code == B.EP_EINVAL and "prefetch" in str(ei.value)
+    with pytest.raises(B.EpError) as ei:  # read as 4-byte words
+        B.ep_layout(*lay(ws=None, wsb=0, T=64, K=2, E=16, A=1, cap=128), prefetch=FAKE + 2,
+                    prefetch_bytes=4096)
+    assert ei.value.code == B.EP_EINVAL and "prefetch" in str(ei.value)
     plan_4 = FAKE + 4  # (entry, slot) pairs need 8-byte alignment
     with pytest.raises(B.EpError) as ei:
         B.ep_layout(*lay(), dispatch_plan=plan_4)

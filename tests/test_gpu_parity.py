@@ -297,6 +297,42 @@ def test_dispatch_plan(T, H, E, K, A, mask, wg_cap, dtype):
     check_dispatch(dc, ref["dst_slot"])
 
 
+READ_AHEAD = [
+    # T, E, K, A, read-ahead bytes, workgroup cap: every layout launch shape
+    (100, 256, 8, 1, 100 * 14336, 0),            # one tile
+    (1024, 64, 8, 1, 1024 * 14336, 0),           # one launch over 8 tiles
+    (4096, 256, 8, 128, 4096 * 14336, 0),        # two launches, split read-ahead
+    (20000, 1024, 8, 4, 20000 * 512 + 1000, 0),  # tile scan; not whole 128-byte lines
+    (4096, 256, 8, 128, 200 << 20, 0),           # beyond the 128 MiB it reads
+    (4096, 256, 8, 128, 4096 * 14336, 7),        # capped: ignored
+    (333, 16, 2, 1, 3, 0),                       # less than one line
+]
+
+
+@pytest.mark.parametrize("T,E,K,A,nbytes,wg_cap", READ_AHEAD)
+def test_layout_read_ahead_changes_nothing(T, E, K, A, nbytes, wg_cap):
+    """ep_layout with a read-ahead region writes exactly what it writes without one."""
+    _say(f"[read-ahead] T={T} E={E} K={K} A={A} bytes={nbytes} cap={wg_cap}")
+    g = np.random.default_rng([T, E, 77])
+    idx = I.routing_uniform(g, T, E, K)
+    idx[g.random(idx.shape) < 0.05] = -1
+    region = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    s = torch.cuda.Stream()
+    try:
+        B.ep_set_workgroup_limit(s, wg_cap)
+        idx_d = to_dev(idx)
+        torch.cuda.synchronize()
+        lay = dev_layout(idx_d, T, K, E, A, T * K + E * (A - 1), stream=s, plan=True,
+                         prefetch=region)
+        s.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        B.ep_set_workgroup_limit(s, 0)
+    ref = oracle.layout(idx, E, A)
+    check_layout(layout_to_host(lay), ref)
+    assert np.array_equal(to_host(lay["plan"]), pins.dispatch_plan(ref["dst_slot"], E, K))
+
+
 FUSED = [
     # T, H, E, K, A, mask, dtype, scales, routing, workgroup cap: one tile fuses layout and
     # dispatch into one launch; larger batches fall back to two
