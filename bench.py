@@ -14,6 +14,8 @@ A batch that fits one layout tile (a decode step) calls ep_layout_dispatch
 (ep_layout_dispatch_compact) instead of the first two calls: one launch;
 --no-fused keeps them apart. Batches of at least 256 MiB of expand rows ask
 the layout for the dispatch plan and dispatch by it (--no-plan: token-major).
+--read-ahead hands x to ep_layout as its read-ahead region, so that x is in
+the last-level cache when dispatch starts.
 Each run times two cache modes (--cache both, the default; --cache warm or
 --cache cold, or --cold, times one). Warm: steps back to back on one buffer
 set, so x, read by the step before, is still in the 256 MB last-level cache
@@ -41,8 +43,9 @@ whole-step throughput: algorithmic HBM bytes of the three passes per step
 divided by the wall-clock step time (K steps bracketed by device
 synchronisation, no events inside). Per-kernel times come right after the
 timed loop: each pass is launched --event-steps times back to back (default
-50, at least 20) on the same stream and buffer rotation between two HIP
-events, and kernel_us is the mean per launch (an event drains the pipeline,
+50, at least 20; the C calls marshalled beforehand, so the host keeps ahead
+of even the layout's launches) with the step's buffer rotation between two
+HIP events, and kernel_us is the mean per launch (an event drains the pipeline,
 about 3 us, so events around each single launch would read several
 microseconds above the kernel's own duration as rocprofv3 reports it). The
 roofline object reports the dominant kernel's algorithmic bytes over that
@@ -347,6 +350,10 @@ def main():
     ap.add_argument("--no-plan", action="store_true",
                     help="expand path: never ask ep_layout for the dispatch plan (by default it is "
                          "used when the expand rows total at least PLAN_MIN_BYTES)")
+    ap.add_argument("--read-ahead", action="store_true",
+                    help="hand x to ep_layout as its read-ahead region: the layout's launches "
+                         "pull x into the last-level cache for dispatch (helps a cold x, costs a "
+                         "few microseconds when x is cached)")
     ap.add_argument("--no-fused", action="store_true",
                     help="call ep_layout and ep_dispatch (ep_dispatch_compact) separately even "
                          "when the batch fits one layout tile (by default ep_layout_dispatch "
@@ -487,7 +494,8 @@ def main():
                                      S["expand"], S["expand_s"], None, stream)
             else:
                 B.ep_layout(idx, w.T, w.K, w.E, w.A, w.cap, counts, offsets, dst, meta, nrecv, ws,
-                            wsb, stream, dispatch_plan=plan)
+                            wsb, stream, dispatch_plan=plan,
+                            prefetch=X["x"] if args.read_ahead else None)
 
         def run_dispatch(i, stream=stream):
             S, X = sets[i % nsets], x_sets[i % nx]
@@ -526,18 +534,25 @@ def main():
         # n_ev times back to back on the same stream, with the step's buffer
         # rotation, between two HIP events (an event drains the pipeline, about
         # 3 us each, so events around single launches would read several
-        # microseconds above the kernel's own duration). The mean per launch is
-        # the kernel's average launch duration.
+        # microseconds above the kernel's own duration). The C calls are
+        # marshalled beforehand, so the host issues them faster than even the
+        # layout's launches run. The mean per launch is the kernel's average
+        # duration.
         n_ev = max(20, args.event_steps)
         us = {}
         for name, fn in (("layout", run_layout), ("dispatch", run_dispatch),
                          ("combine", run_combine)):
+            calls = recorded_calls(B, lambda: [fn(args.steps + j) for j in range(n_ev)])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
             e0.record(stream)
-            for j in range(n_ev):
-                fn(args.steps + j)
+            failed = 0
+            for cfn, cargs in calls:
+                failed |= cfn(*cargs)
             e1.record(stream)
             torch.cuda.synchronize()
+            if failed:
+                raise SystemExit(f"bench: {name} failed: {B.ep_last_error()}")
             us[name] = e0.elapsed_time(e1) * 1e3 / n_ev
         if fused:  # layout ran inside the dispatch launch
             us = {"layout": 0.0, "dispatch": us["layout"], "combine": us["combine"]}
@@ -597,6 +612,36 @@ def main():
         torch.cuda.synchronize()
         B.ep_set_workgroup_limit(stream, 0)
     report(args, w, case, ref, runs, modes, copy_gbps, non_expand, use_plan, fused)
+
+
+class _CallRecorder:
+    """Stands in for the loaded library: records each C call with its marshalled
+    arguments instead of making it."""
+
+    def __init__(self, L):
+        self._L, self.calls = L, []
+
+    def __getattr__(self, name):
+        cfn = getattr(self._L, name)
+
+        def record(*cargs):
+            self.calls.append((cfn, cargs))
+            return 0
+        return record
+
+
+def recorded_calls(B, issue):
+    """The (C function, arguments) pairs the binding would call while `issue()`
+    runs, so a timing loop can make the calls without the binding's per-call
+    Python work (which exceeds a small kernel's own duration)."""
+    L = B.lib()
+    rec = _CallRecorder(L)
+    B._LIB = rec
+    try:
+        issue()
+    finally:
+        B._LIB = L
+    return rec.calls
 
 
 GEMM_SHAPE = (8192, 7168, 2048)  # M, K, N: bf16 [M, K] x [K, N], about one step's duration
@@ -739,6 +784,7 @@ def report(args, w, case, ref, runs, modes, copy_gbps, non_expand, plan_used=Fal
                    "dispatch_dtype": DTYPE_NAMES[w.dtype], "combine_dtype": DTYPE_NAMES[w.out_dtype],
                    "parallelism": "one GPU, all experts local", "path": args.path,
                    "dispatch_plan": plan_used,
+                   "layout_read_ahead": bool(args.read_ahead and not fused),
                    "layout_dispatch": (("one launch (ep_layout_dispatch_compact)" if non_expand
                                         else "one launch (ep_layout_dispatch)")
                                        if fused else "separate launches"),

@@ -132,3 +132,15 @@ def test_one_layout_tile_follows_the_tile_rule(T, K, E, one):
     """The step fuses layout and dispatch exactly when T*K fits one layout tile
     (floor(W / K) tokens, W by expert count, as the header states)."""
     assert bench.one_layout_tile(T, K, E) == one
+
+
+def test_recorded_calls_replay_the_binding():
+    """The per-kernel timing loop replays the C calls the binding would make: the
+    recorder captures each function with its marshalled arguments and restores the
+    library afterwards."""
+    from combine_ep_layout_amd import binding as B
+    L = B.lib()
+    calls = bench.recorded_calls(B, lambda: [B.ep_set_workgroup_limit(None, 0) for _ in range(3)])
+    assert B.lib() is L
+    assert len(calls) == 3 and all(cfn is L.ep_set_workgroup_limit for cfn, _ in calls)
+    assert all(cfn(*cargs) == 0 for cfn, cargs in calls)  # a cap of 0 on the null stream
