@@ -33,6 +33,11 @@ int fail(int code, const char *fmt, ...) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// A HIP error left on this thread by an earlier, unrelated call (another
+// library's, say) would otherwise be read back after our launch and reported
+// as its failure: each entry point drops it before launching anything.
+void discard_stale_error() { (void)hipGetLastError(); }
+
 int from_launch(int rc, const char *what) {
   if (rc == 0) {
     g_last_error[0] = '\0';
@@ -285,6 +290,7 @@ int ep_layout(const int32_t *topk_idx, int32_t num_tokens, int32_t topk, int32_t
               const void *prefetch, size_t prefetch_bytes, void *stream) {
   try {
     const char *what = "ep_layout";
+    discard_stale_error();
     if (int rc = check_layout(what, topk_idx, num_tokens, topk, num_experts, expert_alignment,
                               capacity_rows, counts, offsets, dst_slot, recv_src_metadata,
                               num_recv, workspace, workspace_bytes))
@@ -310,6 +316,7 @@ int ep_layout_noalloc(const int32_t *topk_idx, int32_t num_tokens, int32_t topk,
                       const void *prefetch, size_t prefetch_bytes, void *stream) {
   try {
     const char *what = "ep_layout_noalloc";
+    discard_stale_error();
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
     if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
       return fail(EP_EINVAL, "%s: num_experts must be in 1..%d (got %d)", what, EP_MAX_EXPERTS,
@@ -359,6 +366,7 @@ int ep_dispatch(const void *x, const float *x_scales, const float *topk_weights,
                 float *expand_weights, const int32_t *dispatch_plan, void *stream) {
   try {
     const char *what = "ep_dispatch";
+    discard_stale_error();
     int64_t row_bytes = 0;
     if (int rc = check_dispatch(what, x, x_scales, topk_weights, dst_slot, num_tokens, hidden,
                                 topk, dtype, capacity_rows, expand_x, expand_scales,
@@ -386,6 +394,7 @@ int ep_layout_dispatch(const int32_t *topk_idx, int32_t num_tokens, int32_t topk
                        float *expand_scales, float *expand_weights, void *stream) {
   try {
     const char *what = "ep_layout_dispatch";
+    discard_stale_error();
     if (int rc = check_layout(what, topk_idx, num_tokens, topk, num_experts, expert_alignment,
                               capacity_rows, counts, offsets, dst_slot, recv_src_metadata,
                               num_recv, workspace, workspace_bytes))
@@ -423,6 +432,7 @@ int ep_combine(const void *expert_out, const float *topk_weights, const void *bi
                int32_t dtype, int64_t capacity_rows, void *out, void *stream) {
   try {
     const char *what = "ep_combine";
+    discard_stale_error();
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
     if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2)
       return fail(EP_EINVAL, "%s: combine sums its input; byte dtype %d is rejected", what, dtype);
@@ -457,6 +467,7 @@ int ep_zero_padding(void *expand_x, int64_t row_bytes, float *expand_scales, int
                     void *stream) {
   try {
     const char *what = "ep_zero_padding";
+    discard_stale_error();
     if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
       return fail(EP_EINVAL, "%s: num_experts must be in 1..%d (got %d)", what, EP_MAX_EXPERTS,
                   num_experts);
@@ -492,6 +503,7 @@ int ep_dispatch_compact(const void *x, const float *x_scales, const int32_t *top
                         float *recv_topk_weights, void *stream) {
   try {
     const char *what = "ep_dispatch_compact";
+    discard_stale_error();
     int64_t row_bytes = 0, scale_cols = 0;
     if (int rc = check_dispatch_compact(what, x, x_scales, topk_idx, topk_weights, num_tokens,
                                         hidden, topk, dtype, recv_x, recv_scales, recv_topk_idx,
@@ -522,6 +534,7 @@ int ep_layout_dispatch_compact(const int32_t *topk_idx, int32_t num_tokens, int3
                                int32_t *recv_topk_idx, float *recv_topk_weights, void *stream) {
   try {
     const char *what = "ep_layout_dispatch_compact";
+    discard_stale_error();
     if (int rc = check_layout(what, topk_idx, num_tokens, topk, num_experts, expert_alignment,
                               capacity_rows, counts, offsets, dst_slot, recv_src_metadata,
                               num_recv, workspace, workspace_bytes))
@@ -559,6 +572,7 @@ int ep_combine_compact(const void *expert_out, const void *bias, const int32_t *
                        void *stream) {
   try {
     const char *what = "ep_combine_compact";
+    discard_stale_error();
     if (int rc = check_topk(what, num_tokens, topk)) return rc;
     if (dtype == EP_FP8_E4M3 || dtype == EP_FP4X2)
       return fail(EP_EINVAL, "%s: combine adds its input; byte dtype %d is rejected", what, dtype);
