@@ -41,7 +41,9 @@ Prints ONE JSON line: the first mode's figures at the top level, the other
 mode's in an object named after it ("cold" by default). `value` is
 whole-step throughput: algorithmic HBM bytes of the three passes per step
 divided by the wall-clock step time (K steps bracketed by device
-synchronisation, no events inside). Per-kernel times come right after the
+synchronisation, no events inside; the steps' C calls are marshalled
+beforehand and made directly, as a native caller would make them, so the
+Python binding's per-call work does not set the pace of small steps). Per-kernel times come right after the
 timed loop: each pass is launched --event-steps times back to back (default
 50, at least 20; the C calls marshalled beforehand, so the host keeps ahead
 of even the layout's launches) with the step's buffer rotation between two
@@ -524,12 +526,20 @@ def main():
         torch.cuda.synchronize()  # inputs were written on the default stream
         for i in range(max(args.warmup, nsets, nx)):
             step(i)
+        # The timed steps make the library's C calls directly, with their arguments
+        # marshalled beforehand: the binding's per-call Python work (about 5 us)
+        # would otherwise set the pace of small steps (a decode step whose
+        # dispatch kernel did nothing took as long as the real one).
+        timed_calls = recorded_calls(B, lambda: [step(i) for i in range(args.steps)])
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):  # the timed region: steps only, no events
-            step(i)
+        failed = 0
+        for cfn, cargs in timed_calls:  # the timed region: steps only, no events
+            failed |= cfn(*cargs)
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        if failed:
+            raise SystemExit(f"bench: a timed call failed: {B.ep_last_error()}")
         # Per-kernel times: right after the timed loop, each pass is launched
         # n_ev times back to back on the same stream, with the step's buffer
         # rotation, between two HIP events (an event drains the pipeline, about
