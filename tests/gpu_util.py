@@ -79,9 +79,11 @@ class DeviceCase:
             self.out = torch.full((max(w.T, 1), self.H_out), 0x7FC1, dtype=torch.int16, device=DEV)
         self.sentinel = sentinel
 
-    def layout(self, stream=None, plan=False):
+    def layout(self, stream=None, plan=False, read_ahead=False):
+        """ep_layout (with the dispatch plan if asked, and x as its read-ahead region if asked)."""
         w = self.w
-        self.lay = dev_layout(self.idx, w.T, w.K, w.E, w.A, w.cap, stream, plan=plan)
+        self.lay = dev_layout(self.idx, w.T, w.K, w.E, w.A, w.cap, stream, plan=plan,
+                              prefetch=self.x if read_ahead else None)
         return self.lay
 
     def layout_dispatch(self, stream=None, weights=True):

@@ -3,8 +3,10 @@
 Each case draws a compiled (hidden, topk, dtype), a token count, an expert
 count up to 1024, an alignment, a masking fraction, out-of-range ids, an
 optional bias and an optional workgroup cap, then runs layout, dispatch,
-combine (and, for bf16, the non-expand pair) through the C ABI; even seeds
-also ask the layout for the dispatch plan and dispatch through it. A second
+combine (and, for bf16, the non-expand pair, its combine also on binary32
+rows) through the C ABI; even seeds also ask the layout for the dispatch plan
+and dispatch through it, and seeds that are multiples of 3 hand the layout x
+as its read-ahead region. A second
 sweep draws batches that fit one layout tile and runs ep_layout_dispatch (one
 launch), with or without router weights and scale rows. A third draws large
 layouts alone (up to 70K tokens, every launch path of the layout). Bar as in
@@ -61,7 +63,7 @@ def test_random_shape(seed):
         B.ep_set_workgroup_limit(s, c["cap"])
         with torch.cuda.stream(s):
             dc = DeviceCase(case)
-            lay = dc.layout(stream=s, plan=plan)
+            lay = dc.layout(stream=s, plan=plan, read_ahead=seed % 3 == 0)
             dc.dispatch(stream=s, plan=plan)
             bias = None
             if c["bias"]:
@@ -120,6 +122,17 @@ def test_random_shape(seed):
         want2 = oracle.combine_compact(case.y[:max(n, 1)], ref["dst_slot"], ref["recv_src_metadata"],
                                        n, bias_h)
         assert pins.bf16_ulp_distance(to_host(out2, np.uint16), want2).max() <= 1
+        # binary32 rows through the same non-expand combine
+        y32 = I.normal_f32(w.seed, 4, max(w.T, 1), w.H)
+        b32 = I.normal_f32(w.seed, 9, w.T, w.H) if c["bias"] else None
+        out3 = torch.empty((w.T, w.H), dtype=torch.float32, device=DEV)
+        y32_d, b32_d = to_dev(y32), (to_dev(b32) if b32 is not None else None)
+        torch.cuda.synchronize()
+        B.ep_combine_compact(y32_d, b32_d, lay["dst_slot"], lay["meta"], lay["num_recv"], w.T, w.H,
+                             w.K, B.EP_FP32, out3)
+        torch.cuda.synchronize()
+        want3 = oracle.combine_compact_f32(y32, ref["dst_slot"], ref["recv_src_metadata"], n, b32)
+        assert np.array_equal(to_host(out3).view(np.uint32), want3.view(np.uint32)), "fp32 compact"
 
 
 def draw_one_tile(seed):
