@@ -12,8 +12,11 @@ ep_dispatch_compact (one row per received token, with its expert ids and
 router weights) and ep_combine_compact (rows back to token order).
 A batch that fits one layout tile (a decode step) calls ep_layout_dispatch
 (ep_layout_dispatch_compact) instead of the first two calls: one launch;
---no-fused keeps them apart. Batches of at least 256 MiB of expand rows ask
-the layout for the dispatch plan and dispatch by it (--no-plan: token-major).
+--no-fused keeps them apart, --one-call uses the fused call at every batch
+size (on the expand path with ep_layout_dispatch_workspace_bytes, so that
+large batches walk the plan it keeps in the workspace). Batches of at least
+256 MiB of expand rows ask the layout for the dispatch plan and dispatch by it
+(--no-plan: token-major).
 --read-ahead hands x to ep_layout as its read-ahead region, so that x is in
 the last-level cache when dispatch starts.
 Each run times two cache modes (--cache both, the default; --cache warm or
@@ -356,6 +359,10 @@ def main():
                     help="hand x to ep_layout as its read-ahead region: the layout's launches "
                          "pull x into the last-level cache for dispatch (helps a cold x, costs a "
                          "few microseconds when x is cached)")
+    ap.add_argument("--one-call", action="store_true",
+                    help="run layout and dispatch through ep_layout_dispatch "
+                         "(ep_layout_dispatch_compact) at every batch size, not only for one-tile "
+                         "batches (with the plan-sized workspace on the expand path)")
     ap.add_argument("--no-fused", action="store_true",
                     help="call ep_layout and ep_dispatch (ep_dispatch_compact) separately even "
                          "when the batch fits one layout tile (by default ep_layout_dispatch "
@@ -427,12 +434,14 @@ def main():
     dst = torch.empty((w.T, w.K), dtype=torch.int32, device=dev)
     meta = torch.empty((w.T, w.K + 2), dtype=torch.int32, device=dev)
     nrecv = torch.empty(1, dtype=torch.int32, device=dev)
-    wsb = B.ep_layout_workspace_bytes(w.T, w.K, w.E)
+    one_tile = one_layout_tile(w.T, w.K, w.E)
+    fused = not args.no_fused and (one_tile or args.one_call)
+    wsb = (B.ep_layout_dispatch_workspace_bytes(w.T, w.K, w.E) if fused and not non_expand
+           else B.ep_layout_workspace_bytes(w.T, w.K, w.E))
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     rows_out = w.T if non_expand else w.cap
-    use_plan = (not non_expand and not args.no_plan
+    use_plan = (not non_expand and not args.no_plan and not fused
                 and w.T * w.K * case.x.view(np.uint8).reshape(w.T, -1).shape[1] >= PLAN_MIN_BYTES)
-    fused = not args.no_fused and one_layout_tile(w.T, w.K, w.E)
     plan = torch.empty((w.T * w.K, 2), dtype=torch.int32, device=dev) if use_plan else None
 
     def x_set():
@@ -621,7 +630,11 @@ def main():
     if args.workgroups > 0:
         torch.cuda.synchronize()
         B.ep_set_workgroup_limit(stream, 0)
-    report(args, w, case, ref, runs, modes, copy_gbps, non_expand, use_plan, fused)
+    rows_bytes = w.T * w.K * case.x.view(np.uint8).reshape(w.T, -1).shape[1]
+    plan_inside = (fused and not one_tile and not non_expand and not args.workgroups
+                   and rows_bytes >= PLAN_MIN_BYTES)  # ep_layout_dispatch's own plan
+    report(args, w, case, ref, runs, modes, copy_gbps, non_expand, use_plan or plan_inside, fused,
+           one_tile)
 
 
 class _CallRecorder:
@@ -770,7 +783,8 @@ def mode_figures(w, nb, run, non_expand, workload) -> dict:
             "roofline": roofline}
 
 
-def report(args, w, case, ref, runs, modes, copy_gbps, non_expand, plan_used=False, fused=False):
+def report(args, w, case, ref, runs, modes, copy_gbps, non_expand, plan_used=False, fused=False,
+           one_tile=True):
     n_valid = int((ref["dst_slot"] >= 0).sum())
     nb = algorithmic_bytes(w, n_valid, ref["num_recv"], args.path)
     main_run = runs[modes[0]]
@@ -795,9 +809,10 @@ def report(args, w, case, ref, runs, modes, copy_gbps, non_expand, plan_used=Fal
                    "parallelism": "one GPU, all experts local", "path": args.path,
                    "dispatch_plan": plan_used,
                    "layout_read_ahead": bool(args.read_ahead and not fused),
-                   "layout_dispatch": (("one launch (ep_layout_dispatch_compact)" if non_expand
-                                        else "one launch (ep_layout_dispatch)")
-                                       if fused else "separate launches"),
+                   "layout_dispatch": ((("one launch" if one_tile else "one call") +
+                                        (" (ep_layout_dispatch_compact)" if non_expand
+                                         else " (ep_layout_dispatch)"))
+                                       if fused else "separate calls"),
                    "workgroup_cap": args.workgroups or None,
                    "cache": main_run["cache"], "launch": main_run["launch"]},
         **{k: fig[k] for k in ("pct_of_peak", "tokens_per_s", "dispatch_combine_GBps",
@@ -806,7 +821,9 @@ def report(args, w, case, ref, runs, modes, copy_gbps, non_expand, plan_used=Fal
         "dispatch_combine_pct_of_copy": round(100 * fig["dispatch_combine_GBps"] / copy_gbps, 2),
         "kernel_us": fig["kernel_us"],
         "kernel_timing": f"HIP events around {main_run['event_steps']} back-to-back launches of "
-                         f"each pass, run right after the timed loop; mean per launch",
+                         f"each pass, run right after the timed loop; mean per launch" +
+                         ("; the fused call's time (layout included) is dispatch's" if fused
+                          else ""),
         "algorithmic_bytes": nb,
         **({"overlap": main_run["overlap"]} if main_run["overlap"] else {}),
         "roofline": fig["roofline"],

@@ -35,7 +35,8 @@ SYMBOLS = ("ep_layout_workspace_bytes", "ep_layout", "ep_dispatch", "ep_layout_d
            "ep_combine",
            "ep_dispatch_compact", "ep_layout_dispatch_compact", "ep_combine_compact",
            "ep_zero_padding", "ep_set_workgroup_limit",
-           "ep_get_workgroup_limit", "ep_last_error", "ep_supported", "ep_layout_noalloc")
+           "ep_get_workgroup_limit", "ep_last_error", "ep_supported", "ep_layout_noalloc",
+           "ep_layout_dispatch_workspace_bytes")
 
 
 class EpError(RuntimeError):
@@ -66,6 +67,8 @@ def lib(path: str = None) -> ctypes.CDLL:
     L = ctypes.CDLL(p)
     L.ep_layout_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.ep_layout_workspace_bytes.restype = _sz
+    L.ep_layout_dispatch_workspace_bytes.argtypes = [_i32, _i32, _i32]
+    L.ep_layout_dispatch_workspace_bytes.restype = _sz
     L.ep_layout.argtypes = [_vp, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp,
                             _vp, _sz, _vp]
     L.ep_layout.restype = ctypes.c_int
@@ -144,6 +147,10 @@ def _nbytes(a, nbytes):
     if a is None:
         return 0
     return int(a.nbytes) if nbytes is None else int(nbytes)
+
+
+def ep_layout_dispatch_workspace_bytes(num_tokens: int, topk: int, num_experts: int) -> int:
+    return int(lib().ep_layout_dispatch_workspace_bytes(num_tokens, topk, num_experts))
 
 
 def ep_layout(topk_idx, num_tokens, topk, num_experts, expert_alignment, capacity_rows,

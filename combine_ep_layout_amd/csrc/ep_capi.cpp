@@ -33,6 +33,16 @@ int fail(int code, const char *fmt, ...) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Expand rows (bytes) from which ep_layout_dispatch walks a dispatch plan when
+// its workspace has room for one. Measured on MI355X: at prefill (470 MB of
+// rows) the plan saves 3-5 us of dispatch for 0.1 us of layout; at 117-120 MB
+// of rows and below the two cancel.
+constexpr int64_t kPlanMinBytes = int64_t(256) << 20;
+
+// Byte offset of the dispatch plan inside ep_layout_dispatch's workspace: after
+// the layout's own workspace, on a 256-byte boundary.
+size_t plan_offset(size_t layout_bytes) { return (layout_bytes + 255) & ~(size_t)255; }
+
 // A HIP error left on this thread by an earlier, unrelated call (another
 // library's, say) would otherwise be read back after our launch and reported
 // as its failure: each entry point drops it before launching anything.
@@ -133,6 +143,18 @@ int ep_supported(int32_t pass, int32_t hidden, int32_t topk, int32_t dtype) {
   } catch (...) {
   }
   return 0;
+}
+
+size_t ep_layout_dispatch_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_experts) {
+  try {
+    if (num_tokens < 0 || topk < 1 || topk > EP_MAX_TOPK || num_experts < 1 ||
+        num_experts > EP_MAX_EXPERTS || (int64_t)num_tokens * topk > INT32_MAX)
+      return 0;
+    return plan_offset(ep::layout_workspace(num_tokens, topk, num_experts)) +
+           (size_t)num_tokens * topk * 8;
+  } catch (...) {
+    return 0;
+  }
 }
 
 size_t ep_layout_workspace_bytes(int32_t num_tokens, int32_t topk, int32_t num_experts) {
@@ -417,7 +439,16 @@ int ep_layout_dispatch(const int32_t *topk_idx, int32_t num_tokens, int32_t topk
       const int rc = ep::launch_layout_dispatch(l, d, (int)(row_bytes / 16), scale_chunks);
       if (rc != -3) return from_launch(rc, what);
     }
-    // more than one tile (or nothing to copy): the two launches of ep_layout and ep_dispatch
+    // more than one tile (or nothing to copy): the two launches of ep_layout and ep_dispatch,
+    // walking a dispatch plan kept in the workspace when it has room and the rows pay for it
+    const size_t base = ep::layout_workspace(num_tokens, topk, num_experts);
+    const size_t plan_bytes = (size_t)num_tokens * topk * 8;
+    if ((int64_t)num_tokens * topk * row_bytes >= kPlanMinBytes && aligned(workspace, 16) &&
+        workspace != nullptr && workspace_bytes >= plan_offset(base) + plan_bytes) {
+      int32_t *plan = (int32_t *)((char *)workspace + plan_offset(base));
+      l.plan = plan;
+      d.plan = plan;
+    }
     if (int rc = from_launch(ep::launch_layout(l), what)) return rc;
     return from_launch(ep::launch_dispatch(d), what);
   } catch (const std::exception &e) {

@@ -86,8 +86,9 @@ class DeviceCase:
                               prefetch=self.x if read_ahead else None)
         return self.lay
 
-    def layout_dispatch(self, stream=None, weights=True):
-        """ep_layout_dispatch: the layout's outputs and the expand buffer in one call."""
+    def layout_dispatch(self, stream=None, weights=True, plan_workspace=False):
+        """ep_layout_dispatch: the layout's outputs and the expand buffer in one call (with a
+        workspace that holds a dispatch plan if asked)."""
         w = self.w
         T, K, E = w.T, w.K, w.E
         counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
@@ -95,7 +96,8 @@ class DeviceCase:
         dst = torch.full((max(T, 1), K), -7, dtype=torch.int32, device=DEV)
         meta = torch.full((max(T, 1), K + 2), -7, dtype=torch.int32, device=DEV)
         nrecv = torch.full((1,), -7, dtype=torch.int32, device=DEV)
-        wsb = B.ep_layout_workspace_bytes(T, K, E)
+        wsb = (B.ep_layout_dispatch_workspace_bytes(T, K, E) if plan_workspace
+               else B.ep_layout_workspace_bytes(T, K, E))
         ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
         B.ep_layout_dispatch(self.idx if T else None, T, K, E, w.A, w.cap, counts, offsets,
                              dst if T else None, meta if T else None, nrecv, ws, wsb,

@@ -85,6 +85,17 @@ def lay(T=4096, K=8, E=256, A=128, cap=65280, ws=FAKE, wsb=1 << 20, idx=FAKE, co
     return (idx, T, K, E, A, cap, counts, FAKE, FAKE, FAKE, FAKE, ws, wsb)
 
 
+def test_layout_dispatch_workspace_bytes(L):
+    """The fused call's plan-sized workspace: the layout's, rounded up to 256 bytes, plus
+    8 bytes per entry; 0 for out-of-range arguments."""
+    for T, K, E in [(64, 2, 16), (4096, 8, 256), (20000, 8, 1024), (1, 1, 1), (0, 8, 256)]:
+        base = B.ep_layout_workspace_bytes(T, K, E)
+        assert B.ep_layout_dispatch_workspace_bytes(T, K, E) == -(-base // 256) * 256 + T * K * 8
+    assert B.ep_layout_dispatch_workspace_bytes(-1, 8, 256) == 0
+    assert B.ep_layout_dispatch_workspace_bytes(16, 65, 256) == 0
+    assert B.ep_layout_dispatch_workspace_bytes(16, 8, 1025) == 0
+
+
 def test_layout_rejections(L):
     assert _code(B.ep_layout, *lay(T=-1)) == B.EP_EINVAL
     assert _code(B.ep_layout, *lay(K=0)) == B.EP_EINVAL

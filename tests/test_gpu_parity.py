@@ -390,6 +390,35 @@ def test_layout_dispatch(T, H, E, K, A, mask, dtype, scales, routing, wg_cap):
     check_dispatch(dc, ref["dst_slot"])
 
 
+@pytest.mark.parametrize("T,H,E,K,A,dtype,scales,wg_cap", [
+    (4096, 7168, 256, 8, 128, I.BF16, False, 0),      # 470 MB of rows: walks the plan
+    (5000, 7168, 256, 8, 1, I.FP8_E4M3, True, 0),     # 296 MB of fp8 rows and scale rows
+    (4096, 7168, 256, 8, 128, I.BF16, False, 16),     # capped: the fan-out ignores the plan
+    (1024, 7168, 64, 8, 1, I.BF16, False, 0),         # 117 MB: below the plan threshold
+])
+def test_layout_dispatch_with_plan_workspace(T, H, E, K, A, dtype, scales, wg_cap):
+    """ep_layout_dispatch given ep_layout_dispatch_workspace_bytes: several-tile batches
+    whose rows total 256 MiB or more walk a dispatch plan kept in the workspace; every
+    output equals the oracle's either way."""
+    w = I.custom(f"fused_pl{T}_{dtype}", 9700 + T, T, H, E, K, A, dtype, "uniform", scales=scales)
+    _say(f"[layout + dispatch, plan workspace] {w} cap {wg_cap}")
+    case = I.make_case(w, with_y=False, mask_frac=0.05)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case, with_y=False)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    try:
+        B.ep_set_workgroup_limit(s, wg_cap)
+        with torch.cuda.stream(s):
+            dc.layout_dispatch(stream=s, plan_workspace=True)
+        s.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        B.ep_set_workgroup_limit(s, 0)
+    check_layout(layout_to_host(dc.lay), ref)
+    check_dispatch(dc, ref["dst_slot"])
+
+
 @pytest.mark.parametrize("T,H,E,K,dtype,scales", [
     (128, 7168, 256, 8, I.BF16, False),     # the decode shape
     (100, 7168, 256, 8, I.FP8_E4M3, True),  # scale rows travel, weights do not
