@@ -31,6 +31,8 @@
 // not HBM, is the limit, so the same copy runs with F = K: one wave per
 // (token, slice) loads the slice once and stores it to all K destinations,
 // (K + 1) KiB per K KiB written instead of 2K KiB.
+#include <algorithm>
+
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -49,6 +51,29 @@ __device__ __forceinline__ int64_t xcd_contiguous_block() {
   return (b % kXcds) * (nb / kXcds) + b / kXcds;
 }
 
+// Moves slice `slice` of x[t] (entry tk) to expand row d; slice 0 also
+// carries the scale row and the router weight.
+template <int ROWB, int SCB>
+__device__ __forceinline__ void copy_slice(const u32x4 *__restrict__ x,
+                                           const u32x4 *__restrict__ x_scales,
+                                           const float *__restrict__ topk_weights, int64_t t,
+                                           int64_t tk, int slice, int d, int lane,
+                                           u32x4 *__restrict__ expand_x,
+                                           u32x4 *__restrict__ expand_scales,
+                                           float *__restrict__ expand_weights) {
+  constexpr int CH = ROWB / 16;
+  constexpr int SCH = SCB / 16;
+  const int i = slice * kWave + lane;
+  if (CH % kWave == 0 || i < CH)
+    store_row<RowStore::kNtDevice>(x[t * CH + i], expand_x + (int64_t)d * CH, ROWB, i * 16);
+  if (slice == 0) {
+    if (SCH > 0 && lane < SCH)
+      __builtin_nontemporal_store(x_scales[t * SCH + lane],
+                                  expand_scales + (int64_t)d * SCH + lane);
+    if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[tk];
+  }
+}
+
 // One wave per (token, k, 1 KiB slice of the row): it reads 16 bytes per lane
 // of x[t] and writes them to expand_x[dst_slot[t, k]] with one non-temporal
 // store. Consecutive waves write consecutive KiB of one destination row, the
@@ -60,6 +85,15 @@ __device__ __forceinline__ int64_t xcd_contiguous_block() {
 // of one expert's segment. Runs of about 4 rows at 128 tokens per tile make
 // HBM absorb the writes faster (prefill copy 79 against 85 us), and a tile's x
 // rows (1.8 MB) stay in the XCD's L2 for its K re-reads.
+// PLANNED launches give each wave exactly one unit, unit0 + its wave index,
+// and the host issues several launches past the grid limit. Without a loop
+// the compiler loads each kernel argument where it is first used instead of
+// all of them before the first unit: the planned prefill copy took 78.4
+// against 80.5 us with x cached and 100.7 against 102.6 us with x evicted,
+// fp8_hot8 85.1 against 88.7 (MI355X, events). The token-major walk measured
+// the other way (mori_default 22.3 against 21.2 us, prefill 87.8 against
+// 84.7), so it keeps a grid-stride loop over all units in one launch
+// (unit0 = 0).
 // DT (the EP_* dtype) only names the kernel: every dtype moves bytes, so
 // instances with equal ROWB and SCB have the same body.
 template <int DT, int ROWB, int SCB, int K, bool PLANNED>
@@ -67,7 +101,7 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot,
     const int2 *__restrict__ plan, int T, int64_t capacity, u32x4 *__restrict__ expand_x,
-    u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights) {
+    u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights, int64_t unit0) {
   constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
   constexpr int SLICES = (CH + kWave - 1) / kWave;  // 1 KiB slices per row
   constexpr int SCH = SCB / 16;                    // 16-byte chunks per scale row
@@ -78,31 +112,26 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   constexpr int wpb = kDefaultThreads / kWave;  // launched uncapped only
   const int64_t total = (int64_t)T * K * SLICES;
-  const int64_t stride = (int64_t)gridDim.x * wpb;
-  for (int64_t gw = xcd_contiguous_block() * wpb + wave_in_block; gw < total; gw += stride) {
+  if constexpr (PLANNED) {
+    const int64_t gw = unit0 + xcd_contiguous_block() * wpb + wave_in_block;
+    if (gw >= total) return;
     const int64_t j = gw / SLICES;  // entry index in walk order
     const int slice = (int)(gw - j * SLICES);
-    int64_t tk;  // flat (token, k)
-    int d;
-    if constexpr (PLANNED) {
-      const int2 pe = plan[j];
-      tk = __builtin_amdgcn_readfirstlane(pe.x);
-      d = __builtin_amdgcn_readfirstlane(pe.y);
-      if (tk < 0 || tk >= (int64_t)T * K) continue;
-    } else {
-      tk = j;
-      d = __builtin_amdgcn_readfirstlane(dst_slot[tk]);
-    }
-    const int64_t t = tk / K;
-    if (d < 0 || d >= capacity) continue;
-    const int i = slice * kWave + lane;
-    if (CH % kWave == 0 || i < CH)
-      store_row<RowStore::kNtDevice>(x[t * CH + i], expand_x + (int64_t)d * CH, ROWB, i * 16);
-    if (slice == 0) {
-      if (SCH > 0 && lane < SCH)
-        __builtin_nontemporal_store(x_scales[t * SCH + lane],
-                                    expand_scales + (int64_t)d * SCH + lane);
-      if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[tk];
+    const int2 pe = plan[j];
+    const int64_t tk = __builtin_amdgcn_readfirstlane(pe.x);  // flat (token, k)
+    const int d = __builtin_amdgcn_readfirstlane(pe.y);
+    if (tk < 0 || tk >= (int64_t)T * K || d < 0 || d >= capacity) return;
+    copy_slice<ROWB, SCB>(x, x_scales, topk_weights, tk / K, tk, slice, d, lane, expand_x,
+                          expand_scales, expand_weights);
+  } else {
+    const int64_t stride = (int64_t)gridDim.x * wpb;
+    for (int64_t gw = xcd_contiguous_block() * wpb + wave_in_block; gw < total; gw += stride) {
+      const int64_t tk = gw / SLICES;  // flat (token, k)
+      const int slice = (int)(gw - tk * SLICES);
+      const int d = __builtin_amdgcn_readfirstlane(dst_slot[tk]);
+      if (d < 0 || d >= capacity) continue;
+      copy_slice<ROWB, SCB>(x, x_scales, topk_weights, tk / K, tk, slice, d, lane, expand_x,
+                            expand_scales, expand_weights);
     }
   }
 }
@@ -200,6 +229,10 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_fanout(
 // beside the other traffic, and past the full 256 MiB it never does.
 constexpr int64_t kCachedXBytes = int64_t(128) << 20;
 
+// Units (waves) per launch of ep_dispatch_expand: 2^24 blocks of four waves,
+// less a block-rounding margin so the grid stays within 2^24 blocks.
+constexpr int64_t kMaxLaunchUnits = (int64_t(1) << 26) - 64;
+
 template <int DT, int ROWB, int SCB, int K>
 int dispatch_impl(const DispatchArgs &a) {
   if (a.T == 0) return 0;
@@ -224,13 +257,21 @@ int dispatch_impl(const DispatchArgs &a) {
       return launch_status();
     }
   }
-  const WaveGrid g = wave_grid((int64_t)a.T * K * SLICES, 0, 1 << 24, kXcds);
-  if (a.plan != nullptr)
-    ep_dispatch_expand<DT, ROWB, SCB, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-        x, xs, a.topk_weights, a.dst_slot, (const int2 *)a.plan, a.T, a.capacity, ex, es, ew);
-  else
+  const int64_t units = (int64_t)a.T * K * SLICES;
+  if (a.plan == nullptr) {  // one launch; its waves loop past the grid limit
+    const WaveGrid g = wave_grid(units, 0, 1 << 24, kXcds);
     ep_dispatch_expand<DT, ROWB, SCB, K, false><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-        x, xs, a.topk_weights, a.dst_slot, nullptr, a.T, a.capacity, ex, es, ew);
+        x, xs, a.topk_weights, a.dst_slot, nullptr, a.T, a.capacity, ex, es, ew, 0);
+    return launch_status();
+  }
+  // One wave per unit; a launch covers kMaxLaunchUnits of them (2^24 - 16
+  // blocks, a multiple of 8) or the rest.
+  for (int64_t u0 = 0; u0 < units; u0 += kMaxLaunchUnits) {
+    const WaveGrid g = wave_grid(std::min(units - u0, kMaxLaunchUnits), 0, 1 << 24, kXcds);
+    ep_dispatch_expand<DT, ROWB, SCB, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+        x, xs, a.topk_weights, a.dst_slot, (const int2 *)a.plan, a.T, a.capacity, ex, es, ew,
+        u0);
+  }
   return launch_status();
 }
 
