@@ -12,7 +12,13 @@
 // 16-byte loads and non-temporal 16-byte stores; the number of received rows
 // stays on the device, so the grid covers T rows and waves past num_recv
 // exit. Shapes are run-time values here: there is no per-element arithmetic
-// to unroll beyond the bias add.
+// to unroll beyond the bias add. Uncapped, each wave moves one unit and exits
+// (no grid-stride loop, so the compiler loads each kernel argument where it
+// is first used): combine 17.4 against 19.0 us at prefill, 5.0 against 5.8 at
+// mori_default, 36.4 against 38.0 at fp8_hot8; dispatch unchanged at prefill,
+// 5.2 against 5.5 at mori_default (MI355X). Under a cap the waves loop.
+#include <algorithm>
+
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -38,21 +44,21 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot,
     const int32_t *__restrict__ meta, const int32_t *__restrict__ num_recv, int T, int K,
     u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales,
-    int32_t *__restrict__ recv_topk_idx, float *__restrict__ recv_topk_weights) {
+    int32_t *__restrict__ recv_topk_idx, float *__restrict__ recv_topk_weights,
+    int64_t unit0) {
   const int lane = lane_id();
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int64_t total = (int64_t)T * slices;
   const int n = __builtin_amdgcn_readfirstlane(*num_recv);
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
-  const int64_t stride = (int64_t)gridDim.x * wpb;
-  for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < total;
-       gw += stride) {
+  const int64_t first = unit0 + (int64_t)blockIdx.x * wpb + wave_in_block;
+  auto move = [&](int64_t gw) {
     const int64_t i = gw / slices;  // receive row
     const int64_t slice = gw - i * slices;
-    if (i >= n) continue;
+    if (i >= n) return;
     const int64_t t = __builtin_amdgcn_readfirstlane(meta[i * (K + 2)]);
-    if (t < 0 || t >= T) continue;
+    if (t < 0 || t >= T) return;
     const int64_t c = slice * kWave + lane;
     if (c < row_chunks)
       store_row<WIDE ? RowStore::kDevice : RowStore::kNt>(x[t * row_chunks + c],
@@ -69,6 +75,12 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
         if (recv_topk_weights != nullptr) recv_topk_weights[i * K + k] = topk_weights[tk];
       }
     }
+  };
+  if constexpr (WIDE) {  // one unit per wave
+    if (first < total) move(first);
+  } else {
+    const int64_t stride = (int64_t)gridDim.x * wpb;
+    for (int64_t gw = first; gw < total; gw += stride) move(gw);
   }
 }
 
@@ -108,49 +120,68 @@ template <bool WIDE, bool FP32>
 __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
     const u32x4 *__restrict__ y, int64_t row_chunks, const u32x4 *__restrict__ bias,
     const int32_t *__restrict__ dst_slot, const int32_t *__restrict__ meta,
-    const int32_t *__restrict__ num_recv, int T, int K, u32x4 *__restrict__ out) {
+    const int32_t *__restrict__ num_recv, int T, int K, u32x4 *__restrict__ out,
+    int64_t unit0) {
   const int lane = lane_id();
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int64_t half = (int64_t)T * slices;
   const int n = __builtin_amdgcn_readfirstlane(*num_recv);
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
-  const int64_t stride = (int64_t)gridDim.x * wpb;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < half + T; gw += stride) {
+  const int64_t first = unit0 + (int64_t)blockIdx.x * wpb + wave_in_block;
+  auto move = [&](int64_t gw) {
     if (gw < half) {
       const int64_t r = gw / slices;
       const int64_t c = (gw - r * slices) * kWave + lane;
-      if (r >= n) continue;
+      if (r >= n) return;
       const int64_t t = __builtin_amdgcn_readfirstlane(meta[r * (K + 2)]);
-      if (t < 0 || t >= T || c >= row_chunks) continue;
+      if (t < 0 || t >= T || c >= row_chunks) return;
       const u32x4 v = __builtin_nontemporal_load(y + r * row_chunks + c);
       put_row_chunk<WIDE, FP32>(v, bias, t, row_chunks, c, out);
     } else {
       const int64_t t = gw - half;
       bool any = false;
       for (int k = lane; k < K; k += kWave) any |= dst_slot[t * K + k] >= 0;
-      if (ballot(any) != 0) continue;  // received: written by its receive row
+      if (ballot(any) != 0) return;  // received: written by its receive row
       for (int64_t c = lane; c < row_chunks; c += kWave)
         put_row_chunk<WIDE, FP32>(zero, bias, t, row_chunks, c, out);
     }
+  };
+  if constexpr (WIDE) {  // one unit per wave
+    if (first < half + T) move(first);
+  } else {
+    const int64_t stride = (int64_t)gridDim.x * wpb;
+    for (int64_t gw = first; gw < half + T; gw += stride) move(gw);
   }
 }
 
+// Uncapped (WIDE): one wave per unit, in launches of at most kMaxLaunchUnits
+// units. Capped: one launch of at most `cap` workgroups whose waves loop.
 template <bool WIDE>
-int dispatch_compact_launch(const CompactDispatchArgs &a, const WaveGrid &g, int64_t row_chunks) {
-  ep_dispatch_compact_rows<WIDE><<<g.blocks, g.threads, 0, a.stream>>>(
-      (const u32x4 *)a.x, row_chunks, a.x_scales, a.scale_cols, a.topk_idx, a.topk_weights,
-      a.dst_slot, a.meta, a.num_recv, a.T, a.K, (u32x4 *)a.recv_x, a.recv_scales,
-      a.recv_topk_idx, a.recv_topk_weights);
+int dispatch_compact_launch(const CompactDispatchArgs &a, int64_t units, int cap,
+                            int64_t row_chunks) {
+  for (int64_t u0 = 0; u0 < units; u0 += WIDE ? kMaxLaunchUnits : units) {
+    const WaveGrid g = WIDE ? wave_grid(std::min(units - u0, kMaxLaunchUnits), 0, 1 << 24)
+                            : wave_grid(units, cap, 1 << 22);
+    ep_dispatch_compact_rows<WIDE><<<g.blocks, g.threads, 0, a.stream>>>(
+        (const u32x4 *)a.x, row_chunks, a.x_scales, a.scale_cols, a.topk_idx, a.topk_weights,
+        a.dst_slot, a.meta, a.num_recv, a.T, a.K, (u32x4 *)a.recv_x, a.recv_scales,
+        a.recv_topk_idx, a.recv_topk_weights, u0);
+  }
   return launch_status();
 }
 
 template <bool WIDE, bool FP32>
-int combine_compact_launch(const CompactCombineArgs &a, const WaveGrid &g, int64_t row_chunks) {
-  ep_combine_compact_rows<WIDE, FP32><<<g.blocks, g.threads, 0, a.stream>>>(
-      (const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias, a.dst_slot, a.meta, a.num_recv, a.T,
-      a.K, (u32x4 *)a.out);
+int combine_compact_launch(const CompactCombineArgs &a, int64_t units, int cap,
+                           int64_t row_chunks) {
+  for (int64_t u0 = 0; u0 < units; u0 += WIDE ? kMaxLaunchUnits : units) {
+    const WaveGrid g = WIDE ? wave_grid(std::min(units - u0, kMaxLaunchUnits), 0, 1 << 24)
+                            : wave_grid(units, cap, 1 << 22);
+    ep_combine_compact_rows<WIDE, FP32><<<g.blocks, g.threads, 0, a.stream>>>(
+        (const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias, a.dst_slot, a.meta, a.num_recv,
+        a.T, a.K, (u32x4 *)a.out, u0);
+  }
   return launch_status();
 }
 
@@ -161,9 +192,9 @@ int launch_dispatch_compact(const CompactDispatchArgs &a) {
   const int64_t row_chunks = a.row_bytes / 16;
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int cap = stream_workgroup_limit(a.stream);
-  const WaveGrid g = wave_grid((int64_t)a.T * slices, cap, 1 << 22);  // larger inputs loop
-  return cap > 0 ? dispatch_compact_launch<false>(a, g, row_chunks)
-                 : dispatch_compact_launch<true>(a, g, row_chunks);
+  const int64_t units = (int64_t)a.T * slices;
+  return cap > 0 ? dispatch_compact_launch<false>(a, units, cap, row_chunks)
+                 : dispatch_compact_launch<true>(a, units, 0, row_chunks);
 }
 
 int launch_combine_compact(const CompactCombineArgs &a) {
@@ -171,12 +202,12 @@ int launch_combine_compact(const CompactCombineArgs &a) {
   const int64_t row_chunks = a.row_bytes / 16;
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int cap = stream_workgroup_limit(a.stream);
-  const WaveGrid g = wave_grid((int64_t)a.T * (slices + 1), cap, 1 << 22);
+  const int64_t units = (int64_t)a.T * (slices + 1);
   if (a.fp32)
-    return cap > 0 ? combine_compact_launch<false, true>(a, g, row_chunks)
-                   : combine_compact_launch<true, true>(a, g, row_chunks);
-  return cap > 0 ? combine_compact_launch<false, false>(a, g, row_chunks)
-                 : combine_compact_launch<true, false>(a, g, row_chunks);
+    return cap > 0 ? combine_compact_launch<false, true>(a, units, cap, row_chunks)
+                   : combine_compact_launch<true, true>(a, units, 0, row_chunks);
+  return cap > 0 ? combine_compact_launch<false, false>(a, units, cap, row_chunks)
+                 : combine_compact_launch<true, false>(a, units, 0, row_chunks);
 }
 
 }  // namespace ep

@@ -107,6 +107,12 @@ struct CompactCombineArgs {
 constexpr int kDefaultThreads = 256;
 constexpr int kCappedThreads = 1024;
 
+// Units (one wave each) per launch of a kernel whose uncapped waves move one
+// unit and exit: 2^24 - 16 workgroups of four waves (a multiple of 8, within
+// the grid limit of 2^32 threads). Larger inputs take further launches, each
+// from a unit offset.
+constexpr int64_t kMaxLaunchUnits = (int64_t(1) << 26) - 64;
+
 // The cap registered for this stream handle, or 0 for none.
 int stream_workgroup_limit(hipStream_t stream);
 
