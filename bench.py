@@ -14,9 +14,9 @@ A batch that fits one layout tile (a decode step) calls ep_layout_dispatch
 (ep_layout_dispatch_compact) instead of the first two calls: one launch;
 --no-fused keeps them apart, --one-call uses the fused call at every batch
 size (on the expand path with ep_layout_dispatch_workspace_bytes, so that
-large batches walk the plan it keeps in the workspace). Batches of at least
-256 MiB of expand rows ask the layout for the dispatch plan and dispatch by it
-(--no-plan: token-major).
+large batches walk the plan it keeps in the workspace). On the expand path
+every batch of more than one layout tile asks the layout for the dispatch
+plan and dispatches by it (--no-plan: token-major).
 --read-ahead hands x to ep_layout as its read-ahead region, so that x is in
 the last-level cache when dispatch starts.
 Each run times two cache modes (--cache both, the default; --cache warm or
@@ -148,12 +148,6 @@ def measured_traffic(workload: str, kernel: str):
     k = d.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
 
-
-# Expand payload from which the step asks ep_layout for the dispatch plan.
-# Measured on MI355X: prefill (470 MB of rows) gains 3.6 us per step; at
-# 117-120 MB (mori_default, fp4x2 prefill) and below the plan's layout cost
-# (about 0.1-0.4 us) cancels or exceeds the gain.
-PLAN_MIN_BYTES = 256 << 20
 
 def one_layout_tile(T: int, K: int, E: int) -> bool:
     """Whether ep_layout_dispatch runs as one launch: T*K fits one layout tile
@@ -353,8 +347,8 @@ def main():
                     help="expand: one row per (token, expert) (the default, headline path); "
                          "non-expand: one row per received token")
     ap.add_argument("--no-plan", action="store_true",
-                    help="expand path: never ask ep_layout for the dispatch plan (by default it is "
-                         "used when the expand rows total at least PLAN_MIN_BYTES)")
+                    help="expand path: never ask ep_layout for the dispatch plan (by default every "
+                         "batch of more than one layout tile dispatches by it)")
     ap.add_argument("--read-ahead", action="store_true",
                     help="hand x to ep_layout as its read-ahead region: the layout's launches "
                          "pull x into the last-level cache for dispatch (helps a cold x, costs a "
@@ -436,12 +430,13 @@ def main():
     nrecv = torch.empty(1, dtype=torch.int32, device=dev)
     one_tile = one_layout_tile(w.T, w.K, w.E)
     fused = not args.no_fused and (one_tile or args.one_call)
-    wsb = (B.ep_layout_dispatch_workspace_bytes(w.T, w.K, w.E) if fused and not non_expand
+    wsb = (B.ep_layout_dispatch_workspace_bytes(w.T, w.K, w.E)
+           if fused and not non_expand and not args.no_plan
            else B.ep_layout_workspace_bytes(w.T, w.K, w.E))
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     rows_out = w.T if non_expand else w.cap
-    use_plan = (not non_expand and not args.no_plan and not fused
-                and w.T * w.K * case.x.view(np.uint8).reshape(w.T, -1).shape[1] >= PLAN_MIN_BYTES)
+    # The capped fan-out dispatch ignores a plan, so a capped step does not ask for one.
+    use_plan = not non_expand and not args.no_plan and not fused and not args.workgroups
     plan = torch.empty((w.T * w.K, 2), dtype=torch.int32, device=dev) if use_plan else None
 
     def x_set():
@@ -630,9 +625,8 @@ def main():
     if args.workgroups > 0:
         torch.cuda.synchronize()
         B.ep_set_workgroup_limit(stream, 0)
-    rows_bytes = w.T * w.K * case.x.view(np.uint8).reshape(w.T, -1).shape[1]
-    plan_inside = (fused and not one_tile and not non_expand and not args.workgroups
-                   and rows_bytes >= PLAN_MIN_BYTES)  # ep_layout_dispatch's own plan
+    plan_inside = (fused and not one_tile and not non_expand and not args.no_plan
+                   and not args.workgroups)  # ep_layout_dispatch's own plan
     report(args, w, case, ref, runs, modes, copy_gbps, non_expand, use_plan or plan_inside, fused,
            one_tile)
 

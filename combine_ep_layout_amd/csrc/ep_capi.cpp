@@ -33,12 +33,6 @@ int fail(int code, const char *fmt, ...) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Expand rows (bytes) from which ep_layout_dispatch walks a dispatch plan when
-// its workspace has room for one. Measured on MI355X: at prefill (470 MB of
-// rows) the plan saves 3-5 us of dispatch for 0.1 us of layout; at 117-120 MB
-// of rows and below the two cancel.
-constexpr int64_t kPlanMinBytes = int64_t(256) << 20;
-
 // Byte offset of the dispatch plan inside ep_layout_dispatch's workspace: after
 // the layout's own workspace, on a 256-byte boundary.
 size_t plan_offset(size_t layout_bytes) { return (layout_bytes + 255) & ~(size_t)255; }
@@ -440,11 +434,11 @@ int ep_layout_dispatch(const int32_t *topk_idx, int32_t num_tokens, int32_t topk
       if (rc != -3) return from_launch(rc, what);
     }
     // more than one tile (or nothing to copy): the two launches of ep_layout and ep_dispatch,
-    // walking a dispatch plan kept in the workspace when it has room and the rows pay for it
+    // walking a dispatch plan kept in the workspace when it has room for one
     const size_t base = ep::layout_workspace(num_tokens, topk, num_experts);
     const size_t plan_bytes = (size_t)num_tokens * topk * 8;
-    if ((int64_t)num_tokens * topk * row_bytes >= kPlanMinBytes && aligned(workspace, 16) &&
-        workspace != nullptr && workspace_bytes >= plan_offset(base) + plan_bytes) {
+    if (aligned(workspace, 16) && workspace != nullptr &&
+        workspace_bytes >= plan_offset(base) + plan_bytes) {
       int32_t *plan = (int32_t *)((char *)workspace + plan_offset(base));
       l.plan = plan;
       d.plan = plan;

@@ -351,7 +351,8 @@ int combine_impl(const CombineArgs &a) {
   const int cap = stream_workgroup_limit(a.stream);  // read once per launch
   if constexpr (StreamGeometry<CH>::OK) {
     if (a.T >= kStreamMinTokens && cap == 0) {
-      const WaveGrid g = wave_grid((int64_t)a.T * StreamGeometry<CH>::PIECES, 0, INT32_MAX);
+      // At most 2^24 workgroups (the grid limit of 2^32 threads); waves loop past it.
+      const WaveGrid g = wave_grid((int64_t)a.T * StreamGeometry<CH>::PIECES, 0, 1 << 24);
       if (a.bias)
         ep_combine_stream<DT, H, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
             (const u32x4 *)a.y, a.topk_weights, (const u32x4 *)a.bias, a.dst_slot, a.T,
@@ -364,7 +365,7 @@ int combine_impl(const CombineArgs &a) {
     }
   }
   constexpr int SPLIT = CombineGeometry<H * Elem<DT>::BYTES / 16>::SPLIT;
-  const WaveGrid g = wave_grid((int64_t)a.T * SPLIT, cap, INT32_MAX, 1, kCombineCappedThreads);
+  const WaveGrid g = wave_grid((int64_t)a.T * SPLIT, cap, 1 << 24, 1, kCombineCappedThreads);
   if (g.threads == kCombineCappedThreads)
     return combine_launch<DT, H, K, kCombineCappedThreads>(a, g);
   return combine_launch<DT, H, K, kDefaultThreads>(a, g);

@@ -394,12 +394,13 @@ def test_layout_dispatch(T, H, E, K, A, mask, dtype, scales, routing, wg_cap):
     (4096, 7168, 256, 8, 128, I.BF16, False, 0),      # 470 MB of rows: walks the plan
     (5000, 7168, 256, 8, 1, I.FP8_E4M3, True, 0),     # 296 MB of fp8 rows and scale rows
     (4096, 7168, 256, 8, 128, I.BF16, False, 16),     # capped: the fan-out ignores the plan
-    (1024, 7168, 64, 8, 1, I.BF16, False, 0),         # 117 MB: below the plan threshold
+    (1024, 7168, 64, 8, 1, I.BF16, False, 0),         # the MORI default shape
+    (300, 1024, 300, 6, 4, I.FP32, False, 0),         # 512-entry tiles, fp32 rows
+    (3000, 512, 1024, 2, 16, I.FP4X2, True, 0),       # 256-entry tiles, fp4x2 with scale rows
 ])
 def test_layout_dispatch_with_plan_workspace(T, H, E, K, A, dtype, scales, wg_cap):
     """ep_layout_dispatch given ep_layout_dispatch_workspace_bytes: several-tile batches
-    whose rows total 256 MiB or more walk a dispatch plan kept in the workspace; every
-    output equals the oracle's either way."""
+    walk a dispatch plan kept in the workspace; every output equals the oracle's."""
     w = I.custom(f"fused_pl{T}_{dtype}", 9700 + T, T, H, E, K, A, dtype, "uniform", scales=scales)
     _say(f"[layout + dispatch, plan workspace] {w} cap {wg_cap}")
     case = I.make_case(w, with_y=False, mask_frac=0.05)
