@@ -79,61 +79,75 @@ __device__ __forceinline__ void copy_slice(const u32x4 *__restrict__ x,
 // store. Consecutive waves write consecutive KiB of one destination row, the
 // order in which HBM absorbs writes fastest (a wave that scatters to K rows
 // in turn is slower). The fp8 scale row and the router weight travel with
-// slice 0. PLANNED: the entries are taken in the order of the layout's
-// dispatch plan instead of token-major. Inside each tile of tokens the plan
-// lists entries by ascending slot, so consecutive entries are consecutive rows
-// of one expert's segment. Runs of about 4 rows at 128 tokens per tile make
-// HBM absorb the writes faster (prefill copy 79 against 85 us), and a tile's x
-// rows (1.8 MB) stay in the XCD's L2 for its K re-reads.
-// PLANNED launches give each wave exactly one unit, unit0 + its wave index,
-// and the host issues several launches past the grid limit. Without a loop
-// the compiler loads each kernel argument where it is first used instead of
-// all of them before the first unit: the planned prefill copy took 78.4
-// against 80.5 us with x cached and 100.7 against 102.6 us with x evicted,
-// fp8_hot8 85.1 against 88.7 (MI355X, events). The token-major walk measured
-// the other way (mori_default 22.3 against 21.2 us, prefill 87.8 against
-// 84.7), so it keeps a grid-stride loop over all units in one launch
-// (unit0 = 0).
+// slice 0. Waves are ordered token-major, then k, then slice, and loop over
+// the units past the grid limit.
 // DT (the EP_* dtype) only names the kernel: every dtype moves bytes, so
 // instances with equal ROWB and SCB have the same body.
-template <int DT, int ROWB, int SCB, int K, bool PLANNED>
+template <int DT, int ROWB, int SCB, int K>
 __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
-    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot,
-    const int2 *__restrict__ plan, int T, int64_t capacity, u32x4 *__restrict__ expand_x,
-    u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights, int64_t unit0) {
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
+    int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
+    float *__restrict__ expand_weights) {
   constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
   constexpr int SLICES = (CH + kWave - 1) / kWave;  // 1 KiB slices per row
   constexpr int SCH = SCB / 16;                    // 16-byte chunks per scale row
   static_assert(ROWB % 16 == 0 && SCB % 16 == 0 && SCH <= kWave, "row geometry");
   static_assert(K >= 1 && K <= kWave, "topk must fit one wavefront");
-
   const int lane = lane_id();
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   constexpr int wpb = kDefaultThreads / kWave;  // launched uncapped only
   const int64_t total = (int64_t)T * K * SLICES;
-  if constexpr (PLANNED) {
-    const int64_t gw = unit0 + xcd_contiguous_block() * wpb + wave_in_block;
-    if (gw >= total) return;
-    const int64_t j = gw / SLICES;  // entry index in walk order
-    const int slice = (int)(gw - j * SLICES);
-    const int2 pe = plan[j];
-    const int64_t tk = __builtin_amdgcn_readfirstlane(pe.x);  // flat (token, k)
-    const int d = __builtin_amdgcn_readfirstlane(pe.y);
-    if (tk < 0 || tk >= (int64_t)T * K || d < 0 || d >= capacity) return;
+  const int64_t stride = (int64_t)gridDim.x * wpb;
+  for (int64_t gw = xcd_contiguous_block() * wpb + wave_in_block; gw < total; gw += stride) {
+    const int64_t tk = gw / SLICES;  // flat (token, k)
+    const int slice = (int)(gw - tk * SLICES);
+    const int d = __builtin_amdgcn_readfirstlane(dst_slot[tk]);
+    if (d < 0 || d >= capacity) continue;
     copy_slice<ROWB, SCB>(x, x_scales, topk_weights, tk / K, tk, slice, d, lane, expand_x,
                           expand_scales, expand_weights);
-  } else {
-    const int64_t stride = (int64_t)gridDim.x * wpb;
-    for (int64_t gw = xcd_contiguous_block() * wpb + wave_in_block; gw < total; gw += stride) {
-      const int64_t tk = gw / SLICES;  // flat (token, k)
-      const int slice = (int)(gw - tk * SLICES);
-      const int d = __builtin_amdgcn_readfirstlane(dst_slot[tk]);
-      if (d < 0 || d >= capacity) continue;
-      copy_slice<ROWB, SCB>(x, x_scales, topk_weights, tk / K, tk, slice, d, lane, expand_x,
-                            expand_scales, expand_weights);
-    }
   }
+}
+
+// The same copy in the order of the layout's dispatch plan. Inside each tile
+// of tokens the plan lists entries by ascending slot, so consecutive entries
+// are consecutive rows of one expert's segment. Runs of about 4 rows at 128
+// tokens per tile make HBM absorb the writes faster (prefill copy 79 against
+// 85 us), and a tile's x rows (1.8 MB) stay in the XCD's L2 for its K
+// re-reads.
+// Each wave moves exactly one unit: slice (w mod SLICES) of plan entry
+// entry0 + w / SLICES, w its wave index in the launch (w < units); the host
+// issues further launches past the grid limit. This kernel's cost is its
+// per-wave scalar work: one scalar unit serves a compute unit's four SIMDs,
+// and at prefill each compute unit runs about 1800 of these waves. So the
+// index arithmetic is 32-bit (entries, slots and a launch's units all fit),
+// and without a loop the compiler loads each kernel argument where it is
+// first used instead of all of them up front (prefill copy 78.4 against 80.5
+// us with a grid-stride loop and 64-bit indices; MI355X, events).
+template <int DT, int ROWB, int SCB, int K>
+__global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_planned(
+    const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
+    const float *__restrict__ topk_weights, const int2 *__restrict__ plan, int entries,
+    int capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
+    float *__restrict__ expand_weights, int entry0, int units) {
+  constexpr int CH = ROWB / 16;
+  constexpr int SLICES = (CH + kWave - 1) / kWave;
+  constexpr int SCH = SCB / 16;
+  static_assert(ROWB % 16 == 0 && SCB % 16 == 0 && SCH <= kWave, "row geometry");
+  static_assert(K >= 1 && K <= kWave, "topk must fit one wavefront");
+  constexpr uint32_t wpb = kDefaultThreads / kWave;
+  const uint32_t nb = gridDim.x, b = blockIdx.x;  // nb: a multiple of kXcds
+  const uint32_t w = ((b % kXcds) * (nb / kXcds) + b / kXcds) * wpb +
+                     __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (w >= (uint32_t)units) return;
+  const uint32_t jl = w / SLICES;
+  const int slice = (int)(w - jl * SLICES);
+  const int2 pe = plan[entry0 + (int)jl];
+  const int tk = __builtin_amdgcn_readfirstlane(pe.x);  // flat (token, k)
+  const int d = __builtin_amdgcn_readfirstlane(pe.y);
+  if ((uint32_t)tk >= (uint32_t)entries || (uint32_t)d >= (uint32_t)capacity) return;
+  copy_slice<ROWB, SCB>(x, x_scales, topk_weights, (int)((uint32_t)tk / K), tk, slice, d,
+                        lane_id(), expand_x, expand_scales, expand_weights);
 }
 
 // Copies slice `slice` of token t's row to the destination rows of the F
@@ -256,20 +270,22 @@ int dispatch_impl(const DispatchArgs &a) {
       return launch_status();
     }
   }
-  const int64_t units = (int64_t)a.T * K * SLICES;
   if (a.plan == nullptr) {  // one launch; its waves loop past the grid limit
-    const WaveGrid g = wave_grid(units, 0, 1 << 24, kXcds);
-    ep_dispatch_expand<DT, ROWB, SCB, K, false><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-        x, xs, a.topk_weights, a.dst_slot, nullptr, a.T, a.capacity, ex, es, ew, 0);
+    const WaveGrid g = wave_grid((int64_t)a.T * K * SLICES, 0, 1 << 24, kXcds);
+    ep_dispatch_expand<DT, ROWB, SCB, K><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+        x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
     return launch_status();
   }
-  // One wave per unit; a launch covers kMaxLaunchUnits of them (2^24 - 16
-  // blocks, a multiple of 8) or the rest.
-  for (int64_t u0 = 0; u0 < units; u0 += kMaxLaunchUnits) {
-    const WaveGrid g = wave_grid(std::min(units - u0, kMaxLaunchUnits), 0, 1 << 24, kXcds);
-    ep_dispatch_expand<DT, ROWB, SCB, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-        x, xs, a.topk_weights, a.dst_slot, (const int2 *)a.plan, a.T, a.capacity, ex, es, ew,
-        u0);
+  // One wave per unit; a launch covers whole entries, at most kMaxLaunchUnits
+  // units. Slots are int32, so a capacity beyond INT32_MAX admits them all.
+  const int entries = a.T * K;  // at most INT32_MAX (checked by the C ABI)
+  const int cap32 = (int)std::min<int64_t>(a.capacity, INT32_MAX);
+  constexpr int kLaunchEntries = (int)(kMaxLaunchUnits / SLICES);
+  for (int e0 = 0; e0 < entries; e0 += std::min(kLaunchEntries, entries - e0)) {
+    const int units = std::min(kLaunchEntries, entries - e0) * SLICES;
+    const WaveGrid g = wave_grid(units, 0, 1 << 24, kXcds);
+    ep_dispatch_planned<DT, ROWB, SCB, K><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+        x, xs, a.topk_weights, (const int2 *)a.plan, entries, cap32, ex, es, ew, e0, units);
   }
   return launch_status();
 }
