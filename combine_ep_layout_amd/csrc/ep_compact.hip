@@ -16,9 +16,11 @@
 // (no grid-stride loop, so the compiler loads each kernel argument where it
 // is first used): combine 17.4 against 19.0 us at prefill, 5.0 against 5.8 at
 // mori_default, 36.4 against 38.0 at fp8_hot8; dispatch unchanged at prefill,
-// 5.2 against 5.5 at mori_default (MI355X). Under a cap the waves loop.
-#include <algorithm>
-
+// 5.2 against 5.5 at mori_default (MI355X). Uncapped waves also find their
+// row with 32-bit indices and a multiply-shift division by the slice count
+// (FastDiv) instead of a 64-bit division sequence: combine 16.6 against 17.3
+// us at prefill, 4.7 against 5.1 at mori_default; dispatch 4.9 against 5.3 at
+// mori_default. Under a cap the waves loop.
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -45,17 +47,14 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     const int32_t *__restrict__ meta, const int32_t *__restrict__ num_recv, int T, int K,
     u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales,
     int32_t *__restrict__ recv_topk_idx, float *__restrict__ recv_topk_weights,
-    int64_t unit0) {
+    FastDiv by_slices) {
   const int lane = lane_id();
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int64_t total = (int64_t)T * slices;
   const int n = __builtin_amdgcn_readfirstlane(*num_recv);
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
-  const int64_t first = unit0 + (int64_t)blockIdx.x * wpb + wave_in_block;
-  auto move = [&](int64_t gw) {
-    const int64_t i = gw / slices;  // receive row
-    const int64_t slice = gw - i * slices;
+  auto move = [&](int64_t i, int64_t slice) {  // receive row i, slice
     if (i >= n) return;
     const int64_t t = __builtin_amdgcn_readfirstlane(meta[i * (K + 2)]);
     if (t < 0 || t >= T) return;
@@ -76,11 +75,17 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
       }
     }
   };
-  if constexpr (WIDE) {  // one unit per wave
-    if (first < total) move(first);
+  if constexpr (WIDE) {  // one unit per wave, all of them in this launch (total < 2^26)
+    const uint32_t w = blockIdx.x * (uint32_t)wpb + wave_in_block;
+    if (w >= (uint32_t)total) return;
+    const uint32_t i = fast_div_apply(w, by_slices);
+    move(i, w - i * (uint32_t)slices);
   } else {
     const int64_t stride = (int64_t)gridDim.x * wpb;
-    for (int64_t gw = first; gw < total; gw += stride) move(gw);
+    for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < total; gw += stride) {
+      const int64_t i = gw / slices;
+      move(i, gw - i * slices);
+    }
   }
 }
 
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
     const u32x4 *__restrict__ y, int64_t row_chunks, const u32x4 *__restrict__ bias,
     const int32_t *__restrict__ dst_slot, const int32_t *__restrict__ meta,
     const int32_t *__restrict__ num_recv, int T, int K, u32x4 *__restrict__ out,
-    int64_t unit0) {
+    FastDiv by_slices) {
   const int lane = lane_id();
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int64_t half = (int64_t)T * slices;
@@ -129,10 +134,9 @@ __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wpb = blockDim.x / kWave;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int64_t first = unit0 + (int64_t)blockIdx.x * wpb + wave_in_block;
-  auto move = [&](int64_t gw) {
+  // unit gw < half: receive row r, slice gw - r * slices; else token gw - half
+  auto move = [&](int64_t gw, int64_t r) {
     if (gw < half) {
-      const int64_t r = gw / slices;
       const int64_t c = (gw - r * slices) * kWave + lane;
       if (r >= n) return;
       const int64_t t = __builtin_amdgcn_readfirstlane(meta[r * (K + 2)]);
@@ -148,40 +152,40 @@ __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
         put_row_chunk<WIDE, FP32>(zero, bias, t, row_chunks, c, out);
     }
   };
-  if constexpr (WIDE) {  // one unit per wave
-    if (first < half + T) move(first);
+  if constexpr (WIDE) {  // one unit per wave, all of them in this launch (half + T < 2^26)
+    const uint32_t w = blockIdx.x * (uint32_t)wpb + wave_in_block;
+    if (w >= (uint32_t)(half + T)) return;
+    move(w, fast_div_apply(w, by_slices));
   } else {
     const int64_t stride = (int64_t)gridDim.x * wpb;
-    for (int64_t gw = first; gw < half + T; gw += stride) move(gw);
+    for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < half + T; gw += stride)
+      move(gw, gw / slices);
   }
 }
 
-// Uncapped (WIDE): one wave per unit, in launches of at most kMaxLaunchUnits
-// units. Capped: one launch of at most `cap` workgroups whose waves loop.
+// Uncapped (WIDE): one launch with one wave per unit and 32-bit indices,
+// which needs units <= kMaxLaunchUnits (4.7M tokens at 14 slices per row).
+// Capped, or beyond that size: one launch of at most `cap` (or 2^22)
+// workgroups whose waves loop, with non-temporal stores.
 template <bool WIDE>
 int dispatch_compact_launch(const CompactDispatchArgs &a, int64_t units, int cap,
                             int64_t row_chunks) {
-  for (int64_t u0 = 0; u0 < units; u0 += WIDE ? kMaxLaunchUnits : units) {
-    const WaveGrid g = WIDE ? wave_grid(std::min(units - u0, kMaxLaunchUnits), 0, 1 << 24)
-                            : wave_grid(units, cap, 1 << 22);
-    ep_dispatch_compact_rows<WIDE><<<g.blocks, g.threads, 0, a.stream>>>(
-        (const u32x4 *)a.x, row_chunks, a.x_scales, a.scale_cols, a.topk_idx, a.topk_weights,
-        a.dst_slot, a.meta, a.num_recv, a.T, a.K, (u32x4 *)a.recv_x, a.recv_scales,
-        a.recv_topk_idx, a.recv_topk_weights, u0);
-  }
+  const WaveGrid g = WIDE ? wave_grid(units, 0, 1 << 24) : wave_grid(units, cap, 1 << 22);
+  ep_dispatch_compact_rows<WIDE><<<g.blocks, g.threads, 0, a.stream>>>(
+      (const u32x4 *)a.x, row_chunks, a.x_scales, a.scale_cols, a.topk_idx, a.topk_weights,
+      a.dst_slot, a.meta, a.num_recv, a.T, a.K, (u32x4 *)a.recv_x, a.recv_scales,
+      a.recv_topk_idx, a.recv_topk_weights,
+      fast_div((uint32_t)((row_chunks + kWave - 1) / kWave)));
   return launch_status();
 }
 
 template <bool WIDE, bool FP32>
 int combine_compact_launch(const CompactCombineArgs &a, int64_t units, int cap,
                            int64_t row_chunks) {
-  for (int64_t u0 = 0; u0 < units; u0 += WIDE ? kMaxLaunchUnits : units) {
-    const WaveGrid g = WIDE ? wave_grid(std::min(units - u0, kMaxLaunchUnits), 0, 1 << 24)
-                            : wave_grid(units, cap, 1 << 22);
-    ep_combine_compact_rows<WIDE, FP32><<<g.blocks, g.threads, 0, a.stream>>>(
-        (const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias, a.dst_slot, a.meta, a.num_recv,
-        a.T, a.K, (u32x4 *)a.out, u0);
-  }
+  const WaveGrid g = WIDE ? wave_grid(units, 0, 1 << 24) : wave_grid(units, cap, 1 << 22);
+  ep_combine_compact_rows<WIDE, FP32><<<g.blocks, g.threads, 0, a.stream>>>(
+      (const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias, a.dst_slot, a.meta, a.num_recv,
+      a.T, a.K, (u32x4 *)a.out, fast_div((uint32_t)((row_chunks + kWave - 1) / kWave)));
   return launch_status();
 }
 
@@ -193,8 +197,9 @@ int launch_dispatch_compact(const CompactDispatchArgs &a) {
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int cap = stream_workgroup_limit(a.stream);
   const int64_t units = (int64_t)a.T * slices;
-  return cap > 0 ? dispatch_compact_launch<false>(a, units, cap, row_chunks)
-                 : dispatch_compact_launch<true>(a, units, 0, row_chunks);
+  return cap > 0 || units > kMaxLaunchUnits
+             ? dispatch_compact_launch<false>(a, units, cap, row_chunks)
+             : dispatch_compact_launch<true>(a, units, 0, row_chunks);
 }
 
 int launch_combine_compact(const CompactCombineArgs &a) {
@@ -203,11 +208,12 @@ int launch_combine_compact(const CompactCombineArgs &a) {
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int cap = stream_workgroup_limit(a.stream);
   const int64_t units = (int64_t)a.T * (slices + 1);
+  const bool wide = cap == 0 && units <= kMaxLaunchUnits;
   if (a.fp32)
-    return cap > 0 ? combine_compact_launch<false, true>(a, units, cap, row_chunks)
-                   : combine_compact_launch<true, true>(a, units, 0, row_chunks);
-  return cap > 0 ? combine_compact_launch<false, false>(a, units, cap, row_chunks)
-                 : combine_compact_launch<true, false>(a, units, 0, row_chunks);
+    return wide ? combine_compact_launch<true, true>(a, units, 0, row_chunks)
+                : combine_compact_launch<false, true>(a, units, cap, row_chunks);
+  return wide ? combine_compact_launch<true, false>(a, units, 0, row_chunks)
+              : combine_compact_launch<false, false>(a, units, cap, row_chunks);
 }
 
 }  // namespace ep

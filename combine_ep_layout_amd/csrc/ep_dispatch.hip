@@ -44,11 +44,14 @@ namespace {
 // them so that each XCD gets one contiguous eighth of the work keeps the K
 // waves that copy the same source slice on one XCD, where all but the first
 // read it from that XCD's L2. The renumbering is a permutation only when the
-// grid is a multiple of 8: the launcher pads the grid to one.
+// grid is a multiple of 8: the launcher pads the grid to one. xcd_wave gives
+// the calling wave's index in a launch of kDefaultThreads-thread workgroups
+// under that renumbering, in 32 bits (grids of at most 2^24 workgroups).
 constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_contiguous_block() {
-  const int64_t nb = gridDim.x, b = blockIdx.x;
-  return (b % kXcds) * (nb / kXcds) + b / kXcds;
+__device__ __forceinline__ uint32_t xcd_wave() {
+  const uint32_t nb = gridDim.x, b = blockIdx.x;
+  return ((b % kXcds) * (nb / kXcds) + b / kXcds) * (kDefaultThreads / kWave) +
+         __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 }
 
 // Moves slice `slice` of x[t] (entry tk) to expand row d; slice 0 also
@@ -56,8 +59,8 @@ __device__ __forceinline__ int64_t xcd_contiguous_block() {
 template <int ROWB, int SCB>
 __device__ __forceinline__ void copy_slice(const u32x4 *__restrict__ x,
                                            const u32x4 *__restrict__ x_scales,
-                                           const float *__restrict__ topk_weights, int64_t t,
-                                           int64_t tk, int slice, int d, int lane,
+                                           const float *__restrict__ topk_weights, int t,
+                                           int tk, int slice, int d, int lane,
                                            u32x4 *__restrict__ expand_x,
                                            u32x4 *__restrict__ expand_scales,
                                            float *__restrict__ expand_weights) {
@@ -65,10 +68,11 @@ __device__ __forceinline__ void copy_slice(const u32x4 *__restrict__ x,
   constexpr int SCH = SCB / 16;
   const int i = slice * kWave + lane;
   if (CH % kWave == 0 || i < CH)
-    store_row<RowStore::kNtDevice>(x[t * CH + i], expand_x + (int64_t)d * CH, ROWB, i * 16);
+    store_row<RowStore::kNtDevice>(x[(int64_t)t * CH + i], expand_x + (int64_t)d * CH, ROWB,
+                                   i * 16);
   if (slice == 0) {
     if (SCH > 0 && lane < SCH)
-      __builtin_nontemporal_store(x_scales[t * SCH + lane],
+      __builtin_nontemporal_store(x_scales[(int64_t)t * SCH + lane],
                                   expand_scales + (int64_t)d * SCH + lane);
     if (expand_weights != nullptr && lane == 0) expand_weights[d] = topk_weights[tk];
   }
@@ -79,75 +83,66 @@ __device__ __forceinline__ void copy_slice(const u32x4 *__restrict__ x,
 // store. Consecutive waves write consecutive KiB of one destination row, the
 // order in which HBM absorbs writes fastest (a wave that scatters to K rows
 // in turn is slower). The fp8 scale row and the router weight travel with
-// slice 0. Waves are ordered token-major, then k, then slice, and loop over
-// the units past the grid limit.
+// slice 0. Entries are taken token-major, or with PLANNED in the order of the
+// layout's dispatch plan. Inside each tile of tokens the plan lists entries by
+// ascending slot, so consecutive entries are consecutive rows of one expert's
+// segment. Runs of about 4 rows at 128 tokens per tile make HBM absorb the
+// writes faster (prefill copy 79 against 85 us), and a tile's x rows (1.8 MB)
+// stay in the XCD's L2 for its K re-reads.
+// PLANNED: each wave moves exactly one unit, slice (w mod SLICES) of plan
+// entry entry0 + w / SLICES, w its wave index in the launch (w < units); the
+// host issues further launches past the grid limit. That walk's cost is its
+// per-wave scalar work: one scalar unit serves a compute unit's four SIMDs,
+// and at prefill each compute unit runs about 1800 of these waves. So its
+// index arithmetic is 32-bit (entries, slots and a launch's units all fit),
+// and without a loop the compiler loads each kernel argument where it is
+// first used instead of all of them up front (prefill copy 75.1 against 80.5
+// us with a grid-stride loop and 64-bit indices; MI355X, events). The
+// token-major walk measured the other way (prefill 86.6 against 83.5 us,
+// mori_default 22.9 against 21.7 in that form), so it keeps one launch
+// whose waves loop over all units (entry0 = 0).
 // DT (the EP_* dtype) only names the kernel: every dtype moves bytes, so
 // instances with equal ROWB and SCB have the same body.
-template <int DT, int ROWB, int SCB, int K>
+template <int DT, int ROWB, int SCB, int K, bool PLANNED>
 __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_expand(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
-    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
-    int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
-    float *__restrict__ expand_weights) {
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot,
+    const int2 *__restrict__ plan, int entries, int capacity, u32x4 *__restrict__ expand_x,
+    u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights, int entry0,
+    int units) {
   constexpr int CH = ROWB / 16;                    // 16-byte chunks per row
   constexpr int SLICES = (CH + kWave - 1) / kWave;  // 1 KiB slices per row
   constexpr int SCH = SCB / 16;                    // 16-byte chunks per scale row
   static_assert(ROWB % 16 == 0 && SCB % 16 == 0 && SCH <= kWave, "row geometry");
   static_assert(K >= 1 && K <= kWave, "topk must fit one wavefront");
-  const int lane = lane_id();
-  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  constexpr int wpb = kDefaultThreads / kWave;  // launched uncapped only
-  const int64_t total = (int64_t)T * K * SLICES;
-  const int64_t stride = (int64_t)gridDim.x * wpb;
-  for (int64_t gw = xcd_contiguous_block() * wpb + wave_in_block; gw < total; gw += stride) {
-    const int64_t tk = gw / SLICES;  // flat (token, k)
-    const int slice = (int)(gw - tk * SLICES);
-    const int d = __builtin_amdgcn_readfirstlane(dst_slot[tk]);
-    if (d < 0 || d >= capacity) continue;
-    copy_slice<ROWB, SCB>(x, x_scales, topk_weights, tk / K, tk, slice, d, lane, expand_x,
-                          expand_scales, expand_weights);
+  if constexpr (PLANNED) {
+    const uint32_t w = xcd_wave();
+    if (w >= (uint32_t)units) return;
+    const uint32_t jl = w / SLICES;
+    const int slice = (int)(w - jl * SLICES);
+    const int2 pe = plan[entry0 + (int)jl];
+    const int tk = __builtin_amdgcn_readfirstlane(pe.x);  // flat (token, k)
+    const int d = __builtin_amdgcn_readfirstlane(pe.y);
+    if ((uint32_t)tk >= (uint32_t)entries || (uint32_t)d >= (uint32_t)capacity) return;
+    copy_slice<ROWB, SCB>(x, x_scales, topk_weights, (int)((uint32_t)tk / K), tk, slice, d,
+                          lane_id(), expand_x, expand_scales, expand_weights);
+  } else {
+    const int lane = lane_id();
+    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    constexpr int wpb = kDefaultThreads / kWave;
+    const int64_t nb = gridDim.x, b = blockIdx.x;
+    const int64_t total = (int64_t)entries * SLICES;
+    const int64_t stride = nb * wpb;
+    for (int64_t gw = ((b % kXcds) * (nb / kXcds) + b / kXcds) * wpb + wave_in_block; gw < total;
+         gw += stride) {
+      const int64_t tk = gw / SLICES;  // flat (token, k)
+      const int slice = (int)(gw - tk * SLICES);
+      const int d = __builtin_amdgcn_readfirstlane(dst_slot[tk]);
+      if (d < 0 || d >= capacity) continue;
+      copy_slice<ROWB, SCB>(x, x_scales, topk_weights, (int)(tk / K), (int)tk, slice, d, lane,
+                            expand_x, expand_scales, expand_weights);
+    }
   }
-}
-
-// The same copy in the order of the layout's dispatch plan. Inside each tile
-// of tokens the plan lists entries by ascending slot, so consecutive entries
-// are consecutive rows of one expert's segment. Runs of about 4 rows at 128
-// tokens per tile make HBM absorb the writes faster (prefill copy 79 against
-// 85 us), and a tile's x rows (1.8 MB) stay in the XCD's L2 for its K
-// re-reads.
-// Each wave moves exactly one unit: slice (w mod SLICES) of plan entry
-// entry0 + w / SLICES, w its wave index in the launch (w < units); the host
-// issues further launches past the grid limit. This kernel's cost is its
-// per-wave scalar work: one scalar unit serves a compute unit's four SIMDs,
-// and at prefill each compute unit runs about 1800 of these waves. So the
-// index arithmetic is 32-bit (entries, slots and a launch's units all fit),
-// and without a loop the compiler loads each kernel argument where it is
-// first used instead of all of them up front (prefill copy 78.4 against 80.5
-// us with a grid-stride loop and 64-bit indices; MI355X, events).
-template <int DT, int ROWB, int SCB, int K>
-__global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_planned(
-    const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
-    const float *__restrict__ topk_weights, const int2 *__restrict__ plan, int entries,
-    int capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
-    float *__restrict__ expand_weights, int entry0, int units) {
-  constexpr int CH = ROWB / 16;
-  constexpr int SLICES = (CH + kWave - 1) / kWave;
-  constexpr int SCH = SCB / 16;
-  static_assert(ROWB % 16 == 0 && SCB % 16 == 0 && SCH <= kWave, "row geometry");
-  static_assert(K >= 1 && K <= kWave, "topk must fit one wavefront");
-  constexpr uint32_t wpb = kDefaultThreads / kWave;
-  const uint32_t nb = gridDim.x, b = blockIdx.x;  // nb: a multiple of kXcds
-  const uint32_t w = ((b % kXcds) * (nb / kXcds) + b / kXcds) * wpb +
-                     __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  if (w >= (uint32_t)units) return;
-  const uint32_t jl = w / SLICES;
-  const int slice = (int)(w - jl * SLICES);
-  const int2 pe = plan[entry0 + (int)jl];
-  const int tk = __builtin_amdgcn_readfirstlane(pe.x);  // flat (token, k)
-  const int d = __builtin_amdgcn_readfirstlane(pe.y);
-  if ((uint32_t)tk >= (uint32_t)entries || (uint32_t)d >= (uint32_t)capacity) return;
-  copy_slice<ROWB, SCB>(x, x_scales, topk_weights, (int)((uint32_t)tk / K), tk, slice, d,
-                        lane_id(), expand_x, expand_scales, expand_weights);
 }
 
 // Copies slice `slice` of token t's row to the destination rows of the F
@@ -157,25 +152,25 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_planned(
 template <int ROWB, int SCB, int K, int F, RowStore P>
 __device__ __forceinline__ void copy_slice_to_group(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
-    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int64_t t,
-    int k0, int slice, int64_t capacity, u32x4 *__restrict__ expand_x,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int t,
+    int k0, int slice, int capacity, u32x4 *__restrict__ expand_x,
     u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights) {
   constexpr int CH = ROWB / 16;
   constexpr int SCH = SCB / 16;
   static_assert(ROWB % 16 == 0 && SCB % 16 == 0 && SCH <= kWave, "row geometry");
   static_assert(F >= 1 && F <= K && K % F == 0 && K <= kWave, "entry group");
   const int lane = lane_id();
-  const int64_t tk0 = t * K + k0;
+  const int tk0 = t * K + k0;  // below num_tokens * topk, an int32
   const int i = slice * kWave + lane;
   const bool in_row = CH % kWave == 0 || i < CH;
   u32x4 v = {0u, 0u, 0u, 0u}, sc = {0u, 0u, 0u, 0u};
-  if (in_row) v = x[t * CH + i];
-  if (SCH > 0 && slice == 0 && lane < SCH) sc = x_scales[t * SCH + lane];
+  if (in_row) v = x[(int64_t)t * CH + i];
+  if (SCH > 0 && slice == 0 && lane < SCH) sc = x_scales[(int64_t)t * SCH + lane];
   // every lane reads a slot (lanes past F repeat entry k0) so that no branch
   // separates this load from the ones above and all are in flight together
   int my_d = dst_slot[tk0 + (lane < F ? lane : 0)];
   wait_vector_memory();
-  if (lane >= F || my_d >= capacity) my_d = -1;
+  if (lane >= F || (uint32_t)my_d >= (uint32_t)capacity) my_d = -1;
 #pragma unroll
   for (int j = 0; j < F; ++j) {
     const int d = read_lane(my_d, j);
@@ -192,27 +187,28 @@ __device__ __forceinline__ void copy_slice_to_group(
 // Uncapped, x larger than the cache can hold: one wave per (token, group of
 // F entries, 1 KiB slice), ordered token-major, then group, then slice, with
 // the blocks of one XCD contiguous as in ep_dispatch_expand. Each wave moves
-// one unit, unit0 + its wave index (no loop: 827 against 832 us at 32K
-// tokens).
+// one unit: slice (w mod SLICES) of group group0 + w / SLICES, w its wave
+// index in the launch (w < units), with 32-bit index arithmetic as in
+// ep_dispatch_expand.
 template <int DT, int ROWB, int SCB, int K, int F>
 __global__ __launch_bounds__(kDefaultThreads) void ep_dispatch_grouped(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ x_scales,
-    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int T,
-    int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
-    float *__restrict__ expand_weights, int64_t unit0) {
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ dst_slot, int capacity,
+    u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
+    float *__restrict__ expand_weights, int group0, int units) {
   constexpr int SLICES = (ROWB / 16 + kWave - 1) / kWave;
-  constexpr int KG = K / F;  // entry groups per token
-  const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  constexpr int wpb = kDefaultThreads / kWave;
-  const int64_t gw = unit0 + xcd_contiguous_block() * wpb + wave_in_block;
-  if (gw >= (int64_t)T * KG * SLICES) return;
-  const int64_t tg = gw / SLICES;  // flat (token, group)
-  const int slice = (int)(gw - tg * SLICES);
-  const int64_t t = tg / KG;
+  constexpr uint32_t KG = K / F;  // entry groups per token
+  const uint32_t w = xcd_wave();
+  if (w >= (uint32_t)units) return;
+  const uint32_t gl = w / SLICES;
+  const int slice = (int)(w - gl * SLICES);
+  const uint32_t tg = (uint32_t)group0 + gl;  // flat (token, group)
+  const uint32_t t = tg / KG;
   const int g = (int)(tg - t * KG);
   copy_slice_to_group<ROWB, SCB, K, F, RowStore::kNtDevice>(x, x_scales, topk_weights, dst_slot,
-                                                            t, g * F, slice, capacity, expand_x,
-                                                            expand_scales, expand_weights);
+                                                            (int)t, g * F, slice, capacity,
+                                                            expand_x, expand_scales,
+                                                            expand_weights);
 }
 
 // Under a workgroup cap: one wave per (token, 1 KiB slice), all K entries.
@@ -227,12 +223,13 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_fanout(
   constexpr int wpb = kCappedThreads / kWave;  // launched under a cap only
   const int64_t total = (int64_t)T * SLICES;
   const int64_t stride = (int64_t)gridDim.x * wpb;
+  const int cap32 = (int)(capacity < INT32_MAX ? capacity : INT32_MAX);
   for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < total; gw += stride) {
-    const int64_t t = gw / SLICES;
-    const int slice = (int)(gw - t * SLICES);
-    copy_slice_to_group<ROWB, SCB, K, K, RowStore::kNt>(x, x_scales, topk_weights, dst_slot, t, 0, slice,
-                                                capacity, expand_x, expand_scales,
-                                                expand_weights);
+    const int t = (int)(gw / SLICES);
+    const int slice = (int)(gw - (int64_t)t * SLICES);
+    copy_slice_to_group<ROWB, SCB, K, K, RowStore::kNt>(x, x_scales, topk_weights, dst_slot, t, 0,
+                                                        slice, cap32, expand_x, expand_scales,
+                                                        expand_weights);
   }
 }
 
@@ -259,33 +256,37 @@ int dispatch_impl(const DispatchArgs &a) {
         x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
     return launch_status();
   }
+  // Uncapped: one wave per unit, in launches of whole entries (or entry
+  // groups) of at most kMaxLaunchUnits units. Slots are int32, so a capacity
+  // beyond INT32_MAX admits them all.
+  const int cap32 = (int)std::min<int64_t>(a.capacity, INT32_MAX);
   if constexpr (F > 1) {
     if ((int64_t)a.T * ROWB > kCachedXBytes) {
-      const int64_t units = (int64_t)a.T * (K / F) * SLICES;
-      for (int64_t u0 = 0; u0 < units; u0 += kMaxLaunchUnits) {
-        const WaveGrid g = wave_grid(std::min(units - u0, kMaxLaunchUnits), 0, 1 << 24, kXcds);
+      const int groups = a.T * (K / F);
+      constexpr int kLaunchGroups = (int)(kMaxLaunchUnits / SLICES);
+      for (int g0 = 0; g0 < groups; g0 += std::min(kLaunchGroups, groups - g0)) {
+        const int units = std::min(kLaunchGroups, groups - g0) * SLICES;
+        const WaveGrid g = wave_grid(units, 0, 1 << 24, kXcds);
         ep_dispatch_grouped<DT, ROWB, SCB, K, F><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-            x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew, u0);
+            x, xs, a.topk_weights, a.dst_slot, cap32, ex, es, ew, g0, units);
       }
       return launch_status();
     }
   }
+  const int entries = a.T * K;  // at most INT32_MAX (checked by the C ABI)
   if (a.plan == nullptr) {  // one launch; its waves loop past the grid limit
-    const WaveGrid g = wave_grid((int64_t)a.T * K * SLICES, 0, 1 << 24, kXcds);
-    ep_dispatch_expand<DT, ROWB, SCB, K><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-        x, xs, a.topk_weights, a.dst_slot, a.T, a.capacity, ex, es, ew);
+    const WaveGrid g = wave_grid((int64_t)entries * SLICES, 0, 1 << 24, kXcds);
+    ep_dispatch_expand<DT, ROWB, SCB, K, false><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+        x, xs, a.topk_weights, a.dst_slot, nullptr, entries, cap32, ex, es, ew, 0, 0);
     return launch_status();
   }
-  // One wave per unit; a launch covers whole entries, at most kMaxLaunchUnits
-  // units. Slots are int32, so a capacity beyond INT32_MAX admits them all.
-  const int entries = a.T * K;  // at most INT32_MAX (checked by the C ABI)
-  const int cap32 = (int)std::min<int64_t>(a.capacity, INT32_MAX);
   constexpr int kLaunchEntries = (int)(kMaxLaunchUnits / SLICES);
   for (int e0 = 0; e0 < entries; e0 += std::min(kLaunchEntries, entries - e0)) {
     const int units = std::min(kLaunchEntries, entries - e0) * SLICES;
     const WaveGrid g = wave_grid(units, 0, 1 << 24, kXcds);
-    ep_dispatch_planned<DT, ROWB, SCB, K><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
-        x, xs, a.topk_weights, (const int2 *)a.plan, entries, cap32, ex, es, ew, e0, units);
+    ep_dispatch_expand<DT, ROWB, SCB, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
+        x, xs, a.topk_weights, a.dst_slot, (const int2 *)a.plan, entries, cap32, ex, es, ew, e0,
+        units);
   }
   return launch_status();
 }

@@ -107,6 +107,25 @@ struct CompactCombineArgs {
 constexpr int kDefaultThreads = 256;
 constexpr int kCappedThreads = 1024;
 
+// Division of n < 2^31 by a divisor d (1 <= d < 2^31) fixed per launch, by
+// multiplication: q = (n * m) >> s with s = 31 + ceil(log2 d) and
+// m = floor(2^s / d) + 1 (below 2^32). m exceeds 2^s / d by at most 1, so
+// n * m / 2^s exceeds n / d by less than n / 2^s < 2^-ceil(log2 d) <= 1 / d,
+// which never reaches the next multiple of 1 / d above n / d: the floor is
+// exact. Costs a 32 x 32 -> 64-bit multiply and a shift instead of a
+// division sequence.
+struct FastDiv {
+  uint32_t m, s;
+};
+inline FastDiv fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  return {(uint32_t)((uint64_t(1) << (31 + l)) / d + 1), 31 + l};
+}
+__device__ __forceinline__ uint32_t fast_div_apply(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)n * f.m) >> f.s);
+}
+
 // Units (one wave each) per launch of a kernel whose uncapped waves move one
 // unit and exit: 2^24 - 16 workgroups of four waves (a multiple of 8, within
 // the grid limit of 2^32 threads). Larger inputs take further launches, each
