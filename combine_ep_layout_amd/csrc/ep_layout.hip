@@ -358,7 +358,7 @@ __device__ __forceinline__ void copy_counted(
     const int32_t *__restrict__ topk_idx, int T, int E, const u32x4 *__restrict__ x,
     int row_chunks, const u32x4 *__restrict__ x_scales, int scale_chunks,
     const float *__restrict__ topk_weights, int64_t capacity, u32x4 *__restrict__ expand_x,
-    u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights) {
+    u32x4 *__restrict__ expand_scales, float *__restrict__ expand_weights, FastDiv by_slices) {
   constexpr int kNoKey = 0x7fffffff;
   constexpr int kPre = 4;  // units per wave whose row slices load before the keys
   int *s_key = (int *)g_smem;  // kThreads keys
@@ -366,14 +366,17 @@ __device__ __forceinline__ void copy_counted(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = T * K;  // <= kThreads (one tile)
   const int slices = (row_chunks + kWave - 1) / kWave;
-  const int64_t units = (int64_t)n * slices;
-  const int64_t stride = (int64_t)(gridDim.x - 1) * kWavesMax;
-  const int64_t u0 = (int64_t)(blockIdx.x - 1) * kWavesMax + wave;
-  auto load = [&](int64_t u) {
+  // 32-bit unit indices (n * slices < 2^20) and a multiply-shift division by
+  // the slice count: the index arithmetic sits on each wave's path to its
+  // first load.
+  const int units = n * slices;
+  const int stride = (int)(gridDim.x - 1) * kWavesMax;
+  const int u0 = (int)(blockIdx.x - 1) * kWavesMax + wave;
+  auto load = [&](int u) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (u < units) {
-      const int j = (int)(u / slices);
-      const int c = (int)(u - (int64_t)j * slices) * kWave + lane;
+      const int j = (int)fast_div_apply((uint32_t)u, by_slices);
+      const int c = (u - j * slices) * kWave + lane;
       if (c < row_chunks) v = x[(int64_t)(j / K) * row_chunks + c];
     }
     return v;
@@ -387,9 +390,9 @@ __device__ __forceinline__ void copy_counted(
   int key[kWavesMax];  // entries q * 64 + lane
 #pragma unroll
   for (int q = 0; q < kWavesMax; ++q) key[q] = s_key[q * kWave + lane];
-  auto copy = [&](int64_t u, const u32x4 &v) {
-    const int j = (int)(u / slices);
-    const int slice = (int)(u - (int64_t)j * slices);
+  auto copy = [&](int u, const u32x4 &v) {
+    const int j = (int)fast_div_apply((uint32_t)u, by_slices);
+    const int slice = u - j * slices;
     const int kj = __builtin_amdgcn_readfirstlane(s_key[j]);
     if (kj == kNoKey) return;  // masked: no slot
     int below = 0;
@@ -403,7 +406,7 @@ __device__ __forceinline__ void copy_counted(
 #pragma unroll
   for (int p = 0; p < kPre; ++p)
     if (u0 + p * stride < units) copy(u0 + p * stride, pre[p]);
-  for (int64_t u = u0 + kPre * stride; u < units; u += stride) copy(u, load(u));
+  for (int u = u0 + kPre * stride; u < units; u += stride) copy(u, load(u));
 }
 
 // Layout and dispatch in one launch for a batch that fits one tile (a
@@ -427,10 +430,10 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
     int32_t *__restrict__ num_recv, const u32x4 *__restrict__ x, int row_chunks,
     const u32x4 *__restrict__ x_scales, int scale_chunks, const float *__restrict__ topk_weights,
     int64_t capacity, u32x4 *__restrict__ expand_x, u32x4 *__restrict__ expand_scales,
-    float *__restrict__ expand_weights) {
+    float *__restrict__ expand_weights, FastDiv by_slices) {
   if (COUNTED && blockIdx.x != 0) {
     copy_counted<K, WIDE>(topk_idx, T, E, x, row_chunks, x_scales, scale_chunks, topk_weights,
-                          capacity, expand_x, expand_scales, expand_weights);
+                          capacity, expand_x, expand_scales, expand_weights, by_slices);
     return;
   }
   __shared__ int s_scan[kWavesMax];
@@ -472,11 +475,11 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int slices = (row_chunks + kWave - 1) / kWave;
-  const int64_t units = (int64_t)T * K * slices;
-  const int64_t stride = (int64_t)gridDim.x * kWavesMax;
-  for (int64_t u = (int64_t)blockIdx.x * kWavesMax + wave; u < units; u += stride) {
-    const int j = (int)(u / slices);  // entry t*K + k
-    const int slice = (int)(u - (int64_t)j * slices);
+  const int units = T * K * slices;  // one tile: below 2^20
+  const int stride = (int)gridDim.x * kWavesMax;
+  for (int u = (int)blockIdx.x * kWavesMax + wave; u < units; u += stride) {
+    const int j = (int)fast_div_apply((uint32_t)u, by_slices);  // entry t*K + k
+    const int slice = u - j * slices;
     const int d = __builtin_amdgcn_readfirstlane(s_slot[j]);
     if (d < 0 || d >= capacity) continue;
     const int64_t t = j / K;
@@ -504,7 +507,8 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_compact_tile(
     int32_t *__restrict__ num_recv, const u32x4 *__restrict__ x, int row_chunks,
     const float *__restrict__ x_scales, int scale_cols, const float *__restrict__ topk_weights,
     u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales,
-    int32_t *__restrict__ recv_topk_idx, float *__restrict__ recv_topk_weights) {
+    int32_t *__restrict__ recv_topk_idx, float *__restrict__ recv_topk_weights,
+    FastDiv by_slices) {
   __shared__ int s_scan[kWavesMax];
   __shared__ int s_flag[kWavesMax];
   const RankLds s = rank_lds(E, NW);
@@ -540,11 +544,11 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_compact_tile(
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int slices = (row_chunks + kWave - 1) / kWave;
-  const int64_t units = (int64_t)T * slices;
-  const int64_t stride = (int64_t)gridDim.x * kWavesMax;
-  for (int64_t u = (int64_t)blockIdx.x * kWavesMax + wave; u < units; u += stride) {
-    const int t = (int)(u / slices);
-    const int slice = (int)(u - (int64_t)t * slices);
+  const int units = T * slices;  // one tile: below 2^20
+  const int stride = (int)gridDim.x * kWavesMax;
+  for (int u = (int)blockIdx.x * kWavesMax + wave; u < units; u += stride) {
+    const int t = (int)fast_div_apply((uint32_t)u, by_slices);
+    const int slice = u - t * slices;
     const int i = __builtin_amdgcn_readfirstlane(s.tok[t]);  // receive row, or -1
     if (i < 0) continue;
     const int c = slice * kWave + lane;
@@ -1060,7 +1064,7 @@ int layout_dispatch_impl(const LayoutArgs &l, const DispatchArgs &d, int row_chu
             l.topk_idx, l.T, l.E, l.A, l.counts, l.offsets, l.dst_slot, l.meta, l.num_recv,
             (const u32x4 *)d.x, row_chunks, (const u32x4 *)d.x_scales, scale_chunks,
             d.topk_weights, d.capacity, (u32x4 *)d.expand_x, (u32x4 *)d.expand_scales,
-            fwd_w ? d.expand_weights : nullptr);
+            fwd_w ? d.expand_weights : nullptr, fast_div((uint32_t)slices));
   };
   if (cap > 0) go(std::false_type{}, std::false_type{}, blocks);
   else if (l.A == 1)  // workgroup 0 lays out, the others copy
@@ -1086,7 +1090,8 @@ int layout_dispatch_compact_impl(const LayoutArgs &l, const CompactDispatchArgs 
         <<<(unsigned)blocks, kThreads, shm, l.stream>>>(
             l.topk_idx, l.T, l.E, l.A, l.counts, l.offsets, l.dst_slot, l.meta, l.num_recv,
             (const u32x4 *)d.x, row_chunks, d.x_scales, (int)d.scale_cols, d.topk_weights,
-            (u32x4 *)d.recv_x, d.recv_scales, d.recv_topk_idx, d.recv_topk_weights);
+            (u32x4 *)d.recv_x, d.recv_scales, d.recv_topk_idx, d.recv_topk_weights,
+            fast_div((uint32_t)slices));
   };
   if (cap > 0) go(std::false_type{});
   else go(std::true_type{});
