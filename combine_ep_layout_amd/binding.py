@@ -107,6 +107,16 @@ def lib(path: str = None) -> ctypes.CDLL:
     return L
 
 
+def use_library(path: str = None) -> ctypes.CDLL:
+    """Make the module's functions call the library at `path` (another build of the same
+    library, as EP_MI355X_LIB does at import), or the default one for None; returns it."""
+    global _LIB
+    _LIB = None
+    L = lib(path or LIB_PATH)
+    _LIB = L
+    return L
+
+
 def _p(a):
     if a is None:
         return None

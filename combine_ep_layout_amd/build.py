@@ -7,6 +7,11 @@ to this file. Objects go to <repo>/_build/.
 `python build.py --asan-host` instead builds libep_mi355x_asan.so with
 AddressSanitizer on the host code only (device code is unchanged); load it
 with the clang ASan runtime preloaded to check the C ABI's host paths.
+
+build_small_launch() builds libep_mi355x_small_launch.so, a test build in
+which one launch of the one-unit-per-wave kernels covers at most
+SMALL_LAUNCH_UNITS units, so that small GPU tests run the paths that split
+large inputs over several launches (or fall back to looping kernels).
 """
 import concurrent.futures as cf
 import os
@@ -32,6 +37,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 
 ASAN_HOST = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 ASAN_LIB = os.path.join(PKG, "libep_mi355x_asan.so")
+
+SMALL_LAUNCH_UNITS = 4160
+SMALL_LAUNCH_LIB = os.path.join(PKG, "libep_mi355x_small_launch.so")
+SMALL_LAUNCH_SOURCES = ("ep_dispatch.hip", "ep_compact.hip")  # the users of the limit
 
 
 def _compile(src: str, extra=(), tag: str = "") -> str:
@@ -67,6 +76,26 @@ def build(out: str = LIB, extra=(), jobs: int = 4, verbose: bool = False,
     if verbose:
         print(out)
     return out
+
+
+def build_small_launch(jobs: int = 4, verbose: bool = False) -> str:
+    """The test build: the library with EP_MAX_LAUNCH_UNITS = SMALL_LAUNCH_UNITS. Reuses the
+    objects of build() for the sources that do not read the limit (call build() first)."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = (f"-DEP_MAX_LAUNCH_UNITS={SMALL_LAUNCH_UNITS}",)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        small = dict(zip(SMALL_LAUNCH_SOURCES,
+                         ex.map(lambda s: _compile(s, extra, ".small"), SMALL_LAUNCH_SOURCES)))
+    objs = [small.get(s) or os.path.join(BUILD, s + ".o") for s in SOURCES]
+    tmp = SMALL_LAUNCH_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SMALL_LAUNCH_LIB)
+    if verbose:
+        print(SMALL_LAUNCH_LIB)
+    return SMALL_LAUNCH_LIB
 
 
 if __name__ == "__main__":

@@ -129,8 +129,12 @@ __device__ __forceinline__ uint32_t fast_div_apply(uint32_t n, FastDiv f) {
 // Units (one wave each) per launch of a kernel whose uncapped waves move one
 // unit and exit: 2^24 - 16 workgroups of four waves (a multiple of 8, within
 // the grid limit of 2^32 threads). Larger inputs take further launches, each
-// from a unit offset.
-constexpr int64_t kMaxLaunchUnits = (int64_t(1) << 26) - 64;
+// from a unit offset. A test build sets EP_MAX_LAUNCH_UNITS to a few thousand
+// so that those paths run on small inputs.
+#ifndef EP_MAX_LAUNCH_UNITS
+#define EP_MAX_LAUNCH_UNITS ((int64_t(1) << 26) - 64)
+#endif
+constexpr int64_t kMaxLaunchUnits = EP_MAX_LAUNCH_UNITS;
 
 // The cap registered for this stream handle, or 0 for none.
 int stream_workgroup_limit(hipStream_t stream);
