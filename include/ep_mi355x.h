@@ -145,10 +145,12 @@ size_t ep_layout_dispatch_workspace_bytes(int32_t num_tokens, int32_t topk, int3
  *                     masked entry. This array is not part of the pages'
  *                     handle: it is a gfx950-specific write-order aid, and
  *                     every other output is the same with or without it.
- *                     Measured on MI355X it pays for large expand buffers
- *                     (prefill with 470 MB of rows: dispatch 87 -> 83 us for
- *                     0.1 us more layout). At 120 MB of rows and below it
- *                     gains about what it costs the layout (0.1-0.4 us).
+ *                     Measured on MI355X (steps with ep_dispatch following
+ *                     the plan against token-major): prefill with 470 MB of
+ *                     rows 167.5 against 175.9 us with the rows cached,
+ *                     190.9 against 231.5 us with them evicted; mori_default
+ *                     (1024 tokens) 46.0 against 49.7 and 52.5 against
+ *                     63.5 us. The layout pays 0.1-0.4 us for it.
  *   prefetch,         optional read-ahead (NULL and 0: none): device memory
  *   prefetch_bytes    the caller reads next, typically the token rows x
  *                     (and their scale rows) that ep_dispatch copies. The
@@ -163,8 +165,8 @@ size_t ep_layout_dispatch_workspace_bytes(int32_t num_tokens, int32_t topk, int3
  *                     aligned; NULL with nonzero bytes is EP_EINVAL.
  *                     Measured on MI355X (prefill step, 4096 tokens of
  *                     hidden 7168, 58.7 MB of rows): with the rows not in the
- *                     cache the step takes 184 us with the read-ahead against
- *                     197 us without; with the rows cached, 177 against 173
+ *                     cache the step takes 177 us with the read-ahead against
+ *                     191 us without; with the rows cached, 172 against 167
  *                     us (the reads then only add work). Worth asking for
  *                     when x was produced long before dispatch.
  * Results are a pure function of the inputs (no atomics whose order matters).
