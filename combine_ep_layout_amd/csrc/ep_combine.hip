@@ -268,11 +268,23 @@ __device__ __forceinline__ void stream_fold(const u32x4 *__restrict__ y, const i
 // chip's 2048 wave slots at its two waves per SIMD.
 constexpr int kStreamMinTokens = 1024;
 
+// Output bytes above which ep_combine_stream stores its rows non-temporally:
+// half of MI355X's 256 MiB last-level cache. Below it the kept rows are
+// absorbed by that cache (prefill, 59 MB: 86.9 against 91.6 us; fp8_hot8 and
+// binary32 rows, 117 MB: 167.4 against 177.2 us and 170.8 against 179.4);
+// above it they only evict other lines (32K tokens, 470 MB: 731 against
+// 753 us with them kept).
+constexpr int64_t kCachedOutBytes = int64_t(128) << 20;
+
+// stream_out: the output rows are larger than the last-level cache can keep
+// beside the other traffic, so they are stored non-temporally at device scope
+// (RowStore::kNtDevice) instead of kept (RowStore::kDevice); a wave-uniform
+// branch around the stores.
 template <int DT, int H, int K, bool BIAS>
 __global__ __launch_bounds__(kDefaultThreads) void ep_combine_stream(
     const u32x4 *__restrict__ y, const float *__restrict__ topk_weights,
     const u32x4 *__restrict__ bias, const int32_t *__restrict__ dst_slot, int T,
-    int64_t capacity, u32x4 *__restrict__ out) {
+    int64_t capacity, u32x4 *__restrict__ out, int stream_out) {
   constexpr int CH = H * Elem<DT>::BYTES / 16;
   constexpr int PC = Elem<DT>::PER_CHUNK;
   using Geo = StreamGeometry<CH>;
@@ -326,7 +338,10 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_combine_stream(
 #pragma unroll
         for (int j = 0; j < PC; ++j) acc[c][j] = acc[c][j] + Elem<DT>::get(b, j);
       }
-      store_row<RowStore::kDevice>(Elem<DT>::put(acc[c]), o, CH * 16, i * 16);
+      if (stream_out)
+        store_row<RowStore::kNtDevice>(Elem<DT>::put(acc[c]), o, CH * 16, i * 16);
+      else
+        store_row<RowStore::kDevice>(Elem<DT>::put(acc[c]), o, CH * 16, i * 16);
     }
   }
 }
@@ -353,14 +368,15 @@ int combine_impl(const CombineArgs &a) {
     if (a.T >= kStreamMinTokens && cap == 0) {
       // At most 2^24 workgroups (the grid limit of 2^32 threads); waves loop past it.
       const WaveGrid g = wave_grid((int64_t)a.T * StreamGeometry<CH>::PIECES, 0, 1 << 24);
+      const int stream_out = (int64_t)a.T * CH * 16 > kCachedOutBytes;
       if (a.bias)
         ep_combine_stream<DT, H, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
             (const u32x4 *)a.y, a.topk_weights, (const u32x4 *)a.bias, a.dst_slot, a.T,
-            a.capacity, (u32x4 *)a.out);
+            a.capacity, (u32x4 *)a.out, stream_out);
       else
         ep_combine_stream<DT, H, K, false><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
             (const u32x4 *)a.y, a.topk_weights, nullptr, a.dst_slot, a.T, a.capacity,
-            (u32x4 *)a.out);
+            (u32x4 *)a.out, stream_out);
       return launch_status();
     }
   }

@@ -38,7 +38,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // WIDE: launched over the whole chip (no workgroup cap), which selects the
 // store policy: the receive rows and combine's output rows (one row per
 // token, 59 MB at prefill) are stored at device scope and kept
-// (RowStore::kDevice); under a cap, non-temporally.
+// (RowStore::kDevice), unless they are larger than the last-level cache can
+// keep beside the other traffic (stream_out: more than 128 MiB), when they
+// are stored non-temporally at device scope (RowStore::kNtDevice; 32K tokens,
+// 470 MB of rows: dispatch 152.2 against 157.8 us, step 308.7 against 322.5;
+// at 117 MB, fp8_hot8, the kept rows are faster: combine 36.4 against 38.0).
+// Under a cap, non-temporally.
+template <bool WIDE>
+__device__ __forceinline__ void store_out_row(const u32x4 &v, void *row, int row_bytes, int off,
+                                              int stream_out) {
+  if constexpr (!WIDE) {
+    store_row<RowStore::kNt>(v, row, row_bytes, off);
+  } else if (stream_out) {
+    store_row<RowStore::kNtDevice>(v, row, row_bytes, off);
+  } else {
+    store_row<RowStore::kDevice>(v, row, row_bytes, off);
+  }
+}
+
 template <bool WIDE>
 __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     const u32x4 *__restrict__ x, int64_t row_chunks, const float *__restrict__ x_scales,
@@ -47,7 +64,7 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     const int32_t *__restrict__ meta, const int32_t *__restrict__ num_recv, int T, int K,
     u32x4 *__restrict__ recv_x, float *__restrict__ recv_scales,
     int32_t *__restrict__ recv_topk_idx, float *__restrict__ recv_topk_weights,
-    FastDiv by_slices) {
+    FastDiv by_slices, int stream_out) {
   const int lane = lane_id();
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int64_t total = (int64_t)T * slices;
@@ -60,10 +77,8 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
     if (t < 0 || t >= T) return;
     const int64_t c = slice * kWave + lane;
     if (c < row_chunks)
-      store_row<WIDE ? RowStore::kDevice : RowStore::kNt>(x[t * row_chunks + c],
-                                                          recv_x + i * row_chunks,
-                                                          (int)(row_chunks * 16),
-                         (int)(c * 16));
+      store_out_row<WIDE>(x[t * row_chunks + c], recv_x + i * row_chunks,
+                          (int)(row_chunks * 16), (int)(c * 16), stream_out);
     if (slice == 0) {
       if (recv_scales != nullptr)
         for (int64_t j = lane; j < scale_cols; j += kWave)
@@ -95,7 +110,7 @@ __global__ __launch_bounds__(kCappedThreads) void ep_dispatch_compact_rows(
 template <bool WIDE, bool FP32>
 __device__ __forceinline__ void put_row_chunk(u32x4 v, const u32x4 *__restrict__ bias, int64_t t,
                                               int64_t row_chunks, int64_t c,
-                                              u32x4 *__restrict__ out) {
+                                              u32x4 *__restrict__ out, int stream_out) {
 #pragma clang fp contract(off)
   if (bias != nullptr) {
     const u32x4 b = bias[t * row_chunks + c];
@@ -113,8 +128,8 @@ __device__ __forceinline__ void put_row_chunk(u32x4 v, const u32x4 *__restrict__
     }
     v = r;
   }
-  store_row<WIDE ? RowStore::kDevice : RowStore::kNt>(v, out + t * row_chunks,
-                                                      (int)(row_chunks * 16), (int)(c * 16));
+  store_out_row<WIDE>(v, out + t * row_chunks, (int)(row_chunks * 16), (int)(c * 16),
+                      stream_out);
 }
 
 // Waves [0, T*slices): (receive row, slice) back to its token. Waves
@@ -126,7 +141,7 @@ __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
     const u32x4 *__restrict__ y, int64_t row_chunks, const u32x4 *__restrict__ bias,
     const int32_t *__restrict__ dst_slot, const int32_t *__restrict__ meta,
     const int32_t *__restrict__ num_recv, int T, int K, u32x4 *__restrict__ out,
-    FastDiv by_slices) {
+    FastDiv by_slices, int stream_out) {
   const int lane = lane_id();
   const int64_t slices = (row_chunks + kWave - 1) / kWave;
   const int64_t half = (int64_t)T * slices;
@@ -142,14 +157,14 @@ __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
       const int64_t t = __builtin_amdgcn_readfirstlane(meta[r * (K + 2)]);
       if (t < 0 || t >= T || c >= row_chunks) return;
       const u32x4 v = __builtin_nontemporal_load(y + r * row_chunks + c);
-      put_row_chunk<WIDE, FP32>(v, bias, t, row_chunks, c, out);
+      put_row_chunk<WIDE, FP32>(v, bias, t, row_chunks, c, out, stream_out);
     } else {
       const int64_t t = gw - half;
       bool any = false;
       for (int k = lane; k < K; k += kWave) any |= dst_slot[t * K + k] >= 0;
       if (ballot(any) != 0) return;  // received: written by its receive row
       for (int64_t c = lane; c < row_chunks; c += kWave)
-        put_row_chunk<WIDE, FP32>(zero, bias, t, row_chunks, c, out);
+        put_row_chunk<WIDE, FP32>(zero, bias, t, row_chunks, c, out, stream_out);
     }
   };
   if constexpr (WIDE) {  // one unit per wave, all of them in this launch (half + T < 2^26)
@@ -163,6 +178,10 @@ __global__ __launch_bounds__(kCappedThreads) void ep_combine_compact_rows(
   }
 }
 
+// Output rows (bytes, at most T rows) above which uncapped launches store
+// them non-temporally (store_out_row): half of the 256 MiB last-level cache.
+constexpr int64_t kCachedRowsBytes = int64_t(128) << 20;
+
 // Uncapped (WIDE): one launch with one wave per unit and 32-bit indices,
 // which needs units <= kMaxLaunchUnits (4.7M tokens at 14 slices per row).
 // Capped, or beyond that size: one launch of at most `cap` (or 2^22)
@@ -175,7 +194,8 @@ int dispatch_compact_launch(const CompactDispatchArgs &a, int64_t units, int cap
       (const u32x4 *)a.x, row_chunks, a.x_scales, a.scale_cols, a.topk_idx, a.topk_weights,
       a.dst_slot, a.meta, a.num_recv, a.T, a.K, (u32x4 *)a.recv_x, a.recv_scales,
       a.recv_topk_idx, a.recv_topk_weights,
-      fast_div((uint32_t)((row_chunks + kWave - 1) / kWave)));
+      fast_div((uint32_t)((row_chunks + kWave - 1) / kWave)),
+      (int64_t)a.T * row_chunks * 16 > kCachedRowsBytes);
   return launch_status();
 }
 
@@ -185,7 +205,8 @@ int combine_compact_launch(const CompactCombineArgs &a, int64_t units, int cap,
   const WaveGrid g = WIDE ? wave_grid(units, 0, 1 << 24) : wave_grid(units, cap, 1 << 22);
   ep_combine_compact_rows<WIDE, FP32><<<g.blocks, g.threads, 0, a.stream>>>(
       (const u32x4 *)a.y, row_chunks, (const u32x4 *)a.bias, a.dst_slot, a.meta, a.num_recv,
-      a.T, a.K, (u32x4 *)a.out, fast_div((uint32_t)((row_chunks + kWave - 1) / kWave)));
+      a.T, a.K, (u32x4 *)a.out, fast_div((uint32_t)((row_chunks + kWave - 1) / kWave)),
+      (int64_t)a.T * row_chunks * 16 > kCachedRowsBytes);
   return launch_status();
 }
 
