@@ -40,7 +40,7 @@ ASAN_LIB = os.path.join(PKG, "libep_mi355x_asan.so")
 
 SMALL_LAUNCH_UNITS = 4160
 SMALL_LAUNCH_LIB = os.path.join(PKG, "libep_mi355x_small_launch.so")
-SMALL_LAUNCH_SOURCES = ("ep_dispatch.hip", "ep_compact.hip")  # the users of the limit
+SMALL_LAUNCH_SOURCES = ("ep_dispatch.hip", "ep_compact.hip", "ep_combine.hip")  # its users
 
 
 def _compile(src: str, extra=(), tag: str = "") -> str:

@@ -32,6 +32,8 @@
 // are rounded separately (contraction off), in k order, so the result is a
 // pure function of the inputs; the final pack uses the hardware binary32 ->
 // bf16 convert, which rounds to nearest even.
+#include <algorithm>
+
 #include "ep_device.hpp"
 #include "ep_launch.hpp"
 
@@ -141,7 +143,7 @@ template <int DT, int H, int K, bool BIAS, int NT>
 __global__ __launch_bounds__(NT) void ep_combine_gather(
     const u32x4 *__restrict__ y, const float *__restrict__ topk_weights,
     const u32x4 *__restrict__ bias, const int32_t *__restrict__ dst_slot, int T,
-    int64_t capacity, u32x4 *__restrict__ out) {
+    int64_t capacity, u32x4 *__restrict__ out, int t0, int units) {
   constexpr int CH = H * Elem<DT>::BYTES / 16;  // 16-byte chunks per row
   constexpr int PC = Elem<DT>::PER_CHUNK;
   using Geo = CombineGeometry<CH>;
@@ -152,12 +154,8 @@ __global__ __launch_bounds__(NT) void ep_combine_gather(
   const int lane = lane_id();
   const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   constexpr int wpb = NT / kWave;
-  const int64_t first = (int64_t)blockIdx.x * wpb + wave_in_block;
-  const int64_t stride = (int64_t)gridDim.x * wpb;
-
-  for (int64_t gw = first; gw < (int64_t)T * SPLIT; gw += stride) {
-    const int t = (int)(gw / SPLIT);
-    const int c0 = (int)(gw - (int64_t)t * SPLIT) * G;  // first chunk (per lane) of this wave
+  // Token t, slices from chunk c0 (per lane) on.
+  auto unit = [&](const int t, const int c0) {
     int my_dst = -1;
     float my_w = 0.f;
     if (lane < K) {
@@ -205,6 +203,22 @@ __global__ __launch_bounds__(NT) void ep_combine_gather(
         store_row<NT == kDefaultThreads ? RowStore::kDevice : RowStore::kNt>(
             Elem<DT>::put(acc[g]), o, CH * 16, i * 16);
       }
+    }
+  };
+  if constexpr (NT == kDefaultThreads) {
+    // Uncapped: wave w moves unit w of tokens [t0, t0 + units / SPLIT), with
+    // 32-bit indices (the index arithmetic sits on the wave's path to its
+    // first loads).
+    const uint32_t w = blockIdx.x * (uint32_t)wpb + wave_in_block;
+    if (w >= (uint32_t)units) return;
+    const uint32_t tl = w / SPLIT;
+    unit(t0 + (int)tl, (int)(w - tl * SPLIT) * G);
+  } else {  // under a cap the waves loop over every token
+    const int64_t stride = (int64_t)gridDim.x * wpb;
+    for (int64_t gw = (int64_t)blockIdx.x * wpb + wave_in_block; gw < (int64_t)T * SPLIT;
+         gw += stride) {
+      const int t = (int)(gw / SPLIT);
+      unit(t, (int)(gw - (int64_t)t * SPLIT) * G);
     }
   }
 }
@@ -347,16 +361,15 @@ __global__ __launch_bounds__(kDefaultThreads) void ep_combine_stream(
 }
 
 template <int DT, int H, int K, int NT>
-int combine_launch(const CombineArgs &a, const WaveGrid &g) {
+void combine_launch(const CombineArgs &a, const WaveGrid &g, int t0, int units) {
   if (a.bias)
     ep_combine_gather<DT, H, K, true, NT><<<g.blocks, NT, 0, a.stream>>>(
         (const u32x4 *)a.y, a.topk_weights, (const u32x4 *)a.bias, a.dst_slot, a.T, a.capacity,
-        (u32x4 *)a.out);
+        (u32x4 *)a.out, t0, units);
   else
     ep_combine_gather<DT, H, K, false, NT><<<g.blocks, NT, 0, a.stream>>>(
         (const u32x4 *)a.y, a.topk_weights, nullptr, a.dst_slot, a.T, a.capacity,
-        (u32x4 *)a.out);
-  return launch_status();
+        (u32x4 *)a.out, t0, units);
 }
 
 template <int DT, int H, int K>
@@ -381,10 +394,18 @@ int combine_impl(const CombineArgs &a) {
     }
   }
   constexpr int SPLIT = CombineGeometry<H * Elem<DT>::BYTES / 16>::SPLIT;
-  const WaveGrid g = wave_grid((int64_t)a.T * SPLIT, cap, 1 << 24, 1, kCombineCappedThreads);
-  if (g.threads == kCombineCappedThreads)
-    return combine_launch<DT, H, K, kCombineCappedThreads>(a, g);
-  return combine_launch<DT, H, K, kDefaultThreads>(a, g);
+  if (cap > 0) {
+    combine_launch<DT, H, K, kCombineCappedThreads>(
+        a, wave_grid((int64_t)a.T * SPLIT, cap, 1 << 24, 1, kCombineCappedThreads), 0, 0);
+    return launch_status();
+  }
+  // Uncapped: launches of whole tokens, at most kMaxLaunchUnits units each.
+  constexpr int kLaunchTokens = (int)(kMaxLaunchUnits / SPLIT);
+  for (int t0 = 0; t0 < a.T; t0 += std::min(kLaunchTokens, a.T - t0)) {
+    const int units = std::min(kLaunchTokens, a.T - t0) * SPLIT;
+    combine_launch<DT, H, K, kDefaultThreads>(a, wave_grid(units, 0, 1 << 24), t0, units);
+  }
+  return launch_status();
 }
 
 }  // namespace

@@ -1,7 +1,8 @@
 """Inputs split over several launches, on a test build with a small launch limit.
 
 The uncapped one-unit-per-wave kernels (the planned and grouped dispatch, the
-non-expand dispatch and combine) take at most 2^26 - 64 units per launch, so
+sliced combine, the non-expand dispatch and combine) take at most 2^26 - 64
+units per launch, so
 batches past that size run as several launches from a unit offset, or, on
 the non-expand path, as one launch of the looping kernel. No test input is
 that large. libep_mi355x_small_launch.so is the same library built with the
@@ -11,6 +12,7 @@ the CPU oracle as in the other parity tests.
 """
 import os
 
+import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -23,7 +25,8 @@ import oracle  # noqa: E402
 from combine_ep_layout_amd import binding as B  # noqa: E402
 from combine_ep_layout_amd import build as hip_build  # noqa: E402
 from combine_ep_layout_amd import inputs as I  # noqa: E402
-from tests.gpu_util import DeviceCase, layout_to_host  # noqa: E402
+from tests import pins  # noqa: E402
+from tests.gpu_util import DeviceCase, layout_to_host, to_host  # noqa: E402
 from tests.test_gpu_non_expand import _run  # noqa: E402
 from tests.test_gpu_parity import check_dispatch, check_layout  # noqa: E402
 
@@ -80,6 +83,29 @@ def test_grouped_dispatch_over_several_launches():
     dc.dispatch()
     torch.cuda.synchronize()
     check_dispatch(dc, ref["dst_slot"])
+
+
+@pytest.mark.parametrize("T,H,E,K,A,mask,out_dtype", [
+    (1000, 7168, 256, 8, 1, 0.2, I.BF16),    # 7,000 units of 2 KiB slices: 2 launches
+    (1023, 7168, 64, 6, 4, 0.3, I.FP32),     # binary32 rows: 14,322 units, 4 launches
+    (900, 2048, 32, 2, 1, 0.0, I.BF16),      # 1,800 units: one launch
+])
+def test_sliced_combine_over_several_launches(T, H, E, K, A, mask, out_dtype):
+    w = I.custom(f"split_comb{T}_{H}", 7500 + T, T, H, E, K, A, I.BF16, "uniform",
+                 out_dtype=out_dtype, scales=False)
+    _say(f"[sliced combine, launch limit {LIMIT}] {w}")
+    case = I.make_case(w, mask_frac=mask)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case)
+    dc.layout()
+    got = dc.combine()
+    torch.cuda.synchronize()
+    if out_dtype == I.FP32:
+        want = oracle.combine_f32(case.y, ref["dst_slot"], case.topk_weights)
+        assert np.array_equal(to_host(got).view(np.uint32), want.view(np.uint32))
+    else:
+        want = oracle.combine(case.y, ref["dst_slot"], case.topk_weights)
+        assert pins.bf16_ulp_distance(to_host(got, np.uint16), want).max() <= 1
 
 
 @pytest.mark.parametrize("T,H,E,K,dtype,combine_fp32", [
