@@ -46,7 +46,8 @@ constexpr int kRankBits = 10;  // rank inside a tile < 1024
 // Largest T*K laid out by the single-launch multi-tile kernel (every block
 // scans all entries); above it, two launches share per-tile histograms
 // through the workspace. Measured on MI355X (E=256, top-8): one launch wins
-// up to 16K entries (11.4 vs 12.8 us), two launches from 32K (12.3 vs 13.3).
+// up to 16K entries (11.4 vs 12.8 us), two launches from 32K (12.3 vs 13.3;
+// re-measured in the prefill step at 32K entries, 167.4 against 168.8 us).
 constexpr int64_t kFusedMaxEntries = 1 << 14;
 // Longest walk over tiles (loads per thread) the second launch of the
 // many-tile path does itself; beyond it a tile-scan launch runs first.
