@@ -404,8 +404,9 @@ int combine_impl(const CombineArgs &a) {
   for (int t0 = 0; t0 < a.T; t0 += std::min(kLaunchTokens, a.T - t0)) {
     const int units = std::min(kLaunchTokens, a.T - t0) * SPLIT;
     combine_launch<DT, H, K, kDefaultThreads>(a, wave_grid(units, 0, 1 << 24), t0, units);
+    if (int r = launch_status()) return r;  // before the next launch
   }
-  return launch_status();
+  return 0;
 }
 
 }  // namespace

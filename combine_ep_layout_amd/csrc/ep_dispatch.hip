@@ -269,8 +269,9 @@ int dispatch_impl(const DispatchArgs &a) {
         const WaveGrid g = wave_grid(units, 0, 1 << 24, kXcds);
         ep_dispatch_grouped<DT, ROWB, SCB, K, F><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
             x, xs, a.topk_weights, a.dst_slot, cap32, ex, es, ew, g0, units);
+        if (int r = launch_status()) return r;  // before the next launch
       }
-      return launch_status();
+      return 0;
     }
   }
   const int entries = a.T * K;  // at most INT32_MAX (checked by the C ABI)
@@ -287,8 +288,9 @@ int dispatch_impl(const DispatchArgs &a) {
     ep_dispatch_expand<DT, ROWB, SCB, K, true><<<g.blocks, kDefaultThreads, 0, a.stream>>>(
         x, xs, a.topk_weights, a.dst_slot, (const int2 *)a.plan, entries, cap32, ex, es, ew, e0,
         units);
+    if (int r = launch_status()) return r;  // before the next launch
   }
-  return launch_status();
+  return 0;
 }
 
 // Row and scale-row bytes per dtype. hidden counts elements for bf16, fp32

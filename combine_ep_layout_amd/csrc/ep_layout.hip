@@ -990,6 +990,8 @@ int layout_launch(const LayoutArgs &a, int B, unsigned G, int cap) {
   int32_t *tile_recv = tile_counts + (size_t)B * a.E;
   ep_layout_tile_histogram<K, NW, LOOP><<<G + pf0.blocks, kThreads, shm_rank, a.stream>>>(
       a.topk_idx, a.T, a.E, B, a.dst_slot, tile_counts, tile_recv, pf0);
+  // each launch's status is read before the next launch can overwrite it
+  if (int r = launch_status()) return r;
   const size_t shm_assign = sizeof(int) * (size_t)(3 * a.E);
   if (use_tile_scan(B, a.E)) {
     int32_t *tile_base = tile_recv + B;
@@ -1000,6 +1002,7 @@ int layout_launch(const LayoutArgs &a, int B, unsigned G, int cap) {
     if (cap > 0 && gs > (unsigned)cap) gs = (unsigned)cap;
     ep_layout_tile_scan<<<gs, kThreads, 0, a.stream>>>(tile_counts, tile_recv, B, a.E, tile_base,
                                                         expert_total, recv_base, recv_total);
+    if (int r = launch_status()) return r;
     const TileScan scan{tile_base, expert_total, recv_base, recv_total};
     ep_layout_tile_assign<K, NW, LOOP, true><<<G + pf1.blocks, kThreads, shm_assign, a.stream>>>(
         a.T, a.E, a.A, B, tile_counts, tile_recv, scan, a.counts, a.offsets, a.dst_slot, a.meta,
