@@ -47,10 +47,10 @@ divided by the wall-clock step time (K steps bracketed by device
 synchronisation, no events inside; the steps' C calls are marshalled
 beforehand and made directly, as a native caller would make them, so the
 Python binding's per-call work does not set the pace of small steps). Per-kernel times come right after the
-timed loop: each pass is launched --event-steps times back to back (default
-50, at least 20; the C calls marshalled beforehand, so the host keeps ahead
-of even the layout's launches) with the step's buffer rotation between two
-HIP events, and kernel_us is the mean per launch (an event drains the pipeline,
+timed loop: each pass is launched a few times untimed, then --event-steps
+times back to back (default 50, at least 20; the C calls marshalled
+beforehand, so the host keeps ahead of even the layout's launches) with the
+step's buffer rotation between two HIP events, and kernel_us is the mean per launch (an event drains the pipeline,
 about 3 us, so events around each single launch would read several
 microseconds above the kernel's own duration as rocprofv3 reports it). The
 roofline object reports the dominant kernel's algorithmic bytes over that
@@ -72,6 +72,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+N_PRE_LAUNCHES = 5  # untimed launches of a pass before its per-kernel events
+GATE_CYCLES_PER_LAUNCH = 50_000  # GPU spin ahead of the timed launches, per launch queued
 METRIC = "dispatch+combine effective HBM GB/s (% of peak) + tokens/s, 1 MI355X"
 KERNEL_SOURCES = {  # the sources whose kernels each path's traffic counters measured
     "expand": ["combine_ep_layout_amd/csrc/ep_dispatch.hip",
@@ -553,14 +555,26 @@ def main():
         # layout's launches run. The mean per launch is the kernel's average
         # duration.
         n_ev = max(20, args.event_steps)
+        n_pre = min(N_PRE_LAUNCHES, args.steps)
         us = {}
         for name, fn in (("layout", run_layout), ("dispatch", run_dispatch),
                          ("combine", run_combine)):
+            # A few untimed launches of the same pass first, on buffer sets the
+            # timed loop has just used (so a cold pass stays cold).
+            pre = recorded_calls(B, lambda: [fn(args.steps - n_pre + j) for j in range(n_pre)])
             calls = recorded_calls(B, lambda: [fn(args.steps + j) for j in range(n_ev)])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
-            e0.record(stream)
             failed = 0
+            for cfn, cargs in pre:
+                failed |= cfn(*cargs)
+            # Hold the stream with a bounded GPU spin while the host queues
+            # the timed calls, so the launches run back to back whatever the
+            # host's per-call time (a layout call takes about as long on the
+            # host as its two launches on the GPU).
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(GATE_CYCLES_PER_LAUNCH * n_ev)
+            e0.record(stream)
             for cfn, cargs in calls:
                 failed |= cfn(*cargs)
             e1.record(stream)
@@ -815,7 +829,8 @@ def report(args, w, case, ref, runs, modes, copy_gbps, non_expand, plan_used=Fal
         "dispatch_combine_pct_of_copy": round(100 * fig["dispatch_combine_GBps"] / copy_gbps, 2),
         "kernel_us": fig["kernel_us"],
         "kernel_timing": f"HIP events around {main_run['event_steps']} back-to-back launches of "
-                         f"each pass, run right after the timed loop; mean per launch" +
+                         f"each pass after {N_PRE_LAUNCHES} untimed ones, run right after the "
+                         f"timed loop; mean per launch" +
                          ("; the fused call's time (layout included) is dispatch's" if fused
                           else ""),
         "algorithmic_bytes": nb,
