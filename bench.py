@@ -47,10 +47,11 @@ divided by the wall-clock step time (K steps bracketed by device
 synchronisation, no events inside; the steps' C calls are marshalled
 beforehand and made directly, as a native caller would make them, so the
 Python binding's per-call work does not set the pace of small steps). Per-kernel times come right after the
-timed loop: each pass is launched a few times untimed, then --event-steps
-times back to back (default 50, at least 20; the C calls marshalled
-beforehand, so the host keeps ahead of even the layout's launches) with the
-step's buffer rotation between two HIP events, and kernel_us is the mean per launch (an event drains the pipeline,
+timed loop: for each pass, a bounded GPU spin holds the stream while the host
+queues a few untimed launches and then --event-steps launches (default 50,
+at least 20) with the step's buffer rotation, the timed ones between two HIP
+events, so they run back to back whatever the host's per-call time. kernel_us
+is the mean per launch (an event drains the pipeline,
 about 3 us, so events around each single launch would read several
 microseconds above the kernel's own duration as rocprofv3 reports it). The
 roofline object reports the dominant kernel's algorithmic bytes over that
@@ -559,21 +560,21 @@ def main():
         us = {}
         for name, fn in (("layout", run_layout), ("dispatch", run_dispatch),
                          ("combine", run_combine)):
-            # A few untimed launches of the same pass first, on buffer sets the
-            # timed loop has just used (so a cold pass stays cold).
+            # A bounded GPU spin holds the stream while the host queues every
+            # call, so the launches run back to back whatever the host's
+            # per-call time (a layout call takes about as long on the host as
+            # its two launches on the GPU). A few untimed launches of the same
+            # pass follow the spin, on buffer sets the timed loop has just used
+            # (so a cold pass stays cold), before the first event.
             pre = recorded_calls(B, lambda: [fn(args.steps - n_pre + j) for j in range(n_pre)])
             calls = recorded_calls(B, lambda: [fn(args.steps + j) for j in range(n_ev)])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(GATE_CYCLES_PER_LAUNCH * (n_ev + n_pre))
             failed = 0
             for cfn, cargs in pre:
                 failed |= cfn(*cargs)
-            # Hold the stream with a bounded GPU spin while the host queues
-            # the timed calls, so the launches run back to back whatever the
-            # host's per-call time (a layout call takes about as long on the
-            # host as its two launches on the GPU).
-            with torch.cuda.stream(stream):
-                torch.cuda._sleep(GATE_CYCLES_PER_LAUNCH * n_ev)
             e0.record(stream)
             for cfn, cargs in calls:
                 failed |= cfn(*cargs)
