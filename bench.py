@@ -553,14 +553,15 @@ def main():
         # rotation, between two HIP events (an event drains the pipeline, about
         # 3 us each, so events around single launches would read several
         # microseconds above the kernel's own duration); the mean per launch
-        # is the kernel's average duration. Each pass is timed twice and the
-        # lower mean kept, because each way has its own upward bias:
-        # - as the host issues the calls: a layout call takes about as long on
-        #   the host as its two launches on the GPU, so the host can set the pace;
-        # - queued behind a bounded GPU spin (about 1 ms) that holds the stream
-        #   until the host has issued every call: the launches then run back to
-        #   back, but dispatch's write-heavy launches slow down partway through
-        #   such a series (75 to 82 us at prefill in a kernel trace).
+        # is the kernel's average duration. Each pass is timed twice, once as
+        # the host issues the calls and once queued behind a bounded GPU spin
+        # (about 1 ms) that holds the stream until the host has issued them
+        # all, and the lower mean is kept. Both biases only raise a mean: as
+        # issued, the host can set the pace (a layout call takes about as long
+        # on the host as its two launches on the GPU); and in a long series of
+        # dispatch launches alone, the write-heavy launches sometimes slow down
+        # in steps partway through (75 to about 80 us at prefill in kernel
+        # traces, in either series), which the timed steps do not show.
         # A few untimed launches of the same pass precede the first event, on
         # buffer sets the timed loop has just used (so a cold pass stays cold).
         n_ev = max(20, args.event_steps)
