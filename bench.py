@@ -46,19 +46,24 @@ whole-step throughput: algorithmic HBM bytes of the three passes per step
 divided by the wall-clock step time (K steps bracketed by device
 synchronisation, no events inside; the steps' C calls are marshalled
 beforehand and made directly, as a native caller would make them, so the
-Python binding's per-call work does not set the pace of small steps). Per-kernel times come right after the
-timed loop: each pass is launched a few times untimed and then --event-steps
-times (default 50, at least 20) back to back with the step's buffer rotation,
-the timed launches between two HIP events; this is done twice, once as the
-host issues the calls and once queued behind a bounded GPU spin that holds
-the stream until the host has issued them all, and kernel_us is the lower
-of the two means per launch (an event drains the pipeline,
-about 3 us, so events around each single launch would read several
-microseconds above the kernel's own duration as rocprofv3 reports it). The
-roofline object reports the dominant kernel's algorithmic bytes over that
-mean against the MI355X HBM peak (8 TB/s). The CPU baseline times the CPU oracle on the host, on one
-thread and on all host threads (test infrastructure, never on the product
-path).
+Python binding's per-call work does not set the pace of small steps).
+Warm-up: about 25 ms (at most 512 steps) of untimed steps queued back to
+back, then the W warm-up steps, then the timed steps, each after a
+synchronisation. After an idle spell this GPU runs a memory-bound load
+about 10% slower from about 2 ms to about 10 ms into it; a short run that
+started from idle would time that dip, not the path (warmup_steps_run
+counts every untimed step). Per-kernel times come right after the timed
+loop: each pass is launched a few times untimed and
+then --event-steps times (default 50, at least 20) back to back with the
+step's buffer rotation, the timed launches between two HIP events, after
+the same untimed load and queued behind a GPU spin of under 1 ms that holds
+the stream until the host has issued every call; kernel_us is the mean per
+launch (an event drains the pipeline, about 3 us, so events around each
+single launch would read several microseconds above the kernel's own
+duration as rocprofv3 reports it). The roofline object reports the dominant
+kernel's algorithmic bytes over that mean against the MI355X HBM peak
+(8 TB/s). The CPU baseline times the CPU oracle on the host, on one thread
+and on all host threads (test infrastructure, never on the product path).
 """
 import argparse
 import hashlib
@@ -75,7 +80,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 N_PRE_LAUNCHES = 5  # untimed launches of a pass before its per-kernel events
-GATE_CYCLES_PER_LAUNCH = 50_000  # GPU spin ahead of the timed launches, per launch queued
+GATE_CYCLES_PER_LAUNCH = 35_000  # GPU spin ahead of the timed launches, per launch queued
+LOAD_MS = 25.0  # untimed full steps, back to back, before each timed region
+LOAD_CHUNK_STEPS = 8  # steps per chunk of that load (one chunk is timed to size it)
+LOAD_MAX_STEPS = 512  # bound on the steps queued for that load
 METRIC = "dispatch+combine effective HBM GB/s (% of peak) + tokens/s, 1 MI355X"
 KERNEL_SOURCES = {  # the sources whose kernels each path's traffic counters measured
     "expand": ["combine_ep_layout_amd/csrc/ep_dispatch.hip",
@@ -531,19 +539,72 @@ def main():
             run_dispatch(i, stream)
             run_combine(i, stream)
 
+        def issue(calls) -> int:
+            failed = 0
+            for cfn, cargs in calls:
+                failed |= cfn(*cargs)
+            return failed
+
         torch.cuda.synchronize()  # inputs were written on the default stream
-        for i in range(max(args.warmup, nsets, nx)):
-            step(i)
-        # The timed steps make the library's C calls directly, with their arguments
-        # marshalled beforehand: the binding's per-call Python work (about 5 us)
-        # would otherwise set the pace of small steps (a decode step whose
-        # dispatch kernel did nothing took as long as the real one).
+        # Every call is marshalled before any of them runs (the library's C
+        # functions with their arguments, made directly as a native caller
+        # would: the binding's per-call Python work, about 5 us, would
+        # otherwise set the pace of small steps), so no host work leaves the
+        # GPU idle between the warm-up and the timed steps.
+        n_warm = max(args.warmup, nsets, nx)
+        warm_calls = recorded_calls(B, lambda: [step(i) for i in range(n_warm)])
         timed_calls = recorded_calls(B, lambda: [step(i) for i in range(args.steps)])
-        torch.cuda.synchronize()
+        load_calls = recorded_calls(B, lambda: [step(i) for i in range(LOAD_CHUNK_STEPS)])
+
+        def load() -> int:
+            """About LOAD_MS of untimed full steps, queued back to back; returns how many.
+
+            After an idle spell this GPU runs a memory-bound load at full speed
+            for about 2 ms, then about 10% slower for about 8 ms before it
+            settles (dispatch at prefill: 75, then up to 84-90, then 75 us), and
+            a load broken by a synchronisation every few steps does not reach
+            the settled state (20 prefill steps timed after 25 ms of such a load
+            read 177 against 168 us). So a chunk is timed to size the load (the
+            second of two: a process's first steps also pay for first touches
+            of their buffers), and the rest is queued without waiting; the
+            caller's next work follows it in the queue. At most LOAD_MAX_STEPS
+            steps are queued: after a burst of some thousands of short launches
+            (decode steps, whose chunk is mostly host time) the next launches
+            took about 200 us longer in all, and short steps draw too little
+            power for the dip to matter.
+            """
+            for _ in range(2):
+                t0 = time.perf_counter()
+                if issue(load_calls):
+                    raise SystemExit(f"bench: an untimed step failed: {B.ep_last_error()}")
+                torch.cuda.synchronize()
+                chunk_ms = (time.perf_counter() - t0) * 1e3
+            chunks = min(LOAD_MAX_STEPS // LOAD_CHUNK_STEPS,
+                         max(1, int(LOAD_MS / max(chunk_ms, 1e-3))))
+            for _ in range(chunks):
+                if issue(load_calls):
+                    raise SystemExit(f"bench: an untimed step failed: {B.ep_last_error()}")
+            return (chunks + 2) * LOAD_CHUNK_STEPS
+
+        def drain():
+            """torch.cuda.synchronize(), after polling an event recorded behind
+            the queued work, so the host thread stays awake through a long
+            wait: a host-bound step (decode) issued right after a blocking wait
+            of several ms ran slower for a while (20 decode steps: 17.5 against
+            12.8 us each)."""
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            while not ev.query():
+                pass
+            torch.cuda.synchronize()
+
+        n_load = load()
+        drain()
+        if issue(warm_calls):
+            raise SystemExit(f"bench: a warm-up step failed: {B.ep_last_error()}")
+        drain()
         t0 = time.perf_counter()
-        failed = 0
-        for cfn, cargs in timed_calls:  # the timed region: steps only, no events
-            failed |= cfn(*cargs)
+        failed = issue(timed_calls)  # the timed region: steps only, no events
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
         if failed:
@@ -553,17 +614,14 @@ def main():
         # rotation, between two HIP events (an event drains the pipeline, about
         # 3 us each, so events around single launches would read several
         # microseconds above the kernel's own duration); the mean per launch
-        # is the kernel's average duration. Each pass is timed twice, once as
-        # the host issues the calls and once queued behind a bounded GPU spin
-        # (about 1 ms) that holds the stream until the host has issued them
-        # all, and the lower mean is kept. Both biases only raise a mean: as
-        # issued, the host can set the pace (a layout call takes about as long
-        # on the host as its two launches on the GPU); and in a long series of
-        # dispatch launches alone, the write-heavy launches sometimes slow down
-        # in steps partway through (75 to about 80 us at prefill in kernel
-        # traces, in either series), which the timed steps do not show.
-        # A few untimed launches of the same pass precede the first event, on
-        # buffer sets the timed loop has just used (so a cold pass stays cold).
+        # is the kernel's average duration. Before each series the GPU is
+        # loaded with full steps (load(): no post-idle dip inside the series),
+        # then a bounded GPU spin (under 1 ms) holds the stream while the host
+        # issues every call, so the launches run back to back even where a
+        # call takes as long on the host as its launches on the GPU (the
+        # layout's, decode's). A few untimed launches of the same pass precede
+        # the first event, on buffer sets the timed loop has just used (so a
+        # cold pass stays cold).
         n_ev = max(20, args.event_steps)
         n_pre = min(N_PRE_LAUNCHES, args.steps)
         us = {}
@@ -571,24 +629,18 @@ def main():
                          ("combine", run_combine)):
             pre = recorded_calls(B, lambda: [fn(args.steps - n_pre + j) for j in range(n_pre)])
             calls = recorded_calls(B, lambda: [fn(args.steps + j) for j in range(n_ev)])
-            for gated in (False, True):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                if gated:
-                    with torch.cuda.stream(stream):
-                        torch.cuda._sleep(GATE_CYCLES_PER_LAUNCH * (n_ev + n_pre))
-                failed = 0
-                for cfn, cargs in pre:
-                    failed |= cfn(*cargs)
-                e0.record(stream)
-                for cfn, cargs in calls:
-                    failed |= cfn(*cargs)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                if failed:
-                    raise SystemExit(f"bench: {name} failed: {B.ep_last_error()}")
-                t = e0.elapsed_time(e1) * 1e3 / n_ev
-                us[name] = min(us.get(name, t), t)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            load()
+            with torch.cuda.stream(stream):
+                torch.cuda._sleep(GATE_CYCLES_PER_LAUNCH * (n_ev + n_pre))
+            failed = issue(pre)
+            e0.record(stream)
+            failed |= issue(calls)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if failed:
+                raise SystemExit(f"bench: {name} failed: {B.ep_last_error()}")
+            us[name] = e0.elapsed_time(e1) * 1e3 / n_ev
         if fused:  # layout ran inside the dispatch launch
             us = {"layout": 0.0, "dispatch": us["layout"], "combine": us["combine"]}
         launch = "eager"
@@ -600,7 +652,8 @@ def main():
             for _ in range(3):
                 g.replay()
             reps = max(1, args.steps // args.graph)
-            torch.cuda.synchronize()
+            load()
+            drain()
             t0 = time.perf_counter()
             for _ in range(reps):
                 g.replay()
@@ -634,7 +687,8 @@ def main():
         del sets, x_sets, last
         torch.cuda.empty_cache()
         return {"ms_per_step": ms_per_step, "us": us, "event_steps": n_ev,
-                "launch": launch, "overlap": overlap, "cache": cache}
+                "launch": launch, "overlap": overlap, "cache": cache,
+                "warmup_steps_run": n_load + n_warm}
 
     modes = ["cold"] if args.cold or args.cache == "cold" else \
         ["warm"] if args.cache == "warm" else ["warm", "cold"]
@@ -835,10 +889,15 @@ def report(args, w, case, ref, runs, modes, copy_gbps, non_expand, plan_used=Fal
         "copy_reference_GBps": round(copy_gbps, 1),
         "dispatch_combine_pct_of_copy": round(100 * fig["dispatch_combine_GBps"] / copy_gbps, 2),
         "kernel_us": fig["kernel_us"],
+        "warmup_steps_run": main_run["warmup_steps_run"],
+        "warmup_detail": f"about {LOAD_MS:.0f} ms (at most {LOAD_MAX_STEPS} steps) of untimed "
+                         f"steps queued back to back, then the {args.warmup} warm-up steps (more "
+                         f"where cold mode rotates more buffer sets or x copies), then the timed "
+                         f"steps, each after a synchronisation",
         "kernel_timing": f"HIP events around {main_run['event_steps']} back-to-back launches of "
                          f"each pass after {N_PRE_LAUNCHES} untimed ones, run right after the "
-                         f"timed loop, once as issued and once queued behind a GPU spin; "
-                         f"the lower mean per launch" +
+                         f"timed loop, each series queued after about {LOAD_MS:.0f} ms of untimed "
+                         f"steps and a GPU spin of under 1 ms; mean per launch" +
                          ("; the fused call's time (layout included) is dispatch's" if fused
                           else ""),
         "algorithmic_bytes": nb,
@@ -848,7 +907,8 @@ def report(args, w, case, ref, runs, modes, copy_gbps, non_expand, plan_used=Fal
     for m in modes[1:]:
         sub = mode_figures(w, nb, runs[m], non_expand, w.name)
         sub["roofline"]["traffic"] = None  # counters are taken on the warm loop only
-        result[m] = {**sub, "cache": runs[m]["cache"]}
+        result[m] = {**sub, "cache": runs[m]["cache"],
+                     "warmup_steps_run": runs[m]["warmup_steps_run"]}
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(case, path=args.path)
