@@ -124,7 +124,7 @@ def algorithmic_bytes(w, n_valid: int, n_recv: int, path: str = "expand") -> dic
     L = w.T * w.K * 4 + 4 * w.E + 4 * (w.E + 1) + w.T * w.K * 4 + n_recv * (w.K + 2) * 4 + 4
     if path == "non-expand":
         D = 2 * n_recv * row_in + n_recv * (4 + 5 * 4 * w.K) + 4
-        C = n_recv * (H_out * 2 + 4) + w.T * (H_out * 2 + 4 * w.K) + 4
+        C = n_recv * (H_out * elt_out + 4) + w.T * (H_out * elt_out + 4 * w.K) + 4
         return {"layout": L, "dispatch": D, "combine": C}
     D = w.T * row_in + n_valid * row_in + w.T * w.K * 4
     C = n_valid * H_out * elt_out + w.T * H_out * elt_out + w.T * w.K * 8
@@ -277,6 +277,7 @@ def cpu_baseline(case, budget_s: float = 8.0, max_reps: int = 100_000, path: str
 
     if path == "non-expand":
         y = case.extra["y_ne"]
+        combine_rows = oracle.combine_compact_f32 if w.out_dtype == 1 else oracle.combine_compact
 
         def one_step(parts):
             lay = oracle.layout(case.topk_idx, w.E, w.A)
@@ -290,7 +291,7 @@ def cpu_baseline(case, budget_s: float = 8.0, max_reps: int = 100_000, path: str
                 i0, i1 = np.searchsorted(meta[:, 0], [a, b])
                 m = meta[i0:i1].copy()
                 m[:, 0] -= a
-                oracle.combine_compact(y[i0:i1], lay["dst_slot"][a:b], m, i1 - i0)
+                combine_rows(y[i0:i1], lay["dst_slot"][a:b], m, i1 - i0)
 
             split(disp, parts)
             split(comb, parts)
@@ -428,10 +429,9 @@ def main():
 
     _, scale_cols, H_out, _ = geometry(w)
     if non_expand:
-        if w.out_dtype != 0:
-            raise SystemExit("the non-expand combine moves bf16 rows only")
-        # the expert side's reduced output: one bf16 row per received token
-        case.extra["y_ne"] = I.normal_bf16(w.seed, I.STREAM_Y, w.T, H_out)
+        # the expert side's reduced output: one row per received token, of combine's type
+        case.extra["y_ne"] = (I.normal_bf16(w.seed, I.STREAM_Y, w.T, H_out) if w.out_dtype == 0
+                              else I.normal_f32(w.seed, I.STREAM_Y, w.T, H_out))
         case.y = case.extra["y_ne"]
     idx, wts = up(case.topk_idx), up(case.topk_weights)
     rowb = case.x.view(np.uint8).reshape(w.T, -1).shape[1]
@@ -528,8 +528,8 @@ def main():
         def run_combine(i, stream=stream):
             S = sets[i % nsets]
             if non_expand:
-                B.ep_combine_compact(S["y"], None, dst, meta, nrecv, w.T, H_out, w.K, 0, S["out"],
-                                     stream)
+                B.ep_combine_compact(S["y"], None, dst, meta, nrecv, w.T, H_out, w.K, w.out_dtype,
+                                     S["out"], stream)
             else:
                 B.ep_combine(S["y"], wts, None, dst, w.T, H_out, w.K, w.out_dtype, w.cap, S["out"],
                              stream)
@@ -802,6 +802,10 @@ def validate_non_expand(oracle, case, ref, recv_x, recv_i, recv_w, out, sample) 
     ok = np.array_equal(recv_x.cpu().numpy()[:n], rx)
     ok = ok and np.array_equal(recv_i.cpu().numpy()[:n], ri)
     ok = ok and np.array_equal(recv_w.cpu().numpy()[:n].view(np.uint32), rw.view(np.uint32))
+    if w.out_dtype == 1:
+        want = oracle.combine_compact_f32(case.y, ref["dst_slot"], ref["recv_src_metadata"], n)
+        return ok and np.array_equal(out.cpu().numpy().view(np.uint32)[sample],
+                                     want.view(np.uint32)[sample])
     want = oracle.combine_compact(case.y, ref["dst_slot"], ref["recv_src_metadata"], n)
     return ok and np.array_equal(out.cpu().numpy().view(np.uint16)[sample], want[sample])
 
