@@ -66,14 +66,17 @@ WORKLOADS = {
 
 
 # The same prefill shape with the other transport / reduction types: fp4x2 rows
-# (3584 bytes = 7168 e2m1 values, 56 scales per token) and binary32 expert
-# outputs for combine; and a long prefill batch of 32768 tokens, whose x
-# (470 MB) is larger than the 256 MB last-level cache.
+# (3584 bytes = 7168 e2m1 values, 56 scales per token), binary32 expert
+# outputs for combine, and binary32 throughout (rows and expert outputs); and
+# a long prefill batch of 32768 tokens, whose x (470 MB) is larger than the
+# 256 MB last-level cache.
 EXTRA_WORKLOADS = {
     "prefill_fp4x2": Workload("prefill_fp4x2", 6, 4096, 3584, 256, 8, 128, FP4X2, "uniform"),
     "prefill_fp32_combine": Workload("prefill_fp32_combine", 7, 4096, 7168, 256, 8, 128, BF16,
                                      "uniform", out_dtype=FP32),
     "prefill_32k": Workload("prefill_32k", 8, 32768, 7168, 256, 8, 128, BF16, "uniform"),
+    "prefill_fp32": Workload("prefill_fp32", 9, 4096, 7168, 256, 8, 128, FP32, "uniform",
+                             out_dtype=FP32),
 }
 
 
