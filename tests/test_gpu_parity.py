@@ -84,6 +84,36 @@ def test_workload_full_size(name):
     check_combine(to_host(out, np.uint16), ref_out, name)
 
 
+@pytest.mark.parametrize("name", ["prefill_fp4x2", "prefill_fp32_combine", "prefill_fp32"])
+def test_dtype_variant_full_size(name):
+    """The prefill shape with the other row types, at full size and in the launch
+    configuration the benchmark times (layout with the dispatch plan, the plan
+    walked): fp4x2 rows with scale rows, bf16 rows with fp32 combine rows, and
+    fp32 throughout. Layout and dispatch bit-exact; combine 1 ulp (bf16 rows)
+    or bit-exact (fp32 rows)."""
+    w = I.EXTRA_WORKLOADS[name]
+    _say(f"[workload {name}] T={w.T} H={w.H} E={w.E} K={w.K} A={w.A} dtype={w.dtype} "
+         f"out_dtype={w.out_dtype} cap={w.cap}")
+    case = I.make_case(w)
+    ref = oracle.layout(case.topk_idx, w.E, w.A)
+    dc = DeviceCase(case)
+    dc.layout(plan=True)
+    dc.dispatch(plan=True)
+    out = dc.combine()
+    torch.cuda.synchronize()
+    check_layout(layout_to_host(dc.lay), ref)
+    check_dispatch(dc, ref["dst_slot"])
+    if w.out_dtype == I.FP32:
+        want = oracle.combine_f32(case.y, ref["dst_slot"], case.topk_weights)
+        assert np.array_equal(to_host(out, np.float32).view(np.uint32), want.view(np.uint32)), \
+            "fp32 combine not bit-exact"
+    else:
+        check_combine(to_host(out, np.uint16), oracle.combine(case.y, ref["dst_slot"],
+                                                              case.topk_weights), name)
+    del dc, out
+    torch.cuda.empty_cache()
+
+
 RAGGED = [
     # T, H, E, K, A, mask, dtype, routing
     (1000, 256, 16, 2, 1, 0.0, I.BF16, "uniform"),
