@@ -24,6 +24,7 @@ from combine_ep_layout_amd import binding as B  # noqa: E402
 from combine_ep_layout_amd import inputs as I  # noqa: E402
 from tests import pins  # noqa: E402
 from tests.gpu_util import DeviceCase, dev_layout, layout_to_host, to_dev, to_host  # noqa: E402
+import bench  # noqa: E402  (the launch configuration it times)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -67,15 +68,27 @@ def check_combine(got_bits, ref_bits, label=""):
     assert d.size == 0 or d.max() <= 1, f"combine beyond 1 bf16 ulp: {int((d > 1).sum())} elements"
 
 
+@pytest.mark.parametrize("config", ["bench", "separate"])
 @pytest.mark.parametrize("name", list(I.WORKLOADS))
-def test_workload_full_size(name):
+def test_workload_full_size(name, config):
+    """Every workload at full size, in the launch configuration the benchmark times
+    ("bench": ep_layout_dispatch for a batch of one layout tile, else the layout with
+    the dispatch plan and the planned dispatch) and as separate plain calls."""
     w = I.WORKLOADS[name]
-    _say(f"[workload {name}] T={w.T} H={w.H} E={w.E} K={w.K} A={w.A} dtype={w.dtype} cap={w.cap}")
+    fused = bench.one_layout_tile(w.T, w.K, w.E)
+    _say(f"[workload {name}, {config}{' (one call)' if config == 'bench' and fused else ''}] "
+         f"T={w.T} H={w.H} E={w.E} K={w.K} A={w.A} dtype={w.dtype} cap={w.cap}")
     case = I.make_case(w)
     ref = oracle.layout(case.topk_idx, w.E, w.A)
     dc = DeviceCase(case)
-    dc.layout()
-    dc.dispatch()
+    if config == "bench" and fused:
+        dc.layout_dispatch()
+    elif config == "bench":
+        dc.layout(plan=True)
+        dc.dispatch(plan=True)
+    else:
+        dc.layout()
+        dc.dispatch()
     out = dc.combine()
     torch.cuda.synchronize()
     check_layout(layout_to_host(dc.lay), ref)
