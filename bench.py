@@ -169,10 +169,12 @@ def one_layout_tile(T: int, K: int, E: int) -> bool:
 
 
 CALIBRATION_BYTES = 1 << 30  # fp32 elementwise negate: reads and writes this many bytes
-# Kernel-name fragments per pass: each pass launches one of its kernels, chosen by shape and cap.
-KERNEL_TAGS = {"dispatch": ("ep_dispatch_expand", "ep_dispatch_grouped", "ep_dispatch_fanout"),
+# Kernel-name fragments per pass: each pass launches one of its kernels, chosen by shape and cap
+# (a one-tile batch's layout + dispatch kernel counts as dispatch, as its time does).
+KERNEL_TAGS = {"dispatch": ("ep_dispatch_expand", "ep_dispatch_grouped", "ep_dispatch_fanout",
+                            "ep_layout_dispatch_tile"),
                "combine": ("ep_combine_stream", "ep_combine_gather"),
-               "dispatch_compact": ("ep_dispatch_compact_rows",),
+               "dispatch_compact": ("ep_dispatch_compact_rows", "ep_layout_dispatch_compact_tile"),
                "combine_compact": ("ep_combine_compact_rows",),
                "layout_histogram": ("ep_layout_tile_histogram",),
                "layout_assign": ("ep_layout_tile_assign",)}

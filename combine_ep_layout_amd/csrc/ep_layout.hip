@@ -342,6 +342,19 @@ __device__ __forceinline__ void copy_unit(const u32x4 &v, int64_t t, int j, int 
   }
 }
 
+// Rank of copy workgroup g among the n workgroups first .. first+n-1 of a
+// launch once they are grouped by XCD: the dispatcher deals workgroups to the
+// 8 XCDs in turn, so workgroups whose offsets from `first` agree modulo 8 share
+// an XCD and its L2, and each such group gets a contiguous range of ranks (a
+// bijection onto [0, n) for any n). Consecutive copy units then run on one XCD,
+// so the K entries of a token read its x slices through one L2 instead of up
+// to K of them.
+constexpr int kXcdCount = 8;
+__device__ __forceinline__ int xcd_rank(int g, int first, int n) {
+  const int b = g - first, y = b % kXcdCount, q = n / kXcdCount, r = n % kXcdCount;
+  return y * q + (y < r ? y : r) + b / kXcdCount;
+}
+
 // The copy workgroups of the fused launch when expert_alignment is 1
 // (COUNTED): no ranking at all. Without alignment padding an entry's slot is
 // the number of unmasked entries whose key (expert id, entry index) is
@@ -371,8 +384,9 @@ __device__ __forceinline__ void copy_counted(
   // the slice count: the index arithmetic sits on each wave's path to its
   // first load.
   const int units = n * slices;
-  const int stride = (int)(gridDim.x - 1) * kWavesMax;
-  const int u0 = (int)(blockIdx.x - 1) * kWavesMax + wave;
+  const int ncopy = (int)gridDim.x - 1;
+  const int stride = ncopy * kWavesMax;
+  const int u0 = xcd_rank((int)blockIdx.x, 1, ncopy) * kWavesMax + wave;
   auto load = [&](int u) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (u < units) {
@@ -478,7 +492,8 @@ __global__ __launch_bounds__(kThreads) void ep_layout_dispatch_tile(
   const int slices = (row_chunks + kWave - 1) / kWave;
   const int units = T * K * slices;  // one tile: below 2^20
   const int stride = (int)gridDim.x * kWavesMax;
-  for (int u = (int)blockIdx.x * kWavesMax + wave; u < units; u += stride) {
+  const int u0 = xcd_rank((int)blockIdx.x, 0, (int)gridDim.x) * kWavesMax + wave;
+  for (int u = u0; u < units; u += stride) {
     const int j = (int)fast_div_apply((uint32_t)u, by_slices);  // entry t*K + k
     const int slice = u - j * slices;
     const int d = __builtin_amdgcn_readfirstlane(s_slot[j]);
